@@ -1,0 +1,158 @@
+"""fp64 CPU oracle for the selective state-space scan -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding in ``selective_state_space_19_amd``) never imports it, and
+it never imports the product.
+
+The arithmetic lives in ``mssm_oracle.c`` (a plain sequential recurrence in
+fp64, one thread per block of independent channels); this module only
+converts arrays to contiguous float64 and calls it.  See the C file's header
+for what is computed and which passages of the pages it follows:
+
+* S6 selective scan -- Mamba "Architecture Details" page, "Selective State
+  Space Mechanism / How S6 Works" (update and output), SSM optimisation
+  catalogue section 7 (A_bar = exp(delta*A)) and section 6 (skip term D x),
+  gated by silu(z).
+* Decode step -- the same update for one token, state updated in place
+  ("Hardware-Aware Implementation / Parallel Algorithm", sequential mode).
+* Mamba-2 SSD -- catalogue section 2 "State Space Duality": the recurrence on
+  (head, head channel) with a scalar A per head.
+
+Every function here is pinned by ``tests/test_oracle_pins.py`` against closed
+forms, brute force, invariants and hand-worked values (``tests/golden``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mssm_oracle.c")
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+_lib = None
+
+
+def build(force: bool = True, out: str = LIB_PATH, defines: tuple = ()) -> str:
+    """Compile the oracle with gcc (no fast-math, no FMA contraction)."""
+    if not force and os.path.exists(out):
+        return out
+    cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
+           "-shared", "-pthread", "-o", out, _SRC, "-lm"]
+    cmd[1:1] = [f"-D{d}" for d in defines]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+def _bind(lib):
+    d = ctypes.POINTER(ctypes.c_double)
+    L = ctypes.c_long
+    lib.oracle_s6_scan.argtypes = [d] * 10 + [L] * 4 + [ctypes.c_int]
+    lib.oracle_s6_scan.restype = ctypes.c_int
+    lib.oracle_state_update.argtypes = [d] * 9 + [L] * 3 + [ctypes.c_int]
+    lib.oracle_state_update.restype = ctypes.c_int
+    lib.oracle_ssd.argtypes = [d] * 10 + [L] * 6 + [ctypes.c_int]
+    lib.oracle_ssd.restype = ctypes.c_int
+    return lib
+
+
+def load(path: str | None = None):
+    """Load the compiled oracle (building it if it is not there yet)."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        _lib = _bind(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def _f64(a):
+    if a is None:
+        return None
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a):
+    if a is None:
+        return ctypes.POINTER(ctypes.c_double)()
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def s6_scan(u, delta, A, B, C, D=None, z=None, h0=None, nthreads=None, lib=None):
+    """Selective scan.  u, delta, z: [b, d, L]; A: [d, N]; B, C: [b, N, L];
+    D: [d]; h0: [b, d, N].  Returns (y [b, d, L], h_final [b, d, N]) in fp64."""
+    u, delta, A, B, C = map(_f64, (u, delta, A, B, C))
+    D, z, h0 = _f64(D), _f64(z), _f64(h0)
+    bsz, dim, L = u.shape
+    N = A.shape[1]
+    assert delta.shape == u.shape and A.shape == (dim, N)
+    assert B.shape == (bsz, N, L) and C.shape == (bsz, N, L)
+    assert D is None or D.shape == (dim,)
+    assert z is None or z.shape == u.shape
+    assert h0 is None or h0.shape == (bsz, dim, N)
+    y = np.empty((bsz, dim, L), np.float64)
+    hT = np.empty((bsz, dim, N), np.float64)
+    lib = lib or load()
+    rc = lib.oracle_s6_scan(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                            _ptr(z), _ptr(h0), _ptr(y), _ptr(hT), bsz, dim, L, N,
+                            nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError("oracle_s6_scan failed")
+    return y, hT
+
+
+def state_update(state, u, delta, A, B, C, D=None, z=None, nthreads=None, lib=None):
+    """One decode step.  state: [b, d, N] (not modified; the updated state is
+    returned); u, delta, z: [b, d]; A: [d, N]; B, C: [b, N]; D: [d].
+    Returns (y [b, d], new_state [b, d, N]) in fp64."""
+    st = np.array(state, dtype=np.float64, order="C", copy=True)
+    u, delta, A, B, C = map(_f64, (u, delta, A, B, C))
+    D, z = _f64(D), _f64(z)
+    bsz, dim, N = st.shape
+    assert u.shape == (bsz, dim) and delta.shape == (bsz, dim)
+    assert A.shape == (dim, N) and B.shape == (bsz, N) and C.shape == (bsz, N)
+    y = np.empty((bsz, dim), np.float64)
+    lib = lib or load()
+    rc = lib.oracle_state_update(_ptr(st), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                                 _ptr(D), _ptr(z), _ptr(y), bsz, dim, N,
+                                 nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError("oracle_state_update failed")
+    return y, st
+
+
+def ssd(x, dt, A, B, C, D=None, z=None, h0=None, nthreads=None, lib=None):
+    """Mamba-2 SSD as the recurrence on heads.  x, z: [b, L, H, P];
+    dt: [b, L, H]; A: [H]; B, C: [b, L, G, N]; D: [H]; h0: [b, H, P, N].
+    Returns (y [b, L, H, P], h_final [b, H, P, N]) in fp64."""
+    x, dt, A, B, C = map(_f64, (x, dt, A, B, C))
+    D, z, h0 = _f64(D), _f64(z), _f64(h0)
+    bsz, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    assert dt.shape == (bsz, L, H) and A.shape == (H,)
+    assert B.shape == (bsz, L, G, N) and C.shape == B.shape and H % G == 0
+    assert D is None or D.shape == (H,)
+    assert z is None or z.shape == x.shape
+    assert h0 is None or h0.shape == (bsz, H, P, N)
+    y = np.empty(x.shape, np.float64)
+    hT = np.empty((bsz, H, P, N), np.float64)
+    lib = lib or load()
+    rc = lib.oracle_ssd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                        _ptr(h0), _ptr(y), _ptr(hT), bsz, L, H, P, N, G,
+                        nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError("oracle_ssd failed")
+    return y, hT

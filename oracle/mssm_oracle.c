@@ -1,0 +1,268 @@
+/*
+ * mssm_oracle.c -- TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT PATH.
+ *
+ * A plain, slow, sequential fp64 CPU reference for the selective state-space
+ * scan.  Only the test suite, the smoke check and the benchmark's CPU-baseline
+ * leg may load this library.  It shares no code, header or constant with the
+ * GPU library (selective_state_space_19_amd/csrc).
+ *
+ * What it computes (one "channel" = one independent recurrence over time):
+ *
+ *   Mamba "Architecture Details" page, section "Selective State Space
+ *   Mechanism / How S6 Works": the selective update
+ *       h(t) = discretize(A, delta(t)) * h(t-1) + delta(t) * B(t) * x(t)
+ *       y(t) = C(t) * h(t)
+ *   with the state starting at zero ("Hardware-Aware Implementation /
+ *   Parallel Algorithm", sequential mode: h = 0, then h = A*h + B*x_t,
+ *   y_t = C*h -- the output reads the state AFTER the update).
+ *
+ *   SSM optimisation-pattern catalogue, section 7 "Selective Attention
+ *   Mechanism / Mathematical Formulation": the discretised transition is
+ *   A_bar = exp(delta * A); A is diagonal, so this is one scalar exp per
+ *   (channel, state index).
+ *
+ *   Same catalogue, section 6 "Tensor Core Optimization / SSM-Specific
+ *   Patterns": the output carries a skip term, y = C h + D x.
+ *
+ *   The gate: y is multiplied by silu(z) = z * sigmoid(z) = z / (1 + exp(-z))
+ *   (section 3 "Kernel Fusion" lists gating fused with the state update; the
+ *   formula is the standard SiLU).
+ *
+ *   Reading adopted where the pages differ: the input term is the Euler form
+ *   delta*B*x of the architecture page (the catalogue's section 7 prints the
+ *   zero-order-hold form (A_bar - I) A^-1 B instead).
+ *
+ * Per channel, in this order, for t = 0 .. L-1:
+ *       d = delta[t]; x = u[t]; acc = 0
+ *       for n: h[n] = exp(d*A[n]) * h[n] + (d*x) * B[n,t];  acc += C[n,t]*h[n]
+ *       o = acc + Dskip*x;  if gated: o *= z[t] / (1 + exp(-z[t]))
+ *       y[t] = o
+ *   and h is the final state afterwards.
+ *
+ * Mamba-2 SSD (catalogue section 2 "State Space Duality"): the SSM with a
+ * scalar transition per head is the same recurrence, run per (head, head
+ * channel p), with A[n] = A_h for every n, delta = dt[b,t,h], B and C taken
+ * from the head's group.  The chunked/quadratic SSD algorithm reaches exactly
+ * this result (the duality), so the oracle for SSD is this recurrence.
+ *
+ * Threads split the independent channels only; time is never split.
+ * Build: gcc -O2 -ffp-contract=off -fPIC -shared -pthread (no -ffast-math).
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+/* Strided view of one channel's operands (strides in elements). */
+typedef struct {
+    const double *u, *z;        /* input, gate: element t at [t * s_x] */
+    long s_x;
+    const double *dl;           /* step: element t at [t * s_d] */
+    long s_d;
+    const double *Bm, *Cm;      /* B[n,t] at Bm[n * s_bn + t * s_bt] */
+    long s_bn, s_bt;
+    const double *A;            /* A[n] at A[n * s_a] (s_a = 0: scalar A) */
+    long s_a;
+    double dskip;
+    double *y;                  /* y[t] at y[t * s_x] */
+    const double *h0;           /* h0[n] at h0[n * s_h], may be NULL */
+    double *hT;                 /* final state, h[n] at hT[n * s_h], may be NULL */
+    long s_h;
+} chan_t;
+
+/* The recurrence for one channel, exactly as written in the header. */
+static void run_channel(const chan_t *c, long L, long N, double *h)
+{
+    for (long n = 0; n < N; ++n) h[n] = c->h0 ? c->h0[n * c->s_h] : 0.0;
+    for (long t = 0; t < L; ++t) {
+        const double d = c->dl[t * c->s_d];
+        const double x = c->u[t * c->s_x];
+        double acc = 0.0;
+        for (long n = 0; n < N; ++n) {
+            const double dA = exp(d * c->A[n * c->s_a]);
+            const double dBu = (d * x) * c->Bm[n * c->s_bn + t * c->s_bt];
+            h[n] = dA * h[n] + dBu;
+            acc += c->Cm[n * c->s_bn + t * c->s_bt] * h[n];
+        }
+        double o = acc + c->dskip * x;
+        if (c->z) {
+            const double g = c->z[t * c->s_x];
+            o *= g / (1.0 + exp(-g));
+        }
+        c->y[t * c->s_x] = o;
+    }
+    if (c->hT)
+        for (long n = 0; n < N; ++n) c->hT[n * c->s_h] = h[n];
+}
+
+/* ---------------------------------------------------------------------------
+ * Problem descriptions and the channel -> view mapping of each layout.
+ * ------------------------------------------------------------------------- */
+enum { KIND_S6 = 0, KIND_SSD = 1 };
+
+typedef struct {
+    int kind;
+    /* S6:  u, delta, z, y [B, D, L]; B, C [B, N, L]; A [D, N]; Dskip [D];
+     *      h0, hT [B, D, N].
+     * SSD: x, z, y [B, L, H, P]; dt [B, L, H]; B, C [B, L, G, N]; A [H];
+     *      Dskip [H]; h0, hT [B, H, P, N]. */
+    const double *u, *dl, *A, *Bm, *Cm, *Dskip, *z, *h0;
+    double *y, *hT;
+    long batch, L, N;
+    long D;              /* S6: d_inner */
+    long H, P, G;        /* SSD: heads, head dim, groups */
+    long nchan;
+} prob_t;
+
+static void make_view(const prob_t *p, long ch, chan_t *c)
+{
+    if (p->kind == KIND_S6) {
+        const long b = ch / p->D, d = ch % p->D;
+        const long row = (b * p->D + d) * p->L;
+        c->u = p->u + row;
+        c->dl = p->dl + row;
+        c->s_d = 1;
+        c->z = p->z ? p->z + row : NULL;
+        c->y = p->y + row;
+        c->s_x = 1;
+        c->Bm = p->Bm + b * p->N * p->L;
+        c->Cm = p->Cm + b * p->N * p->L;
+        c->s_bn = p->L;
+        c->s_bt = 1;
+        c->A = p->A + d * p->N;
+        c->s_a = 1;
+        c->dskip = p->Dskip ? p->Dskip[d] : 0.0;
+        c->h0 = p->h0 ? p->h0 + (b * p->D + d) * p->N : NULL;
+        c->hT = p->hT ? p->hT + (b * p->D + d) * p->N : NULL;
+        c->s_h = 1;
+    } else {
+        /* channel = (b, h, p); head h reads group g = h / (H / G). */
+        const long per_b = p->H * p->P;
+        const long b = ch / per_b, hp = ch % per_b;
+        const long h = hp / p->P, q = hp % p->P;
+        const long g = h / (p->H / p->G);
+        const long xoff = (b * p->L * p->H + h) * p->P + q;   /* t = 0 */
+        c->u = p->u + xoff;
+        c->z = p->z ? p->z + xoff : NULL;
+        c->y = p->y + xoff;
+        c->s_x = p->H * p->P;
+        c->dl = p->dl + b * p->L * p->H + h;                  /* dt[b, t, h] */
+        c->s_d = p->H;
+        c->Bm = p->Bm + (b * p->L * p->G + g) * p->N;
+        c->Cm = p->Cm + (b * p->L * p->G + g) * p->N;
+        c->s_bn = 1;
+        c->s_bt = p->G * p->N;
+        c->A = p->A + h;
+        c->s_a = 0;
+        c->dskip = p->Dskip ? p->Dskip[h] : 0.0;
+        c->h0 = p->h0 ? p->h0 + ((b * p->H + h) * p->P + q) * p->N : NULL;
+        c->hT = p->hT ? p->hT + ((b * p->H + h) * p->P + q) * p->N : NULL;
+        c->s_h = 1;
+    }
+}
+
+typedef struct {
+    const prob_t *p;
+    long lo, hi;
+    int err;
+} work_t;
+
+static void *worker(void *arg)
+{
+    work_t *w = (work_t *)arg;
+    double *h = (double *)malloc(sizeof(double) * (size_t)w->p->N);
+    if (!h) {
+        w->err = 1;
+        return NULL;
+    }
+    for (long ch = w->lo; ch < w->hi; ++ch) {
+        chan_t c;
+        make_view(w->p, ch, &c);
+        run_channel(&c, w->p->L, w->p->N, h);
+    }
+    free(h);
+    return NULL;
+}
+
+#define MAX_THREADS 256
+
+static int run(const prob_t *p, int nthreads)
+{
+    if (p->nchan <= 0) return 0;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > MAX_THREADS) nthreads = MAX_THREADS;
+    if ((long)nthreads > p->nchan) nthreads = (int)p->nchan;
+    pthread_t th[MAX_THREADS];
+    work_t w[MAX_THREADS];
+    int started[MAX_THREADS];
+    const long per = (p->nchan + nthreads - 1) / nthreads;
+    int err = 0;
+    for (int i = 0; i < nthreads; ++i) {
+        w[i].p = p;
+        w[i].lo = i * per < p->nchan ? i * per : p->nchan;
+        w[i].hi = (i + 1) * per < p->nchan ? (i + 1) * per : p->nchan;
+        w[i].err = 0;
+        started[i] = w[i].lo < w[i].hi && pthread_create(&th[i], NULL, worker, &w[i]) == 0;
+        if (!started[i] && w[i].lo < w[i].hi) worker(&w[i]);   /* run inline */
+    }
+    for (int i = 0; i < nthreads; ++i) {
+        if (started[i]) pthread_join(th[i], NULL);
+        err |= w[i].err;
+    }
+    return err ? -1 : 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Exported entry points.  All arrays are contiguous fp64 in the layouts above.
+ * Nullable: Dskip (=> 0), z (=> no gate), h0 (=> zeros), hT (=> not written).
+ * Return 0 on success, -1 on bad arguments or allocation failure.
+ * ------------------------------------------------------------------------- */
+int oracle_s6_scan(const double *u, const double *delta, const double *A,
+                   const double *Bm, const double *Cm, const double *Dskip,
+                   const double *z, const double *h0, double *y, double *hT,
+                   long batch, long d_inner, long seqlen, long d_state,
+                   int nthreads)
+{
+    if (!u || !delta || !A || !Bm || !Cm || !y) return -1;
+    if (batch < 0 || d_inner < 0 || seqlen < 0 || d_state < 1) return -1;
+    prob_t p = {0};
+    p.kind = KIND_S6;
+    p.u = u; p.dl = delta; p.A = A; p.Bm = Bm; p.Cm = Cm; p.Dskip = Dskip;
+    p.z = z; p.h0 = h0; p.y = y; p.hT = hT;
+    p.batch = batch; p.L = seqlen; p.N = d_state; p.D = d_inner;
+    p.nchan = batch * d_inner;
+    return run(&p, nthreads);
+}
+
+/* One decode step: the loop body with L = 1, state read from and written
+ * back to `state` [B, D, N]; u, delta, z, y are [B, D]; B, C are [B, N]. */
+int oracle_state_update(double *state, const double *u, const double *delta,
+                        const double *A, const double *Bm, const double *Cm,
+                        const double *Dskip, const double *z, double *y,
+                        long batch, long d_inner, long d_state, int nthreads)
+{
+    if (!state) return -1;
+    /* [B, D] with L = 1 is the [B, D, L] layout; [B, N] is [B, N, L]. */
+    return oracle_s6_scan(u, delta, A, Bm, Cm, Dskip, z, state, y, state,
+                          batch, d_inner, 1, d_state, nthreads);
+}
+
+int oracle_ssd(const double *x, const double *dt, const double *A,
+               const double *Bm, const double *Cm, const double *Dskip,
+               const double *z, const double *h0, double *y, double *hT,
+               long batch, long seqlen, long nheads, long headdim,
+               long d_state, long ngroups, int nthreads)
+{
+    if (!x || !dt || !A || !Bm || !Cm || !y) return -1;
+    if (batch < 0 || seqlen < 0 || nheads < 1 || headdim < 1 || d_state < 1 ||
+        ngroups < 1 || nheads % ngroups != 0)
+        return -1;
+    prob_t p = {0};
+    p.kind = KIND_SSD;
+    p.u = x; p.dl = dt; p.A = A; p.Bm = Bm; p.Cm = Cm; p.Dskip = Dskip;
+    p.z = z; p.h0 = h0; p.y = y; p.hT = hT;
+    p.batch = batch; p.L = seqlen; p.N = d_state;
+    p.H = nheads; p.P = headdim; p.G = ngroups;
+    p.nchan = batch * nheads * headdim;
+    return run(&p, nthreads);
+}
