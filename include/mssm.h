@@ -1,0 +1,176 @@
+/*
+ * mssm.h -- C ABI of libmssm.so, the MI355X (gfx950) selective state-space
+ * scan library.
+ *
+ * Three operations, each defined by the pages it cites:
+ *
+ *   mssm_selective_scan_fwd  the S6 selective scan over a whole sequence;
+ *   mssm_state_update        one decode token of the same recurrence;
+ *   mssm_ssd_chunk_fwd       the Mamba-2 SSD (scalar transition per head),
+ *                            computed chunk by chunk.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers marked (device) are device pointers in the current HIP device's
+ *   memory; every tensor is dense and contiguous in the layout given (row-
+ *   major, last index fastest).  The library does not allocate, free, or
+ *   synchronise: all work is enqueued on `stream` (a hipStream_t; NULL means
+ *   the default stream) and the call returns as soon as it is enqueued.
+ * - The caller owns every buffer.  Inputs are only read; outputs are only
+ *   written; `state` of mssm_state_update is read and then overwritten.
+ *   Outputs must not alias inputs (except `state`, which is in place).
+ * - `dtype` selects the storage type of the per-token tensors (u, delta, z,
+ *   B, C, x, dt, y): MSSM_F32 (IEEE binary32) or MSSM_BF16 (bfloat16).  A, D,
+ *   h0, h_final and `state` are always float32; all arithmetic and the
+ *   recurrent state are float32; a bf16 output is rounded to nearest-even.
+ * - Errors: argument problems are reported synchronously, before anything is
+ *   enqueued, as a negative MSSM_ERR_* code; mssm_last_error() then returns a
+ *   message for the calling thread.  A launch failure returns
+ *   MSSM_ERR_LAUNCH.  Faults during execution surface at the caller's next
+ *   synchronisation of `stream`.  MSSM_OK (0) means the work was enqueued.
+ * - Every base pointer must be aligned to 16 bytes (MSSM_ERR_ALIGN).
+ * - Zero-length sequences are valid: nothing is launched for the scan
+ *   itself; h_final (if requested) receives h0, or zeros.
+ * - The functions are stateless and may be called from several threads.
+ */
+#ifndef MSSM_H
+#define MSSM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MSSM_F32 = 0, MSSM_BF16 = 1 } mssm_dtype;
+
+enum {
+    MSSM_OK = 0,
+    MSSM_ERR_NULL = -1,         /* a required pointer is NULL                 */
+    MSSM_ERR_SHAPE = -2,        /* a dimension is negative or inconsistent    */
+    MSSM_ERR_DTYPE = -3,        /* dtype is not an mssm_dtype value           */
+    MSSM_ERR_UNSUPPORTED = -4,  /* a size outside what the kernels implement  */
+    MSSM_ERR_ALIGN = -5,        /* a base pointer is not 16-byte aligned      */
+    MSSM_ERR_WORKSPACE = -6,    /* workspace missing or too small             */
+    MSSM_ERR_LAUNCH = -7        /* the HIP launch itself failed               */
+};
+
+/*
+ * S6 selective scan (forward).
+ *
+ * Defined by: Mamba "Architecture Details" page, "Selective State Space
+ * Mechanism / How S6 Works" -- input-dependent delta, B, C and the update
+ * h(t) = discretize(A, delta(t)) h(t-1) + delta(t) B(t) x(t), y(t) = C(t) h(t);
+ * the SSM optimisation catalogue, section 7 -- the transition is
+ * exp(delta A), elementwise because A is diagonal; section 6 -- the skip
+ * term D x; section 3 -- the output gate, here silu(z) = z / (1 + exp(-z)).
+ * For every batch row b, channel d and state index n (h starts at h0, or 0):
+ *
+ *   h[n] <- exp(delta[b,d,t] * A[d,n]) * h[n] + delta[b,d,t] * u[b,d,t] * B[b,n,t]
+ *   y[b,d,t] = (sum_n C[b,n,t] * h[n] + D[d] * u[b,d,t]) * silu(z[b,d,t])
+ *
+ * The input term is the first-order (Euler) form delta*B*u; delta is used as
+ * given (it must already be positive: no softplus or bias is applied).
+ *
+ *   u, delta   (device) [batch, d_inner, seqlen]  dtype
+ *   A          (device) [d_inner, d_state]        float32 (any real; Mamba uses A < 0)
+ *   Bm, Cm     (device) [batch, d_state, seqlen]  dtype, shared by all channels
+ *   Dskip      (device) [d_inner] float32, NULL => no skip term
+ *   z          (device) [batch, d_inner, seqlen]  dtype, NULL => no gate
+ *   h0         (device) [batch, d_inner, d_state] float32, NULL => zero start
+ *   y          (device) [batch, d_inner, seqlen]  dtype, output
+ *   h_final    (device) [batch, d_inner, d_state] float32, NULL => not written
+ *
+ * Limits: 1 <= d_state <= 64 (MSSM_ERR_UNSUPPORTED otherwise); batch,
+ * d_inner, seqlen >= 0; batch*d_inner*seqlen < 2^62.
+ */
+int mssm_selective_scan_fwd(const void* u, const void* delta, const float* A,
+                            const void* Bm, const void* Cm, const float* Dskip,
+                            const void* z, const float* h0, void* y, float* h_final,
+                            int64_t batch, int64_t d_inner, int64_t seqlen,
+                            int64_t d_state, mssm_dtype dtype, void* stream);
+
+/*
+ * Decode: one token of the same recurrence, state updated in place.
+ *
+ * Defined by: Mamba "Architecture Details" page, "Hardware-Aware
+ * Implementation / Parallel Algorithm", sequential (inference) mode -- a
+ * constant-size state updated per token, h = A h + B x_t, then y_t = C h
+ * read from the UPDATED state; the transition, skip and gate as above.
+ *
+ *   state      (device) [batch, d_inner, d_state] float32, read and overwritten
+ *   u, delta   (device) [batch, d_inner] dtype
+ *   A          (device) [d_inner, d_state] float32
+ *   Bm, Cm     (device) [batch, d_state] dtype
+ *   Dskip      (device) [d_inner] float32, NULL => no skip term
+ *   z          (device) [batch, d_inner] dtype, NULL => no gate
+ *   y          (device) [batch, d_inner] dtype, output
+ *
+ * Limits: 1 <= d_state <= 64.
+ */
+int mssm_state_update(float* state, const void* u, const void* delta, const float* A,
+                      const void* Bm, const void* Cm, const float* Dskip, const void* z,
+                      void* y, int64_t batch, int64_t d_inner, int64_t d_state,
+                      mssm_dtype dtype, void* stream);
+
+/*
+ * Workspace (bytes) mssm_ssd_chunk_fwd needs for these sizes.  Host-only,
+ * pure; returns 0 for invalid sizes.
+ */
+size_t mssm_ssd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads,
+                               int64_t headdim, int64_t d_state, int64_t ngroups,
+                               int64_t chunk);
+
+/*
+ * Mamba-2 SSD, chunked.
+ *
+ * Defined by: SSM optimisation catalogue, section 2 "State Space Duality" --
+ * Y(T,P) = SSM(A, B(T,N), C(T,N))(X(T,P)) with a scalar transition per
+ * head, equivalently a structured masked attention; section 9 "Chunked
+ * Computation" and section 2's algorithm -- split the sequence into chunks,
+ * compute the chunk-local quadratic form and each chunk's final state, pass
+ * states from chunk to chunk, combine; section 10 -- the mask is
+ * semi-separable.  Mamba-2 layout from the "SKILL" page ("Workflow 3":
+ * d_state, headdim, ngroups).  The result equals, up to rounding, the
+ * recurrence per (b, head h, head channel p) with head h using group
+ * g = h / (nheads / ngroups):
+ *
+ *   H[n] <- exp(dt[b,t,h] * A[h]) * H[n] + dt[b,t,h] * x[b,t,h,p] * Bm[b,t,g,n]
+ *   y[b,t,h,p] = (sum_n Cm[b,t,g,n] * H[n] + D[h] * x[b,t,h,p]) * silu(z[b,t,h,p])
+ *
+ *   x          (device) [batch, seqlen, nheads, headdim] dtype
+ *   dt         (device) [batch, seqlen, nheads] dtype (positive; used as given)
+ *   A          (device) [nheads] float32
+ *   Bm, Cm     (device) [batch, seqlen, ngroups, d_state] dtype
+ *   Dskip      (device) [nheads] float32, NULL => no skip term
+ *   z          (device) [batch, seqlen, nheads, headdim] dtype, NULL => no gate
+ *   h0         (device) [batch, nheads, headdim, d_state] float32, NULL => zero start
+ *   y          (device) [batch, seqlen, nheads, headdim] dtype, output
+ *   h_final    (device) [batch, nheads, headdim, d_state] float32, NULL => not written
+ *   workspace  (device) scratch of at least mssm_ssd_workspace_size(...) bytes,
+ *              owned by the caller; contents on entry are ignored and on exit
+ *              are unspecified.  May be NULL if that size is 0.
+ *
+ * Limits: dtype MSSM_BF16 only; headdim = 64; d_state a multiple of 16 in
+ * [16, 256]; chunk in {64, 128, 256}; nheads % ngroups == 0.  Other sizes
+ * return MSSM_ERR_UNSUPPORTED.
+ */
+int mssm_ssd_chunk_fwd(const void* x, const void* dt, const float* A, const void* Bm,
+                       const void* Cm, const float* Dskip, const void* z, const float* h0,
+                       void* y, float* h_final, int64_t batch, int64_t seqlen,
+                       int64_t nheads, int64_t headdim, int64_t d_state, int64_t ngroups,
+                       int64_t chunk, void* workspace, size_t workspace_bytes,
+                       mssm_dtype dtype, void* stream);
+
+/* Message for the calling thread's last non-OK return ("" if none). */
+const char* mssm_last_error(void);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int mssm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSSM_H */

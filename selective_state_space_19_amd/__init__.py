@@ -1,1 +1,152 @@
-"""MI355X-native selective state-space scan (S6, decode step, Mamba-2 SSD)."""
+"""MI355X-native selective state-space scan: S6 scan, decode step, Mamba-2 SSD.
+
+Every operation runs in libmssm.so's HIP kernels (gfx950).  This module only
+checks tensors and marshals pointers and the current HIP stream through the
+C ABI declared in include/mssm.h; PyTorch provides device memory and streams.
+There is no CPU fallback: calling on CPU tensors, or without the built
+library, raises.
+"""
+from __future__ import annotations
+
+from ._lib import MSSM_BF16, MSSM_F32, MssmError, check, lib
+
+__all__ = ["selective_scan", "state_update", "ssd_chunk", "ssd_workspace_size", "MssmError", "lib"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return MSSM_F32
+    if t.dtype == torch.bfloat16:
+        return MSSM_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _dev(t, name, shape=None, dtype=None, device=None):
+    if t is None:
+        return None
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t if t.is_contiguous() else t.contiguous()
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream, device):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return s.cuda_stream
+
+
+def selective_scan(u, delta, A, B, C, D=None, z=None, h0=None, *, return_final_state=False,
+                   out=None, h_final=None, stream=None):
+    """S6 scan.  u, delta, z: [b, d, L]; B, C: [b, N, L] (float32 or bfloat16,
+    all the same); A: [d, N] float32; D: [d] float32; h0: [b, d, N] float32.
+    Returns y [b, d, L] (u's dtype), and h_final [b, d, N] float32 if asked."""
+    torch = _torch()
+    dev = u.device
+    u = _dev(u, "u")
+    bsz, dim, L = u.shape
+    N = A.shape[-1]
+    dt = u.dtype
+    code = _dtype_code(u)
+    delta = _dev(delta, "delta", u.shape, dt, dev)
+    z = _dev(z, "z", u.shape, dt, dev)
+    B = _dev(B, "B", (bsz, N, L), dt, dev)
+    C = _dev(C, "C", (bsz, N, L), dt, dev)
+    A = _dev(A, "A", (dim, N), torch.float32, dev)
+    D = _dev(D, "D", (dim,), torch.float32, dev)
+    h0 = _dev(h0, "h0", (bsz, dim, N), torch.float32, dev)
+    y = out if out is not None else torch.empty_like(u)
+    _dev(y, "out", u.shape, dt, dev)
+    if not y.is_contiguous():
+        raise ValueError("out must be contiguous")
+    hf = None
+    if return_final_state or h_final is not None:
+        hf = h_final if h_final is not None else torch.empty((bsz, dim, N), dtype=torch.float32, device=dev)
+        _dev(hf, "h_final", (bsz, dim, N), torch.float32, dev)
+        if not hf.is_contiguous():
+            raise ValueError("h_final must be contiguous")
+    check(lib().mssm_selective_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                        _ptr(h0), _ptr(y), _ptr(hf), bsz, dim, L, N, code,
+                                        _stream(stream, dev)))
+    return (y, hf) if hf is not None else y
+
+
+def state_update(state, u, delta, A, B, C, D=None, z=None, *, out=None, stream=None):
+    """One decode token; `state` [b, d, N] float32 is updated in place.
+    u, delta, z: [b, d]; B, C: [b, N]; A: [d, N]; D: [d].  Returns y [b, d]."""
+    torch = _torch()
+    dev = state.device
+    state = _dev(state, "state", dtype=torch.float32)
+    if not state.is_contiguous():
+        raise ValueError("state must be contiguous (it is updated in place)")
+    bsz, dim, N = state.shape
+    dt = u.dtype
+    code = _dtype_code(u)
+    u = _dev(u, "u", (bsz, dim), dt, dev)
+    delta = _dev(delta, "delta", (bsz, dim), dt, dev)
+    z = _dev(z, "z", (bsz, dim), dt, dev)
+    B = _dev(B, "B", (bsz, N), dt, dev)
+    C = _dev(C, "C", (bsz, N), dt, dev)
+    A = _dev(A, "A", (dim, N), torch.float32, dev)
+    D = _dev(D, "D", (dim,), torch.float32, dev)
+    y = out if out is not None else torch.empty((bsz, dim), dtype=dt, device=dev)
+    _dev(y, "out", (bsz, dim), dt, dev)
+    check(lib().mssm_state_update(_ptr(state), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                  _ptr(z), _ptr(y), bsz, dim, N, code, _stream(stream, dev)))
+    return y
+
+
+def ssd_workspace_size(batch, seqlen, nheads, headdim, d_state, ngroups=1, chunk=256):
+    return int(lib().mssm_ssd_workspace_size(batch, seqlen, nheads, headdim, d_state, ngroups, chunk))
+
+
+def ssd_chunk(x, dt, A, B, C, D=None, z=None, h0=None, *, chunk=256, return_final_state=False,
+              out=None, h_final=None, workspace=None, stream=None):
+    """Mamba-2 SSD.  x, z: [b, L, H, P]; dt: [b, L, H]; B, C: [b, L, G, N]
+    (bfloat16); A, D: [H] float32; h0: [b, H, P, N] float32.  Returns y
+    [b, L, H, P] bfloat16, and h_final [b, H, P, N] float32 if asked."""
+    torch = _torch()
+    dev = x.device
+    x = _dev(x, "x")
+    bsz, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    ty = x.dtype
+    code = _dtype_code(x)
+    dt = _dev(dt, "dt", (bsz, L, H), ty, dev)
+    B = _dev(B, "B", (bsz, L, G, N), ty, dev)
+    C = _dev(C, "C", (bsz, L, G, N), ty, dev)
+    z = _dev(z, "z", x.shape, ty, dev)
+    A = _dev(A, "A", (H,), torch.float32, dev)
+    D = _dev(D, "D", (H,), torch.float32, dev)
+    h0 = _dev(h0, "h0", (bsz, H, P, N), torch.float32, dev)
+    y = out if out is not None else torch.empty_like(x)
+    _dev(y, "out", x.shape, ty, dev)
+    hf = None
+    if return_final_state or h_final is not None:
+        hf = h_final if h_final is not None else torch.empty((bsz, H, P, N), dtype=torch.float32, device=dev)
+        _dev(hf, "h_final", (bsz, H, P, N), torch.float32, dev)
+    need = ssd_workspace_size(bsz, L, H, P, N, G, chunk)
+    ws = workspace
+    if need > 0 and ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    check(lib().mssm_ssd_chunk_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
+                                   _ptr(y), _ptr(hf), bsz, L, H, P, N, G, chunk, _ptr(ws), wsb, code,
+                                   _stream(stream, dev)))
+    return (y, hf) if hf is not None else y

@@ -1,0 +1,118 @@
+// common.h -- device helpers shared by the gfx950 kernels of libmssm.
+//
+// Storage types: float (MSSM_F32) and bfloat16 carried as uint16_t
+// (MSSM_BF16).  All arithmetic is float32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mssm {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef __bf16 bf16x2_t __attribute__((__vector_size__(2 * sizeof(__bf16))));
+
+// --- scalar conversions ----------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two floats -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2_t p = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, p);
+}
+__device__ __forceinline__ uint16_t to_bf16(float f) {
+    __bf16 b = (__bf16)f;
+    return __builtin_bit_cast(uint16_t, b);
+}
+
+// 2^x with the hardware transcendental unit (v_exp_f32).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// silu(g) = g * sigmoid(g) = g / (1 + e^-g).
+__device__ __forceinline__ float silu(float g) {
+    const float e = fast_exp2(-g * kLog2e);
+    return g * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// --- per-dtype element access over packed 32-bit words ----------------------
+// A run of CNT elements of type T held as CNT*sizeof(T)/4 words.
+template <typename T> struct Elem;
+
+template <> struct Elem<float> {
+    static constexpr int kPerWord = 1;
+    __device__ __forceinline__ static float get(const uint32_t* w, int j) { return __uint_as_float(w[j]); }
+    __device__ __forceinline__ static float load1(const float* p) { return *p; }
+    __device__ __forceinline__ static void store1(float* p, float v) { *p = v; }
+};
+
+template <> struct Elem<uint16_t> {
+    static constexpr int kPerWord = 2;
+    __device__ __forceinline__ static float get(const uint32_t* w, int j) {
+        const uint32_t x = w[j >> 1];
+        return (j & 1) ? bf16_hi(x) : bf16_lo(x);
+    }
+    __device__ __forceinline__ static float load1(const uint16_t* p) { return __uint_as_float(uint32_t(*p) << 16); }
+    __device__ __forceinline__ static void store1(uint16_t* p, float v) { *p = to_bf16(v); }
+};
+
+// Load CNT consecutive elements starting at src into words w (CNT*sizeof(T)
+// must be a multiple of 16).  `valid` elements are in range; the rest read
+// as zero.  `vec` says src is 16-byte aligned.
+template <typename T, int CNT>
+__device__ __forceinline__ void load_run(const T* __restrict__ src, int valid, bool vec,
+                                         uint32_t (&w)[CNT * sizeof(T) / 4]) {
+    constexpr int kWords = CNT * sizeof(T) / 4;
+    static_assert(kWords % 4 == 0, "runs are whole 16-byte vectors");
+    if (vec && valid >= CNT) {
+        const uint4* s4 = reinterpret_cast<const uint4*>(src);
+#pragma unroll
+        for (int i = 0; i < kWords / 4; ++i) {
+            const uint4 v = s4[i];
+            w[4 * i + 0] = v.x;
+            w[4 * i + 1] = v.y;
+            w[4 * i + 2] = v.z;
+            w[4 * i + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kWords; ++i) w[i] = 0u;
+#pragma unroll
+        for (int j = 0; j < CNT; ++j) {
+            if (j < valid) {
+                if constexpr (sizeof(T) == 4) {
+                    w[j] = __float_as_uint(reinterpret_cast<const float*>(src)[j]);
+                } else {
+                    const uint32_t bits = reinterpret_cast<const uint16_t*>(src)[j];
+                    w[j >> 1] |= (j & 1) ? (bits << 16) : bits;
+                }
+            }
+        }
+    }
+}
+
+// Store CNT floats as T (only the first `valid`), vectorised when aligned.
+template <typename T, int CNT>
+__device__ __forceinline__ void store_run(T* __restrict__ dst, int valid, bool vec, const float (&v)[CNT]) {
+    if (vec && valid >= CNT) {
+        if constexpr (sizeof(T) == 4) {
+            float4* d4 = reinterpret_cast<float4*>(dst);
+#pragma unroll
+            for (int i = 0; i < CNT / 4; ++i)
+                d4[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+        } else {
+            uint4* d4 = reinterpret_cast<uint4*>(dst);
+#pragma unroll
+            for (int i = 0; i < CNT / 8; ++i)
+                d4[i] = make_uint4(pack_bf16x2(v[8 * i + 0], v[8 * i + 1]), pack_bf16x2(v[8 * i + 2], v[8 * i + 3]),
+                                   pack_bf16x2(v[8 * i + 4], v[8 * i + 5]), pack_bf16x2(v[8 * i + 6], v[8 * i + 7]));
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < CNT; ++j)
+            if (j < valid) Elem<T>::store1(dst + j, v[j]);
+    }
+}
+
+}  // namespace mssm

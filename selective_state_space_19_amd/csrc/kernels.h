@@ -1,0 +1,62 @@
+// kernels.h -- internal launchers of libmssm (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mssm {
+
+struct S6Params {
+    const void* u;
+    const void* delta;
+    const void* Bm;
+    const void* Cm;
+    const void* z;        // nullable
+    const float* A;
+    const float* Dskip;   // nullable
+    const float* h0;      // nullable
+    void* y;
+    float* h_final;       // nullable
+    int64_t batch, dim;
+    int32_t L, N;
+};
+
+struct SUParams {
+    float* state;
+    const void* u;
+    const void* delta;
+    const void* Bm;
+    const void* Cm;
+    const void* z;        // nullable
+    const float* A;
+    const float* Dskip;   // nullable
+    void* y;
+    int64_t batch, dim;
+    int32_t N;
+};
+
+struct SSDParams {
+    const void* x;
+    const void* dt;
+    const float* A;
+    const void* Bm;
+    const void* Cm;
+    const float* Dskip;   // nullable
+    const void* z;        // nullable
+    const float* h0;      // nullable
+    void* y;
+    float* h_final;       // nullable
+    void* workspace;
+    int64_t batch;
+    int32_t L, H, P, N, G, Q;
+};
+
+// Each returns hipSuccess or the launch error; is_bf16 selects the storage type.
+hipError_t launch_s6_scan(const S6Params& p, bool is_bf16, hipStream_t stream);
+hipError_t launch_state_update(const SUParams& p, bool is_bf16, hipStream_t stream);
+hipError_t launch_ssd(const SSDParams& p, hipStream_t stream);
+size_t ssd_workspace_bytes(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int64_t Q);
+// dst[i] = src ? src[i] : 0 for i < n (used for zero-length sequences).
+hipError_t launch_copy_or_zero(float* dst, const float* src, int64_t n, hipStream_t stream);
+
+}  // namespace mssm

@@ -1,0 +1,186 @@
+// mssm_api.cpp -- the C ABI of libmssm.so: argument checking, then launch.
+//
+// Every check happens on the host before anything is enqueued; a failed
+// check returns a negative MSSM_ERR_* code and records a message for the
+// calling thread (mssm_last_error).  Nothing here allocates or synchronises.
+#include "mssm.h"
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// a*b*c with overflow check against 2^62.
+bool prod_ok(int64_t a, int64_t b, int64_t c, int64_t* out) {
+    const int64_t lim = int64_t(1) << 62;
+    if (a < 0 || b < 0 || c < 0) return false;
+    __int128 v = (__int128)a * b * c;
+    if (v >= lim) return false;
+    if (out) *out = (int64_t)v;
+    return true;
+}
+
+#define CHECK_PTR(p)                                                           \
+    do {                                                                       \
+        if (!(p)) return fail(MSSM_ERR_NULL, "%s: %s is NULL", fn, #p);         \
+        if (!aligned16(p)) return fail(MSSM_ERR_ALIGN, "%s: %s is not 16-byte aligned", fn, #p); \
+    } while (0)
+#define CHECK_OPT(p)                                                           \
+    do {                                                                       \
+        if ((p) && !aligned16(p)) return fail(MSSM_ERR_ALIGN, "%s: %s is not 16-byte aligned", fn, #p); \
+    } while (0)
+
+int launched(const char* fn, hipError_t e) {
+    if (e != hipSuccess) return fail(MSSM_ERR_LAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return MSSM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mssm_last_error(void) { return g_err.c_str(); }
+
+int mssm_version(void) { return 100; }
+
+int mssm_selective_scan_fwd(const void* u, const void* delta, const float* A, const void* Bm,
+                            const void* Cm, const float* Dskip, const void* z, const float* h0,
+                            void* y, float* h_final, int64_t batch, int64_t d_inner, int64_t seqlen,
+                            int64_t d_state, mssm_dtype dtype, void* stream) {
+    static const char* fn = "mssm_selective_scan_fwd";
+    g_err.clear();
+    if (dtype != MSSM_F32 && dtype != MSSM_BF16) return fail(MSSM_ERR_DTYPE, "%s: unknown dtype %d", fn, (int)dtype);
+    if (batch < 0 || d_inner < 0 || seqlen < 0 || d_state < 0)
+        return fail(MSSM_ERR_SHAPE, "%s: negative dimension", fn);
+    if (d_state < 1 || d_state > 64) return fail(MSSM_ERR_UNSUPPORTED, "%s: d_state %lld not in [1, 64]", fn, (long long)d_state);
+    if (seqlen > INT32_MAX) return fail(MSSM_ERR_UNSUPPORTED, "%s: seqlen %lld too large", fn, (long long)seqlen);
+    if (!prod_ok(batch, d_inner, seqlen, nullptr) || !prod_ok(batch, d_inner, d_state, nullptr))
+        return fail(MSSM_ERR_SHAPE, "%s: tensor too large", fn);
+    if (batch == 0 || d_inner == 0) return MSSM_OK;
+    CHECK_OPT(h0);
+    CHECK_OPT(h_final);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (seqlen == 0) {
+        if (!h_final) return MSSM_OK;
+        return launched(fn, mssm::launch_copy_or_zero(h_final, h0, batch * d_inner * d_state, s));
+    }
+    CHECK_PTR(u);
+    CHECK_PTR(delta);
+    CHECK_PTR(A);
+    CHECK_PTR(Bm);
+    CHECK_PTR(Cm);
+    CHECK_PTR(y);
+    CHECK_OPT(Dskip);
+    CHECK_OPT(z);
+    const int64_t blocks = ((d_inner + 63) / 64) * batch;
+    if (blocks > INT32_MAX) return fail(MSSM_ERR_UNSUPPORTED, "%s: batch*d_inner too large", fn);
+    mssm::S6Params p{u, delta, Bm, Cm, z, A, Dskip, h0, y, h_final, batch, d_inner, (int32_t)seqlen, (int32_t)d_state};
+    return launched(fn, mssm::launch_s6_scan(p, dtype == MSSM_BF16, s));
+}
+
+int mssm_state_update(float* state, const void* u, const void* delta, const float* A, const void* Bm,
+                      const void* Cm, const float* Dskip, const void* z, void* y, int64_t batch,
+                      int64_t d_inner, int64_t d_state, mssm_dtype dtype, void* stream) {
+    static const char* fn = "mssm_state_update";
+    g_err.clear();
+    if (dtype != MSSM_F32 && dtype != MSSM_BF16) return fail(MSSM_ERR_DTYPE, "%s: unknown dtype %d", fn, (int)dtype);
+    if (batch < 0 || d_inner < 0 || d_state < 0) return fail(MSSM_ERR_SHAPE, "%s: negative dimension", fn);
+    if (d_state < 1 || d_state > 64) return fail(MSSM_ERR_UNSUPPORTED, "%s: d_state %lld not in [1, 64]", fn, (long long)d_state);
+    int64_t nthreads = 0;
+    if (!prod_ok(batch, d_inner, d_state, nullptr) || !prod_ok(batch, d_inner, 4, &nthreads))
+        return fail(MSSM_ERR_SHAPE, "%s: tensor too large", fn);
+    if (batch == 0 || d_inner == 0) return MSSM_OK;
+    if ((nthreads + 255) / 256 > INT32_MAX) return fail(MSSM_ERR_UNSUPPORTED, "%s: batch*d_inner too large", fn);
+    CHECK_PTR(state);
+    CHECK_PTR(u);
+    CHECK_PTR(delta);
+    CHECK_PTR(A);
+    CHECK_PTR(Bm);
+    CHECK_PTR(Cm);
+    CHECK_PTR(y);
+    CHECK_OPT(Dskip);
+    CHECK_OPT(z);
+    mssm::SUParams p{state, u, delta, Bm, Cm, z, A, Dskip, y, batch, d_inner, (int32_t)d_state};
+    return launched(fn, mssm::launch_state_update(p, dtype == MSSM_BF16, static_cast<hipStream_t>(stream)));
+}
+
+size_t mssm_ssd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                               int64_t d_state, int64_t ngroups, int64_t chunk) {
+    if (batch < 0 || seqlen < 0 || nheads < 1 || headdim < 1 || d_state < 1 || ngroups < 1 || chunk < 1)
+        return 0;
+    return mssm::ssd_workspace_bytes(batch, seqlen, nheads, headdim, d_state, ngroups, chunk);
+}
+
+int mssm_ssd_chunk_fwd(const void* x, const void* dt, const float* A, const void* Bm, const void* Cm,
+                       const float* Dskip, const void* z, const float* h0, void* y, float* h_final,
+                       int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t d_state,
+                       int64_t ngroups, int64_t chunk, void* workspace, size_t workspace_bytes,
+                       mssm_dtype dtype, void* stream) {
+    static const char* fn = "mssm_ssd_chunk_fwd";
+    g_err.clear();
+    if (dtype != MSSM_F32 && dtype != MSSM_BF16) return fail(MSSM_ERR_DTYPE, "%s: unknown dtype %d", fn, (int)dtype);
+    if (batch < 0 || seqlen < 0 || nheads < 0 || headdim < 0 || d_state < 0 || ngroups < 0 || chunk < 0)
+        return fail(MSSM_ERR_SHAPE, "%s: negative dimension", fn);
+    if (nheads < 1 || ngroups < 1 || nheads % ngroups != 0)
+        return fail(MSSM_ERR_SHAPE, "%s: nheads %lld must be a positive multiple of ngroups %lld", fn,
+                    (long long)nheads, (long long)ngroups);
+    if (dtype != MSSM_BF16) return fail(MSSM_ERR_UNSUPPORTED, "%s: only MSSM_BF16 is implemented", fn);
+    if (headdim != 64) return fail(MSSM_ERR_UNSUPPORTED, "%s: headdim %lld (only 64)", fn, (long long)headdim);
+    if (d_state < 16 || d_state > 256 || d_state % 16 != 0)
+        return fail(MSSM_ERR_UNSUPPORTED, "%s: d_state %lld (multiple of 16 in [16, 256])", fn, (long long)d_state);
+    if (chunk != 64 && chunk != 128 && chunk != 256)
+        return fail(MSSM_ERR_UNSUPPORTED, "%s: chunk %lld (64, 128 or 256)", fn, (long long)chunk);
+    if (seqlen > INT32_MAX || nheads > INT32_MAX) return fail(MSSM_ERR_UNSUPPORTED, "%s: size too large", fn);
+    if (!prod_ok(batch, seqlen, nheads * headdim, nullptr) || !prod_ok(batch, nheads * headdim, d_state, nullptr) ||
+        !prod_ok(batch, seqlen, ngroups * d_state, nullptr))
+        return fail(MSSM_ERR_SHAPE, "%s: tensor too large", fn);
+    if (batch == 0) return MSSM_OK;
+    CHECK_OPT(h0);
+    CHECK_OPT(h_final);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (seqlen == 0) {
+        if (!h_final) return MSSM_OK;
+        return launched(fn, mssm::launch_copy_or_zero(h_final, h0, batch * nheads * headdim * d_state, s));
+    }
+    CHECK_PTR(x);
+    CHECK_PTR(dt);
+    CHECK_PTR(A);
+    CHECK_PTR(Bm);
+    CHECK_PTR(Cm);
+    CHECK_PTR(y);
+    CHECK_OPT(Dskip);
+    CHECK_OPT(z);
+    const size_t need = mssm::ssd_workspace_bytes(batch, seqlen, nheads, headdim, d_state, ngroups, chunk);
+    if (need > 0) {
+        if (!workspace) return fail(MSSM_ERR_WORKSPACE, "%s: workspace is NULL (%zu bytes needed)", fn, need);
+        if (!aligned16(workspace)) return fail(MSSM_ERR_ALIGN, "%s: workspace is not 16-byte aligned", fn);
+        if (workspace_bytes < need)
+            return fail(MSSM_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, workspace_bytes, need);
+    }
+    mssm::SSDParams p{x, dt, A, Bm, Cm, Dskip, z, h0, y, h_final, workspace, batch, (int32_t)seqlen,
+                      (int32_t)nheads, (int32_t)headdim, (int32_t)d_state, (int32_t)ngroups, (int32_t)chunk};
+    return launched(fn, mssm::launch_ssd(p, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,99 @@
+"""The C ABI library loads, exports what include/mssm.h declares, and rejects
+bad arguments on the host -- no GPU needed (no call here reaches a launch)."""
+import ctypes
+
+import pytest
+
+from selective_state_space_19_amd import _lib
+
+ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_UNSUP, ERR_ALIGN, ERR_WS = -1, -2, -3, -4, -5, -6
+FAKE = 0x10000          # an aligned non-NULL address; never dereferenced here
+MISALIGNED = 0x10004
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.lib()
+
+
+def test_exports_every_declared_function(lib):
+    names = _lib.header_functions()
+    assert set(names) == {"mssm_selective_scan_fwd", "mssm_state_update", "mssm_ssd_workspace_size",
+                          "mssm_ssd_chunk_fwd", "mssm_last_error", "mssm_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
+def test_version(lib):
+    assert lib.mssm_version() >= 100
+
+
+def _scan(lib, **kw):
+    a = dict(u=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, h0=None, y=FAKE, hf=None,
+             b=2, d=64, L=128, N=16, dtype=0)
+    a.update(kw)
+    return lib.mssm_selective_scan_fwd(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["h0"],
+                                       a["y"], a["hf"], a["b"], a["d"], a["L"], a["N"], a["dtype"], None)
+
+
+def test_scan_argument_errors(lib):
+    assert _scan(lib, u=None) == ERR_NULL
+    assert b"u is NULL" in lib.mssm_last_error()
+    assert _scan(lib, y=None) == ERR_NULL
+    assert _scan(lib, dtype=7) == ERR_DTYPE
+    assert _scan(lib, L=-1) == ERR_SHAPE
+    assert _scan(lib, N=0) == ERR_UNSUP
+    assert _scan(lib, N=65) == ERR_UNSUP
+    assert _scan(lib, delta=MISALIGNED) == ERR_ALIGN
+    assert _scan(lib, z=MISALIGNED) == ERR_ALIGN
+    assert _scan(lib, b=1 << 40, d=1 << 40) == ERR_SHAPE
+    assert _scan(lib, b=0) == 0           # nothing to do, nothing launched
+
+
+def _su(lib, **kw):
+    a = dict(state=FAKE, u=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, y=FAKE,
+             b=2, d=64, N=16, dtype=1)
+    a.update(kw)
+    return lib.mssm_state_update(a["state"], a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"],
+                                 a["y"], a["b"], a["d"], a["N"], a["dtype"], None)
+
+
+def test_state_update_argument_errors(lib):
+    assert _su(lib, state=None) == ERR_NULL
+    assert _su(lib, B=None) == ERR_NULL
+    assert _su(lib, dtype=-1) == ERR_DTYPE
+    assert _su(lib, N=100) == ERR_UNSUP
+    assert _su(lib, D=MISALIGNED) == ERR_ALIGN
+    assert _su(lib, d=0) == 0
+
+
+def _ssd(lib, **kw):
+    a = dict(x=FAKE, dt=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, h0=None, y=FAKE, hf=None,
+             b=1, L=512, H=4, P=64, N=64, G=1, Q=256, ws=FAKE, wsb=1 << 40, dtype=1)
+    a.update(kw)
+    return lib.mssm_ssd_chunk_fwd(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["z"], a["h0"], a["y"],
+                                  a["hf"], a["b"], a["L"], a["H"], a["P"], a["N"], a["G"], a["Q"], a["ws"],
+                                  a["wsb"], a["dtype"], None)
+
+
+def test_ssd_argument_errors(lib):
+    assert _ssd(lib, x=None) == ERR_NULL
+    assert _ssd(lib, H=3, G=2) == ERR_SHAPE
+    assert _ssd(lib, dtype=0) == ERR_UNSUP
+    assert _ssd(lib, P=32) == ERR_UNSUP
+    assert _ssd(lib, N=24) == ERR_UNSUP
+    assert _ssd(lib, Q=100) == ERR_UNSUP
+    assert _ssd(lib, dtype=9) == ERR_DTYPE
+    assert _ssd(lib, h0=MISALIGNED) == ERR_ALIGN
+    need = lib.mssm_ssd_workspace_size(1, 512, 4, 64, 64, 1, 256)
+    if need:
+        assert _ssd(lib, ws=None) == ERR_WS
+        assert _ssd(lib, wsb=need - 1) == ERR_WS
+    assert _ssd(lib, b=0) == 0
+
+
+def test_workspace_size_is_pure(lib):
+    a = lib.mssm_ssd_workspace_size(4, 4096, 32, 64, 128, 1, 256)
+    assert a == lib.mssm_ssd_workspace_size(4, 4096, 32, 64, 128, 1, 256)
+    assert lib.mssm_ssd_workspace_size(-1, 4096, 32, 64, 128, 1, 256) == 0
