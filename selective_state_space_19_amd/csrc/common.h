@@ -30,10 +30,79 @@ __device__ __forceinline__ uint16_t to_bf16(float f) {
 // 2^x with the hardware transcendental unit (v_exp_f32).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Wait for every outstanding LDS / scalar-memory operation (s_waitcnt
+// lgkmcnt(0): vmcnt and expcnt fields at their maximum, gfx9 encoding), and
+// keep the scheduler from moving instructions across this point.
+__device__ __forceinline__ void lgkm_wait_all() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // silu(g) = g * sigmoid(g) = g / (1 + e^-g).
 __device__ __forceinline__ float silu(float g) {
     const float e = fast_exp2(-g * kLog2e);
     return g * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// --- range-checked buffer access ----------------------------------------------
+// A raw buffer resource (stride 0) covering `bytes` bytes from `base`.  Loads
+// at offsets >= bytes return zero and stores there are dropped by the
+// hardware, so tails and idle lanes need no branches (which also keeps the
+// compiler's wait counting exact).  Offsets are 32-bit byte offsets.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOutOfRange = 0x80000000u;   // any offset >= every buffer size used
+constexpr int kRsrcWord3 = 0x00020000;          // raw 32-bit data format
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+
+typedef unsigned int u32x2_t __attribute__((__vector_size__(2 * sizeof(unsigned int))));
+typedef unsigned int u32x4_t __attribute__((__vector_size__(4 * sizeof(unsigned int))));
+
+// Load / store KW 32-bit words (KW = 2 or 4) at byte offset `off`.
+template <int KW>
+__device__ __forceinline__ void buf_load(rsrc_t r, uint32_t off, uint32_t* w) {
+    static_assert(KW == 2 || KW == 4 || KW == 8, "2, 4 or 8 words");
+    if constexpr (KW == 2) {
+        const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+        w[0] = v[0]; w[1] = v[1];
+    } else {
+#pragma unroll
+        for (int i = 0; i < KW / 4; ++i) {
+            const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * i, 0, 0);
+            w[4 * i] = v[0]; w[4 * i + 1] = v[1]; w[4 * i + 2] = v[2]; w[4 * i + 3] = v[3];
+        }
+    }
+}
+template <int KW>
+__device__ __forceinline__ void buf_store(rsrc_t r, uint32_t off, const uint32_t* w) {
+    static_assert(KW == 2 || KW == 4 || KW == 8, "2, 4 or 8 words");
+    if constexpr (KW == 2) {
+        const u32x2_t v = {w[0], w[1]};
+        __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+    } else {
+#pragma unroll
+        for (int i = 0; i < KW / 4; ++i) {
+            const u32x4_t v = {w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+            __builtin_amdgcn_raw_buffer_store_b128(v, r, off + 16 * i, 0, 0);
+        }
+    }
+}
+__device__ __forceinline__ uint32_t buf_load1(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
+// Pack CNT floats into storage words of type T (bf16 pairs or fp32 bits).
+template <typename T, int CNT>
+__device__ __forceinline__ void pack_words(const float (&v)[CNT], uint32_t (&w)[CNT * sizeof(T) / 4]) {
+    if constexpr (sizeof(T) == 4) {
+#pragma unroll
+        for (int i = 0; i < CNT; ++i) w[i] = __float_as_uint(v[i]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < CNT / 2; ++i) w[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+    }
 }
 
 // --- per-dtype element access over packed 32-bit words ----------------------
@@ -58,22 +127,33 @@ template <> struct Elem<uint16_t> {
 };
 
 // Load CNT consecutive elements starting at src into words w (CNT*sizeof(T)
-// must be a multiple of 16).  `valid` elements are in range; the rest read
-// as zero.  `vec` says src is 16-byte aligned.
+// must be a multiple of 8).  `valid` elements are in range; the rest read
+// as zero.  `vec` says src is aligned to the vector width used (16 bytes
+// when CNT*sizeof(T) is a multiple of 16, else 8).
 template <typename T, int CNT>
 __device__ __forceinline__ void load_run(const T* __restrict__ src, int valid, bool vec,
                                          uint32_t (&w)[CNT * sizeof(T) / 4]) {
     constexpr int kWords = CNT * sizeof(T) / 4;
-    static_assert(kWords % 4 == 0, "runs are whole 16-byte vectors");
+    static_assert(kWords % 2 == 0, "runs are whole 8-byte vectors");
     if (vec && valid >= CNT) {
-        const uint4* s4 = reinterpret_cast<const uint4*>(src);
+        if constexpr (kWords % 4 == 0) {
+            const uint4* s4 = reinterpret_cast<const uint4*>(src);
 #pragma unroll
-        for (int i = 0; i < kWords / 4; ++i) {
-            const uint4 v = s4[i];
-            w[4 * i + 0] = v.x;
-            w[4 * i + 1] = v.y;
-            w[4 * i + 2] = v.z;
-            w[4 * i + 3] = v.w;
+            for (int i = 0; i < kWords / 4; ++i) {
+                const uint4 v = s4[i];
+                w[4 * i + 0] = v.x;
+                w[4 * i + 1] = v.y;
+                w[4 * i + 2] = v.z;
+                w[4 * i + 3] = v.w;
+            }
+        } else {
+            const uint2* s2 = reinterpret_cast<const uint2*>(src);
+#pragma unroll
+            for (int i = 0; i < kWords / 2; ++i) {
+                const uint2 v = s2[i];
+                w[2 * i + 0] = v.x;
+                w[2 * i + 1] = v.y;
+            }
         }
     } else {
 #pragma unroll
@@ -96,7 +176,9 @@ __device__ __forceinline__ void load_run(const T* __restrict__ src, int valid, b
 template <typename T, int CNT>
 __device__ __forceinline__ void store_run(T* __restrict__ dst, int valid, bool vec, const float (&v)[CNT]) {
     if (vec && valid >= CNT) {
-        if constexpr (sizeof(T) == 4) {
+        if constexpr (sizeof(T) == 2 && CNT == 4) {
+            *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        } else if constexpr (sizeof(T) == 4) {
             float4* d4 = reinterpret_cast<float4*>(dst);
 #pragma unroll
             for (int i = 0; i < CNT / 4; ++i)

@@ -6,30 +6,40 @@
 //     h[n] <- exp(delta*A[d,n]) * h[n] + delta*u*B[b,n,t]
 //     y     = (sum_n C[b,n,t]*h[n] + D[d]*u) * silu(z)
 //
-// Design (MI355X-first; the pages' warp/shared-memory notes are prior art):
+// Design (MI355X-first; the pages' warp / shared-memory notes are prior art):
 // - The recurrence is elementwise in n, so the only dependency chain is over
-//   time for a fixed (b, d, n).  There are B*D*N such chains (262 144 at the
-//   Mamba-1.4B layer shape), enough to fill 256 CUs with one wave per SIMD
-//   while every chain runs strictly in time order.  So instead of a
-//   parallel-over-time scan (which costs a second pass and a cross-lane
-//   combine per element), each lane walks time sequentially for NS states of
-//   one channel: per element one exp2, two multiplies and two FMAs -- the
-//   minimum the recurrence needs.  The fp32 state lives in registers for the
-//   whole sequence and touches HBM only as h0 / h_final.
-// - A workgroup (4 waves) owns CW = 64 channels of one batch row; wave g owns
-//   the states [g*NS, (g+1)*NS).  The four partial outputs sum_n C*h of a
-//   channel are combined through LDS once per token.
-// - The sequence is processed in chunks of TC tokens.  Per chunk, all 256
-//   threads load the u / delta / z / B / C tiles with 16-byte vector loads,
-//   stage delta and delta*u (fp32) and the B / C tile (fp32, state-major) in
-//   LDS, and prefetch the next chunk into registers while the waves scan.
-//   B and C are shared by every channel, so a wave reads them with
-//   uniform-address (broadcast) LDS loads.
-// - The epilogue (combine partials, + D*u, * silu(z), convert, store) runs in
-//   the same thread -> (channel, token range) mapping as the loads, so u and
-//   z come straight from registers.
+//   time for a fixed (b, d, n); there are B*D*N such chains (262 144 at the
+//   Mamba-1.4B layer shape).  Each lane walks time strictly in order for NS
+//   states of one channel: per state element one v_exp_f32, two multiplies
+//   and two FMAs -- the least the recurrence needs (a parallel-over-time scan
+//   would add a second pass and a cross-lane combine per element).  The fp32
+//   state lives in registers for the whole sequence and reaches HBM only as
+//   h0 / h_final.
+// - Scan mapping: lanes are channels and waves are state groups.  A
+//   workgroup of NW = 8 waves owns 64 channels of one batch row; wave w owns
+//   the states [w*NS, (w+1)*NS).  B and C are shared by all channels, so
+//   within a wave they are uniform: they are fetched with scalar loads into
+//   SGPRs (bf16 unpacked on the scalar unit) and used as free scalar
+//   operands.  Eight waves of NS = 2 states put two waves on each SIMD, so
+//   one wave's scalar and LDS instructions issue beside the other's VALU work.
+// - Row mapping (loads, staging, epilogue): thread -> (row tid/8, segment
+//   tid%8), TPT consecutive tokens each, so one wave-level load or store
+//   covers 8 rows x 8 contiguous segments -- whole cache-line runs.  The
+//   row mapping stages (delta, delta*u) in LDS for the scan and, after it,
+//   sums the NW per-wave partial outputs sum_n C*h, adds D*u, gates with
+//   silu(z) and stores y; u and z stay in the registers they were loaded into.
+// - Time is processed in chunks of TC tokens; a register ring keeps the
+//   row loads of the next RING-1 chunks in flight.  Inside a chunk, token
+//   groups (16 bytes of a B / C row) are software-pipelined: the next
+//   group's scalar B / C loads and LDS (delta, delta*u) loads are issued
+//   before the current group is computed, and waited for after it.
 // - exp(delta*A) is computed as exp2(delta * (A*log2 e)) with A*log2 e
-//   precomputed per lane (v_exp_f32).
+//   precomputed per lane.
+// - ALIGNED (L % 8 == 0; the common case) addresses rows through
+//   range-checked buffer resources: loads past the end read zero and stores
+//   there are dropped, so the hot loop has no bounds branches and every load
+//   is issued unconditionally.  Other lengths take the same arithmetic with
+//   element-wise bounds checks.
 #include "common.h"
 #include "kernels.h"
 
@@ -37,197 +47,262 @@ namespace mssm {
 
 namespace {
 
-constexpr int kThreads = 256;
-
-template <typename T, int CW, int NS, int TC>
-__global__ __launch_bounds__(kThreads) void s6_scan_kernel(S6Params p) {
-    constexpr int NG = kThreads / CW;              // state groups per workgroup
-    constexpr int NP = NG * NS;                    // padded state count (>= N)
-    constexpr int TPT = TC / NG;                   // tokens per thread (row mapping)
+template <typename T, int NW, int NS, int TC, bool ALIGNED, int RING>
+__global__ __launch_bounds__(NW * 64) void s6_scan_kernel(
+    const T* __restrict__ u_in, const T* __restrict__ dl_in, const T* __restrict__ B_in,
+    const T* __restrict__ C_in, const T* __restrict__ z_in, const float* __restrict__ A_in,
+    const float* __restrict__ D_in, const float* __restrict__ h0_in, T* __restrict__ y_out,
+    float* __restrict__ hT_out, int64_t dim, int L, int N) {
+    // Pointers are separate __restrict__ arguments so the compiler may fetch the
+    // wave-uniform B / C words with scalar loads (it must know no store aliases them).
+    constexpr int SEGS = NW;                       // row segments (threads per row)
+    constexpr int TPT = TC / SEGS;                 // tokens per thread (row mapping)
     constexpr int WPT = TPT * sizeof(T) / 4;       // 32-bit words per thread run
-    constexpr int RB = 16 / sizeof(T);             // tokens per B/C load run (16 B)
-    constexpr int BC_RUNS = NP * TC / RB;          // upper bound on B/C runs per matrix
-    constexpr int BC_PER_THREAD = (BC_RUNS + kThreads - 1) / kThreads;
-    static_assert(TPT * sizeof(T) % 16 == 0, "thread runs are whole vectors");
+    constexpr int G = 16 / sizeof(T);              // tokens per scan group: 16 bytes of a B / C row
+    constexpr int NGRP = TC / G;
+    constexpr int BCW = 4;                         // words per B / C row per group
+    constexpr int PR = TC / 2;                     // token pairs per chunk
+    constexpr int PAD = 1;                         // LDS row padding (bank spreading)
+    static_assert(TPT % 2 == 0 && (WPT == 2 || WPT == 4), "row runs are 8- or 16-byte vectors");
+    static_assert(TC % G == 0, "whole scan groups per chunk");
 
-    __shared__ float2 s_dd[TC][CW];                // (delta, delta*u)
-    __shared__ float4 s_bc4[2 * TC * NP / 4];      // B then C tiles, [TC][NP] each
-    __shared__ float s_y[NG][TC][CW];              // partial outputs per state group
-    float* s_B = reinterpret_cast<float*>(s_bc4);
-    float* s_C = s_B + TC * NP;
+    __shared__ float4 s_dd[PR][64 + PAD];          // (delta_t, (delta*u)_t, delta_t+1, (delta*u)_t+1)
+    __shared__ float2 s_y[NW][PR][64 + PAD];       // per-wave partial outputs, token pairs
 
     const int tid = threadIdx.x;
-    const int c = tid % CW;                        // channel in block (both mappings)
-    const int g = tid / CW;                        // state group / token block
-    const int64_t nblk_d = (p.dim + CW - 1) / CW;
+    const int64_t nblk_d = (dim + 63) / 64;
     const int64_t b = blockIdx.x / nblk_d;
-    const int64_t d = (blockIdx.x % nblk_d) * CW + c;
-    const bool dval = d < p.dim;
-    const int L = p.L, N = p.N;
-    const bool vec = (L % RB) == 0;                // rows are 16-byte aligned
+    const int64_t d0 = (blockIdx.x % nblk_d) * 64;
+    const int nrows = (int)((dim - d0) < 64 ? (dim - d0) : 64);
 
-    const int64_t row = (b * p.dim + (dval ? d : 0)) * (int64_t)L;
-    const T* __restrict__ u_row = static_cast<const T*>(p.u) + row;
-    const T* __restrict__ dl_row = static_cast<const T*>(p.delta) + row;
-    const T* __restrict__ z_row = p.z ? static_cast<const T*>(p.z) + row : nullptr;
-    T* __restrict__ y_row = static_cast<T*>(p.y) + row;
-    const T* __restrict__ Bb = static_cast<const T*>(p.Bm) + b * (int64_t)N * L;
-    const T* __restrict__ Cb = static_cast<const T*>(p.Cm) + b * (int64_t)N * L;
-
-    // Padded states (n >= N) keep B = C = 0 for the whole kernel.
-    for (int i = tid; i < TC * NP; i += kThreads) {
-        if (i % NP >= N) {
-            s_B[i] = 0.f;
-            s_C[i] = 0.f;
-        }
-    }
-
-    // Scan-side state: lane owns channel c, states g*NS + s.
+    // ---- scan mapping: lane = channel cs, wave = state group w --------------
+    const int cs = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool sval_d = cs < nrows;
+    const T* brow[NS];
+    const T* crow[NS];
+    bool sval[NS];
     float h[NS], a2[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-        const int n = g * NS + s;
-        const bool ok = dval && n < N;
-        a2[s] = ok ? p.A[d * N + n] * kLog2e : 0.f;
-        h[s] = (ok && p.h0) ? p.h0[(b * p.dim + d) * N + n] : 0.f;
+        const int n = w * NS + s;
+        sval[s] = n < N;
+        const int64_t off = (b * N + (sval[s] ? n : 0)) * (int64_t)L;
+        brow[s] = B_in + off;
+        crow[s] = C_in + off;
+        const bool ok = sval_d && sval[s];
+        a2[s] = ok ? A_in[(d0 + cs) * N + n] * kLog2e : 0.f;
+        h[s] = (ok && h0_in) ? h0_in[(b * dim + d0 + cs) * N + n] : 0.f;
     }
-    const float dskip = (dval && p.Dskip) ? p.Dskip[d] : 0.f;
 
-    // Row-mapping registers: this thread's token run of u / delta / z.
-    const int toff = g * TPT;
-    uint32_t cu[WPT], cdl[WPT], cz[WPT];           // current chunk
-    uint32_t nu[WPT], ndl[WPT], nz[WPT];           // next chunk (prefetch)
-#pragma unroll
-    for (int i = 0; i < WPT; ++i) cz[i] = nz[i] = 0u;
-    uint32_t bcw[2][BC_PER_THREAD][4];             // B / C runs of the next chunk
+    // ---- row mapping: thread -> (row cr, tokens [toff, toff + TPT)) ----------
+    const int cr = tid / SEGS;
+    const int toff = (tid % SEGS) * TPT;
+    const bool rval = cr < nrows;
+    const float dskip = (rval && D_in) ? D_in[d0 + cr] : 0.f;
+    const int64_t blk0 = (b * dim + d0) * (int64_t)L;            // first element of this block's rows
+    const uint32_t blk_bytes = ALIGNED ? (uint32_t)nrows * (uint32_t)L * (uint32_t)sizeof(T) : 0u;
+    const rsrc_t rs_u = make_rsrc(u_in + blk0, blk_bytes);
+    const rsrc_t rs_dl = make_rsrc(dl_in + blk0, blk_bytes);
+    const rsrc_t rs_z = make_rsrc(z_in ? z_in + blk0 : u_in + blk0, z_in ? blk_bytes : 0u);
+    const rsrc_t rs_y = make_rsrc(y_out + blk0, blk_bytes);
+    auto run_off = [&](int t) -> uint32_t {   // byte offset of this thread's run at token t
+        return (t < L) ? ((uint32_t)cr * (uint32_t)L + (uint32_t)t) * (uint32_t)sizeof(T) : kOutOfRange;
+    };
+    const int64_t rrow = (int64_t)(rval ? cr : 0) * L;
+    const T* u_row = u_in + blk0 + rrow;
+    const T* dl_row = dl_in + blk0 + rrow;
+    const T* z_row = z_in ? z_in + blk0 + rrow : nullptr;
+    T* y_row = y_out + blk0 + rrow;
 
-    auto load_chunk = [&](int t0, uint32_t (&wu)[WPT], uint32_t (&wdl)[WPT], uint32_t (&wz)[WPT]) {
-        const int valid = dval ? (L - t0 - toff) : 0;
-        load_run<T, TPT>(u_row + t0 + toff, valid, vec, wu);
-        load_run<T, TPT>(dl_row + t0 + toff, valid, vec, wdl);
-        if (z_row) load_run<T, TPT>(z_row + t0 + toff, valid, vec, wz);
+    // A ring of RING register sets holds the u / delta / z runs of the next
+    // RING-1 chunks, so several chunks of loads are in flight per CU.
+    uint32_t ru[RING][WPT], rdl[RING][WPT], rz[RING][WPT];
 #pragma unroll
-        for (int k = 0; k < BC_PER_THREAD; ++k) {
-            const int r = tid + k * kThreads;
-            const int n = r / (TC / RB);
-            const int tt = (r % (TC / RB)) * RB;
-            const int v = (n < N) ? (L - t0 - tt) : 0;
-            const int64_t off = (int64_t)(n < N ? n : 0) * L + t0 + tt;
-            load_run<T, RB>(Bb + off, v, vec, bcw[0][k]);
-            load_run<T, RB>(Cb + off, v, vec, bcw[1][k]);
+    for (int r = 0; r < RING; ++r)
+#pragma unroll
+        for (int i = 0; i < WPT; ++i) rz[r][i] = 0u;
+    auto load_chunk = [&](int ck, uint32_t (&wu)[WPT], uint32_t (&wdl)[WPT], uint32_t (&wz)[WPT]) {
+        const int t = ck * TC + toff;
+        if constexpr (ALIGNED) {
+            // Unconditional: without z, rs_z is empty and the load returns 0.
+            const uint32_t off = run_off(t);
+            buf_load<WPT>(rs_u, off, wu);
+            buf_load<WPT>(rs_dl, off, wdl);
+            buf_load<WPT>(rs_z, off, wz);
+        } else {
+            const int valid = rval ? (L - t) : 0;
+            load_run<T, TPT>(u_row + t, valid, false, wu);
+            load_run<T, TPT>(dl_row + t, valid, false, wdl);
+            if (z_row) load_run<T, TPT>(z_row + t, valid, false, wz);
         }
     };
 
-    const int nchunks = (L + TC - 1) / TC;
-    load_chunk(0, cu, cdl, cz);
-
-    for (int ck = 0; ck < nchunks; ++ck) {
-        const int t0 = ck * TC;
-        // ---- stage this chunk in LDS -------------------------------------
+    // B / C words of one group, for NS states (scalar registers).  ALIGNED:
+    // a group is either inside the sequence or wholly past it; a group past
+    // it re-reads the last group (finite data times a zero step: no effect).
+    // A state past N gets C = 0, so it adds nothing to y.
+    auto load_bc = [&](int t, uint32_t (&bw)[NS][BCW], uint32_t (&cw)[NS][BCW]) {
 #pragma unroll
-        for (int j = 0; j < TPT; ++j) {
-            const float dlt = Elem<T>::get(cdl, j);
-            s_dd[toff + j][c] = make_float2(dlt, dlt * Elem<T>::get(cu, j));
-        }
-#pragma unroll
-        for (int k = 0; k < BC_PER_THREAD; ++k) {
-            const int r = tid + k * kThreads;
-            const int n = r / (TC / RB);
-            const int tt = (r % (TC / RB)) * RB;
-            if (n < N) {
-#pragma unroll
-                for (int j = 0; j < RB; ++j) {
-                    s_B[(tt + j) * NP + n] = Elem<T>::get(bcw[0][k], j);
-                    s_C[(tt + j) * NP + n] = Elem<T>::get(bcw[1][k], j);
-                }
-            }
-        }
-        // ---- prefetch the next chunk while this one is scanned -------------
-        if (ck + 1 < nchunks) load_chunk(t0 + TC, nu, ndl, nz);
-        __syncthreads();
-
-        // ---- sequential scan of TC tokens, NS states per lane ---------------
-#pragma unroll 4
-        for (int t = 0; t < TC; ++t) {
-            const float2 dd = s_dd[t][c];
-            float bv[NS], cv[NS];
-            const float4* bp = reinterpret_cast<const float4*>(s_B + t * NP + g * NS);
-            const float4* cp = reinterpret_cast<const float4*>(s_C + t * NP + g * NS);
-            if constexpr (NS % 4 == 0) {
-#pragma unroll
-                for (int q = 0; q < NS / 4; ++q) {
-                    const float4 x = bp[q], w = cp[q];
-                    bv[4 * q] = x.x; bv[4 * q + 1] = x.y; bv[4 * q + 2] = x.z; bv[4 * q + 3] = x.w;
-                    cv[4 * q] = w.x; cv[4 * q + 1] = w.y; cv[4 * q + 2] = w.z; cv[4 * q + 3] = w.w;
-                }
+        for (int s = 0; s < NS; ++s) {
+            if constexpr (ALIGNED) {
+                const int tc = t < L ? t : L - G;
+                const uint4 x = *reinterpret_cast<const uint4*>(brow[s] + tc);
+                const uint4 y = *reinterpret_cast<const uint4*>(crow[s] + tc);
+                const bool ok = sval[s];
+                bw[s][0] = x.x; bw[s][1] = x.y; bw[s][2] = x.z; bw[s][3] = x.w;
+                cw[s][0] = ok ? y.x : 0u; cw[s][1] = ok ? y.y : 0u;
+                cw[s][2] = ok ? y.z : 0u; cw[s][3] = ok ? y.w : 0u;
             } else {
-#pragma unroll
-                for (int s = 0; s < NS; ++s) {
-                    bv[s] = s_B[t * NP + g * NS + s];
-                    cv[s] = s_C[t * NP + g * NS + s];
-                }
+                const int valid = sval[s] ? L - t : 0;
+                load_run<T, G>(brow[s] + t, valid, false, bw[s]);
+                load_run<T, G>(crow[s] + t, valid, false, cw[s]);
             }
-            float yp = 0.f;
+        }
+    };
+
+    uint32_t bw[2][NS][BCW], cw[2][NS][BCW];
+    float4 ddr[2][G / 2];
+    const int nchunks = (L + TC - 1) / TC;
+
+    // One token pair (t, t+1) of the group in buffer `buf`, all NS states.
+    auto pair = [&](int buf, int gi, int k) {
+        const float4 q = ddr[buf][k / 2];
+        float y0 = 0.f, y1 = 0.f;
 #pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                const float dA = fast_exp2(dd.x * a2[s]);
-                h[s] = fmaf(dA, h[s], dd.y * bv[s]);
-                yp = fmaf(cv[s], h[s], yp);
+        for (int s = 0; s < NS; ++s) {
+            const float dA = fast_exp2(q.x * a2[s]);
+            h[s] = fmaf(dA, h[s], q.y * Elem<T>::get(bw[buf][s], k));
+            y0 = fmaf(Elem<T>::get(cw[buf][s], k), h[s], y0);
+        }
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const float dA = fast_exp2(q.z * a2[s]);
+            h[s] = fmaf(dA, h[s], q.w * Elem<T>::get(bw[buf][s], k + 1));
+            y1 = fmaf(Elem<T>::get(cw[buf][s], k + 1), h[s], y1);
+        }
+        s_y[w][gi * (G / 2) + k / 2][cs] = make_float2(y0, y1);
+    };
+
+    // One chunk: stage, scan, epilogue.  (cu, cdl, cz) hold this chunk's
+    // runs; (pu, pdl, pz) receive the prefetch of chunk ck + RING - 1.
+    auto chunk = [&](int ck, uint32_t (&cu)[WPT], uint32_t (&cdl)[WPT], uint32_t (&cz)[WPT],
+                     uint32_t (&pu)[WPT], uint32_t (&pdl)[WPT], uint32_t (&pz)[WPT]) {
+        const int t0 = ck * TC;
+        // ---- stage (delta, delta*u) of this chunk in LDS -------------------
+#pragma unroll
+        for (int j = 0; j < TPT; j += 2) {
+            const float e0 = Elem<T>::get(cdl, j), e1 = Elem<T>::get(cdl, j + 1);
+            s_dd[(toff + j) / 2][cr] = make_float4(e0, e0 * Elem<T>::get(cu, j), e1, e1 * Elem<T>::get(cu, j + 1));
+        }
+        if (ALIGNED || ck + RING - 1 < nchunks) load_chunk(ck + RING - 1, pu, pdl, pz);
+        __syncthreads();
+
+        // ---- sequential scan: NGRP groups of G tokens, NS states per lane ---
+        // Scalar and LDS loads share one wait counter and scalar loads
+        // complete out of order, so any wait on it covers every load in
+        // flight.  Hence: issue group gi+1's loads at the start of group gi,
+        // compute group gi with no wait inside, and wait once at its end.
+#pragma unroll
+        for (int k = 0; k < G / 2; ++k) ddr[0][k] = s_dd[k][cs];
+        lgkm_wait_all();
+#pragma unroll
+        for (int gi = 0; gi < NGRP; ++gi) {
+            const int cur = gi & 1, nxt = cur ^ 1;
+            if (gi + 1 < NGRP) {
+                load_bc(t0 + (gi + 1) * G, bw[nxt], cw[nxt]);
+#pragma unroll
+                for (int k = 0; k < G / 2; ++k) ddr[nxt][k] = s_dd[(gi + 1) * (G / 2) + k][cs];
+            } else if (ALIGNED || ck + 1 < nchunks) {
+                load_bc(t0 + TC, bw[nxt], cw[nxt]);
             }
-            s_y[g][t][c] = yp;
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int k = 0; k < G; k += 2) pair(cur, gi, k);
+            lgkm_wait_all();
         }
         __syncthreads();
 
-        // ---- epilogue: combine groups, skip term, gate, store ----------------
-        {
-            float out[TPT];
+        // ---- epilogue: combine waves, skip term, gate, store -----------------
+        float out[TPT];
 #pragma unroll
-            for (int j = 0; j < TPT; ++j) {
-                float acc = 0.f;
+        for (int j = 0; j < TPT; j += 2) {
+            float2 acc = s_y[0][(toff + j) / 2][cr];
 #pragma unroll
-                for (int q = 0; q < NG; ++q) acc += s_y[q][toff + j][c];
-                acc = fmaf(dskip, Elem<T>::get(cu, j), acc);
-                if (z_row) acc *= silu(Elem<T>::get(cz, j));
-                out[j] = acc;
+            for (int q = 1; q < NW; ++q) {
+                const float2 v = s_y[q][(toff + j) / 2][cr];
+                acc.x += v.x;
+                acc.y += v.y;
             }
-            if (dval) store_run<T, TPT>(y_row + t0 + toff, L - t0 - toff, vec, out);
+            float o0 = fmaf(dskip, Elem<T>::get(cu, j), acc.x);
+            float o1 = fmaf(dskip, Elem<T>::get(cu, j + 1), acc.y);
+            if (z_in) {
+                o0 *= silu(Elem<T>::get(cz, j));
+                o1 *= silu(Elem<T>::get(cz, j + 1));
+            }
+            out[j] = o0;
+            out[j + 1] = o1;
+        }
+        if constexpr (ALIGNED) {
+            uint32_t wy[WPT];
+            pack_words<T, TPT>(out, wy);
+            buf_store<WPT>(rs_y, run_off(t0 + toff), wy);
+        } else {
+            if (rval) store_run<T, TPT>(y_row + t0 + toff, L - t0 - toff, false, out);
         }
         // No barrier here: the epilogue reads only s_y, which the next chunk
         // rewrites after its first barrier; the next staging step writes only
-        // s_dd / s_B / s_C, whose last readers finished before the barrier
-        // above.
+        // s_dd, whose last readers finished before the barrier above.
+    };
+
 #pragma unroll
-        for (int i = 0; i < WPT; ++i) {
-            cu[i] = nu[i];
-            cdl[i] = ndl[i];
-            cz[i] = nz[i];
+    for (int r = 0; r < RING - 1; ++r)
+        if (ALIGNED || r < nchunks) load_chunk(r, ru[r], rdl[r], rz[r]);
+    load_bc(0, bw[0], cw[0]);
+    // ALIGNED: the chunk count is rounded up to a multiple of RING and every
+    // load / store is issued unconditionally (past the end they read zero or
+    // are dropped; a zero step leaves h exactly unchanged).  Straight-line
+    // code lets the compiler keep RING-1 chunks of loads in flight; a branch
+    // around a load would make its wait counting fall back to the worst path.
+    for (int ck0 = 0; ck0 < nchunks; ck0 += RING) {
+#pragma unroll
+        for (int r = 0; r < RING; ++r) {
+            const int pr = (r + RING - 1) % RING;
+            if (ALIGNED || ck0 + r < nchunks) chunk(ck0 + r, ru[r], rdl[r], rz[r], ru[pr], rdl[pr], rz[pr]);
         }
     }
 
-    if (p.h_final && dval) {
+    if (hT_out && sval_d) {
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-            const int n = g * NS + s;
-            if (n < N) p.h_final[(b * p.dim + d) * N + n] = h[s];
+            const int n = w * NS + s;
+            if (n < N) hT_out[(b * dim + d0 + cs) * N + n] = h[s];
         }
     }
 }
 
-template <typename T, int NS>
-hipError_t launch_ns(const S6Params& p, hipStream_t stream) {
-    constexpr int CW = 64, TC = 64;
-    const int64_t blocks = ((p.dim + CW - 1) / CW) * p.batch;
-    hipLaunchKernelGGL((s6_scan_kernel<T, CW, NS, TC>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+template <typename T, int NW, int NS, int TC>
+hipError_t launch_cfg(const S6Params& p, hipStream_t stream) {
+    constexpr int RING = 4;
+    const int64_t blocks = ((p.dim + 63) / 64) * p.batch;
+    // The aligned path addresses a block's rows through 32-bit buffer
+    // offsets, and reads B / C in whole 16-byte groups.
+    const bool aligned = (p.L % 8 == 0) && int64_t(64) * p.L * int64_t(sizeof(T)) < (int64_t(1) << 31);
+    auto kern = aligned ? s6_scan_kernel<T, NW, NS, TC, true, RING> : s6_scan_kernel<T, NW, NS, TC, false, RING>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(NW * 64), 0, stream, static_cast<const T*>(p.u),
+                       static_cast<const T*>(p.delta), static_cast<const T*>(p.Bm), static_cast<const T*>(p.Cm),
+                       static_cast<const T*>(p.z), p.A, p.Dskip, p.h0, static_cast<T*>(p.y), p.h_final, p.dim,
+                       p.L, p.N);
     return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_t(const S6Params& p, hipStream_t stream) {
-    if (p.N <= 4) return launch_ns<T, 1>(p, stream);
-    if (p.N <= 8) return launch_ns<T, 2>(p, stream);
-    if (p.N <= 16) return launch_ns<T, 4>(p, stream);
-    if (p.N <= 32) return launch_ns<T, 8>(p, stream);
-    return launch_ns<T, 16>(p, stream);
+    // 8 waves per 64 channels; NS = ceil(N / 8) states per lane.
+    if (p.N <= 8) return launch_cfg<T, 8, 1, 32>(p, stream);
+    if (p.N <= 16) return launch_cfg<T, 8, 2, 32>(p, stream);
+    if (p.N <= 32) return launch_cfg<T, 8, 4, 32>(p, stream);
+    return launch_cfg<T, 8, 8, 32>(p, stream);
 }
 
 __global__ void copy_or_zero_kernel(float* dst, const float* src, int64_t n) {
