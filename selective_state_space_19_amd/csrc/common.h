@@ -60,32 +60,37 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 typedef unsigned int u32x2_t __attribute__((__vector_size__(2 * sizeof(unsigned int))));
 typedef unsigned int u32x4_t __attribute__((__vector_size__(4 * sizeof(unsigned int))));
 
-// Load / store KW 32-bit words (KW = 2 or 4) at byte offset `off`.
-template <int KW>
+// Cache-policy bits of a buffer access: kStream marks data touched once
+// (non-temporal), so streamed outputs do not displace reused lines in L2.
+constexpr int kCached = 0;
+constexpr int kStream = 2;
+
+// Load / store KW 32-bit words (KW = 2, 4 or 8) at byte offset `off`.
+template <int KW, int AUX = kCached>
 __device__ __forceinline__ void buf_load(rsrc_t r, uint32_t off, uint32_t* w) {
     static_assert(KW == 2 || KW == 4 || KW == 8, "2, 4 or 8 words");
     if constexpr (KW == 2) {
-        const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+        const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, AUX);
         w[0] = v[0]; w[1] = v[1];
     } else {
 #pragma unroll
         for (int i = 0; i < KW / 4; ++i) {
-            const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * i, 0, 0);
+            const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * i, 0, AUX);
             w[4 * i] = v[0]; w[4 * i + 1] = v[1]; w[4 * i + 2] = v[2]; w[4 * i + 3] = v[3];
         }
     }
 }
-template <int KW>
+template <int KW, int AUX = kCached>
 __device__ __forceinline__ void buf_store(rsrc_t r, uint32_t off, const uint32_t* w) {
     static_assert(KW == 2 || KW == 4 || KW == 8, "2, 4 or 8 words");
     if constexpr (KW == 2) {
         const u32x2_t v = {w[0], w[1]};
-        __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, AUX);
     } else {
 #pragma unroll
         for (int i = 0; i < KW / 4; ++i) {
             const u32x4_t v = {w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
-            __builtin_amdgcn_raw_buffer_store_b128(v, r, off + 16 * i, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(v, r, off + 16 * i, 0, AUX);
         }
     }
 }

@@ -29,7 +29,8 @@
 //   sums the NW per-wave partial outputs sum_n C*h, adds D*u, gates with
 //   silu(z) and stores y; u and z stay in the registers they were loaded into.
 // - Time is processed in chunks of TC tokens; a register ring keeps the
-//   row loads of the next RING-1 chunks in flight.  Inside a chunk, token
+//   row loads of the next RING-1 chunks in flight; y is stored with the
+//   streaming (non-temporal) cache policy.  Inside a chunk, token
 //   groups (16 bytes of a B / C row) are software-pipelined: the next
 //   group's scalar B / C loads and LDS (delta, delta*u) loads are issued
 //   before the current group is computed, and waited for after it.
@@ -246,7 +247,7 @@ __global__ __launch_bounds__(NW * 64) void s6_scan_kernel(
         if constexpr (ALIGNED) {
             uint32_t wy[WPT];
             pack_words<T, TPT>(out, wy);
-            buf_store<WPT>(rs_y, run_off(t0 + toff), wy);
+            buf_store<WPT, kStream>(rs_y, run_off(t0 + toff), wy);
         } else {
             if (rval) store_run<T, TPT>(y_row + t0 + toff, L - t0 - toff, false, out);
         }
@@ -283,7 +284,7 @@ __global__ __launch_bounds__(NW * 64) void s6_scan_kernel(
 
 template <typename T, int NW, int NS, int TC>
 hipError_t launch_cfg(const S6Params& p, hipStream_t stream) {
-    constexpr int RING = 4;
+    constexpr int RING = 8;
     const int64_t blocks = ((p.dim + 63) / 64) * p.batch;
     // The aligned path addresses a block's rows through 32-bit buffer
     // offsets, and reads B / C in whole 16-byte groups.
