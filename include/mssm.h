@@ -152,9 +152,12 @@ size_t mssm_ssd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads,
  *              owned by the caller; contents on entry are ignored and on exit
  *              are unspecified.  May be NULL if that size is 0.
  *
- * Limits: dtype MSSM_BF16 only; headdim = 64; d_state a multiple of 16 in
- * [16, 256]; chunk in {64, 128, 256}; nheads % ngroups == 0.  Other sizes
- * return MSSM_ERR_UNSUPPORTED.
+ * Limits: dtype MSSM_BF16 only; headdim = 64; d_state in {32, 64, 128,
+ * 256}; chunk in {64, 128, 256}; nheads % ngroups == 0; one batch row of x,
+ * B and C below 2 GiB.  Other sizes return MSSM_ERR_UNSUPPORTED.  Any
+ * seqlen >= 0 is accepted (a last partial chunk is handled).  The chunk is
+ * the length of the blocks of the quadratic (attention-like) form; the
+ * result does not depend on it beyond rounding.
  */
 int mssm_ssd_chunk_fwd(const void* x, const void* dt, const float* A, const void* Bm,
                        const void* Cm, const float* Dskip, const void* z, const float* h0,

@@ -56,6 +56,8 @@ hipError_t launch_s6_scan(const S6Params& p, bool is_bf16, hipStream_t stream);
 hipError_t launch_state_update(const SUParams& p, bool is_bf16, hipStream_t stream);
 hipError_t launch_ssd(const SSDParams& p, hipStream_t stream);
 size_t ssd_workspace_bytes(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int64_t Q);
+// Sizes the SSD kernels implement (headdim, d_state, chunk, 32-bit offsets).
+bool ssd_supported(int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int64_t Q);
 // dst[i] = src ? src[i] : 0 for i < n (used for zero-length sequences).
 hipError_t launch_copy_or_zero(float* dst, const float* src, int64_t n, hipStream_t stream);
 

@@ -147,11 +147,13 @@ int mssm_ssd_chunk_fwd(const void* x, const void* dt, const float* A, const void
                     (long long)nheads, (long long)ngroups);
     if (dtype != MSSM_BF16) return fail(MSSM_ERR_UNSUPPORTED, "%s: only MSSM_BF16 is implemented", fn);
     if (headdim != 64) return fail(MSSM_ERR_UNSUPPORTED, "%s: headdim %lld (only 64)", fn, (long long)headdim);
-    if (d_state < 16 || d_state > 256 || d_state % 16 != 0)
-        return fail(MSSM_ERR_UNSUPPORTED, "%s: d_state %lld (multiple of 16 in [16, 256])", fn, (long long)d_state);
+    if (!(d_state == 32 || d_state == 64 || d_state == 128 || d_state == 256))
+        return fail(MSSM_ERR_UNSUPPORTED, "%s: d_state %lld (32, 64, 128 or 256)", fn, (long long)d_state);
     if (chunk != 64 && chunk != 128 && chunk != 256)
         return fail(MSSM_ERR_UNSUPPORTED, "%s: chunk %lld (64, 128 or 256)", fn, (long long)chunk);
     if (seqlen > INT32_MAX || nheads > INT32_MAX) return fail(MSSM_ERR_UNSUPPORTED, "%s: size too large", fn);
+    if (!mssm::ssd_supported(seqlen, nheads, headdim, d_state, ngroups, chunk))
+        return fail(MSSM_ERR_UNSUPPORTED, "%s: one batch row exceeds 2 GiB of x, B or C", fn);
     if (!prod_ok(batch, seqlen, nheads * headdim, nullptr) || !prod_ok(batch, nheads * headdim, d_state, nullptr) ||
         !prod_ok(batch, seqlen, ngroups * d_state, nullptr))
         return fail(MSSM_ERR_SHAPE, "%s: tensor too large", fn);

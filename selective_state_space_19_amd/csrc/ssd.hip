@@ -1,12 +1,430 @@
-// ssd.hip -- Mamba-2 SSD chunked forward (gfx950).  Placeholder until the
-// MFMA kernels land: reports "not supported".
+// ssd.hip -- Mamba-2 SSD (state space duality), chunked forward, gfx950.
+//
+// What it computes (SSM optimisation catalogue, section 2 "State Space
+// Duality" and section 9 "Chunked Computation"; layout from the Mamba "SKILL"
+// page, "Workflow 3 / Mamba-2"): for batch row b, head h (group g = h / (H/G))
+// and head channel p, with a scalar transition per head,
+//     H[p,n] <- exp(dt_t*A_h) * H[p,n] + dt_t * x_t[p] * B_t[n]
+//     y_t[p]  = (sum_n C_t[n] * H[p,n] + D_h * x_t[p]) * silu(z_t[p])
+// computed chunk by chunk (chunk length Q): within a chunk the output is the
+// masked quadratic form (L o C B^T)(dt o X) plus the carried-in state,
+//     y_i = sum_{j<=i} exp(s_i - s_j) G_ij dt_j x_j + exp(s_i) C_i H_in + D x_i,
+// with s the running sum of dt*A over the chunk and G = C B^T; the state
+// leaving the chunk is exp(s_end) H_in + sum_j exp(s_end - s_j) dt_j B_j x_j.
+//
+// Design:
+// - ssd_prep_kernel, per (b, chunk, group): G = C B^T on MFMA, only the
+//   blocks the causal mask keeps, stored bf16; and B^T (state-major), so the
+//   main kernel's contractions over tokens read their A operands contiguously.
+//   Both depend on the group only, so they are computed once for all heads.
+// - ssd_main_kernel, one workgroup (4 waves) per (b, head, half of headdim):
+//   walks the chunks in order with the fp32 state H (32 x N) held in MFMA
+//   accumulators -- the state never round-trips through HBM.  Per chunk:
+//   running sum s (wave scan), x staged transposed in LDS (plain, and scaled
+//   by dt*beta), then on v_mfma_f32_16x16x32_bf16:
+//     Y_off  = C H_in^T                    (rows scaled by exp(s_i))
+//     Y_diag = (L o G)(dt o X)             (causal 16 x 32 blocks)
+//     H_out  = exp(s_end) H_in + B^T (w o X)
+// - The decay mask is never formed for off-diagonal blocks.  For a row block
+//   I (rows from i0) and an earlier token block J (ending at jend),
+//     exp(s_i - s_j) = exp(s_i - s_i0) * exp(s_i0 - s_jend) * exp(s_jend - s_j),
+//   three factors that are each <= 1 (no overflow however long the chunk):
+//   the first scales output rows, the last is folded into the staged x, and
+//   the middle one is applied to the accumulator per block (Horner form).  The
+//   state update uses the same staged x and per-block factors.  Only the
+//   diagonal 16 x 32 blocks build the mask element by element.
 #include "common.h"
 #include "kernels.h"
 
 namespace mssm {
 
-size_t ssd_workspace_bytes(int64_t, int64_t, int64_t, int64_t, int64_t, int64_t, int64_t) { return 0; }
+namespace {
 
-hipError_t launch_ssd(const SSDParams&, hipStream_t) { return hipErrorNotSupported; }
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kP = 64;     // head dim handled by this kernel
+constexpr int kPW = 32;    // head channels per workgroup (half of kP)
+
+__device__ __forceinline__ f32x4_t mfma16(const u32x4_t a, const u32x4_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                   c, 0, 0, 0);
+}
+__device__ __forceinline__ u32x4_t lds128(const uint32_t* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+__device__ __forceinline__ u32x4_t gload128(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Prep: G = C B^T (causal blocks, bf16) and B^T for one (b, chunk, group) and
+// one quarter of the chunk's rows.  grid = B * nc * G * (Q / 64), 256 threads.
+// ---------------------------------------------------------------------------
+template <int Q, int N>
+__global__ __launch_bounds__(256) void ssd_prep_kernel(const uint16_t* __restrict__ Bm,
+                                                       const uint16_t* __restrict__ Cm,
+                                                       uint16_t* __restrict__ Gw, uint16_t* __restrict__ BTw,
+                                                       int L, int G, int nc) {
+    constexpr int QB = Q / 64;
+    __shared__ uint32_t sB[64][(N + 8) / 2];     // 64 tokens x N, bf16 pairs along n
+
+    const int q4 = blockIdx.x % QB;
+    const int bcg = blockIdx.x / QB;             // (b * nc + c) * G + g
+    const int g = bcg % G;
+    const int c = (bcg / G) % nc;
+    const int64_t b = (bcg / G) / nc;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int kg = lane >> 4, m = lane & 15;
+
+    const uint32_t rowbytes = (uint32_t)G * N * 2u;
+    const rsrc_t rB = make_rsrc(Bm + b * (int64_t)L * G * N, (uint32_t)L * rowbytes);
+    const rsrc_t rC = make_rsrc(Cm + b * (int64_t)L * G * N, (uint32_t)L * rowbytes);
+    auto tok = [&](int tl, int n) -> uint32_t {  // byte offset of (chunk token tl, state n)
+        const int t = c * Q + tl;
+        return (t < L) ? (uint32_t)t * rowbytes + ((uint32_t)g * N + n) * 2u : kOutOfRange;
+    };
+
+    // ---- G rows of row-block I: the causal extent is 32 * (I/2 + 1) columns ---
+    const int I = q4 * 4 + w;
+    uint16_t* Gout = Gw + (int64_t)bcg * Q * Q;
+    const int ncol = 32 * (I / 2 + 1);
+    for (int jt = 0; jt < ncol / 16; ++jt) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int nk = 0; nk < N / 32; ++nk) {
+            const u32x4_t a = gload128(rC, tok(16 * I + m, 32 * nk + 8 * kg));
+            const u32x4_t bb = gload128(rB, tok(16 * jt + m, 32 * nk + 8 * kg));
+            acc = mfma16(a, bb, acc);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            Gout[(16 * I + 4 * kg + r) * Q + 16 * jt + m] = to_bf16(acc[r]);
+    }
+
+    // ---- B^T for this quarter's 64 tokens -------------------------------------
+    for (int idx = tid; idx < 64 * (N / 8); idx += 256) {
+        const int tl = idx / (N / 8), n8 = idx % (N / 8);
+        const u32x4_t v = gload128(rB, tok(64 * q4 + tl, 8 * n8));
+        *reinterpret_cast<u32x4_t*>(&sB[tl][4 * n8]) = v;
+    }
+    __syncthreads();
+    uint16_t* BTout = BTw + (int64_t)bcg * N * Q;
+    const uint16_t* sB16 = reinterpret_cast<const uint16_t*>(&sB[0][0]);
+    constexpr int SBS = N + 8;                   // sB row stride in bf16
+    for (int idx = tid; idx < N * 8; idx += 256) {
+        const int n = idx / 8, tg = idx % 8;
+        uint32_t wv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t lo = sB16[(8 * tg + 2 * e) * SBS + n];
+            const uint32_t hi = sB16[(8 * tg + 2 * e + 1) * SBS + n];
+            wv[e] = lo | (hi << 16);
+        }
+        *reinterpret_cast<uint4*>(BTout + (int64_t)n * Q + 64 * q4 + 8 * tg) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Main: one workgroup per (b, head, half of headdim); chunks in order.
+// ---------------------------------------------------------------------------
+template <int Q, int N>
+__global__ __launch_bounds__(256) void ssd_main_kernel(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ DT, const float* __restrict__ Ah,
+    const uint16_t* __restrict__ Cm, const float* __restrict__ Dh, const uint16_t* __restrict__ Z,
+    const float* __restrict__ h0, uint16_t* __restrict__ Y, float* __restrict__ hT,
+    const uint16_t* __restrict__ Gw, const uint16_t* __restrict__ BTw, int L, int H, int G, int nc) {
+    constexpr int RB = Q / 16;                   // row blocks (16 tokens)
+    constexpr int KB = Q / 32;                   // token blocks (32 tokens) = MFMA K blocks
+    constexpr int NB = N / 16;                   // state row blocks
+    constexpr int NKB = N / 32;                  // state K blocks
+    constexpr int RBW = RB / 4;                  // row blocks per wave
+    constexpr int NBW = (NB + 3) / 4;            // state blocks per wave
+    constexpr int XS = (Q + 8) / 2;              // xT row stride (bf16 pairs)
+    constexpr int HS = (N + 8) / 2;              // Hb row stride (bf16 pairs)
+    static_assert(Q % 64 == 0 && N % 32 == 0, "Q multiple of 64, N multiple of 32");
+
+    __shared__ float s_s[Q];                     // running sum of dt*A*log2(e) within the chunk
+    __shared__ float s_dt[Q];
+    __shared__ float s_wsum[4];
+    __shared__ uint32_t xT[kPW][XS];             // x^T, bf16 pairs along tokens
+    __shared__ uint32_t xsT[kPW][XS];            // (dt * beta * x)^T
+    __shared__ uint32_t Hb[kPW][HS];             // carried-in state, bf16 pairs along n
+
+    const int ph = blockIdx.x & 1;
+    const int bh = blockIdx.x >> 1;
+    const int h = bh % H;
+    const int64_t b = bh / H;
+    const int g = h / (H / G);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kg = lane >> 4, m = lane & 15;
+
+    const float a_h = Ah[h] * kLog2e;
+    const float dskip = Dh ? Dh[h] : 0.f;
+
+    // Buffers over batch row b (32-bit offsets; the host checks the sizes).
+    const uint32_t xrow = (uint32_t)H * kP * 2u;               // bytes per token of x / y / z
+    const rsrc_t rX = make_rsrc(X + b * (int64_t)L * H * kP, (uint32_t)L * xrow);
+    const rsrc_t rY = make_rsrc(Y + b * (int64_t)L * H * kP, (uint32_t)L * xrow);
+    const rsrc_t rZ = make_rsrc(Z ? Z + b * (int64_t)L * H * kP : X, Z ? (uint32_t)L * xrow : 0u);
+    const rsrc_t rDT = make_rsrc(DT + b * (int64_t)L * H, (uint32_t)L * H * 2u);
+    const uint32_t crow = (uint32_t)G * N * 2u;
+    const rsrc_t rC = make_rsrc(Cm + b * (int64_t)L * G * N, (uint32_t)L * crow);
+
+    // ---- state accumulators: tiles (nb = w + 4*k, p-tile pt) ------------------
+    // C layout of a 16x16 tile: lane holds rows 4*kg + r (r < 4), column m.
+    f32x4_t accH[NBW][2];
+#pragma unroll
+    for (int k = 0; k < NBW; ++k)
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt) {
+            const int nb = w + 4 * k;
+            f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+            if (h0 && nb < NB) {
+                const int p = kPW * ph + 16 * pt + m;
+                const float4 q = *reinterpret_cast<const float4*>(
+                    h0 + (((b * H + h) * kP + p) * (int64_t)N + 16 * nb + 4 * kg));
+                v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+            }
+            accH[k][pt] = v;
+        }
+
+    for (int c = 0; c < nc; ++c) {
+        const int64_t bcg = ((int64_t)b * nc + c) * G + g;
+        // ---- phase A: running sum s_t (log2 units), dt_t ----------------------
+        {
+            float dtv = 0.f, v = 0.f;
+            if (tid < Q) {
+                const int t = c * Q + tid;
+                const uint32_t off = (t < L) ? ((uint32_t)t * H + h) * 2u : kOutOfRange;
+                dtv = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rDT, off, 0, 0) << 16);
+                v = dtv * a_h;
+            }
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const float o = __shfl_up(v, d, 64);
+                if (lane >= d) v += o;
+            }
+            if (lane == 63) s_wsum[w] = v;
+            __syncthreads();
+            float base = 0.f;
+            for (int q = 0; q < w; ++q) base += s_wsum[q];
+            if (tid < Q) {
+                s_s[tid] = v + base;
+                s_dt[tid] = dtv;
+            }
+            __syncthreads();
+        }
+        // ---- phase B: stage x^T and (dt*beta*x)^T; write the carried-in state ---
+        for (int it = tid; it < (Q / 2) * 2; it += 256) {
+            const int tp = it % (Q / 2), pg = it / (Q / 2);
+            const int t0 = 2 * tp, t1 = 2 * tp + 1;
+            const int p0 = kPW * ph + 16 * pg;
+            uint32_t w0[8], w1[8];
+            {
+                const int ta = c * Q + t0, tb = c * Q + t1;
+                const uint32_t oa = (ta < L) ? (uint32_t)ta * xrow + ((uint32_t)h * kP + p0) * 2u : kOutOfRange;
+                const uint32_t ob = (tb < L) ? (uint32_t)tb * xrow + ((uint32_t)h * kP + p0) * 2u : kOutOfRange;
+                buf_load<8>(rX, oa, w0);
+                buf_load<8>(rX, ob, w1);
+            }
+            const float sc0 = s_dt[t0] * fast_exp2(s_s[(t0 | 31)] - s_s[t0]);
+            const float sc1 = s_dt[t1] * fast_exp2(s_s[(t1 | 31)] - s_s[t1]);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const uint32_t a = (e & 1) ? (w0[e >> 1] >> 16) : (w0[e >> 1] & 0xffffu);
+                const uint32_t bb = (e & 1) ? (w1[e >> 1] >> 16) : (w1[e >> 1] & 0xffffu);
+                xT[16 * pg + e][tp] = a | (bb << 16);
+                xsT[16 * pg + e][tp] = pack_bf16x2(__uint_as_float(a << 16) * sc0, __uint_as_float(bb << 16) * sc1);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < NBW; ++k) {
+            const int nb = w + 4 * k;
+            if (nb < NB) {
+#pragma unroll
+                for (int pt = 0; pt < 2; ++pt) {
+                    const int p = 16 * pt + m;
+                    const f32x4_t v = accH[k][pt];
+                    *reinterpret_cast<uint2*>(&Hb[p][(16 * nb + 4 * kg) / 2]) =
+                        make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- phase C1: outputs for row blocks I = w + 4*rb ------------------------
+        const uint16_t* Gc = Gw + bcg * Q * Q;
+        auto send = [&](int J) { return s_s[32 * J + 31]; };   // s at the end of token block J
+#pragma unroll 1
+        for (int rb = 0; rb < RBW; ++rb) {
+            const int I = w + 4 * rb;
+            const int i0 = 16 * I;
+            f32x4_t off_[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+            f32x4_t dg[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+            f32x4_t yo[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+            const int Jd = I / 2;                       // the token block holding row block I
+            // off-diagonal token blocks, Horner over the per-block decay
+            for (int J = 0; J < Jd; ++J) {
+                if (J > 0) {
+                    const float r = fast_exp2(send(J) - send(J - 1));
+#pragma unroll
+                    for (int pt = 0; pt < 2; ++pt) off_[pt] *= r;
+                }
+                const u32x4_t a = *reinterpret_cast<const u32x4_t*>(Gc + (i0 + m) * Q + 32 * J + 8 * kg);
+#pragma unroll
+                for (int pt = 0; pt < 2; ++pt)
+                    off_[pt] = mfma16(a, lds128(&xsT[16 * pt + m][16 * J + 4 * kg]), off_[pt]);
+            }
+            // diagonal token block: explicit mask, dt folded in, plain x
+            {
+                const int i = i0 + m;
+                const float si = s_s[i];
+                const u32x4_t gv = *reinterpret_cast<const u32x4_t*>(Gc + i * Q + 32 * Jd + 8 * kg);
+                uint32_t av[4];
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    const int j = 32 * Jd + 8 * kg + e;
+                    const uint32_t gw = gv[e / 2];
+                    const float v0 = (j <= i) ? __uint_as_float(gw << 16) * s_dt[j] * fast_exp2(si - s_s[j]) : 0.f;
+                    const float v1 = (j + 1 <= i) ? __uint_as_float(gw & 0xffff0000u) * s_dt[j + 1] *
+                                                        fast_exp2(si - s_s[j + 1]) : 0.f;
+                    av[e / 2] = pack_bf16x2(v0, v1);
+                }
+                const u32x4_t a = {av[0], av[1], av[2], av[3]};
+#pragma unroll
+                for (int pt = 0; pt < 2; ++pt) dg[pt] = mfma16(a, lds128(&xT[16 * pt + m][16 * Jd + 4 * kg]), dg[pt]);
+            }
+            // carried-in state: C rows times H_in^T
+            {
+                const int t = c * Q + i0 + m;
+#pragma unroll
+                for (int nk = 0; nk < NKB; ++nk) {
+                    const uint32_t o = (t < L) ? (uint32_t)t * crow + ((uint32_t)g * N + 32 * nk + 8 * kg) * 2u
+                                               : kOutOfRange;
+                    const u32x4_t a = gload128(rC, o);
+#pragma unroll
+                    for (int pt = 0; pt < 2; ++pt) yo[pt] = mfma16(a, lds128(&Hb[16 * pt + m][16 * nk + 4 * kg]), yo[pt]);
+                }
+            }
+            // combine, skip, gate, store
+            const float si0 = s_s[i0];
+            const float gam = (Jd > 0) ? fast_exp2(si0 - send(Jd - 1)) : 0.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = i0 + 4 * kg + r;
+                const float si = s_s[i];
+                const float al = fast_exp2(si - si0) * gam;
+                const float ei = fast_exp2(si);
+                const int t = c * Q + i;
+#pragma unroll
+                for (int pt = 0; pt < 2; ++pt) {
+                    const int p = 16 * pt + m;
+                    const uint32_t xw = xT[p][i >> 1];
+                    const float xv = __uint_as_float((i & 1) ? (xw & 0xffff0000u) : (xw << 16));
+                    float yv = al * off_[pt][r] + dg[pt][r] + ei * yo[pt][r] + dskip * xv;
+                    const uint32_t o = (t < L) ? (uint32_t)t * xrow + ((uint32_t)h * kP + kPW * ph + p) * 2u
+                                               : kOutOfRange;
+                    if (Z) yv *= silu(__uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rZ, o, 0, 0) << 16));
+                    __builtin_amdgcn_raw_buffer_store_b16(to_bf16(yv), rY, o, 0, kStream);
+                }
+            }
+        }
+
+        // ---- phase C2: state update over the chunk's token blocks ----------------
+        {
+            const uint16_t* BTc = BTw + bcg * N * Q;
+#pragma unroll 1
+            for (int J = 0; J < KB; ++J) {
+                const float r = fast_exp2(send(J) - (J > 0 ? send(J - 1) : 0.f));
+#pragma unroll
+                for (int k = 0; k < NBW; ++k) {
+                    const int nb = w + 4 * k;
+                    if (nb < NB) {
+                        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(BTc + (16 * nb + m) * Q + 32 * J + 8 * kg);
+#pragma unroll
+                        for (int pt = 0; pt < 2; ++pt) {
+                            accH[k][pt] *= r;
+                            accH[k][pt] = mfma16(a, lds128(&xsT[16 * pt + m][16 * J + 4 * kg]), accH[k][pt]);
+                        }
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    if (hT) {
+#pragma unroll
+        for (int k = 0; k < NBW; ++k) {
+            const int nb = w + 4 * k;
+            if (nb < NB) {
+#pragma unroll
+                for (int pt = 0; pt < 2; ++pt) {
+                    const int p = kPW * ph + 16 * pt + m;
+                    const f32x4_t v = accH[k][pt];
+                    *reinterpret_cast<float4*>(hT + (((b * H + h) * kP + p) * (int64_t)N + 16 * nb + 4 * kg)) =
+                        make_float4(v[0], v[1], v[2], v[3]);
+                }
+            }
+        }
+    }
+}
+
+template <int Q, int N>
+hipError_t launch_qn(const SSDParams& p, hipStream_t stream) {
+    const int nc = (p.L + Q - 1) / Q;
+    uint16_t* Gw = static_cast<uint16_t*>(p.workspace);
+    uint16_t* BTw = Gw + (int64_t)p.batch * nc * p.G * Q * Q;
+    const int64_t prep_blocks = p.batch * nc * p.G * (Q / 64);
+    hipLaunchKernelGGL((ssd_prep_kernel<Q, N>), dim3((unsigned)prep_blocks), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(p.Bm), static_cast<const uint16_t*>(p.Cm), Gw, BTw, p.L, p.G, nc);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t blocks = p.batch * p.H * 2;
+    hipLaunchKernelGGL((ssd_main_kernel<Q, N>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(p.x), static_cast<const uint16_t*>(p.dt), p.A,
+                       static_cast<const uint16_t*>(p.Cm), p.Dskip, static_cast<const uint16_t*>(p.z), p.h0,
+                       static_cast<uint16_t*>(p.y), p.h_final, Gw, BTw, p.L, p.H, p.G, nc);
+    return hipGetLastError();
+}
+
+template <int Q>
+hipError_t launch_q(const SSDParams& p, hipStream_t stream) {
+    switch (p.N) {
+        case 32: return launch_qn<Q, 32>(p, stream);
+        case 64: return launch_qn<Q, 64>(p, stream);
+        case 128: return launch_qn<Q, 128>(p, stream);
+        case 256: return launch_qn<Q, 256>(p, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+size_t ssd_workspace_bytes(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int64_t Q) {
+    (void)H;
+    (void)P;
+    if (Q <= 0) return 0;
+    const int64_t nc = (L + Q - 1) / Q;
+    return (size_t)(batch * nc * G * Q * (Q + N) * 2);
+}
+
+bool ssd_supported(int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int64_t Q) {
+    if (P != kP) return false;
+    if (!(N == 32 || N == 64 || N == 128 || N == 256)) return false;
+    if (!(Q == 64 || Q == 128 || Q == 256)) return false;
+    const int64_t lim = int64_t(1) << 31;
+    // 32-bit buffer offsets over one batch row
+    return L * H * P * 2 < lim && L * G * N * 2 < lim && L * H * 2 < lim;
+}
+
+hipError_t launch_ssd(const SSDParams& p, hipStream_t stream) {
+    switch (p.Q) {
+        case 64: return launch_q<64>(p, stream);
+        case 128: return launch_q<128>(p, stream);
+        case 256: return launch_q<256>(p, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
 
 }  // namespace mssm

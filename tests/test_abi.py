@@ -83,6 +83,7 @@ def test_ssd_argument_errors(lib):
     assert _ssd(lib, dtype=0) == ERR_UNSUP
     assert _ssd(lib, P=32) == ERR_UNSUP
     assert _ssd(lib, N=24) == ERR_UNSUP
+    assert _ssd(lib, N=16) == ERR_UNSUP
     assert _ssd(lib, Q=100) == ERR_UNSUP
     assert _ssd(lib, dtype=9) == ERR_DTYPE
     assert _ssd(lib, h0=MISALIGNED) == ERR_ALIGN
