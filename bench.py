@@ -3,18 +3,19 @@
 
 Headline: mssm_selective_scan_fwd on the Mamba-1.4B layer shape (batch 4,
 d_inner 4096, seqlen 8192, d_state 16; u, delta, B, C, z in bf16; A, D fp32;
-fp32 state; final state written), inputs resident in HBM.  A "step" is one
-call of the scan over that batch.  `value` is the effective HBM bandwidth:
-algorithmic bytes (every input read once, every output written once) divided
-by the time per step.  Also reported: tokens-ch/s (batch*seqlen*d_inner per
-second), the roofline of the scan kernel, the fp64 CPU oracle timed on a
-bounded sample of the same workload, and the other two entry points (decode
-step on the Mamba-2.8B shape, Mamba-2 SSD) as secondary lines inside the
-same JSON object.
+fp32 state; z gate, D skip, final state written), inputs resident in HBM.
+A "step" is one call of the scan over that batch.  `value` is the effective
+HBM bandwidth: algorithmic bytes (every input read once, every output
+written once) divided by the time per step; also reported: tokens-ch/s
+(batch*seqlen*d_inner per second), the roofline of the scan kernel, the
+fp64 CPU oracle timed on the same workload, and the other two entry points
+(decode step at the Mamba-2.8B shape, Mamba-2 SSD) inside the same object.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--only s6,decode,ssd,copy]
 
-Prints exactly one JSON line on stdout; progress goes to stderr.
+Prints exactly one JSON line on stdout; progress goes to stderr.  `--only`
+restricts the run (for profiling); `copy` times a plain 1 GiB device copy,
+the reference used to scale the HBM byte counters.
 """
 from __future__ import annotations
 
@@ -30,9 +31,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "selective-scan effective HBM GB/s (% of peak) + B·L·D_inner tokens-ch/s"
-HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
-# Non-packed fp32 VALU issue rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz.
-VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9
+HBM_PEAK_GBS = 8000.0                  # MI355X HBM3E, 8 TB/s
+# fp32 VALU issue rate without packed math: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz.
+VALU_LANE_INSTR = 256 * 4 * 16 * 2.4e9
+# One S6 state element: v_mul (delta*A), v_exp, v_mul (delta*u*B), v_fma (h), v_fma (y):
+# 5 VALU instructions, counted as 7 flop (mul 1, exp 1, fma 2).
+S6_INSTR_PER_ELEM, S6_FLOP_PER_ELEM = 5, 7
+S6_ALU_PEAK_TFLOPS = VALU_LANE_INSTR / S6_INSTR_PER_ELEM * S6_FLOP_PER_ELEM / 1e12   # 55.05
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -41,8 +46,8 @@ def log(*a):
 
 
 def s6_bytes(batch, dim, L, N, esize, gate=True, skip=True, h0=False, final=True):
-    """Algorithmic HBM bytes of one scan: u, delta, (z), y once each; B, C;
-    A; (D); (h0); (h_final)."""
+    """Algorithmic HBM bytes of one scan: u, delta, (z), y once each; B, C; A;
+    (D); (h0); (h_final)."""
     per_tok = (3 + (1 if gate else 0)) * batch * dim * L * esize
     bc = 2 * batch * N * L * esize
     small = dim * N * 4 + (dim * 4 if skip else 0)
@@ -101,15 +106,19 @@ def time_launches(fn, steps, warmup, stream):
     return evs[0].elapsed_time(evs[-1]), per
 
 
-def bench_s6(args, wl):
+# --------------------------------------------------------------------------
+# S6 scan (headline)
+# --------------------------------------------------------------------------
+def bench_s6(args):
     import torch
     import selective_state_space_19_amd as mssm
     from selective_state_space_19_amd import synth
+    wl = synth.WORKLOADS["s6_mamba1p4b_bf16"]
     s = wl.shape
-    log(f"[bench] generating {wl.name} inputs {s} ({wl.dtype}) ...")
+    log(f"[bench] s6: generating {wl.name} inputs {s} ({wl.dtype})")
     t0 = time.time()
     inp = synth.s6_inputs(**s, dtype=wl.dtype, seed=wl.seed)
-    log(f"[bench] generated in {time.time() - t0:.1f}s; uploading")
+    log(f"[bench] s6: generated in {time.time() - t0:.1f}s; uploading")
     d = {k: to_dev(inp[k]) for k in ("u", "delta", "A", "B", "C", "D", "z", "h0")}
     y = torch.empty_like(d["u"])
     hf = torch.empty((s["batch"], s["d_inner"], s["d_state"]), dtype=torch.float32, device="cuda")
@@ -119,13 +128,12 @@ def bench_s6(args, wl):
         mssm.selective_scan(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["h0"],
                             out=y, h_final=hf, stream=stream)
 
-    log(f"[bench] timing {args.steps} steps after {args.warmup} warm-up")
+    log(f"[bench] s6: timing {args.steps} steps after {args.warmup} warm-up")
+    torch.cuda.synchronize()
     total_ms, per = time_launches(step, args.steps, args.warmup, stream)
-    esize = 2 if wl.dtype == "bf16" else 4
-    nbytes = s6_bytes(s["batch"], s["d_inner"], s["seqlen"], s["d_state"], esize)
-    ms = total_ms / args.steps
-    kern_ms = float(np.mean(per))
-    return dict(inp=inp, y=y, hf=hf, ms=ms, per=per, kern_ms=kern_ms, bytes=nbytes)
+    nbytes = s6_bytes(s["batch"], s["d_inner"], s["seqlen"], s["d_state"], 2 if wl.dtype == "bf16" else 4)
+    return dict(wl=wl, inp=inp, y=y, hf=hf, ms=total_ms / args.steps, per=per,
+                kern_ms=float(np.mean(per)), bytes=nbytes)
 
 
 def parity_sample(inp, y, hf, rows=32, seed=0):
@@ -147,38 +155,35 @@ def parity_sample(inp, y, hf, rows=32, seed=0):
                 ok=bool(ey <= 2e-2 and eh <= 2e-2))
 
 
-def cpu_baseline(inp, target_s=12.0):
-    """Time the fp64 oracle (as it stands) on a bounded sample of the
-    benchmarked workload: the first k channels of batch row 0, full length;
-    k grows until the run takes about target_s seconds of wall time."""
+def cpu_baseline(inp, budget_s=30.0):
+    """The fp64 oracle, as it stands, on the benchmarked workload: whole batch
+    rows, as many as fit in about budget_s seconds of wall time (all of them
+    on a host with enough cores)."""
     import oracle
     from selective_state_space_19_amd import synth
     nth = oracle.default_threads()
     dt = inp["dtype"]
     bsz, dim, L = inp["u"].shape
     N = inp["A"].shape[1]
-    B = synth.widen(inp["B"][0:1], dt)
-    C = synth.widen(inp["C"][0:1], dt)
-
-    def run(k):
-        sub = {key: synth.widen(inp[key][0:1, :k], dt) for key in ("u", "delta", "z")}
+    used, rows = 0.0, 0
+    for b in range(bsz):
+        sub = {k: synth.widen(inp[k][b:b + 1], dt) for k in ("u", "delta", "z", "B", "C")}
         t = time.perf_counter()
-        oracle.s6_scan(sub["u"], sub["delta"], inp["A"][:k], B, C, inp["D"][:k], sub["z"], nthreads=nth)
-        return time.perf_counter() - t
-
-    k = min(dim, max(nth, 64))
-    el = run(k)
-    while el < target_s / 4 and k < dim:
-        k = min(dim, int(k * max(2.0, min(8.0, target_s / max(el, 1e-3)))))
-        el = run(k)
-    esize = 2 if dt == "bf16" else 4
-    nbytes = s6_bytes(1, k, L, N, esize)
-    return {"value": nbytes / el / 1e9, "unit": "GB/s", "cores": nth, "kind": "oracle",
-            "sample": f"batch row 0, channels 0..{k - 1} of {dim}, all {L} tokens, d_state {N} "
-                      f"({k * L} tokens-ch, fp64 sequential recurrence, {el:.2f} s wall)",
-            "tokens_ch_per_s": k * L / el, "seconds": el}
+        oracle.s6_scan(sub["u"], sub["delta"], inp["A"], sub["B"], sub["C"], inp["D"], sub["z"], nthreads=nth)
+        used += time.perf_counter() - t
+        rows += 1
+        if used * (rows + 1) / rows > budget_s:
+            break
+    nbytes = s6_bytes(rows, dim, L, N, 2 if dt == "bf16" else 4)
+    return {"value": nbytes / used / 1e9, "unit": "GB/s", "cores": nth, "kind": "oracle",
+            "sample": f"{rows} of {bsz} batch rows of the benchmarked workload ({rows * dim} channels x "
+                      f"{L} tokens, d_state {N}), fp64 sequential recurrence, {used:.2f} s wall",
+            "tokens_ch_per_s": rows * dim * L / used, "seconds": used}
 
 
+# --------------------------------------------------------------------------
+# Decode (Mamba-2.8B shape, 256 tokens)
+# --------------------------------------------------------------------------
 def bench_decode(args):
     import torch
     import selective_state_space_19_amd as mssm
@@ -189,50 +194,63 @@ def bench_decode(args):
     log(f"[bench] decode: generating {steps} tokens of inputs")
     init = synth.decode_initial(bsz, dim, N, seed=wl.seed)
     toks = [synth.decode_step(init, i, bsz, dim, N, dtype=wl.dtype, seed=wl.seed) for i in range(steps)]
-    dev_toks = [{k: to_dev(t[k]) for k in ("u", "delta", "z", "B", "C")} for t in toks]
+    dtk = [{k: to_dev(t[k]) for k in ("u", "delta", "z", "B", "C")} for t in toks]
     A, D = to_dev(init["A"]), to_dev(init["D"])
-    # 16 state buffers (16 x 21 MB > 256 MB Infinity Cache): step i uses
-    # buffer i % 16, as 16 layers would, so state traffic reaches HBM.
+    # 16 state buffers (16 x 21 MB > the 256 MB Infinity Cache): token i uses
+    # buffer i % 16, as 16 layers would, so the state traffic reaches HBM.
     K = 16
     states = [to_dev(init["state"]) for _ in range(K)]
     ys = [torch.empty((bsz, dim), dtype=torch.bfloat16, device="cuda") for _ in range(steps)]
     stream = torch.cuda.current_stream()
+    nb = decode_bytes(bsz, dim, N, 2)
 
     def run_all(rotate):
         for i in range(steps):
-            t = dev_toks[i]
+            t = dtk[i]
             mssm.state_update(states[i % K] if rotate else states[0], t["u"], t["delta"], A, t["B"], t["C"], D,
                               t["z"], out=ys[i], stream=stream)
 
-    res = {}
+    res = {"workload": f"{wl.name}: batch {bsz}, d_inner {dim}, d_state {N}, bf16, {steps} tokens",
+           "bytes_per_step": nb}
     for label, rot in (("cold_16_buffers", True), ("hot_single_buffer", False)):
-        total, per = time_launches(lambda: run_all(rot), 3, 1, stream)
-        per_step_ms = total / 3 / steps
-        nb = decode_bytes(bsz, dim, N, 2)
-        res[label] = dict(us_per_step_wall=per_step_ms * 1e3, GBs=nb / (per_step_ms * 1e-3) / 1e9)
-    # kernel-only per-step time via events around single launches (cold set)
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
-    for i in range(steps):
-        t = dev_toks[i]
-        evs[2 * i].record(stream)
-        mssm.state_update(states[i % K], t["u"], t["delta"], A, t["B"], t["C"], D, t["z"], out=ys[i], stream=stream)
-        evs[2 * i + 1].record(stream)
-    torch.cuda.synchronize()
-    per = [evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(steps)]
-    nb = decode_bytes(bsz, dim, N, 2)
-    res["cold_event_us_per_step"] = float(np.median(per)) * 1e3
-    res["cold_event_GBs"] = nb / (np.median(per) * 1e-3) / 1e9
-    res["bytes_per_step"] = nb
-    res["workload"] = f"{wl.name}: batch {bsz}, d_inner {dim}, d_state {N}, bf16, {steps} tokens"
+        total, _ = time_launches(lambda: run_all(rot), 3, 1, stream)
+        us = total / 3 / steps * 1e3
+        res[label + "_launches"] = {"us_per_step": us, "GBs": nb / (us * 1e-6) / 1e9}
+    # The same 256 tokens captured in one HIP graph (launch overhead removed).
+    try:
+        for label, rot in (("cold_16_buffers", True), ("hot_single_buffer", False)):
+            g = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                run_all(rot)
+            torch.cuda.current_stream().wait_stream(side)
+            with torch.cuda.graph(g):
+                for i in range(steps):
+                    t = dtk[i]
+                    mssm.state_update(states[i % K] if rot else states[0], t["u"], t["delta"], A, t["B"], t["C"],
+                                      D, t["z"], out=ys[i])
+            total, _ = time_launches(g.replay, 5, 2, torch.cuda.current_stream())
+            us = total / 5 / steps * 1e3
+            res[label + "_graph"] = {"us_per_step": us, "GBs": nb / (us * 1e-6) / 1e9,
+                                     "hbm_frac": nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+    except Exception as e:  # reported, not hidden
+        res["graph_error"] = repr(e)
+    res["tokens_ch_per_s_cold_graph"] = (bsz * dim / (res["cold_16_buffers_graph"]["us_per_step"] * 1e-6)
+                                         if "cold_16_buffers_graph" in res else None)
     return res
 
 
+# --------------------------------------------------------------------------
+# Mamba-2 SSD
+# --------------------------------------------------------------------------
 def bench_ssd(args):
     import torch
     import selective_state_space_19_amd as mssm
     from selective_state_space_19_amd import synth
     wl = synth.WORKLOADS["ssd_mamba2_bf16"]
     s = wl.shape
+    log("[bench] ssd: generating inputs")
     inp = synth.ssd_inputs(s["batch"], s["seqlen"], s["nheads"], s["headdim"], s["d_state"], s["ngroups"],
                            dtype=wl.dtype, seed=wl.seed)
     d = {k: to_dev(inp[k]) for k in ("x", "dt", "A", "B", "C", "D")}
@@ -250,12 +268,25 @@ def bench_ssd(args):
     ms = total / 20
     nb = ssd_bytes(s["batch"], s["seqlen"], s["nheads"], s["headdim"], s["d_state"], s["ngroups"], 2)
     fl = ssd_flops(s["batch"], s["seqlen"], s["nheads"], s["headdim"], s["d_state"], s["ngroups"], s["chunk"])
-    return dict(workload=f"{wl.name}: batch 4, seqlen 4096, 32 heads x 64, d_state 128, chunk 256, bf16",
+    return dict(workload=f"{wl.name}: batch 4, seqlen 4096, 32 heads x 64, d_state 128, ngroups 1, chunk 256, bf16",
                 us=ms * 1e3, GBs=nb / (ms * 1e-3) / 1e9, hbm_frac=nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                mfma_TFLOPs=fl / (ms * 1e-3) / 1e12,
-                mfma_frac=fl / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                mfma_TFLOPs=fl / (ms * 1e-3) / 1e12, mfma_frac=fl / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                 tokens_ch_per_s=s["batch"] * s["seqlen"] * s["nheads"] * s["headdim"] / (ms * 1e-3),
-                algorithmic_bytes=nb, algorithmic_flops=fl)
+                algorithmic_bytes=nb, algorithmic_flops=fl, workspace_bytes=need)
+
+
+def bench_copy(args):
+    """A plain 1 GiB device-to-device copy: the reference for scaling the
+    FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    stream = torch.cuda.current_stream()
+    total, _ = time_launches(lambda: b.copy_(a), 5, 2, stream)
+    ms = total / 5
+    return {"bytes_read": n, "bytes_written": n, "ms": ms, "GBs": 2 * n / (ms * 1e-3) / 1e9}
 
 
 def main():
@@ -263,70 +294,71 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", default="s6,decode,ssd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(the scan shards by batch/channel with no exchange; see DESIGN.md).", file=sys.stderr)
+              "(the scan shards by batch / channel with no exchange).", file=sys.stderr)
         sys.exit(2)
+    parts = set(args.only.split(","))
 
     import torch
-    from selective_state_space_19_amd import synth
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    wl = synth.WORKLOADS["s6_mamba1p4b_bf16"]
-    r = bench_s6(args, wl)
-    s = wl.shape
-    tok = s["batch"] * s["seqlen"] * s["d_inner"]
-    gbs = r["bytes"] / (r["ms"] * 1e-3) / 1e9
-    kern_gbs = r["bytes"] / (r["kern_ms"] * 1e-3) / 1e9
-    elems = tok * s["d_state"]
-    out = {
-        "metric": METRIC,
-        "value": round(gbs, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(r["ms"], 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded Mamba-shaped inputs, see DESIGN.md)",
-        "config": {"workload": f"{wl.name}: S6 selective scan, batch {s['batch']}, d_inner {s['d_inner']}, "
-                               f"seqlen {s['seqlen']}, d_state {s['d_state']}, bf16 in / fp32 state, "
-                               f"z gate, D skip, h_final out",
-                   "batch": s["batch"], "d_inner": s["d_inner"], "seqlen": s["seqlen"],
-                   "d_state": s["d_state"]},
-        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-        "tokens_ch_per_s": tok / (r["ms"] * 1e-3),
-        "roofline": {"bound": "hbm", "achieved": round(kern_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(kern_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "s6_scan_kernel", "algorithmic_bytes_per_launch": r["bytes"],
-                     "avg_launch_ms": round(r["kern_ms"], 5)},
-        "alu": {"state_updates_per_s": elems / (r["kern_ms"] * 1e-3),
-                "valu_lane_instr_per_update": 5,
-                "valu_frac_if_exp_full_rate": elems * 5 / (r["kern_ms"] * 1e-3) / VALU_LANE_OPS},
-    }
-    if not args.no_parity:
-        log("[bench] parity sample vs the fp64 oracle")
-        out["parity_sample"] = parity_sample(r["inp"], r["y"], r["hf"])
-    if not args.no_cpu_baseline:
-        log("[bench] cpu baseline (oracle on a sample)")
-        out["cpu_baseline"] = cpu_baseline(r["inp"])
-    if not args.no_secondary:
+
+    out = {}
+    if "s6" in parts:
+        r = bench_s6(args)
+        s = r["wl"].shape
+        tok = s["batch"] * s["seqlen"] * s["d_inner"]
+        elems = tok * s["d_state"]
+        gbs = r["bytes"] / (r["ms"] * 1e-3) / 1e9
+        kern_s = r["kern_ms"] * 1e-3
+        alu_tflops = elems * S6_FLOP_PER_ELEM / kern_s / 1e12
+        out.update({
+            "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(r["ms"], 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded Mamba-shaped inputs)",
+            "config": {"workload": f"{r['wl'].name}: S6 selective scan, batch {s['batch']}, d_inner {s['d_inner']}, "
+                                   f"seqlen {s['seqlen']}, d_state {s['d_state']}, bf16 in / fp32 state, z gate, "
+                                   f"D skip, h_final out",
+                       "batch": s["batch"], "d_inner": s["d_inner"], "seqlen": s["seqlen"], "d_state": s["d_state"]},
+            "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+            "tokens_ch_per_s": tok / (r["ms"] * 1e-3),
+            # The scan is bound by VALU work, not HBM: 5 VALU instructions per
+            # state element take longer at peak (273 us here) than its bytes
+            # (135 us at 8 TB/s).  Peak = non-packed fp32 VALU issue rate.
+            "roofline": {"bound": "alu", "achieved": round(alu_tflops, 3), "peak": round(S6_ALU_PEAK_TFLOPS, 3),
+                         "unit": "TFLOP/s", "frac": round(alu_tflops / S6_ALU_PEAK_TFLOPS, 4), "traffic": None,
+                         "kernel": "s6_scan_kernel", "avg_launch_ms": round(r["kern_ms"], 5),
+                         "state_elements_per_launch": elems, "flop_per_element": S6_FLOP_PER_ELEM},
+            "roofline_hbm": {"achieved": round(r["bytes"] / kern_s / 1e9, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(r["bytes"] / kern_s / 1e9 / HBM_PEAK_GBS, 4),
+                             "algorithmic_bytes_per_launch": r["bytes"]},
+        })
+        if not args.no_parity:
+            log("[bench] s6: parity sample vs the fp64 oracle")
+            out["parity_sample"] = parity_sample(r["inp"], r["y"], r["hf"])
+        if not args.no_cpu_baseline:
+            log("[bench] s6: cpu baseline (the oracle on the same workload)")
+            out["cpu_baseline"] = cpu_baseline(r["inp"])
+        del r
+    if "decode" in parts:
         try:
             out["secondary_decode"] = bench_decode(args)
         except Exception as e:  # reported, not hidden
             out["secondary_decode"] = {"error": repr(e)}
+    if "ssd" in parts:
         try:
             out["secondary_ssd"] = bench_ssd(args)
         except Exception as e:
             out["secondary_ssd"] = {"error": repr(e)}
+    if "copy" in parts:
+        out["copy_reference"] = bench_copy(args)
     print(json.dumps(out), flush=True)
 
 

@@ -53,6 +53,20 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr uint32_t kOutOfRange = 0x80000000u;   // any offset >= every buffer size used
 constexpr int kRsrcWord3 = 0x00020000;          // raw 32-bit data format
 
+// `off` if `ok`, else kOutOfRange.  The value goes through an empty asm, so
+// the compiler must keep the choice a select: left visible, it may rewrite
+// the select as a branch around the load and then, at the join, wait for
+// every load in flight -- prefetched ones included.
+__device__ __forceinline__ uint32_t off_if(bool ok, uint32_t off) {
+    uint32_t v = ok ? off : kOutOfRange;
+    asm("" : "+v"(v));
+    return v;
+}
+
+// Makes `v` opaque to the optimiser, so a later `cond ? v : 0` stays a
+// select instead of a branch around the code that computes v.
+__device__ __forceinline__ void keep_select(float& v) { asm("" : "+v"(v)); }
+
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
 }

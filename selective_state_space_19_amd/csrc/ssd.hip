@@ -80,24 +80,34 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(const uint16_t* __restric
     const rsrc_t rC = make_rsrc(Cm + b * (int64_t)L * G * N, (uint32_t)L * rowbytes);
     auto tok = [&](int tl, int n) -> uint32_t {  // byte offset of (chunk token tl, state n)
         const int t = c * Q + tl;
-        return (t < L) ? (uint32_t)t * rowbytes + ((uint32_t)g * N + n) * 2u : kOutOfRange;
+        return off_if(t < L, (uint32_t)t * rowbytes + ((uint32_t)g * N + n) * 2u);
     };
 
     // ---- G rows of row-block I: the causal extent is 32 * (I/2 + 1) columns ---
+    // The C tiles of the row block are loaded once; B tiles one column tile ahead.
     const int I = q4 * 4 + w;
     uint16_t* Gout = Gw + (int64_t)bcg * Q * Q;
     const int ncol = 32 * (I / 2 + 1);
-    for (int jt = 0; jt < ncol / 16; ++jt) {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    u32x4_t ct[N / 32], bt[2][N / 32];
 #pragma unroll
-        for (int nk = 0; nk < N / 32; ++nk) {
-            const u32x4_t a = gload128(rC, tok(16 * I + m, 32 * nk + 8 * kg));
-            const u32x4_t bb = gload128(rB, tok(16 * jt + m, 32 * nk + 8 * kg));
-            acc = mfma16(a, bb, acc);
+    for (int nk = 0; nk < N / 32; ++nk) {
+        ct[nk] = gload128(rC, tok(16 * I + m, 32 * nk + 8 * kg));
+        bt[0][nk] = gload128(rB, tok(m, 32 * nk + 8 * kg));
+    }
+    for (int jt = 0; jt < ncol / 16; jt += 2) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {            // two column tiles per step: static buffer index
+            const int j = jt + u;
+            if (j + 1 < ncol / 16) {
+#pragma unroll
+                for (int nk = 0; nk < N / 32; ++nk) bt[u ^ 1][nk] = gload128(rB, tok(16 * (j + 1) + m, 32 * nk + 8 * kg));
+            }
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int nk = 0; nk < N / 32; ++nk) acc = mfma16(ct[nk], bt[u][nk], acc);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Gout[(16 * I + 4 * kg + r) * Q + 16 * j + m] = to_bf16(acc[r]);
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            Gout[(16 * I + 4 * kg + r) * Q + 16 * jt + m] = to_bf16(acc[r]);
     }
 
     // ---- B^T for this quarter's 64 tokens -------------------------------------
@@ -142,8 +152,8 @@ __global__ __launch_bounds__(256) void ssd_main_kernel(
     constexpr int HS = (N + 8) / 2;              // Hb row stride (bf16 pairs)
     static_assert(Q % 64 == 0 && N % 32 == 0, "Q multiple of 64, N multiple of 32");
 
-    __shared__ float s_s[Q];                     // running sum of dt*A*log2(e) within the chunk
-    __shared__ float s_dt[Q];
+    __shared__ __align__(16) float s_s[Q];       // running sum of dt*A*log2(e) within the chunk
+    __shared__ __align__(16) float s_dt[Q];
     __shared__ float s_wsum[4];
     __shared__ uint32_t xT[kPW][XS];             // x^T, bf16 pairs along tokens
     __shared__ uint32_t xsT[kPW][XS];            // (dt * beta * x)^T
@@ -188,17 +198,72 @@ __global__ __launch_bounds__(256) void ssd_main_kernel(
             accH[k][pt] = v;
         }
 
+    // ---- operand tiles loaded ahead of use ---------------------------------------
+    // MFMA A operands come from global memory (G and B^T from the workspace, C
+    // from the input), double-buffered one step ahead: the G/C tiles and gate
+    // values of row block rb+1 while rb computes (row block 0 of the next
+    // chunk during the state update), B^T of state block k+1 while k
+    // accumulates, and the next chunk's x and dt during this chunk's outputs.
+    // Tiles a row block does not need are read at an out-of-range offset (no
+    // memory traffic, value 0), so every load is unconditional.
+    u32x4_t ga[2][KB];                           // G tiles of one row block, token block J
+    u32x4_t ca[2][NKB];                          // C tiles of one row block, state K block
+    uint32_t zz[2][8];                           // gate values of one row block
+    u32x4_t ba[2][KB];                           // B^T tiles of one state block
+    const uint32_t gbytes = (uint32_t)Q * Q * 2u, btbytes = (uint32_t)N * Q * 2u;
+    auto load_rb = [&](int c, int rb, int sl) {
+        const int I = w + 4 * rb;
+        const rsrc_t rG = make_rsrc(Gw + (((int64_t)b * nc + c) * G + g) * Q * Q, gbytes);
+#pragma unroll
+        for (int J = 0; J < KB; ++J)
+            ga[sl][J] = gload128(rG, off_if(J <= I / 2, ((uint32_t)(16 * I + m) * Q + 32 * J + 8 * kg) * 2u));
+        const int t = c * Q + 16 * I + m;
+#pragma unroll
+        for (int nk = 0; nk < NKB; ++nk)
+            ca[sl][nk] = gload128(rC, off_if(t < L, (uint32_t)t * crow + ((uint32_t)g * N + 32 * nk + 8 * kg) * 2u));
+        if (Z) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int tr = c * Q + 16 * I + 4 * kg + r;
+#pragma unroll
+                for (int pt = 0; pt < 2; ++pt) {
+                    const uint32_t o = off_if(tr < L, (uint32_t)tr * xrow + ((uint32_t)h * kP + kPW * ph + 16 * pt + m) * 2u);
+                    zz[sl][2 * r + pt] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rZ, o, 0, 0);
+                }
+            }
+        }
+    };
+    auto load_bt = [&](int c, int k, int sl) {
+        const rsrc_t rBT = make_rsrc(BTw + (((int64_t)b * nc + c) * G + g) * N * Q, btbytes);
+        const int nb = w + 4 * k;
+#pragma unroll
+        for (int J = 0; J < KB; ++J)
+            ba[sl][J] = gload128(rBT, off_if(nb < NB, ((uint32_t)(16 * nb + m) * Q + 32 * J + 8 * kg) * 2u));
+    };
+    // Staging item of this thread (tid < Q): token pair tp, channel group pg.
+    const int tp = tid % (Q / 2), pg = tid / (Q / 2);
+    const int p0 = kPW * ph + 16 * pg;
+    uint32_t xw0[8], xw1[8];
+    float dtn = 0.f;
+    auto load_xdt = [&](int c) {
+        if (tid < Q) {
+            const int t = c * Q + tid;
+            const uint32_t od = off_if(t < L, ((uint32_t)t * H + h) * 2u);
+            dtn = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rDT, od, 0, 0) << 16);
+            const int ta = c * Q + 2 * tp, tb = ta + 1;
+            buf_load<8>(rX, off_if(ta < L, (uint32_t)ta * xrow + ((uint32_t)h * kP + p0) * 2u), xw0);
+            buf_load<8>(rX, off_if(tb < L, (uint32_t)tb * xrow + ((uint32_t)h * kP + p0) * 2u), xw1);
+        }
+    };
+    auto send = [&](int J) { return s_s[32 * J + 31]; };   // s at the end of token block J
+
+    load_xdt(0);
+    load_rb(0, 0, 0);
     for (int c = 0; c < nc; ++c) {
-        const int64_t bcg = ((int64_t)b * nc + c) * G + g;
         // ---- phase A: running sum s_t (log2 units), dt_t ----------------------
         {
-            float dtv = 0.f, v = 0.f;
-            if (tid < Q) {
-                const int t = c * Q + tid;
-                const uint32_t off = (t < L) ? ((uint32_t)t * H + h) * 2u : kOutOfRange;
-                dtv = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rDT, off, 0, 0) << 16);
-                v = dtv * a_h;
-            }
+            const float dtv = (tid < Q) ? dtn : 0.f;
+            float v = dtv * a_h;
 #pragma unroll
             for (int d = 1; d < 64; d <<= 1) {
                 const float o = __shfl_up(v, d, 64);
@@ -215,24 +280,14 @@ __global__ __launch_bounds__(256) void ssd_main_kernel(
             __syncthreads();
         }
         // ---- phase B: stage x^T and (dt*beta*x)^T; write the carried-in state ---
-        for (int it = tid; it < (Q / 2) * 2; it += 256) {
-            const int tp = it % (Q / 2), pg = it / (Q / 2);
+        if (tid < Q) {
             const int t0 = 2 * tp, t1 = 2 * tp + 1;
-            const int p0 = kPW * ph + 16 * pg;
-            uint32_t w0[8], w1[8];
-            {
-                const int ta = c * Q + t0, tb = c * Q + t1;
-                const uint32_t oa = (ta < L) ? (uint32_t)ta * xrow + ((uint32_t)h * kP + p0) * 2u : kOutOfRange;
-                const uint32_t ob = (tb < L) ? (uint32_t)tb * xrow + ((uint32_t)h * kP + p0) * 2u : kOutOfRange;
-                buf_load<8>(rX, oa, w0);
-                buf_load<8>(rX, ob, w1);
-            }
             const float sc0 = s_dt[t0] * fast_exp2(s_s[(t0 | 31)] - s_s[t0]);
             const float sc1 = s_dt[t1] * fast_exp2(s_s[(t1 | 31)] - s_s[t1]);
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const uint32_t a = (e & 1) ? (w0[e >> 1] >> 16) : (w0[e >> 1] & 0xffffu);
-                const uint32_t bb = (e & 1) ? (w1[e >> 1] >> 16) : (w1[e >> 1] & 0xffffu);
+                const uint32_t a = (e & 1) ? (xw0[e >> 1] >> 16) : (xw0[e >> 1] & 0xffffu);
+                const uint32_t bb = (e & 1) ? (xw1[e >> 1] >> 16) : (xw1[e >> 1] & 0xffffu);
                 xT[16 * pg + e][tp] = a | (bb << 16);
                 xsT[16 * pg + e][tp] = pack_bf16x2(__uint_as_float(a << 16) * sc0, __uint_as_float(bb << 16) * sc1);
             }
@@ -251,61 +306,70 @@ __global__ __launch_bounds__(256) void ssd_main_kernel(
             }
         }
         __syncthreads();
+        if (c + 1 < nc) load_xdt(c + 1);
 
         // ---- phase C1: outputs for row blocks I = w + 4*rb ------------------------
-        const uint16_t* Gc = Gw + bcg * Q * Q;
-        auto send = [&](int J) { return s_s[32 * J + 31]; };   // s at the end of token block J
-#pragma unroll 1
+#pragma unroll
         for (int rb = 0; rb < RBW; ++rb) {
+            const int sl = rb & 1;
+            if (rb + 1 < RBW) load_rb(c, rb + 1, sl ^ 1);
+            if (rb + 1 == RBW) load_bt(c, 0, 0);
             const int I = w + 4 * rb;
             const int i0 = 16 * I;
+            const int Jd = I / 2;                       // the token block holding row block I
             f32x4_t off_[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
             f32x4_t dg[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
             f32x4_t yo[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-            const int Jd = I / 2;                       // the token block holding row block I
             // off-diagonal token blocks, Horner over the per-block decay
-            for (int J = 0; J < Jd; ++J) {
-                if (J > 0) {
-                    const float r = fast_exp2(send(J) - send(J - 1));
 #pragma unroll
-                    for (int pt = 0; pt < 2; ++pt) off_[pt] *= r;
+            for (int J = 0; J < KB; ++J) {
+                if (J < Jd) {
+                    if (J > 0) {
+                        const float r = fast_exp2(send(J) - send(J - 1));
+#pragma unroll
+                        for (int pt = 0; pt < 2; ++pt) off_[pt] *= r;
+                    }
+#pragma unroll
+                    for (int pt = 0; pt < 2; ++pt)
+                        off_[pt] = mfma16(ga[sl][J], lds128(&xsT[16 * pt + m][16 * J + 4 * kg]), off_[pt]);
                 }
-                const u32x4_t a = *reinterpret_cast<const u32x4_t*>(Gc + (i0 + m) * Q + 32 * J + 8 * kg);
-#pragma unroll
-                for (int pt = 0; pt < 2; ++pt)
-                    off_[pt] = mfma16(a, lds128(&xsT[16 * pt + m][16 * J + 4 * kg]), off_[pt]);
             }
-            // diagonal token block: explicit mask, dt folded in, plain x
+            // diagonal token block: explicit mask, dt folded in, plain x.  Every
+            // element is computed and then masked (no branch around the LDS reads).
             {
                 const int i = i0 + m;
                 const float si = s_s[i];
-                const u32x4_t gv = *reinterpret_cast<const u32x4_t*>(Gc + i * Q + 32 * Jd + 8 * kg);
+                u32x4_t gv = ga[sl][0];
+#pragma unroll
+                for (int J = 1; J < KB; ++J)
+                    if (J == Jd) gv = ga[sl][J];
+                const int j0 = 32 * Jd + 8 * kg;
+                const float4 d0 = *reinterpret_cast<const float4*>(&s_dt[j0]);
+                const float4 d1 = *reinterpret_cast<const float4*>(&s_dt[j0 + 4]);
+                const float4 q0 = *reinterpret_cast<const float4*>(&s_s[j0]);
+                const float4 q1 = *reinterpret_cast<const float4*>(&s_s[j0 + 4]);
+                const float dj[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+                const float sj[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
                 uint32_t av[4];
 #pragma unroll
                 for (int e = 0; e < 8; e += 2) {
-                    const int j = 32 * Jd + 8 * kg + e;
                     const uint32_t gw = gv[e / 2];
-                    const float v0 = (j <= i) ? __uint_as_float(gw << 16) * s_dt[j] * fast_exp2(si - s_s[j]) : 0.f;
-                    const float v1 = (j + 1 <= i) ? __uint_as_float(gw & 0xffff0000u) * s_dt[j + 1] *
-                                                        fast_exp2(si - s_s[j + 1]) : 0.f;
-                    av[e / 2] = pack_bf16x2(v0, v1);
+                    float v0 = __uint_as_float(gw << 16) * dj[e] * fast_exp2(si - sj[e]);
+                    float v1 = __uint_as_float(gw & 0xffff0000u) * dj[e + 1] * fast_exp2(si - sj[e + 1]);
+                    keep_select(v0);
+                    keep_select(v1);
+                    av[e / 2] = pack_bf16x2(j0 + e <= i ? v0 : 0.f, j0 + e + 1 <= i ? v1 : 0.f);
                 }
                 const u32x4_t a = {av[0], av[1], av[2], av[3]};
 #pragma unroll
                 for (int pt = 0; pt < 2; ++pt) dg[pt] = mfma16(a, lds128(&xT[16 * pt + m][16 * Jd + 4 * kg]), dg[pt]);
             }
             // carried-in state: C rows times H_in^T
-            {
-                const int t = c * Q + i0 + m;
 #pragma unroll
-                for (int nk = 0; nk < NKB; ++nk) {
-                    const uint32_t o = (t < L) ? (uint32_t)t * crow + ((uint32_t)g * N + 32 * nk + 8 * kg) * 2u
-                                               : kOutOfRange;
-                    const u32x4_t a = gload128(rC, o);
+            for (int nk = 0; nk < NKB; ++nk)
 #pragma unroll
-                    for (int pt = 0; pt < 2; ++pt) yo[pt] = mfma16(a, lds128(&Hb[16 * pt + m][16 * nk + 4 * kg]), yo[pt]);
-                }
-            }
+                for (int pt = 0; pt < 2; ++pt)
+                    yo[pt] = mfma16(ca[sl][nk], lds128(&Hb[16 * pt + m][16 * nk + 4 * kg]), yo[pt]);
             // combine, skip, gate, store
             const float si0 = s_s[i0];
             const float gam = (Jd > 0) ? fast_exp2(si0 - send(Jd - 1)) : 0.f;
@@ -322,32 +386,29 @@ __global__ __launch_bounds__(256) void ssd_main_kernel(
                     const uint32_t xw = xT[p][i >> 1];
                     const float xv = __uint_as_float((i & 1) ? (xw & 0xffff0000u) : (xw << 16));
                     float yv = al * off_[pt][r] + dg[pt][r] + ei * yo[pt][r] + dskip * xv;
-                    const uint32_t o = (t < L) ? (uint32_t)t * xrow + ((uint32_t)h * kP + kPW * ph + p) * 2u
-                                               : kOutOfRange;
-                    if (Z) yv *= silu(__uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rZ, o, 0, 0) << 16));
+                    if (Z) yv *= silu(__uint_as_float(zz[sl][2 * r + pt] << 16));
+                    const uint32_t o = off_if(t < L, (uint32_t)t * xrow + ((uint32_t)h * kP + kPW * ph + p) * 2u);
                     __builtin_amdgcn_raw_buffer_store_b16(to_bf16(yv), rY, o, 0, kStream);
                 }
             }
         }
+        if (c + 1 < nc) load_rb(c + 1, 0, 0);
 
-        // ---- phase C2: state update over the chunk's token blocks ----------------
-        {
-            const uint16_t* BTc = BTw + bcg * N * Q;
-#pragma unroll 1
-            for (int J = 0; J < KB; ++J) {
-                const float r = fast_exp2(send(J) - (J > 0 ? send(J - 1) : 0.f));
+        // ---- phase C2: state update, one state block at a time ----------------------
+        float rJ[KB];                                   // decay across token block J
 #pragma unroll
-                for (int k = 0; k < NBW; ++k) {
-                    const int nb = w + 4 * k;
-                    if (nb < NB) {
-                        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(BTc + (16 * nb + m) * Q + 32 * J + 8 * kg);
+        for (int J = 0; J < KB; ++J) rJ[J] = fast_exp2(send(J) - (J > 0 ? send(J - 1) : 0.f));
 #pragma unroll
-                        for (int pt = 0; pt < 2; ++pt) {
-                            accH[k][pt] *= r;
-                            accH[k][pt] = mfma16(a, lds128(&xsT[16 * pt + m][16 * J + 4 * kg]), accH[k][pt]);
-                        }
+        for (int k = 0; k < NBW; ++k) {
+            if (k + 1 < NBW) load_bt(c, k + 1, (k + 1) & 1);
+            if (w + 4 * k < NB) {
+#pragma unroll
+                for (int J = 0; J < KB; ++J)
+#pragma unroll
+                    for (int pt = 0; pt < 2; ++pt) {
+                        accH[k][pt] *= rJ[J];
+                        accH[k][pt] = mfma16(ba[k & 1][J], lds128(&xsT[16 * pt + m][16 * J + 4 * kg]), accH[k][pt]);
                     }
-                }
             }
         }
         __syncthreads();
