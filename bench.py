@@ -20,6 +20,7 @@ the reference used to scale the HBM byte counters.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -80,6 +81,31 @@ def ssd_flops(batch, L, H, P, N, G, Q):
     return cb + ydiag + states + yoff + spass
 
 
+def profiled_traffic(profile):
+    """HBM bytes per launch of a kernel, from its committed rocprofv3 counter
+    summary under profiles/ (FETCH_SIZE and WRITE_SIZE, each scaled by what
+    the counter reads for a plain 1 GiB copy).  None when the summary is
+    missing or the kernel's sources changed after the counters were taken."""
+    try:
+        text = open(os.path.join(ROOT, "profiles", profile)).read()
+    except OSError:
+        return None
+    kv = {}
+    for line in text.splitlines():
+        k, sep, v = line.partition(": ")
+        if sep and k in ("traffic_bytes_per_launch", "kernel_sources", "kernel_source_sha256"):
+            kv[k] = v.strip()
+    if len(kv) != 3:
+        return None
+    h = hashlib.sha256()
+    for f in kv["kernel_sources"].split():
+        try:
+            h.update(open(os.path.join(ROOT, "selective_state_space_19_amd", "csrc", f), "rb").read())
+        except OSError:
+            return None
+    return int(kv["traffic_bytes_per_launch"]) if h.hexdigest() == kv["kernel_source_sha256"] else None
+
+
 def to_dev(a):
     import torch
     if a is None:
@@ -89,19 +115,24 @@ def to_dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def time_launches(fn, steps, warmup, stream):
+def time_launches(fn, steps, warmup, stream, wall=None):
     """Warm up, then time `steps` calls with HIP events on `stream` (the
-    stream the kernels are launched on).  Returns (total ms, per-call ms)."""
+    stream the kernels are launched on), bracketed by device synchronisation.
+    Returns (total ms, per-call ms); if `wall` is a list, the host wall-clock
+    ms of the same bracketed region is appended to it."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    t0 = time.perf_counter()
     evs[0].record(stream)
     for i in range(steps):
         fn()
         evs[i + 1].record(stream)
     torch.cuda.synchronize()
+    if wall is not None:
+        wall.append((time.perf_counter() - t0) * 1e3)
     per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
     return evs[0].elapsed_time(evs[-1]), per
 
@@ -130,9 +161,10 @@ def bench_s6(args):
 
     log(f"[bench] s6: timing {args.steps} steps after {args.warmup} warm-up")
     torch.cuda.synchronize()
-    total_ms, per = time_launches(step, args.steps, args.warmup, stream)
+    wall = []
+    total_ms, per = time_launches(step, args.steps, args.warmup, stream, wall)
     nbytes = s6_bytes(s["batch"], s["d_inner"], s["seqlen"], s["d_state"], 2 if wl.dtype == "bf16" else 4)
-    return dict(wl=wl, inp=inp, y=y, hf=hf, ms=total_ms / args.steps, per=per,
+    return dict(wl=wl, inp=inp, y=y, hf=hf, ms=wall[0] / args.steps, event_ms=total_ms / args.steps, per=per,
                 kern_ms=float(np.mean(per)), bytes=nbytes)
 
 
@@ -211,7 +243,7 @@ def bench_decode(args):
                               t["z"], out=ys[i], stream=stream)
 
     res = {"workload": f"{wl.name}: batch {bsz}, d_inner {dim}, d_state {N}, bf16, {steps} tokens",
-           "bytes_per_step": nb}
+           "bytes_per_step": nb, "traffic_bytes_per_launch": profiled_traffic("state_update_mamba2p8b_decode.md")}
     for label, rot in (("cold_16_buffers", True), ("hot_single_buffer", False)):
         total, _ = time_launches(lambda: run_all(rot), 3, 1, stream)
         us = total / 3 / steps * 1e3
@@ -272,7 +304,9 @@ def bench_ssd(args):
                 us=ms * 1e3, GBs=nb / (ms * 1e-3) / 1e9, hbm_frac=nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                 mfma_TFLOPs=fl / (ms * 1e-3) / 1e12, mfma_frac=fl / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                 tokens_ch_per_s=s["batch"] * s["seqlen"] * s["nheads"] * s["headdim"] / (ms * 1e-3),
-                algorithmic_bytes=nb, algorithmic_flops=fl, workspace_bytes=need)
+                algorithmic_bytes=nb, algorithmic_flops=fl, workspace_bytes=need,
+                traffic_bytes_per_call={"ssd_prep_kernel": profiled_traffic("ssd_prep_mamba2_chunk256.md"),
+                                        "ssd_main_kernel": profiled_traffic("ssd_main_mamba2_chunk256.md")})
 
 
 def bench_copy(args):
@@ -329,11 +363,13 @@ def main():
                        "batch": s["batch"], "d_inner": s["d_inner"], "seqlen": s["seqlen"], "d_state": s["d_state"]},
             "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
             "tokens_ch_per_s": tok / (r["ms"] * 1e-3),
+            "event_ms_per_step": round(r["event_ms"], 5),
             # The scan is bound by VALU work, not HBM: 5 VALU instructions per
             # state element take longer at peak (273 us here) than its bytes
             # (135 us at 8 TB/s).  Peak = non-packed fp32 VALU issue rate.
             "roofline": {"bound": "alu", "achieved": round(alu_tflops, 3), "peak": round(S6_ALU_PEAK_TFLOPS, 3),
-                         "unit": "TFLOP/s", "frac": round(alu_tflops / S6_ALU_PEAK_TFLOPS, 4), "traffic": None,
+                         "unit": "TFLOP/s", "frac": round(alu_tflops / S6_ALU_PEAK_TFLOPS, 4),
+                         "traffic": profiled_traffic("s6_scan_mamba1p4b_bf16.md"),
                          "kernel": "s6_scan_kernel", "avg_launch_ms": round(r["kern_ms"], 5),
                          "state_elements_per_launch": elems, "flop_per_element": S6_FLOP_PER_ELEM},
             "roofline_hbm": {"achieved": round(r["bytes"] / kern_s / 1e9, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -59,10 +59,10 @@ enum {
 /*
  * S6 selective scan (forward).
  *
- * Defined by: Mamba "Architecture Details" page, "Selective State Space
+ * Defined by: "Mamba Architecture Details" page, "Selective State Space
  * Mechanism / How S6 Works" -- input-dependent delta, B, C and the update
  * h(t) = discretize(A, delta(t)) h(t-1) + delta(t) B(t) x(t), y(t) = C(t) h(t);
- * the SSM optimisation catalogue, section 7 -- the transition is
+ * the "State-Space Model Optimization Patterns" page, section 7 -- the transition is
  * exp(delta A), elementwise because A is diagonal; section 6 -- the skip
  * term D x; section 3 -- the output gate, here silu(z) = z / (1 + exp(-z)).
  * For every batch row b, channel d and state index n (h starts at h0, or 0):
@@ -94,7 +94,7 @@ int mssm_selective_scan_fwd(const void* u, const void* delta, const float* A,
 /*
  * Decode: one token of the same recurrence, state updated in place.
  *
- * Defined by: Mamba "Architecture Details" page, "Hardware-Aware
+ * Defined by: "Mamba Architecture Details" page, "Hardware-Aware
  * Implementation / Parallel Algorithm", sequential (inference) mode -- a
  * constant-size state updated per token, h = A h + B x_t, then y_t = C h
  * read from the UPDATED state; the transition, skip and gate as above.
@@ -125,13 +125,13 @@ size_t mssm_ssd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads,
 /*
  * Mamba-2 SSD, chunked.
  *
- * Defined by: SSM optimisation catalogue, section 2 "State Space Duality" --
+ * Defined by: "State-Space Model Optimization Patterns" page, section 2 "State Space Duality" --
  * Y(T,P) = SSM(A, B(T,N), C(T,N))(X(T,P)) with a scalar transition per
  * head, equivalently a structured masked attention; section 9 "Chunked
  * Computation" and section 2's algorithm -- split the sequence into chunks,
  * compute the chunk-local quadratic form and each chunk's final state, pass
  * states from chunk to chunk, combine; section 10 -- the mask is
- * semi-separable.  Mamba-2 layout from the "SKILL" page ("Workflow 3":
+ * semi-separable.  Mamba-2 layout from the "Mamba - Selective State Space Models" page ("Workflow 3":
  * d_state, headdim, ngroups).  The result equals, up to rounding, the
  * recurrence per (b, head h, head channel p) with head h using group
  * g = h / (nheads / ngroups):

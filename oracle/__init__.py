@@ -10,13 +10,13 @@ fp64, one thread per block of independent channels); this module only
 converts arrays to contiguous float64 and calls it.  See the C file's header
 for what is computed and which passages of the pages it follows:
 
-* S6 selective scan -- Mamba "Architecture Details" page, "Selective State
+* S6 selective scan -- "Mamba Architecture Details" page, "Selective State
   Space Mechanism / How S6 Works" (update and output), SSM optimisation
-  catalogue section 7 (A_bar = exp(delta*A)) and section 6 (skip term D x),
+  Optimization Patterns page, section 7 (A_bar = exp(delta*A)) and section 6 (skip term D x),
   gated by silu(z).
 * Decode step -- the same update for one token, state updated in place
   ("Hardware-Aware Implementation / Parallel Algorithm", sequential mode).
-* Mamba-2 SSD -- catalogue section 2 "State Space Duality": the recurrence on
+* Mamba-2 SSD -- Optimization Patterns page, section 2 "State Space Duality": the recurrence on
   (head, head channel) with a scalar A per head.
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` against closed

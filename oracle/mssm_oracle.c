@@ -8,7 +8,7 @@
  *
  * What it computes (one "channel" = one independent recurrence over time):
  *
- *   Mamba "Architecture Details" page, section "Selective State Space
+ *   "Mamba Architecture Details" page, section "Selective State Space
  *   Mechanism / How S6 Works": the selective update
  *       h(t) = discretize(A, delta(t)) * h(t-1) + delta(t) * B(t) * x(t)
  *       y(t) = C(t) * h(t)
@@ -16,12 +16,12 @@
  *   Parallel Algorithm", sequential mode: h = 0, then h = A*h + B*x_t,
  *   y_t = C*h -- the output reads the state AFTER the update).
  *
- *   SSM optimisation-pattern catalogue, section 7 "Selective Attention
+ *   "State-Space Model Optimization Patterns" page, section 7 "Selective Attention
  *   Mechanism / Mathematical Formulation": the discretised transition is
  *   A_bar = exp(delta * A); A is diagonal, so this is one scalar exp per
  *   (channel, state index).
  *
- *   Same catalogue, section 6 "Tensor Core Optimization / SSM-Specific
+ *   Same page, section 6 "Tensor Core Optimization / SSM-Specific
  *   Patterns": the output carries a skip term, y = C h + D x.
  *
  *   The gate: y is multiplied by silu(z) = z * sigmoid(z) = z / (1 + exp(-z))
@@ -29,7 +29,7 @@
  *   formula is the standard SiLU).
  *
  *   Reading adopted where the pages differ: the input term is the Euler form
- *   delta*B*x of the architecture page (the catalogue's section 7 prints the
+ *   delta*B*x of the architecture page (that page's section 7 prints the
  *   zero-order-hold form (A_bar - I) A^-1 B instead).
  *
  * Per channel, in this order, for t = 0 .. L-1:
@@ -39,7 +39,7 @@
  *       y[t] = o
  *   and h is the final state afterwards.
  *
- * Mamba-2 SSD (catalogue section 2 "State Space Duality"): the SSM with a
+ * Mamba-2 SSD (Optimization Patterns page, section 2 "State Space Duality"): the SSM with a
  * scalar transition per head is the same recurrence, run per (head, head
  * channel p), with A[n] = A_h for every n, delta = dt[b,t,h], B and C taken
  * from the head's group.  The chunked/quadratic SSD algorithm reaches exactly

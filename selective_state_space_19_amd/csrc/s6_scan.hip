@@ -1,7 +1,7 @@
 // s6_scan.hip -- S6 selective scan forward for gfx950.
 //
-// What it computes (Mamba "Architecture Details" page, "Selective State
-// Space Mechanism / How S6 Works"; SSM optimisation catalogue sections 6, 7
+// What it computes ("Mamba Architecture Details" page, "Selective State
+// Space Mechanism / How S6 Works"; "State-Space Model Optimization Patterns" page sections 6, 7
 // and 3): per batch row b, channel d, state n, with h starting at h0 or 0,
 //     h[n] <- exp(delta*A[d,n]) * h[n] + delta*u*B[b,n,t]
 //     y     = (sum_n C[b,n,t]*h[n] + D[d]*u) * silu(z)

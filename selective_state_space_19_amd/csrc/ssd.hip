@@ -1,8 +1,8 @@
 // ssd.hip -- Mamba-2 SSD (state space duality), chunked forward, gfx950.
 //
-// What it computes (SSM optimisation catalogue, section 2 "State Space
-// Duality" and section 9 "Chunked Computation"; layout from the Mamba "SKILL"
-// page, "Workflow 3 / Mamba-2"): for batch row b, head h (group g = h / (H/G))
+// What it computes ("State-Space Model Optimization Patterns" page, section 2 "State Space
+// Duality" and section 9 "Chunked Computation"; layout from the "Mamba - Selective State
+// Space Models" page, "Workflow 3 / Mamba-2"): for batch row b, head h (group g = h / (H/G))
 // and head channel p, with a scalar transition per head,
 //     H[p,n] <- exp(dt_t*A_h) * H[p,n] + dt_t * x_t[p] * B_t[n]
 //     y_t[p]  = (sum_n C_t[n] * H[p,n] + D_h * x_t[p]) * silu(z_t[p])

@@ -1,6 +1,6 @@
 // state_update.hip -- one decode token of the selective SSM, state in place.
 //
-// What it computes (Mamba "Architecture Details" page, "Hardware-Aware
+// What it computes ("Mamba Architecture Details" page, "Hardware-Aware
 // Implementation / Parallel Algorithm", sequential mode; transition, skip and
 // gate as in the scan): for every (b, d),
 //     state[b,d,n] <- exp(delta*A[d,n]) * state[b,d,n] + delta*u*B[b,n]

@@ -4,14 +4,14 @@ This module draws random numbers and rounds them to the storage dtype; it
 holds none of the scan's arithmetic.  Both the HIP path and the fp64 oracle
 consume exactly the arrays produced here (the oracle widens bf16 exactly).
 
-Distributions (Mamba "Architecture Details" page, "Initialization Strategy"):
+Distributions ("Mamba Architecture Details" page, "Initialization Strategy"):
 the per-channel step dt is log-uniform in [dt_min, dt_max] = [1e-3, 0.1],
 floored at 1e-4; the per-token step is delta = softplus(0.5*eps + softplus^-1(dt))
 with eps ~ N(0, 1), so that delta > 0 and is centred on dt.  u, z, B, C ~ N(0, 1);
 A[d, n] = -(n + 1) (negative, as the page requires); D = 1.  B and C are
 per token and shared by all channels of a batch row ([B, N, L]).
 
-Mamba-2 SSD workloads ("SKILL" page, "Workflow 3 / Mamba-2"): headdim 64,
+Mamba-2 SSD workloads ("Mamba - Selective State Space Models" page, "Workflow 3 / Mamba-2"): headdim 64,
 d_state 128, ngroups 1; the scalar per-head A_h = -U[1, 16); dt per head.
 
 RNG: numpy PCG64.  The base generator ``PCG64(seed)`` draws the small

@@ -8,16 +8,16 @@ shows up as a disagreement.
       h_t = (prod_{r<=t} dA_r) h0 + sum_{s<=t} (prod_{r=s+1..t} dA_r) dBu_s,
   brute-forced with explicit products (O(L^2) per channel).
 * ``blelloch_s6``     -- the work-efficient up-sweep / down-sweep scan of the
-  SSM optimisation catalogue, section 11, with the addition replaced by the
+  "State-Space Model Optimization Patterns" page, section 11, with the addition replaced by the
   composition of affine maps h -> a h + b:
       (a1, b1) (+) (a2, b2) = (a1 a2, a2 b1 + b2)   ("apply 1, then 2"),
   which is associative; the scan identity of section 1 then gives every h_t.
-* ``ssd_quadratic``   -- catalogue section 2 "State Space Duality": for a
+* ``ssd_quadratic``   -- Optimization Patterns page, section 2 "State Space Duality": for a
   scalar-per-head A the SSM output is a masked attention-like product
       Y = (Lmask o (C B^T)) (dt o X) + D X,
   Lmask[i, j] = exp(A_h sum_{r=j+1..i} dt_r) for i >= j (a semi-separable
   mask, section 10), plus the decayed contribution of the initial state.
-* ``ssd_chunked``     -- catalogue section 9 "Chunked Computation": split into
+* ``ssd_chunked``     -- Optimization Patterns page, section 9 "Chunked Computation": split into
   chunks, local quadratic form plus the chunk's final state, pass states from
   chunk to chunk, combine.  Used to show chunk-size invariance.
 """

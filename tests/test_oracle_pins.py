@@ -2,14 +2,14 @@
 mathematics, never by the oracle itself.  CPU only.
 
 Passages (page titles; sections as printed there):
-  [S6]   Mamba "Architecture Details", "Selective State Space Mechanism /
+  [S6]   "Mamba Architecture Details" page, "Selective State Space Mechanism /
          How S6 Works": h(t) = discretize(A, delta) h(t-1) + delta B x, y = C h.
   [SEQ]  same page, "Hardware-Aware Implementation / Parallel Algorithm":
          sequential mode starts from h = 0 and reads y after the update.
-  [DISC] SSM optimisation catalogue, section 7: A_bar = exp(delta A).
-  [SKIP] catalogue section 6: y = C h + D x.
-  [SCAN] catalogue sections 1 and 11: associative scan; Blelloch up/down sweep.
-  [SSD]  catalogue section 2 (duality), 9 (chunking), 10 (semi-separable).
+  [DISC] "State-Space Model Optimization Patterns" page, section 7: A_bar = exp(delta A).
+  [SKIP] Optimization Patterns page, section 6: y = C h + D x.
+  [SCAN] Optimization Patterns page, sections 1 and 11: associative scan; Blelloch up/down sweep.
+  [SSD]  Optimization Patterns page, section 2 (duality), 9 (chunking), 10 (semi-separable).
 """
 import json
 import math
