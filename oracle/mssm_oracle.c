@@ -29,8 +29,8 @@
  *   formula is the standard SiLU).
  *
  *   Reading adopted where the pages differ: the input term is the Euler form
- *   delta*B*x of the architecture page (that page's section 7 prints the
- *   zero-order-hold form (A_bar - I) A^-1 B instead).
+ *   delta*B*x of the architecture page (the Optimization Patterns page's
+ *   section 7 prints the zero-order-hold form (A_bar - I) A^-1 B instead).
  *
  * Per channel, in this order, for t = 0 .. L-1:
  *       d = delta[t]; x = u[t]; acc = 0
