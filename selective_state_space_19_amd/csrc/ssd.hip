@@ -51,6 +51,14 @@ __device__ __forceinline__ f32x4_t mfma16(const u32x4_t a, const u32x4_t b, f32x
                                                    c, 0, 0, 0);
 }
 __device__ __forceinline__ u32x4_t lds128(const uint32_t* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+// Eight packed bf16 values times f, rounded back to bf16.
+__device__ __forceinline__ u32x4_t scale_bf16x8(const u32x4_t v, float f) {
+    u32x4_t o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        o[q] = pack_bf16x2(__uint_as_float(v[q] << 16) * f, __uint_as_float(v[q] & 0xffff0000u) * f);
+    return o;
+}
 __device__ __forceinline__ u32x4_t gload128(rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
@@ -135,296 +143,402 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(const uint16_t* __restric
 
 // ---------------------------------------------------------------------------
 // Main: one workgroup per (b, head, half of headdim); chunks in order.
+// 512 threads in two roles (one wave of each on every SIMD):
+//   output waves 0-3: the chunk's outputs from the staged chunk and the
+//     carried-in state (Y_diag, Y_off, skip, gate, store);
+//   state waves 4-7: the state update for the chunk, then the staging of the
+//     next chunk (running sum, x^T and its two scaled copies), so staging is
+//     off the output waves' path.  Every LDS buffer a chunk is read from is
+//     double-buffered by chunk parity: one barrier per chunk.
 // ---------------------------------------------------------------------------
 template <int Q, int N>
-__global__ __launch_bounds__(256) void ssd_main_kernel(
+__global__ __launch_bounds__(512) void ssd_main_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ DT, const float* __restrict__ Ah,
     const uint16_t* __restrict__ Cm, const float* __restrict__ Dh, const uint16_t* __restrict__ Z,
     const float* __restrict__ h0, uint16_t* __restrict__ Y, float* __restrict__ hT,
     const uint16_t* __restrict__ Gw, const uint16_t* __restrict__ BTw, int L, int H, int G, int nc) {
     constexpr int RB = Q / 16;                   // row blocks (16 tokens)
-    constexpr int KB = Q / 32;                   // token blocks (32 tokens) = MFMA K blocks
-    constexpr int NB = N / 16;                   // state row blocks
-    constexpr int NKB = N / 32;                  // state K blocks
-    constexpr int RBW = RB / 4;                  // row blocks per wave
-    constexpr int NBW = (NB + 3) / 4;            // state blocks per wave
-    constexpr int XS = (Q + 8) / 2;              // xT row stride (bf16 pairs)
+    constexpr int RBW = RB / 4;                  // row blocks per output wave
+    constexpr int KB = Q / 32;                   // token blocks (32 tokens, one MFMA K step)
+    constexpr int NB = N / 16;                   // state blocks (16 states)
+    constexpr int NKB = N / 32;                  // 32-state K steps
+    constexpr int NBW = (NB + 3) / 4;            // state blocks per state wave
+    constexpr int TPL = Q / 64;                  // tokens per lane when staging
+    constexpr int XS = (Q + 8) / 2;              // x^T row stride (bf16 pairs)
     constexpr int HS = (N + 8) / 2;              // Hb row stride (bf16 pairs)
     static_assert(Q % 64 == 0 && N % 32 == 0, "Q multiple of 64, N multiple of 32");
 
-    __shared__ __align__(16) float s_s[Q];       // running sum of dt*A*log2(e) within the chunk
-    __shared__ __align__(16) float s_dt[Q];
-    __shared__ float s_wsum[4];
-    __shared__ uint32_t xT[kPW][XS];             // x^T, bf16 pairs along tokens
-    __shared__ uint32_t xsT[kPW][XS];            // (dt * beta * x)^T
-    __shared__ uint32_t Hb[kPW][HS];             // carried-in state, bf16 pairs along n
+    __shared__ __align__(16) float s_s[2][Q];    // running sum of dt*A*log2(e) within the chunk
+    __shared__ __align__(16) float s_dt[2][Q];
+    __shared__ __align__(16) uint32_t xT[2][kPW][XS];    // x^T, bf16 pairs along tokens
+    __shared__ __align__(16) uint32_t xsT[2][kPW][XS];   // (dt * e^(s_blockend - s) * x)^T
+    __shared__ __align__(16) uint32_t xwT[2][kPW][XS];   // (dt * e^(s_chunkend - s) * x)^T
+    __shared__ __align__(16) uint32_t Hb[2][kPW][HS];    // carried-in state, bf16 pairs along n
+    __shared__ __align__(16) uint32_t ytile[4][16][kPW / 2];  // per output wave: one 16 x 32 bf16 output tile
 
-    const int ph = blockIdx.x & 1;
-    const int bh = blockIdx.x >> 1;
+    // Blocks are dispatched round-robin over the 8 XCDs; number them so that
+    // consecutive ids (the heads of one batch row) share an XCD and its L2,
+    // where that row's G, B^T and C tiles are cached.
+    uint32_t lid = blockIdx.x;
+    if ((gridDim.x & 7u) == 0u) lid = (blockIdx.x & 7u) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+    const int ph = lid & 1;
+    const int bh = lid >> 1;
     const int h = bh % H;
     const int64_t b = bh / H;
     const int g = h / (H / G);
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wr = w & 3;                        // index within the role
     const int kg = lane >> 4, m = lane & 15;
 
     const float a_h = Ah[h] * kLog2e;
-    const float dskip = Dh ? Dh[h] : 0.f;
 
     // Buffers over batch row b (32-bit offsets; the host checks the sizes).
     const uint32_t xrow = (uint32_t)H * kP * 2u;               // bytes per token of x / y / z
     const rsrc_t rX = make_rsrc(X + b * (int64_t)L * H * kP, (uint32_t)L * xrow);
-    const rsrc_t rY = make_rsrc(Y + b * (int64_t)L * H * kP, (uint32_t)L * xrow);
-    const rsrc_t rZ = make_rsrc(Z ? Z + b * (int64_t)L * H * kP : X, Z ? (uint32_t)L * xrow : 0u);
-    const rsrc_t rDT = make_rsrc(DT + b * (int64_t)L * H, (uint32_t)L * H * 2u);
-    const uint32_t crow = (uint32_t)G * N * 2u;
-    const rsrc_t rC = make_rsrc(Cm + b * (int64_t)L * G * N, (uint32_t)L * crow);
+    const uint32_t chan0 = ((uint32_t)h * kP + kPW * ph) * 2u;  // byte offset of this half-head in a token row
+    auto send = [&](int pb, int J) { return s_s[pb][32 * J + 31]; };   // s at the end of token block J
 
-    // ---- state accumulators: tiles (nb = w + 4*k, p-tile pt) ------------------
-    // C layout of a 16x16 tile: lane holds rows 4*kg + r (r < 4), column m.
-    f32x4_t accH[NBW][2];
-#pragma unroll
-    for (int k = 0; k < NBW; ++k)
-#pragma unroll
-        for (int pt = 0; pt < 2; ++pt) {
-            const int nb = w + 4 * k;
-            f32x4_t v = {0.f, 0.f, 0.f, 0.f};
-            if (h0 && nb < NB) {
-                const int p = kPW * ph + 16 * pt + m;
-                const float4 q = *reinterpret_cast<const float4*>(
-                    h0 + (((b * H + h) * kP + p) * (int64_t)N + 16 * nb + 4 * kg));
-                v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
-            }
-            accH[k][pt] = v;
-        }
+    if (w < 4) {
+        // ======================= output waves ======================================
+        const float dskip = Dh ? Dh[h] : 0.f;
+        const rsrc_t rY = make_rsrc(Y + b * (int64_t)L * H * kP, (uint32_t)L * xrow);
+        const rsrc_t rZ = make_rsrc(Z ? Z + b * (int64_t)L * H * kP : X, Z ? (uint32_t)L * xrow : 0u);
+        const uint32_t crow = (uint32_t)G * N * 2u;
+        const rsrc_t rC = make_rsrc(Cm + b * (int64_t)L * G * N, (uint32_t)L * crow);
+        const uint32_t gbytes = (uint32_t)Q * Q * 2u;
+        const int jhi = wr >> 1;                 // row block I = wr + 4 rb lies in token block 2 rb + jhi
 
-    // ---- operand tiles loaded ahead of use ---------------------------------------
-    // MFMA A operands come from global memory (G and B^T from the workspace, C
-    // from the input), double-buffered one step ahead: the G/C tiles and gate
-    // values of row block rb+1 while rb computes (row block 0 of the next
-    // chunk during the state update), B^T of state block k+1 while k
-    // accumulates, and the next chunk's x and dt during this chunk's outputs.
-    // Tiles a row block does not need are read at an out-of-range offset (no
-    // memory traffic, value 0), so every load is unconditional.
-    u32x4_t ga[2][KB];                           // G tiles of one row block, token block J
-    u32x4_t ca[2][NKB];                          // C tiles of one row block, state K block
-    uint32_t zz[2][8];                           // gate values of one row block
-    u32x4_t ba[2][KB];                           // B^T tiles of one state block
-    const uint32_t gbytes = (uint32_t)Q * Q * 2u, btbytes = (uint32_t)N * Q * 2u;
-    auto load_rb = [&](int c, int rb, int sl) {
-        const int I = w + 4 * rb;
-        const rsrc_t rG = make_rsrc(Gw + (((int64_t)b * nc + c) * G + g) * Q * Q, gbytes);
+        // G tiles: every row block has its own registers (row block rb needs
+        // G tiles J <= 2 rb + 1, at offset rb (rb + 1) in `ga`), and a row
+        // block's tiles for the next chunk are requested as soon as its MFMAs
+        // have read them, a whole chunk ahead of use.  C tiles and gate values
+        // are double-buffered one row block ahead.  Tiles a row block does not
+        // need are read at an out-of-range offset (no traffic, value 0), so
+        // every load is unconditional.
+        constexpr int NGA = RBW * (RBW + 1);
+        u32x4_t ga[NGA];
+        u32x4_t ca[2][NKB];
+        uint32_t zz[2][8];
+        auto load_g = [&](int cc, int rb) {
+            const int I = wr + 4 * rb;
+            const rsrc_t rG = make_rsrc(Gw + (((int64_t)b * nc + cc) * G + g) * Q * Q, gbytes);
+            const uint32_t gb = ((uint32_t)(16 * I + m) * Q + 8 * kg) * 2u;
+            const uint32_t glast = off_if(jhi != 0, gb + 64u * (2 * rb + 1));
 #pragma unroll
-        for (int J = 0; J < KB; ++J)
-            ga[sl][J] = gload128(rG, off_if(J <= I / 2, ((uint32_t)(16 * I + m) * Q + 32 * J + 8 * kg) * 2u));
-        const int t = c * Q + 16 * I + m;
+            for (int J = 0; J <= 2 * rb + 1; ++J)
+                ga[rb * (rb + 1) + J] = gload128(rG, J <= 2 * rb ? gb + 64u * J : glast);
+        };
+        auto load_cz = [&](int cc, int rb, int sl) {
+            const int I = wr + 4 * rb;
+            const int t = cc * Q + 16 * I + m;
+            const uint32_t cb = off_if(t < L, (uint32_t)t * crow + (uint32_t)g * N * 2u + 16u * kg);
 #pragma unroll
-        for (int nk = 0; nk < NKB; ++nk)
-            ca[sl][nk] = gload128(rC, off_if(t < L, (uint32_t)t * crow + ((uint32_t)g * N + 32 * nk + 8 * kg) * 2u));
-        if (Z) {
+            for (int nk = 0; nk < NKB; ++nk) ca[sl][nk] = gload128(rC, cb + 64u * nk);
+            if (Z) {
+                const int I = wr + 4 * rb;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int tr = c * Q + 16 * I + 4 * kg + r;
-#pragma unroll
-                for (int pt = 0; pt < 2; ++pt) {
-                    const uint32_t o = off_if(tr < L, (uint32_t)tr * xrow + ((uint32_t)h * kP + kPW * ph + 16 * pt + m) * 2u);
-                    zz[sl][2 * r + pt] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rZ, o, 0, 0);
-                }
-            }
-        }
-    };
-    auto load_bt = [&](int c, int k, int sl) {
-        const rsrc_t rBT = make_rsrc(BTw + (((int64_t)b * nc + c) * G + g) * N * Q, btbytes);
-        const int nb = w + 4 * k;
-#pragma unroll
-        for (int J = 0; J < KB; ++J)
-            ba[sl][J] = gload128(rBT, off_if(nb < NB, ((uint32_t)(16 * nb + m) * Q + 32 * J + 8 * kg) * 2u));
-    };
-    // Staging item of this thread (tid < Q): token pair tp, channel group pg.
-    const int tp = tid % (Q / 2), pg = tid / (Q / 2);
-    const int p0 = kPW * ph + 16 * pg;
-    uint32_t xw0[8], xw1[8];
-    float dtn = 0.f;
-    auto load_xdt = [&](int c) {
-        if (tid < Q) {
-            const int t = c * Q + tid;
-            const uint32_t od = off_if(t < L, ((uint32_t)t * H + h) * 2u);
-            dtn = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rDT, od, 0, 0) << 16);
-            const int ta = c * Q + 2 * tp, tb = ta + 1;
-            buf_load<8>(rX, off_if(ta < L, (uint32_t)ta * xrow + ((uint32_t)h * kP + p0) * 2u), xw0);
-            buf_load<8>(rX, off_if(tb < L, (uint32_t)tb * xrow + ((uint32_t)h * kP + p0) * 2u), xw1);
-        }
-    };
-    auto send = [&](int J) { return s_s[32 * J + 31]; };   // s at the end of token block J
-
-    load_xdt(0);
-    load_rb(0, 0, 0);
-    for (int c = 0; c < nc; ++c) {
-        // ---- phase A: running sum s_t (log2 units), dt_t ----------------------
-        {
-            const float dtv = (tid < Q) ? dtn : 0.f;
-            float v = dtv * a_h;
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                const float o = __shfl_up(v, d, 64);
-                if (lane >= d) v += o;
-            }
-            if (lane == 63) s_wsum[w] = v;
-            __syncthreads();
-            float base = 0.f;
-            for (int q = 0; q < w; ++q) base += s_wsum[q];
-            if (tid < Q) {
-                s_s[tid] = v + base;
-                s_dt[tid] = dtv;
-            }
-            __syncthreads();
-        }
-        // ---- phase B: stage x^T and (dt*beta*x)^T; write the carried-in state ---
-        if (tid < Q) {
-            const int t0 = 2 * tp, t1 = 2 * tp + 1;
-            const float sc0 = s_dt[t0] * fast_exp2(s_s[(t0 | 31)] - s_s[t0]);
-            const float sc1 = s_dt[t1] * fast_exp2(s_s[(t1 | 31)] - s_s[t1]);
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const uint32_t a = (e & 1) ? (xw0[e >> 1] >> 16) : (xw0[e >> 1] & 0xffffu);
-                const uint32_t bb = (e & 1) ? (xw1[e >> 1] >> 16) : (xw1[e >> 1] & 0xffffu);
-                xT[16 * pg + e][tp] = a | (bb << 16);
-                xsT[16 * pg + e][tp] = pack_bf16x2(__uint_as_float(a << 16) * sc0, __uint_as_float(bb << 16) * sc1);
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < NBW; ++k) {
-            const int nb = w + 4 * k;
-            if (nb < NB) {
-#pragma unroll
-                for (int pt = 0; pt < 2; ++pt) {
-                    const int p = 16 * pt + m;
-                    const f32x4_t v = accH[k][pt];
-                    *reinterpret_cast<uint2*>(&Hb[p][(16 * nb + 4 * kg) / 2]) =
-                        make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-                }
-            }
-        }
-        __syncthreads();
-        if (c + 1 < nc) load_xdt(c + 1);
-
-        // ---- phase C1: outputs for row blocks I = w + 4*rb ------------------------
-#pragma unroll
-        for (int rb = 0; rb < RBW; ++rb) {
-            const int sl = rb & 1;
-            if (rb + 1 < RBW) load_rb(c, rb + 1, sl ^ 1);
-            if (rb + 1 == RBW) load_bt(c, 0, 0);
-            const int I = w + 4 * rb;
-            const int i0 = 16 * I;
-            const int Jd = I / 2;                       // the token block holding row block I
-            f32x4_t off_[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-            f32x4_t dg[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-            f32x4_t yo[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-            // off-diagonal token blocks, Horner over the per-block decay
-#pragma unroll
-            for (int J = 0; J < KB; ++J) {
-                if (J < Jd) {
-                    if (J > 0) {
-                        const float r = fast_exp2(send(J) - send(J - 1));
-#pragma unroll
-                        for (int pt = 0; pt < 2; ++pt) off_[pt] *= r;
-                    }
+                for (int r = 0; r < 4; ++r) {
+                    const int tr = cc * Q + 16 * I + 4 * kg + r;
+                    const uint32_t zb = off_if(tr < L, (uint32_t)tr * xrow + chan0 + 2u * m);
 #pragma unroll
                     for (int pt = 0; pt < 2; ++pt)
-                        off_[pt] = mfma16(ga[sl][J], lds128(&xsT[16 * pt + m][16 * J + 4 * kg]), off_[pt]);
+                        zz[sl][2 * r + pt] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rZ, zb + 32u * pt, 0, 0);
                 }
             }
-            // diagonal token block: explicit mask, dt folded in, plain x.  Every
-            // element is computed and then masked (no branch around the LDS reads).
-            {
-                const int i = i0 + m;
-                const float si = s_s[i];
-                u32x4_t gv = ga[sl][0];
-#pragma unroll
-                for (int J = 1; J < KB; ++J)
-                    if (J == Jd) gv = ga[sl][J];
-                const int j0 = 32 * Jd + 8 * kg;
-                const float4 d0 = *reinterpret_cast<const float4*>(&s_dt[j0]);
-                const float4 d1 = *reinterpret_cast<const float4*>(&s_dt[j0 + 4]);
-                const float4 q0 = *reinterpret_cast<const float4*>(&s_s[j0]);
-                const float4 q1 = *reinterpret_cast<const float4*>(&s_s[j0 + 4]);
-                const float dj[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-                const float sj[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-                uint32_t av[4];
-#pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    const uint32_t gw = gv[e / 2];
-                    float v0 = __uint_as_float(gw << 16) * dj[e] * fast_exp2(si - sj[e]);
-                    float v1 = __uint_as_float(gw & 0xffff0000u) * dj[e + 1] * fast_exp2(si - sj[e + 1]);
-                    keep_select(v0);
-                    keep_select(v1);
-                    av[e / 2] = pack_bf16x2(j0 + e <= i ? v0 : 0.f, j0 + e + 1 <= i ? v1 : 0.f);
-                }
-                const u32x4_t a = {av[0], av[1], av[2], av[3]};
-#pragma unroll
-                for (int pt = 0; pt < 2; ++pt) dg[pt] = mfma16(a, lds128(&xT[16 * pt + m][16 * Jd + 4 * kg]), dg[pt]);
-            }
-            // carried-in state: C rows times H_in^T
-#pragma unroll
-            for (int nk = 0; nk < NKB; ++nk)
-#pragma unroll
-                for (int pt = 0; pt < 2; ++pt)
-                    yo[pt] = mfma16(ca[sl][nk], lds128(&Hb[16 * pt + m][16 * nk + 4 * kg]), yo[pt]);
-            // combine, skip, gate, store
-            const float si0 = s_s[i0];
-            const float gam = (Jd > 0) ? fast_exp2(si0 - send(Jd - 1)) : 0.f;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = i0 + 4 * kg + r;
-                const float si = s_s[i];
-                const float al = fast_exp2(si - si0) * gam;
-                const float ei = fast_exp2(si);
-                const int t = c * Q + i;
-#pragma unroll
-                for (int pt = 0; pt < 2; ++pt) {
-                    const int p = 16 * pt + m;
-                    const uint32_t xw = xT[p][i >> 1];
-                    const float xv = __uint_as_float((i & 1) ? (xw & 0xffff0000u) : (xw << 16));
-                    float yv = al * off_[pt][r] + dg[pt][r] + ei * yo[pt][r] + dskip * xv;
-                    if (Z) yv *= silu(__uint_as_float(zz[sl][2 * r + pt] << 16));
-                    const uint32_t o = off_if(t < L, (uint32_t)t * xrow + ((uint32_t)h * kP + kPW * ph + p) * 2u);
-                    __builtin_amdgcn_raw_buffer_store_b16(to_bf16(yv), rY, o, 0, kStream);
-                }
-            }
-        }
-        if (c + 1 < nc) load_rb(c + 1, 0, 0);
+        };
 
-        // ---- phase C2: state update, one state block at a time ----------------------
-        float rJ[KB];                                   // decay across token block J
 #pragma unroll
-        for (int J = 0; J < KB; ++J) rJ[J] = fast_exp2(send(J) - (J > 0 ? send(J - 1) : 0.f));
+        for (int rb = 0; rb < RBW; ++rb) load_g(0, rb);
+        load_cz(0, 0, 0);
+        __syncthreads();                         // chunk 0 staged, carried-in state written
+        for (int c = 0; c < nc; ++c) {
+            const int pb = c & 1;
 #pragma unroll
-        for (int k = 0; k < NBW; ++k) {
-            if (k + 1 < NBW) load_bt(c, k + 1, (k + 1) & 1);
-            if (w + 4 * k < NB) {
+            for (int rb = 0; rb < RBW; ++rb) {
+                const int sl = rb & 1;
+                if (rb + 1 < RBW) load_cz(c, rb + 1, sl ^ 1);
+                const int I = wr + 4 * rb;
+                const int i0 = 16 * I;
+                const int Jd = 2 * rb + jhi;     // the token block holding row block I
+                const u32x4_t* gt = &ga[rb * (rb + 1)];
+                f32x4_t off_[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+                f32x4_t dg[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+                f32x4_t yo[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+                // off-diagonal token blocks J < Jd: the G tile is scaled by the
+                // decay from the end of block J to the first row of block I
+                // (<= 1), so the MFMAs accumulate back to back.
+                const float si0 = s_s[pb][i0];
 #pragma unroll
-                for (int J = 0; J < KB; ++J)
+                for (int J = 0; J <= 2 * rb; ++J) {
+                    if (J < Jd) {
+                        const u32x4_t a = scale_bf16x8(gt[J], fast_exp2(si0 - send(pb, J)));
+#pragma unroll
+                        for (int pt = 0; pt < 2; ++pt)
+                            off_[pt] = mfma16(a, lds128(&xsT[pb][16 * pt + m][16 * J + 4 * kg]), off_[pt]);
+                    }
+                }
+                // diagonal token block: mask built element by element, dt folded in, plain x
+                {
+                    const int i = i0 + m;
+                    const float si = s_s[pb][i];
+                    const u32x4_t gv = jhi ? gt[2 * rb + 1] : gt[2 * rb];
+                    const int j0 = 32 * Jd + 8 * kg;
+                    const float4 d0 = *reinterpret_cast<const float4*>(&s_dt[pb][j0]);
+                    const float4 d1 = *reinterpret_cast<const float4*>(&s_dt[pb][j0 + 4]);
+                    const float4 q0 = *reinterpret_cast<const float4*>(&s_s[pb][j0]);
+                    const float4 q1 = *reinterpret_cast<const float4*>(&s_s[pb][j0 + 4]);
+                    const float dj[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+                    const float sj[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+                    uint32_t av[4];
+#pragma unroll
+                    for (int e = 0; e < 8; e += 2) {
+                        const uint32_t gw = gv[e / 2];
+                        float v0 = __uint_as_float(gw << 16) * dj[e] * fast_exp2(si - sj[e]);
+                        float v1 = __uint_as_float(gw & 0xffff0000u) * dj[e + 1] * fast_exp2(si - sj[e + 1]);
+                        keep_select(v0);
+                        keep_select(v1);
+                        av[e / 2] = pack_bf16x2(j0 + e <= i ? v0 : 0.f, j0 + e + 1 <= i ? v1 : 0.f);
+                    }
+                    const u32x4_t a = {av[0], av[1], av[2], av[3]};
+#pragma unroll
+                    for (int pt = 0; pt < 2; ++pt)
+                        dg[pt] = mfma16(a, lds128(&xT[pb][16 * pt + m][16 * Jd + 4 * kg]), dg[pt]);
+                }
+                // carried-in state: C rows times H_in^T
+#pragma unroll
+                for (int nk = 0; nk < NKB; ++nk)
+#pragma unroll
+                    for (int pt = 0; pt < 2; ++pt)
+                        yo[pt] = mfma16(ca[sl][nk], lds128(&Hb[pb][16 * pt + m][16 * nk + 4 * kg]), yo[pt]);
+                // this row block's G tiles for the next chunk
+                if (c + 1 < nc) load_g(c + 1, rb);
+                // Next chunk's row block 0 goes to slot 0; with one row block
+                // per wave that slot still holds the gate values read below.
+                if constexpr (RBW > 1)
+                    if (rb + 1 == RBW && c + 1 < nc) load_cz(c + 1, 0, 0);
+                // combine, skip, gate; the tile goes through LDS so that each
+                // lane stores 8 consecutive head channels of one token (16 bytes).
+                uint16_t* yt16 = reinterpret_cast<uint16_t*>(&ytile[wr][0][0]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = i0 + 4 * kg + r;
+                    const float si = s_s[pb][i];
+                    const float al = fast_exp2(si - si0);
+                    const float ei = fast_exp2(si);
 #pragma unroll
                     for (int pt = 0; pt < 2; ++pt) {
-                        accH[k][pt] *= rJ[J];
-                        accH[k][pt] = mfma16(ba[k & 1][J], lds128(&xsT[16 * pt + m][16 * J + 4 * kg]), accH[k][pt]);
+                        const uint32_t xw = xT[pb][16 * pt + m][i >> 1];
+                        const float xv = __uint_as_float((i & 1) ? (xw & 0xffff0000u) : (xw << 16));
+                        float yv = al * off_[pt][r] + dg[pt][r] + ei * yo[pt][r] + dskip * xv;
+                        if (Z) yv *= silu(__uint_as_float(zz[sl][2 * r + pt] << 16));
+                        yt16[(4 * kg + r) * kPW + 16 * pt + m] = to_bf16(yv);
                     }
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                {
+                    const int tr = lane >> 2, cg = lane & 3;          // token row, 8-channel group
+                    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&ytile[wr][tr][4 * cg]);
+                    const int t = c * Q + i0 + tr;
+                    __builtin_amdgcn_raw_buffer_store_b128(v, rY, off_if(t < L, (uint32_t)t * xrow + chan0 + 16u * cg),
+                                                           0, kCached);
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                if constexpr (RBW == 1)
+                    if (c + 1 < nc) load_cz(c + 1, 0, 0);
             }
+            __syncthreads();
         }
-        __syncthreads();
-    }
+    } else {
+        // ======================= state waves =======================================
+        const rsrc_t rDT = make_rsrc(DT + b * (int64_t)L * H, (uint32_t)L * H * 2u);
+        const uint32_t btbytes = (uint32_t)N * Q * 2u;
 
-    if (hT) {
+        // State tiles (state block nb = wr + 4 k, head-channel tile pt): lane
+        // holds states 16 nb + 4 kg + r (r < 4) of head channel 16 pt + m.
+        f32x4_t accH[NBW][2];
 #pragma unroll
-        for (int k = 0; k < NBW; ++k) {
-            const int nb = w + 4 * k;
-            if (nb < NB) {
+        for (int k = 0; k < NBW; ++k)
 #pragma unroll
-                for (int pt = 0; pt < 2; ++pt) {
+            for (int pt = 0; pt < 2; ++pt) {
+                const int nb = wr + 4 * k;
+                f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+                if (h0 && nb < NB) {
                     const int p = kPW * ph + 16 * pt + m;
-                    const f32x4_t v = accH[k][pt];
-                    *reinterpret_cast<float4*>(hT + (((b * H + h) * kP + p) * (int64_t)N + 16 * nb + 4 * kg)) =
-                        make_float4(v[0], v[1], v[2], v[3]);
+                    const float4 q = *reinterpret_cast<const float4*>(
+                        h0 + (((b * H + h) * kP + p) * (int64_t)N + 16 * nb + 4 * kg));
+                    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+                }
+                accH[k][pt] = v;
+            }
+        auto write_hb = [&](int pb) {
+#pragma unroll
+            for (int k = 0; k < NBW; ++k) {
+                const int nb = wr + 4 * k;
+                if (nb < NB) {
+#pragma unroll
+                    for (int pt = 0; pt < 2; ++pt) {
+                        const f32x4_t v = accH[k][pt];
+                        *reinterpret_cast<uint2*>(&Hb[pb][16 * pt + m][(16 * nb + 4 * kg) / 2]) =
+                            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                    }
+                }
+            }
+        };
+
+        // B^T tiles of this wave's state blocks.  Up to two state blocks are
+        // held (slot k % 2): blocks 0 and 1 of a chunk are loaded a chunk
+        // ahead, block k + 2 while block k accumulates.
+        constexpr int BSL = NBW < 2 ? NBW : 2;
+        u32x4_t ba[BSL][KB];
+        auto load_bt = [&](int cc, int k) {
+            const rsrc_t rBT = make_rsrc(BTw + (((int64_t)b * nc + cc) * G + g) * N * Q, btbytes);
+            const int nb = wr + 4 * k;
+            const uint32_t base = off_if(nb < NB, ((uint32_t)(16 * nb + m) * Q + 8 * kg) * 2u);
+#pragma unroll
+            for (int J = 0; J < KB; ++J) ba[k % BSL][J] = gload128(rBT, base + 64u * J);
+        };
+        auto load_bt_ahead = [&](int cc) {
+#pragma unroll
+            for (int k = 0; k < BSL; ++k) load_bt(cc, k);
+        };
+
+        // Staging of one chunk: lane l takes tokens l*TPL .. l*TPL+TPL-1 and
+        // this wave's 8 head channels 8 wr .. 8 wr + 7.  Every state wave
+        // computes the chunk's running sum itself (no cross-wave step); wave
+        // 4 also publishes s and dt for the output waves.
+        uint32_t xv[TPL][4];
+        uint32_t dtw[TPL];
+        auto stage_load = [&](int cc) {
+#pragma unroll
+            for (int i = 0; i < TPL; ++i) {
+                const int t = cc * Q + lane * TPL + i;
+                dtw[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rDT, off_if(t < L, ((uint32_t)t * H + h) * 2u), 0, 0);
+                buf_load<4>(rX, off_if(t < L, (uint32_t)t * xrow + chan0 + 16u * wr), xv[i]);
+            }
+        };
+        auto stage_store = [&](int pb) -> float {
+            float dv[TPL], sv[TPL];
+            float run = 0.f;
+#pragma unroll
+            for (int i = 0; i < TPL; ++i) {
+                dv[i] = __uint_as_float(dtw[i] << 16);
+                run += dv[i] * a_h;
+                sv[i] = run;
+            }
+            float tot = run;                     // inclusive scan of the lane totals
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const float o = __shfl_up(tot, d, 64);
+                if (lane >= d) tot += o;
+            }
+            const float base = tot - run;
+#pragma unroll
+            for (int i = 0; i < TPL; ++i) sv[i] += base;
+            const float s_be = __shfl(tot, ((lane * TPL) | 31) / TPL, 64);   // end of my 32-token block
+            const float s_end = __shfl(tot, 63, 64);                        // end of the chunk
+            if (wr == 0) {
+#pragma unroll
+                for (int i = 0; i < TPL; ++i) {
+                    s_s[pb][lane * TPL + i] = sv[i];
+                    s_dt[pb][lane * TPL + i] = dv[i];
+                }
+            }
+            float fs[TPL], fw[TPL];
+#pragma unroll
+            for (int i = 0; i < TPL; ++i) {
+                fs[i] = dv[i] * fast_exp2(s_be - sv[i]);
+                fw[i] = dv[i] * fast_exp2(s_end - sv[i]);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {        // head channel 8 wr + e
+                float xf[TPL];
+                uint32_t xb[TPL];
+#pragma unroll
+                for (int i = 0; i < TPL; ++i) {
+                    const uint32_t wv = xv[i][e >> 1];
+                    xb[i] = (e & 1) ? (wv >> 16) : (wv & 0xffffu);
+                    xf[i] = __uint_as_float(xb[i] << 16);
+                }
+                const int row = 8 * wr + e;
+                if constexpr (TPL == 1) {
+                    uint16_t* p0 = reinterpret_cast<uint16_t*>(&xT[pb][row][0]) + lane;
+                    uint16_t* p1 = reinterpret_cast<uint16_t*>(&xsT[pb][row][0]) + lane;
+                    uint16_t* p2 = reinterpret_cast<uint16_t*>(&xwT[pb][row][0]) + lane;
+                    *p0 = (uint16_t)xb[0];
+                    *p1 = to_bf16(xf[0] * fs[0]);
+                    *p2 = to_bf16(xf[0] * fw[0]);
+                } else {
+                    constexpr int WPL = TPL / 2;     // words per lane
+                    uint32_t a0[WPL], a1[WPL], a2[WPL];
+#pragma unroll
+                    for (int q = 0; q < WPL; ++q) {
+                        a0[q] = xb[2 * q] | (xb[2 * q + 1] << 16);
+                        a1[q] = pack_bf16x2(xf[2 * q] * fs[2 * q], xf[2 * q + 1] * fs[2 * q + 1]);
+                        a2[q] = pack_bf16x2(xf[2 * q] * fw[2 * q], xf[2 * q + 1] * fw[2 * q + 1]);
+                    }
+                    if constexpr (WPL == 1) {
+                        xT[pb][row][lane] = a0[0];
+                        xsT[pb][row][lane] = a1[0];
+                        xwT[pb][row][lane] = a2[0];
+                    } else {
+                        *reinterpret_cast<uint2*>(&xT[pb][row][2 * lane]) = make_uint2(a0[0], a0[1]);
+                        *reinterpret_cast<uint2*>(&xsT[pb][row][2 * lane]) = make_uint2(a1[0], a1[1]);
+                        *reinterpret_cast<uint2*>(&xwT[pb][row][2 * lane]) = make_uint2(a2[0], a2[1]);
+                    }
+                }
+            }
+            return s_end;
+        };
+
+        stage_load(0);
+        load_bt_ahead(0);
+        write_hb(0);
+        float s_end = stage_store(0);
+        if (nc > 1) stage_load(1);
+        __syncthreads();                         // chunk 0 staged, carried-in state written
+        for (int c = 0; c < nc; ++c) {
+            const int pb = c & 1;
+            // H_out = e^(s_end) H_in + B^T (w o X), w_j = dt_j e^(s_end - s_j) <= 1
+            const float dec = fast_exp2(s_end);
+#pragma unroll
+            for (int k = 0; k < NBW; ++k) {
+                if (wr + 4 * k < NB) {
+#pragma unroll
+                    for (int pt = 0; pt < 2; ++pt) {
+                        accH[k][pt] *= dec;
+#pragma unroll
+                        for (int J = 0; J < KB; ++J)
+                            accH[k][pt] = mfma16(ba[k % BSL][J], lds128(&xwT[pb][16 * pt + m][16 * J + 4 * kg]),
+                                                 accH[k][pt]);
+                    }
+                }
+                if (k + BSL < NBW) load_bt(c, k + BSL);
+            }
+            if (c + 1 < nc) {
+                load_bt_ahead(c + 1);
+                write_hb(pb ^ 1);
+                s_end = stage_store(pb ^ 1);
+                if (c + 2 < nc) stage_load(c + 2);
+            }
+            __syncthreads();
+        }
+        if (hT) {
+#pragma unroll
+            for (int k = 0; k < NBW; ++k) {
+                const int nb = wr + 4 * k;
+                if (nb < NB) {
+#pragma unroll
+                    for (int pt = 0; pt < 2; ++pt) {
+                        const int p = kPW * ph + 16 * pt + m;
+                        const f32x4_t v = accH[k][pt];
+                        *reinterpret_cast<float4*>(hT + (((b * H + h) * kP + p) * (int64_t)N + 16 * nb + 4 * kg)) =
+                            make_float4(v[0], v[1], v[2], v[3]);
+                    }
                 }
             }
         }
@@ -442,7 +556,7 @@ hipError_t launch_qn(const SSDParams& p, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t blocks = p.batch * p.H * 2;
-    hipLaunchKernelGGL((ssd_main_kernel<Q, N>), dim3((unsigned)blocks), dim3(256), 0, stream,
+    hipLaunchKernelGGL((ssd_main_kernel<Q, N>), dim3((unsigned)blocks), dim3(512), 0, stream,
                        static_cast<const uint16_t*>(p.x), static_cast<const uint16_t*>(p.dt), p.A,
                        static_cast<const uint16_t*>(p.Cm), p.Dskip, static_cast<const uint16_t*>(p.z), p.h0,
                        static_cast<uint16_t*>(p.y), p.h_final, Gw, BTw, p.L, p.H, p.G, nc);
