@@ -48,7 +48,7 @@ namespace mssm {
 
 namespace {
 
-template <typename T, int NW, int NS, int TC, bool ALIGNED, int RING>
+template <typename T, int NW, int NS, int TC, bool ALIGNED, bool FULLN, int RING>
 __global__ __launch_bounds__(NW * 64) void s6_scan_kernel(
     const T* __restrict__ u_in, const T* __restrict__ dl_in, const T* __restrict__ B_in,
     const T* __restrict__ C_in, const T* __restrict__ z_in, const float* __restrict__ A_in,
@@ -150,10 +150,10 @@ __global__ __launch_bounds__(NW * 64) void s6_scan_kernel(
                 const int tc = t < L ? t : L - G;
                 const uint4 x = *reinterpret_cast<const uint4*>(brow[s] + tc);
                 const uint4 y = *reinterpret_cast<const uint4*>(crow[s] + tc);
-                const bool ok = sval[s];
+                // Raw words: a state past N is zeroed where C is used, after
+                // the group's wait, so these loads stay in flight meanwhile.
                 bw[s][0] = x.x; bw[s][1] = x.y; bw[s][2] = x.z; bw[s][3] = x.w;
-                cw[s][0] = ok ? y.x : 0u; cw[s][1] = ok ? y.y : 0u;
-                cw[s][2] = ok ? y.z : 0u; cw[s][3] = ok ? y.w : 0u;
+                cw[s][0] = y.x; cw[s][1] = y.y; cw[s][2] = y.z; cw[s][3] = y.w;
             } else {
                 const int valid = sval[s] ? L - t : 0;
                 load_run<T, G>(brow[s] + t, valid, false, bw[s]);
@@ -166,23 +166,45 @@ __global__ __launch_bounds__(NW * 64) void s6_scan_kernel(
     float4 ddr[2][G / 2];
     const int nchunks = (L + TC - 1) / TC;
 
-    // One token pair (t, t+1) of the group in buffer `buf`, all NS states.
-    auto pair = [&](int buf, int gi, int k) {
-        const float4 q = ddr[buf][k / 2];
-        float y0 = 0.f, y1 = 0.f;
+    // C of state s at token k of the group in buffer `buf`; 0 for a state
+    // past N (FULLN: every state of every wave is below N).
+    auto cval = [&](int buf, int s, int k) -> float {
+        const float c = Elem<T>::get(cw[buf][s], k);
+        if constexpr (ALIGNED && !FULLN) return sval[s] ? c : 0.f;
+        return c;
+    };
+    // One group of G tokens in buffer `buf`, all NS states.  The decay
+    // factors and input terms of the whole group are formed first (they do
+    // not depend on h), so each exp has independent work behind it; then the
+    // recurrence runs token by token.
+    auto group = [&](int buf, int gi) {
+        float dA[G][NS], bu[G][NS];
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            const float dA = fast_exp2(q.x * a2[s]);
-            h[s] = fmaf(dA, h[s], q.y * Elem<T>::get(bw[buf][s], k));
-            y0 = fmaf(Elem<T>::get(cw[buf][s], k), h[s], y0);
+        for (int k = 0; k < G; k += 2) {
+            const float4 q = ddr[buf][k / 2];
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                dA[k][s] = fast_exp2(q.x * a2[s]);
+                dA[k + 1][s] = fast_exp2(q.z * a2[s]);
+                bu[k][s] = q.y * Elem<T>::get(bw[buf][s], k);
+                bu[k + 1][s] = q.w * Elem<T>::get(bw[buf][s], k + 1);
+            }
         }
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            const float dA = fast_exp2(q.z * a2[s]);
-            h[s] = fmaf(dA, h[s], q.w * Elem<T>::get(bw[buf][s], k + 1));
-            y1 = fmaf(Elem<T>::get(cw[buf][s], k + 1), h[s], y1);
+        for (int k = 0; k < G; k += 2) {
+            float y0 = 0.f, y1 = 0.f;
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                h[s] = fmaf(dA[k][s], h[s], bu[k][s]);
+                y0 = fmaf(cval(buf, s, k), h[s], y0);
+            }
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                h[s] = fmaf(dA[k + 1][s], h[s], bu[k + 1][s]);
+                y1 = fmaf(cval(buf, s, k + 1), h[s], y1);
+            }
+            s_y[w][gi * (G / 2) + k / 2][cs] = make_float2(y0, y1);
         }
-        s_y[w][gi * (G / 2) + k / 2][cs] = make_float2(y0, y1);
     };
 
     // One chunk: stage, scan, epilogue.  (cu, cdl, cz) hold this chunk's
@@ -218,8 +240,7 @@ __global__ __launch_bounds__(NW * 64) void s6_scan_kernel(
                 load_bc(t0 + TC, bw[nxt], cw[nxt]);
             }
             __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int k = 0; k < G; k += 2) pair(cur, gi, k);
+            group(cur, gi);
             lgkm_wait_all();
         }
         __syncthreads();
@@ -289,7 +310,10 @@ hipError_t launch_cfg(const S6Params& p, hipStream_t stream) {
     // The aligned path addresses a block's rows through 32-bit buffer
     // offsets, and reads B / C in whole 16-byte groups.
     const bool aligned = (p.L % 8 == 0) && int64_t(64) * p.L * int64_t(sizeof(T)) < (int64_t(1) << 31);
-    auto kern = aligned ? s6_scan_kernel<T, NW, NS, TC, true, RING> : s6_scan_kernel<T, NW, NS, TC, false, RING>;
+    const bool fulln = p.N == NW * NS;
+    auto kern = aligned ? (fulln ? s6_scan_kernel<T, NW, NS, TC, true, true, RING>
+                                 : s6_scan_kernel<T, NW, NS, TC, true, false, RING>)
+                        : s6_scan_kernel<T, NW, NS, TC, false, false, RING>;
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(NW * 64), 0, stream, static_cast<const T*>(p.u),
                        static_cast<const T*>(p.delta), static_cast<const T*>(p.Bm), static_cast<const T*>(p.Cm),
                        static_cast<const T*>(p.z), p.A, p.Dskip, p.h0, static_cast<T*>(p.y), p.h_final, p.dim,
