@@ -11,13 +11,16 @@ converts arrays to contiguous float64 and calls it.  See the C file's header
 for what is computed and which passages of the pages it follows:
 
 * S6 selective scan -- "Mamba Architecture Details" page, "Selective State
-  Space Mechanism / How S6 Works" (update and output), SSM optimisation
-  Optimization Patterns page, section 7 (A_bar = exp(delta*A)) and section 6 (skip term D x),
-  gated by silu(z).
+  Space Mechanism / How S6 Works" (update and output); "State-Space Model
+  Optimization Patterns" page, section 7 (A_bar = exp(delta*A)) and section 6
+  (skip term D x); gated by silu(z).
 * Decode step -- the same update for one token, state updated in place
   ("Hardware-Aware Implementation / Parallel Algorithm", sequential mode).
-* Mamba-2 SSD -- Optimization Patterns page, section 2 "State Space Duality": the recurrence on
-  (head, head channel) with a scalar A per head.
+* Mamba-2 SSD -- Optimization Patterns page, section 2 "State Space Duality":
+  the recurrence on (head, head channel) with a scalar A per head.
+* Mamba-2 decode step -- one token of that recurrence with the state
+  [b, H, P, N] updated in place ("Mamba - Selective State Space Models"
+  page, "Workflow 3": the Mamba-2 block with headdim and d_state).
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` against closed
 forms, brute force, invariants and hand-worked values (``tests/golden``).
@@ -156,3 +159,18 @@ def ssd(x, dt, A, B, C, D=None, z=None, h0=None, nthreads=None, lib=None):
     if rc != 0:
         raise RuntimeError("oracle_ssd failed")
     return y, hT
+
+
+def ssd_state_update(state, x, dt, A, B, C, D=None, z=None, nthreads=None, lib=None):
+    """One Mamba-2 decode token: the SSD recurrence with seqlen 1 starting
+    from `state`.  state: [b, H, P, N]; x, z: [b, H, P]; dt: [b, H];
+    A: [H]; B, C: [b, G, N]; D: [H].  Returns (y [b, H, P], new state
+    [b, H, P, N]) in fp64; `state` itself is not modified."""
+    x, dt, B, C = map(_f64, (x, dt, B, C))
+    bsz, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    assert dt.shape == (bsz, H) and B.shape == (bsz, G, N) and C.shape == B.shape
+    assert np.shape(state) == (bsz, H, P, N)
+    y, hT = ssd(x[:, None], dt[:, None], A, B[:, None], C[:, None], D,
+                None if z is None else _f64(z)[:, None], state, nthreads=nthreads, lib=lib)
+    return y[:, 0], hT

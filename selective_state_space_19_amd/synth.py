@@ -178,12 +178,40 @@ def ssd_inputs(batch, seqlen, nheads, headdim, d_state, ngroups=1, dtype="bf16",
 
 
 # --------------------------------------------------------------------------
-# The five named workloads (Mamba layer shapes from the pages' model table)
+# Mamba-2 decode (single-token SSD state update) inputs
+# --------------------------------------------------------------------------
+def mamba2_decode_initial(batch, nheads, headdim, d_state, seed=0):
+    """Initial state [batch, nheads, headdim, d_state] f32 ~ N(0, 0.1); A [nheads]
+    = -U[1, 16); D [nheads] = 1; and the per-head softplus^-1(dt) used by every step."""
+    base = np.random.Generator(np.random.PCG64(seed))
+    A = (-base.uniform(1.0, 16.0, nheads)).astype(np.float32)
+    dt_inv = _softplus_inv(_dt_per_channel(base, nheads))[None, :]
+    state = base.normal(0.0, 0.1, (batch, nheads, headdim, d_state)).astype(np.float32)
+    D = np.ones(nheads, np.float32)
+    return dict(state=state, A=A, D=D, dt_inv=dt_inv)
+
+
+def mamba2_decode_step(init, step, batch, nheads, headdim, d_state, ngroups=1, dtype="bf16", seed=0,
+                       gate=True):
+    """Per-token inputs of Mamba-2 decode step `step`: x, z [batch, nheads, headdim];
+    dt [batch, nheads]; B, C [batch, ngroups, d_state] (stored dtype)."""
+    rng = np.random.Generator(np.random.PCG64([seed, 1000 + step]))
+    dt = round_to(_delta(rng, init["dt_inv"], (batch, nheads)), dtype)
+    x = round_to(rng.standard_normal((batch, nheads, headdim)), dtype)
+    zb = rng.standard_normal((batch, nheads, headdim))
+    z = round_to(zb, dtype) if gate else None
+    Bm = round_to(rng.standard_normal((batch, ngroups, d_state)), dtype)
+    Cm = round_to(rng.standard_normal((batch, ngroups, d_state)), dtype)
+    return dict(x=x, dt=dt, z=z, B=Bm, C=Cm, dtype=dtype)
+
+
+# --------------------------------------------------------------------------
+# The named workloads (Mamba layer shapes from the pages' model table)
 # --------------------------------------------------------------------------
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str                 # "s6" | "decode" | "ssd"
+    kind: str                 # "s6" | "decode" | "ssd" | "decode2"
     dtype: str
     seed: int
     shape: dict = field(default_factory=dict)
@@ -212,4 +240,8 @@ WORKLOADS = {
                                 dict(batch=4, seqlen=4096, nheads=32, headdim=64,
                                      d_state=128, ngroups=1, chunk=256),
                                 "Mamba-2 SSD chunked scan"),
+    # Mamba-2 layer decode (same layer as above), batch 64, 256 successive tokens.
+    "decode_mamba2_bf16": Workload("decode_mamba2_bf16", "decode2", "bf16", 19005,
+                                   dict(batch=64, nheads=32, headdim=64, d_state=128, ngroups=1, steps=256),
+                                   "Mamba-2 decode state update"),
 }

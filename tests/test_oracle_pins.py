@@ -265,6 +265,61 @@ def test_ssd_equals_s6_on_heads(oracle_lib):
 
 
 # ----------------------------------------------------------------------------
+# Mamba-2 decode step (one SSD token, state [b, H, P, N] in place)
+# ----------------------------------------------------------------------------
+def _rand_m2dec(rng, b, H, P, N, G):
+    return dict(state=rng.normal(0, 0.5, (b, H, P, N)), x=rng.standard_normal((b, H, P)),
+                dt=rng.uniform(0.01, 0.5, (b, H)), A=-rng.uniform(0.5, 4.0, H),
+                B=rng.standard_normal((b, G, N)), C=rng.standard_normal((b, G, N)),
+                D=rng.standard_normal(H), z=rng.standard_normal((b, H, P)))
+
+
+def test_mamba2_decode_steps_equal_ssd(oracle_lib):
+    """k decode steps from h0 reproduce one SSD pass over the same k tokens
+    (same y at every step, same final state)."""
+    rng = np.random.default_rng(21)
+    b, L, H, P, N, G = 2, 6, 4, 3, 5, 2
+    i = _rand_ssd(rng, b, L, H, P, N, G)
+    y_ref, h_ref = oracle.ssd(**i, lib=oracle_lib)
+    st = i["h0"].copy()
+    for t in range(L):
+        y, st = oracle.ssd_state_update(st, i["x"][:, t], i["dt"][:, t], i["A"], i["B"][:, t], i["C"][:, t],
+                                        i["D"], i["z"][:, t], lib=oracle_lib)
+        np.testing.assert_allclose(y, y_ref[:, t], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(st, h_ref, rtol=0, atol=1e-13)
+
+
+def test_mamba2_decode_zero_step(oracle_lib):
+    """dt = 0: the transition is the identity and the input term vanishes,
+    so the state is unchanged and y = (C . state + D x) silu(z)."""
+    rng = np.random.default_rng(22)
+    b, H, P, N, G = 3, 4, 5, 6, 2
+    i = _rand_m2dec(rng, b, H, P, N, G)
+    i["dt"][:] = 0.0
+    y, st = oracle.ssd_state_update(**i, lib=oracle_lib)
+    np.testing.assert_array_equal(st, i["state"])
+    g = np.arange(H) // (H // G)
+    cs = np.einsum("bhn,bhpn->bhp", i["C"][:, g, :], i["state"])
+    expect = (cs + i["D"][None, :, None] * i["x"]) * silu(i["z"])
+    np.testing.assert_allclose(y, expect, rtol=1e-13, atol=1e-13)
+
+
+def test_mamba2_decode_equals_s6_decode(oracle_lib):
+    """One group: the Mamba-2 step is the S6 decode step on d_inner = H*P
+    channels with A[(h,p), n] = A_h and delta[(h,p)] = dt[h]."""
+    rng = np.random.default_rng(23)
+    b, H, P, N = 2, 3, 4, 5
+    i = _rand_m2dec(rng, b, H, P, N, 1)
+    y, st = oracle.ssd_state_update(**i, lib=oracle_lib)
+    ys, ss = oracle.state_update(i["state"].reshape(b, H * P, N), i["x"].reshape(b, H * P),
+                                 np.repeat(i["dt"], P, axis=1), np.repeat(i["A"], P)[:, None] * np.ones((1, N)),
+                                 i["B"][:, 0], i["C"][:, 0], np.repeat(i["D"], P), i["z"].reshape(b, H * P),
+                                 lib=oracle_lib)
+    np.testing.assert_allclose(y.reshape(b, H * P), ys, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(st.reshape(b, H * P, N), ss, rtol=0, atol=1e-13)
+
+
+# ----------------------------------------------------------------------------
 # p11: the inputs both sides read
 # ----------------------------------------------------------------------------
 def test_bf16_rounding_matches_torch():
@@ -290,3 +345,15 @@ def test_generator_distributions():
     assert np.all(med > 5e-4) and np.all(med < 0.2)
     again = synth.s6_inputs(2, 64, 256, 16, dtype="f32", seed=1)
     np.testing.assert_array_equal(again["u"], inp["u"])
+
+
+def test_mamba2_decode_generator():
+    """Shapes and support of the Mamba-2 decode inputs."""
+    init = synth.mamba2_decode_initial(3, 4, 8, 16, seed=2)
+    assert init["state"].shape == (3, 4, 8, 16) and init["state"].dtype == np.float32
+    assert np.all(init["A"] <= -1.0) and np.all(init["A"] > -16.0)
+    tk = synth.mamba2_decode_step(init, 5, 3, 4, 8, 16, ngroups=2, dtype="bf16", seed=2)
+    assert tk["x"].shape == (3, 4, 8) and tk["dt"].shape == (3, 4) and tk["B"].shape == (3, 2, 16)
+    assert np.all(synth.widen(tk["dt"], "bf16") > 0)
+    again = synth.mamba2_decode_step(init, 5, 3, 4, 8, 16, ngroups=2, dtype="bf16", seed=2)
+    np.testing.assert_array_equal(again["x"], tk["x"])
