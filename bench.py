@@ -8,10 +8,10 @@ A "step" is one call of the scan over that batch.  `value` is the effective
 HBM bandwidth: algorithmic bytes (every input read once, every output
 written once) divided by the time per step; also reported: tokens-ch/s
 (batch*seqlen*d_inner per second), the roofline of the scan kernel, the
-fp64 CPU oracle timed on the same workload, and the other two entry points
+fp64 CPU oracle timed on the same workload, and the other entry points
 (decode step at the Mamba-2.8B shape, Mamba-2 SSD) inside the same object.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--only s6,decode,ssd,copy]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--only s6,decode,decode2,ssd,copy]
 
 Prints exactly one JSON line on stdout; progress goes to stderr.  `--only`
 restricts the run (for profiling); `copy` times a plain 1 GiB device copy,
@@ -60,6 +60,12 @@ def decode_bytes(batch, dim, N, esize, gate=True, skip=True):
     """State read + write; u, delta, (z), y; B, C; A; (D)."""
     return (2 * batch * dim * N * 4 + (3 + (1 if gate else 0)) * batch * dim * esize
             + 2 * batch * N * esize + dim * N * 4 + (dim * 4 if skip else 0))
+
+
+def decode2_bytes(batch, H, P, N, G, esize, gate=True, skip=True):
+    """Mamba-2 decode step: state read + write; x, (z), y; dt; B, C; A, (D)."""
+    return (2 * batch * H * P * N * 4 + (2 + (1 if gate else 0)) * batch * H * P * esize + batch * H * esize
+            + 2 * batch * G * N * esize + H * 4 + (H * 4 if skip else 0))
 
 
 def ssd_bytes(batch, L, H, P, N, G, esize, gate=False, skip=True, h0=False, final=False):
@@ -274,6 +280,62 @@ def bench_decode(args):
 
 
 # --------------------------------------------------------------------------
+# Mamba-2 decode (one SSD token)
+# --------------------------------------------------------------------------
+def bench_decode2(args):
+    import torch
+    import selective_state_space_19_amd as mssm
+    from selective_state_space_19_amd import synth
+    wl = synth.WORKLOADS["decode_mamba2_bf16"]
+    s = wl.shape
+    bsz, H, P, N, G, steps = s["batch"], s["nheads"], s["headdim"], s["d_state"], s["ngroups"], s["steps"]
+    log(f"[bench] mamba2 decode: generating {steps} tokens of inputs")
+    init = synth.mamba2_decode_initial(bsz, H, P, N, seed=wl.seed)
+    toks = [synth.mamba2_decode_step(init, i, bsz, H, P, N, ngroups=G, dtype=wl.dtype, seed=wl.seed)
+            for i in range(steps)]
+    dtk = [{k: to_dev(t[k]) for k in ("x", "dt", "z", "B", "C")} for t in toks]
+    A, D = to_dev(init["A"]), to_dev(init["D"])
+    # 8 state buffers (8 x 67 MB > the 256 MB Infinity Cache), token i uses i % 8.
+    K = 8
+    states = [to_dev(init["state"]) for _ in range(K)]
+    ys = [torch.empty((bsz, H, P), dtype=torch.bfloat16, device="cuda") for _ in range(steps)]
+    stream = torch.cuda.current_stream()
+    nb = decode2_bytes(bsz, H, P, N, G, 2)
+
+    def run_all(rot, strm=None):
+        for i in range(steps):
+            t = dtk[i]
+            mssm.ssd_state_update(states[i % K] if rot else states[0], t["x"], t["dt"], A, t["B"], t["C"], D, t["z"],
+                                  out=ys[i], stream=strm)
+
+    res = {"workload": f"{wl.name}: batch {bsz}, {H} heads x {P}, d_state {N}, ngroups {G}, bf16, {steps} tokens",
+           "bytes_per_step": nb, "traffic_bytes_per_launch": profiled_traffic("ssd_state_update_mamba2_decode.md")}
+    for label, rot in (("cold_8_buffers", True), ("hot_single_buffer", False)):
+        total, _ = time_launches(lambda: run_all(rot, stream), 3, 1, stream)
+        us = total / 3 / steps * 1e3
+        res[label + "_launches"] = {"us_per_step": us, "GBs": nb / (us * 1e-6) / 1e9}
+    try:
+        for label, rot in (("cold_8_buffers", True), ("hot_single_buffer", False)):
+            g = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                run_all(rot)
+            torch.cuda.current_stream().wait_stream(side)
+            with torch.cuda.graph(g):
+                run_all(rot)
+            total, _ = time_launches(g.replay, 5, 2, torch.cuda.current_stream())
+            us = total / 5 / steps * 1e3
+            res[label + "_graph"] = {"us_per_step": us, "GBs": nb / (us * 1e-6) / 1e9,
+                                     "hbm_frac": nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+    except Exception as e:  # reported, not hidden
+        res["graph_error"] = repr(e)
+    res["tokens_ch_per_s_cold_graph"] = (bsz * H * P / (res["cold_8_buffers_graph"]["us_per_step"] * 1e-6)
+                                         if "cold_8_buffers_graph" in res else None)
+    return res
+
+
+# --------------------------------------------------------------------------
 # Mamba-2 SSD
 # --------------------------------------------------------------------------
 def bench_ssd(args):
@@ -328,7 +390,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="s6,decode,ssd")
+    ap.add_argument("--only", default="s6,decode,decode2,ssd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
     args = ap.parse_args()
@@ -388,6 +450,11 @@ def main():
             out["secondary_decode"] = bench_decode(args)
         except Exception as e:  # reported, not hidden
             out["secondary_decode"] = {"error": repr(e)}
+    if "decode2" in parts:
+        try:
+            out["secondary_mamba2_decode"] = bench_decode2(args)
+        except Exception as e:
+            out["secondary_mamba2_decode"] = {"error": repr(e)}
     if "ssd" in parts:
         try:
             out["secondary_ssd"] = bench_ssd(args)

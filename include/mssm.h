@@ -2,12 +2,13 @@
  * mssm.h -- C ABI of libmssm.so, the MI355X (gfx950) selective state-space
  * scan library.
  *
- * Three operations, each defined by the pages it cites:
+ * Four operations, each defined by the pages it cites:
  *
  *   mssm_selective_scan_fwd  the S6 selective scan over a whole sequence;
  *   mssm_state_update        one decode token of the same recurrence;
  *   mssm_ssd_chunk_fwd       the Mamba-2 SSD (scalar transition per head),
- *                            computed chunk by chunk.
+ *                            computed chunk by chunk;
+ *   mssm_ssd_state_update    one Mamba-2 decode token of that recurrence.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -165,6 +166,40 @@ int mssm_ssd_chunk_fwd(const void* x, const void* dt, const float* A, const void
                        int64_t nheads, int64_t headdim, int64_t d_state, int64_t ngroups,
                        int64_t chunk, void* workspace, size_t workspace_bytes,
                        mssm_dtype dtype, void* stream);
+
+/*
+ * Mamba-2 decode: one token of the SSD recurrence, state updated in place.
+ *
+ * Defined by: "Mamba - Selective State Space Models" page, "Workflow 3" --
+ * the Mamba-2 block (multi-head, headdim, d_state, ngroups); "State-Space
+ * Model Optimization Patterns" page, section 2 -- a scalar transition per
+ * head; "Mamba Architecture Details" page, "Hardware-Aware Implementation",
+ * sequential mode -- a constant-size state updated per token, y read from
+ * the UPDATED state.  For every (b, head h, head channel p), with group
+ * g = h / (nheads / ngroups):
+ *
+ *   state[b,h,p,n] <- exp(dt[b,h] * A[h]) * state[b,h,p,n] + dt[b,h] * x[b,h,p] * Bm[b,g,n]
+ *   y[b,h,p] = (sum_n Cm[b,g,n] * state[b,h,p,n] + D[h] * x[b,h,p]) * silu(z[b,h,p])
+ *
+ * It equals one token of mssm_ssd_chunk_fwd started from h0 = state.
+ *
+ *   state      (device) [batch, nheads, headdim, d_state] float32, read and overwritten
+ *   x          (device) [batch, nheads, headdim] dtype
+ *   dt         (device) [batch, nheads] dtype (positive; used as given)
+ *   A          (device) [nheads] float32
+ *   Bm, Cm     (device) [batch, ngroups, d_state] dtype
+ *   Dskip      (device) [nheads] float32, NULL => no skip term
+ *   z          (device) [batch, nheads, headdim] dtype, NULL => no gate
+ *   y          (device) [batch, nheads, headdim] dtype, output
+ *
+ * Limits: d_state in {16, 32, 64, 128, 256} (MSSM_ERR_UNSUPPORTED otherwise);
+ * nheads % ngroups == 0 (MSSM_ERR_SHAPE).  batch, nheads or headdim = 0 is a
+ * no-op.
+ */
+int mssm_ssd_state_update(float* state, const void* x, const void* dt, const float* A,
+                          const void* Bm, const void* Cm, const float* Dskip, const void* z,
+                          void* y, int64_t batch, int64_t nheads, int64_t headdim,
+                          int64_t d_state, int64_t ngroups, mssm_dtype dtype, void* stream);
 
 /* Message for the calling thread's last non-OK return ("" if none). */
 const char* mssm_last_error(void);

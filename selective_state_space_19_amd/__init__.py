@@ -10,7 +10,7 @@ from __future__ import annotations
 
 from ._lib import MSSM_BF16, MSSM_F32, MssmError, check, lib
 
-__all__ = ["selective_scan", "state_update", "ssd_chunk", "ssd_workspace_size", "MssmError", "lib"]
+__all__ = ["selective_scan", "state_update", "ssd_chunk", "ssd_state_update", "ssd_workspace_size", "MssmError", "lib"]
 
 
 def _torch():
@@ -109,6 +109,33 @@ def state_update(state, u, delta, A, B, C, D=None, z=None, *, out=None, stream=N
     _dev(y, "out", (bsz, dim), dt, dev)
     check(lib().mssm_state_update(_ptr(state), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
                                   _ptr(z), _ptr(y), bsz, dim, N, code, _stream(stream, dev)))
+    return y
+
+
+def ssd_state_update(state, x, dt, A, B, C, D=None, z=None, *, out=None, stream=None):
+    """One Mamba-2 decode token; `state` [b, H, P, N] float32 is updated in
+    place.  x, z: [b, H, P]; dt: [b, H]; B, C: [b, G, N]; A, D: [H] float32.
+    Returns y [b, H, P]."""
+    torch = _torch()
+    dev = state.device
+    state = _dev(state, "state", dtype=torch.float32)
+    if not state.is_contiguous():
+        raise ValueError("state must be contiguous (it is updated in place)")
+    bsz, H, P, N = state.shape
+    G = B.shape[1]
+    ty = x.dtype
+    code = _dtype_code(x)
+    x = _dev(x, "x", (bsz, H, P), ty, dev)
+    dt = _dev(dt, "dt", (bsz, H), ty, dev)
+    z = _dev(z, "z", (bsz, H, P), ty, dev)
+    B = _dev(B, "B", (bsz, G, N), ty, dev)
+    C = _dev(C, "C", (bsz, G, N), ty, dev)
+    A = _dev(A, "A", (H,), torch.float32, dev)
+    D = _dev(D, "D", (H,), torch.float32, dev)
+    y = out if out is not None else torch.empty((bsz, H, P), dtype=ty, device=dev)
+    _dev(y, "out", (bsz, H, P), ty, dev)
+    check(lib().mssm_ssd_state_update(_ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                      _ptr(z), _ptr(y), bsz, H, P, N, G, code, _stream(stream, dev)))
     return y
 
 

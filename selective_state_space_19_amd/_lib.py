@@ -41,6 +41,8 @@ def _bind(lib):
     lib.mssm_selective_scan_fwd.restype = _i32
     lib.mssm_state_update.argtypes = [_vp] * 9 + [_i64] * 3 + [_i32, _vp]
     lib.mssm_state_update.restype = _i32
+    lib.mssm_ssd_state_update.argtypes = [_vp] * 9 + [_i64] * 5 + [_i32, _vp]
+    lib.mssm_ssd_state_update.restype = _i32
     lib.mssm_ssd_workspace_size.argtypes = [_i64] * 7
     lib.mssm_ssd_workspace_size.restype = _sz
     lib.mssm_ssd_chunk_fwd.argtypes = [_vp] * 10 + [_i64] * 7 + [_vp, _sz, _i32, _vp]

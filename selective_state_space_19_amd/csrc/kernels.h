@@ -51,6 +51,20 @@ struct SSDParams {
     int32_t L, H, P, N, G, Q;
 };
 
+struct SSDUParams {
+    float* state;         // [batch, H, P, N] fp32, in place
+    const void* x;        // [batch, H, P]
+    const void* dt;       // [batch, H]
+    const float* A;       // [H]
+    const void* Bm;       // [batch, G, N]
+    const void* Cm;       // [batch, G, N]
+    const float* Dskip;   // nullable, [H]
+    const void* z;        // nullable, [batch, H, P]
+    void* y;              // [batch, H, P]
+    int64_t batch;
+    int32_t H, P, N, G;
+};
+
 // Each returns hipSuccess or the launch error; is_bf16 selects the storage type.
 hipError_t launch_s6_scan(const S6Params& p, bool is_bf16, hipStream_t stream);
 hipError_t launch_state_update(const SUParams& p, bool is_bf16, hipStream_t stream);
@@ -58,6 +72,9 @@ hipError_t launch_ssd(const SSDParams& p, hipStream_t stream);
 size_t ssd_workspace_bytes(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int64_t Q);
 // Sizes the SSD kernels implement (headdim, d_state, chunk, 32-bit offsets).
 bool ssd_supported(int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int64_t Q);
+hipError_t launch_ssd_state_update(const SSDUParams& p, bool is_bf16, hipStream_t stream);
+// d_state values the Mamba-2 decode kernel implements.
+bool ssd_state_update_supported(int64_t N);
 // dst[i] = src ? src[i] : 0 for i < n (used for zero-length sequences).
 hipError_t launch_copy_or_zero(float* dst, const float* src, int64_t n, hipStream_t stream);
 

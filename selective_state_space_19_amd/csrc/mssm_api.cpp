@@ -125,6 +125,39 @@ int mssm_state_update(float* state, const void* u, const void* delta, const floa
     return launched(fn, mssm::launch_state_update(p, dtype == MSSM_BF16, static_cast<hipStream_t>(stream)));
 }
 
+int mssm_ssd_state_update(float* state, const void* x, const void* dt, const float* A, const void* Bm,
+                          const void* Cm, const float* Dskip, const void* z, void* y, int64_t batch,
+                          int64_t nheads, int64_t headdim, int64_t d_state, int64_t ngroups, mssm_dtype dtype,
+                          void* stream) {
+    static const char* fn = "mssm_ssd_state_update";
+    g_err.clear();
+    if (dtype != MSSM_F32 && dtype != MSSM_BF16) return fail(MSSM_ERR_DTYPE, "%s: unknown dtype %d", fn, (int)dtype);
+    if (batch < 0 || nheads < 0 || headdim < 0 || d_state < 0 || ngroups < 0)
+        return fail(MSSM_ERR_SHAPE, "%s: negative dimension", fn);
+    if (batch == 0 || nheads == 0 || headdim == 0) return MSSM_OK;
+    if (ngroups < 1 || nheads % ngroups != 0)
+        return fail(MSSM_ERR_SHAPE, "%s: nheads %lld not a multiple of ngroups %lld", fn, (long long)nheads,
+                    (long long)ngroups);
+    if (!mssm::ssd_state_update_supported(d_state))
+        return fail(MSSM_ERR_UNSUPPORTED, "%s: d_state %lld not in {16, 32, 64, 128, 256}", fn, (long long)d_state);
+    int64_t rows = 0;
+    if (!prod_ok(batch, nheads, headdim, &rows) || !prod_ok(rows, d_state, 1, nullptr) || nheads > INT32_MAX ||
+        headdim > INT32_MAX || !prod_ok(batch, ngroups, d_state, nullptr))
+        return fail(MSSM_ERR_SHAPE, "%s: tensor too large", fn);
+    CHECK_PTR(state);
+    CHECK_PTR(x);
+    CHECK_PTR(dt);
+    CHECK_PTR(A);
+    CHECK_PTR(Bm);
+    CHECK_PTR(Cm);
+    CHECK_PTR(y);
+    CHECK_OPT(Dskip);
+    CHECK_OPT(z);
+    mssm::SSDUParams p{state, x, dt, A, Bm, Cm, Dskip, z, y, batch, (int32_t)nheads, (int32_t)headdim,
+                       (int32_t)d_state, (int32_t)ngroups};
+    return launched(fn, mssm::launch_ssd_state_update(p, dtype == MSSM_BF16, static_cast<hipStream_t>(stream)));
+}
+
 size_t mssm_ssd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                                int64_t d_state, int64_t ngroups, int64_t chunk) {
     if (batch < 0 || seqlen < 0 || nheads < 1 || headdim < 1 || d_state < 1 || ngroups < 1 || chunk < 1)

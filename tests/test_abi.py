@@ -19,7 +19,7 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = _lib.header_functions()
     assert set(names) == {"mssm_selective_scan_fwd", "mssm_state_update", "mssm_ssd_workspace_size",
-                          "mssm_ssd_chunk_fwd", "mssm_last_error", "mssm_version"}
+                          "mssm_ssd_chunk_fwd", "mssm_ssd_state_update", "mssm_last_error", "mssm_version"}
     for n in names:
         assert hasattr(lib, n), n
         assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
@@ -98,3 +98,23 @@ def test_workspace_size_is_pure(lib):
     a = lib.mssm_ssd_workspace_size(4, 4096, 32, 64, 128, 1, 256)
     assert a == lib.mssm_ssd_workspace_size(4, 4096, 32, 64, 128, 1, 256)
     assert lib.mssm_ssd_workspace_size(-1, 4096, 32, 64, 128, 1, 256) == 0
+
+
+def _m2(lib, **kw):
+    a = dict(state=FAKE, x=FAKE, dt=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, y=FAKE,
+             b=2, H=4, P=64, N=128, G=1, dtype=1)
+    a.update(kw)
+    return lib.mssm_ssd_state_update(a["state"], a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["z"], a["y"],
+                                     a["b"], a["H"], a["P"], a["N"], a["G"], a["dtype"], None)
+
+
+def test_ssd_state_update_argument_errors(lib):
+    assert _m2(lib, state=None) == ERR_NULL
+    assert _m2(lib, dt=None) == ERR_NULL
+    assert _m2(lib, dtype=5) == ERR_DTYPE
+    assert _m2(lib, N=48) == ERR_UNSUP
+    assert _m2(lib, N=512) == ERR_UNSUP
+    assert _m2(lib, H=3, G=2) == ERR_SHAPE
+    assert _m2(lib, P=-1) == ERR_SHAPE
+    assert _m2(lib, z=MISALIGNED) == ERR_ALIGN
+    assert _m2(lib, b=0) == 0
