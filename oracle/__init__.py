@@ -174,3 +174,40 @@ def ssd_state_update(state, x, dt, A, B, C, D=None, z=None, nthreads=None, lib=N
     y, hT = ssd(x[:, None], dt[:, None], A, B[:, None], C[:, None], D,
                 None if z is None else _f64(z)[:, None], state, nthreads=nthreads, lib=lib)
     return y[:, 0], hT
+
+
+def causal_conv_silu(x, conv_w, conv_b=None, conv_init=None):
+    """u = silu(causal depthwise conv1d(x)) in fp64 ("Mamba Architecture
+    Details" page, "Model Configuration": d_conv; "Mamba Block Structure":
+    the convolution and SiLU before the SSM).  x: [b, d, L]; conv_w: [d, K];
+    conv_b: [d]; conv_init: [b, d, K-1], the K-1 inputs preceding x (zeros if
+    None).  u[b, d, t] = silu(sum_k conv_w[d, k] * xx[b, d, t + k] + conv_b[d])
+    with xx = concat(conv_init, x) along t."""
+    x, w = _f64(x), _f64(conv_w)
+    bsz, dim, L = x.shape
+    K = w.shape[1]
+    init = np.zeros((bsz, dim, K - 1)) if conv_init is None else _f64(conv_init)
+    xx = np.concatenate([init, x], axis=2)
+    acc = np.zeros((bsz, dim, L))
+    for k in range(K):
+        acc += w[None, :, k, None] * xx[:, :, k:k + L]
+    if conv_b is not None:
+        acc += _f64(conv_b)[None, :, None]
+    return acc / (1.0 + np.exp(-acc))
+
+
+def softplus(v):
+    """log(1 + e^v), evaluated without overflow."""
+    return np.logaddexp(0.0, _f64(v))
+
+
+def s6_scan_fused(x, conv_w, conv_b, conv_init, delta_raw, delta_bias, A, B, C, D=None, z=None, h0=None,
+                  nthreads=None, lib=None):
+    """The S6 scan with its front end: u = causal_conv_silu(x, ...),
+    delta = softplus(delta_raw + delta_bias), then s6_scan.  Returns
+    (y, h_final) in fp64."""
+    u = causal_conv_silu(x, conv_w, conv_b, conv_init)
+    dr = _f64(delta_raw)
+    if delta_bias is not None:
+        dr = dr + _f64(delta_bias)[None, :, None]
+    return s6_scan(u, softplus(dr), A, B, C, D, z, h0, nthreads=nthreads, lib=lib)

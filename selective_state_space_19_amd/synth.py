@@ -117,6 +117,45 @@ def s6_inputs(batch, d_inner, seqlen, d_state, dtype="f32", seed=0,
     return dict(u=u, delta=dl, A=A, B=Bm, C=Cm, D=D, z=z, h0=h0, dtype=dtype)
 
 
+def s6_fused_inputs(batch, d_inner, seqlen, d_state, d_conv=4, dtype="f32", seed=0, gate=True, skip=True,
+                    init_state=False, conv_history=False):
+    """Inputs of the scan with its front end: x (before the causal conv) and
+    the raw step delta_raw (before softplus) [B, D, L] in the stored dtype;
+    conv_w [D, d_conv] and conv_b [D] ~ U(-1/sqrt(d_conv), 1/sqrt(d_conv))
+    (the default init of a depthwise conv1d); delta_bias[d] =
+    softplus^-1(dt[d]) and delta_raw = 0.5 eps, so that
+    softplus(delta_raw + delta_bias) has the distribution of s6_inputs'
+    delta; conv_init [B, D, d_conv - 1] (stored dtype) if conv_history; the
+    rest as s6_inputs."""
+    base = np.random.Generator(np.random.PCG64(seed))
+    dt_inv = _softplus_inv(_dt_per_channel(base, d_inner))
+    bound = 1.0 / np.sqrt(d_conv)
+    conv_w = base.uniform(-bound, bound, (d_inner, d_conv)).astype(np.float32)
+    conv_b = base.uniform(-bound, bound, d_inner).astype(np.float32)
+    h0 = base.normal(0.0, 0.1, (batch, d_inner, d_state)).astype(np.float32) if init_state else None
+    store = np.uint16 if dtype == "bf16" else np.float32
+    x = np.empty((batch, d_inner, seqlen), store)
+    dr = np.empty((batch, d_inner, seqlen), store)
+    z = np.empty((batch, d_inner, seqlen), store) if gate else None
+    Bm = np.empty((batch, d_state, seqlen), store)
+    Cm = np.empty((batch, d_state, seqlen), store)
+    ci = np.empty((batch, d_inner, d_conv - 1), store) if conv_history else None
+    for b in range(batch):
+        rng = np.random.Generator(np.random.PCG64([seed, b]))
+        dr[b] = round_to(0.5 * rng.standard_normal((d_inner, seqlen)), dtype)
+        x[b] = round_to(rng.standard_normal((d_inner, seqlen)), dtype)
+        Bm[b] = round_to(rng.standard_normal((d_state, seqlen)), dtype)
+        Cm[b] = round_to(rng.standard_normal((d_state, seqlen)), dtype)
+        if gate:
+            z[b] = round_to(rng.standard_normal((d_inner, seqlen)), dtype)
+        if conv_history:
+            ci[b] = round_to(rng.standard_normal((d_inner, d_conv - 1)), dtype)
+    A = np.broadcast_to(-(np.arange(d_state, dtype=np.float32) + 1.0), (d_inner, d_state)).copy()
+    D = np.ones(d_inner, np.float32) if skip else None
+    return dict(x=x, conv_w=conv_w, conv_b=conv_b, conv_init=ci, delta_raw=dr,
+                delta_bias=dt_inv.astype(np.float32), A=A, B=Bm, C=Cm, D=D, z=z, h0=h0, dtype=dtype)
+
+
 # --------------------------------------------------------------------------
 # Decode (single-token state update) inputs
 # --------------------------------------------------------------------------
@@ -240,6 +279,10 @@ WORKLOADS = {
                                 dict(batch=4, seqlen=4096, nheads=32, headdim=64,
                                      d_state=128, ngroups=1, chunk=256),
                                 "Mamba-2 SSD chunked scan"),
+    # Mamba-1.4B layer S6 scan with its front end (causal conv d_conv 4 + SiLU, softplus step).
+    "s6fused_mamba1p4b_bf16": Workload("s6fused_mamba1p4b_bf16", "s6fused", "bf16", 19006,
+                                       dict(batch=4, d_inner=4096, seqlen=8192, d_state=16, d_conv=4),
+                                       "Mamba-1.4B layer shape S6 scan with fused conv1d front end"),
     # Mamba-2 layer decode (same layer as above), batch 64, 256 successive tokens.
     "decode_mamba2_bf16": Workload("decode_mamba2_bf16", "decode2", "bf16", 19005,
                                    dict(batch=64, nheads=32, headdim=64, d_state=128, ngroups=1, steps=256),

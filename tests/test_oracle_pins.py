@@ -357,3 +357,80 @@ def test_mamba2_decode_generator():
     assert np.all(synth.widen(tk["dt"], "bf16") > 0)
     again = synth.mamba2_decode_step(init, 5, 3, 4, 8, 16, ngroups=2, dtype="bf16", seed=2)
     np.testing.assert_array_equal(again["x"], tk["x"])
+
+
+
+# ----------------------------------------------------------------------------
+# Front end: causal depthwise conv1d + SiLU, softplus of the raw step
+# ----------------------------------------------------------------------------
+def test_conv_matches_numpy_convolve():
+    """Each channel's causal conv equals numpy's full convolution with the
+    reversed kernel, truncated to the first L outputs."""
+    rng = np.random.default_rng(31)
+    b, d, L, K = 2, 5, 17, 4
+    x, w, cb = rng.standard_normal((b, d, L)), rng.standard_normal((d, K)), rng.standard_normal(d)
+    u = oracle.causal_conv_silu(x, w, cb)
+    for bi in range(b):
+        for di in range(d):
+            a = np.convolve(x[bi, di], w[di, ::-1])[:L] + cb[di]
+            np.testing.assert_allclose(u[bi, di], a / (1 + np.exp(-a)), rtol=1e-13, atol=1e-13)
+
+
+def test_conv_identity_kernel_is_silu():
+    rng = np.random.default_rng(32)
+    x = rng.standard_normal((1, 3, 9))
+    w = np.zeros((3, 4))
+    w[:, 3] = 1.0
+    np.testing.assert_allclose(oracle.causal_conv_silu(x, w), silu(x), rtol=1e-14, atol=0)
+
+
+def test_conv_is_causal_and_uses_history():
+    """A change at token t0 leaves u[:t0] unchanged; the history enters only
+    the first K-1 outputs."""
+    rng = np.random.default_rng(33)
+    x, w = rng.standard_normal((1, 2, 12)), rng.standard_normal((2, 4))
+    u0 = oracle.causal_conv_silu(x, w)
+    x2 = x.copy()
+    x2[:, :, 7] += 1.0
+    u1 = oracle.causal_conv_silu(x2, w)
+    np.testing.assert_array_equal(u0[:, :, :7], u1[:, :, :7])
+    assert np.all(u0[:, :, 7] != u1[:, :, 7])
+    hist = rng.standard_normal((1, 2, 3))
+    u2 = oracle.causal_conv_silu(x, w, conv_init=hist)
+    np.testing.assert_array_equal(u2[:, :, 3:], u0[:, :, 3:])
+
+
+def test_softplus_closed_forms():
+    np.testing.assert_allclose(oracle.softplus(np.array([0.0])), [math.log(2.0)], rtol=1e-15)
+    np.testing.assert_allclose(oracle.softplus(np.array([800.0])), [800.0], rtol=1e-15)
+    np.testing.assert_allclose(oracle.softplus(np.array([-50.0])), [math.exp(-50.0)], rtol=1e-12)
+
+
+def test_fused_chaining(oracle_lib):
+    """Two calls, the second fed the last K-1 inputs and the final state of
+    the first, equal one call over the whole sequence."""
+    rng = np.random.default_rng(34)
+    b, d, L, N, K, L1 = 2, 3, 20, 4, 4, 9
+    x, dr = rng.standard_normal((b, d, L)), rng.standard_normal((b, d, L)) - 2.0
+    w, cb, db = rng.standard_normal((d, K)), rng.standard_normal(d), rng.standard_normal(d) * 0.1
+    A = -rng.uniform(0.5, 3.0, (d, N))
+    Bm, Cm, z = rng.standard_normal((b, N, L)), rng.standard_normal((b, N, L)), rng.standard_normal((b, d, L))
+    D = rng.standard_normal(d)
+    y, hT = oracle.s6_scan_fused(x, w, cb, None, dr, db, A, Bm, Cm, D, z, lib=oracle_lib)
+    y1, h1 = oracle.s6_scan_fused(x[:, :, :L1], w, cb, None, dr[:, :, :L1], db, A, Bm[:, :, :L1], Cm[:, :, :L1],
+                                  D, z[:, :, :L1], lib=oracle_lib)
+    y2, h2 = oracle.s6_scan_fused(x[:, :, L1:], w, cb, x[:, :, L1 - K + 1:L1], dr[:, :, L1:], db, A, Bm[:, :, L1:],
+                                  Cm[:, :, L1:], D, z[:, :, L1:], h1, lib=oracle_lib)
+    np.testing.assert_allclose(np.concatenate([y1, y2], axis=2), y, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(h2, hT, rtol=0, atol=1e-12)
+
+
+def test_fused_generator_matches_step_distribution():
+    """softplus(delta_raw + delta_bias) of the fused inputs is positive and
+    centred like s6_inputs' delta; conv weights are bounded by 1/sqrt(d_conv)."""
+    inp = synth.s6_fused_inputs(2, 64, 256, 16, d_conv=4, dtype="f32", seed=3, conv_history=True)
+    delta = oracle.softplus(inp["delta_raw"].astype(np.float64) + inp["delta_bias"][None, :, None])
+    assert np.all(delta > 0)
+    med = np.median(delta, axis=(0, 2))
+    assert np.all(med > 5e-4) and np.all(med < 0.2)
+    assert np.all(np.abs(inp["conv_w"]) <= 0.5) and inp["conv_init"].shape == (2, 64, 3)
