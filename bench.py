@@ -11,7 +11,7 @@ written once) divided by the time per step; also reported: tokens-ch/s
 fp64 CPU oracle timed on the same workload, and the other entry points
 (decode step at the Mamba-2.8B shape, Mamba-2 SSD) inside the same object.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--only s6,decode,decode2,ssd,copy]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--only s6,s6fused,decode,decode2,ssd,copy]
 
 Prints exactly one JSON line on stdout; progress goes to stderr.  `--only`
 restricts the run (for profiling); `copy` times a plain 1 GiB device copy,
@@ -172,6 +172,34 @@ def bench_s6(args):
     nbytes = s6_bytes(s["batch"], s["d_inner"], s["seqlen"], s["d_state"], 2 if wl.dtype == "bf16" else 4)
     return dict(wl=wl, inp=inp, y=y, hf=hf, ms=wall[0] / args.steps, event_ms=total_ms / args.steps, per=per,
                 kern_ms=float(np.mean(per)), bytes=nbytes)
+
+
+def bench_s6fused(args):
+    """The scan with its front end fused in, same layer shape as the headline."""
+    import torch
+    import selective_state_space_19_amd as mssm
+    from selective_state_space_19_amd import synth
+    wl = synth.WORKLOADS["s6fused_mamba1p4b_bf16"]
+    s = wl.shape
+    log(f"[bench] s6 fused: generating {wl.name} inputs")
+    inp = synth.s6_fused_inputs(**s, dtype=wl.dtype, seed=wl.seed)
+    d = {k: to_dev(inp[k]) for k in ("x", "conv_w", "conv_b", "delta_raw", "delta_bias", "A", "B", "C", "D", "z")}
+    y = torch.empty_like(d["x"])
+    hf = torch.empty((s["batch"], s["d_inner"], s["d_state"]), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        mssm.selective_scan_fused(d["x"], d["conv_w"], d["delta_raw"], d["A"], d["B"], d["C"], d["D"], d["z"],
+                                  conv_b=d["conv_b"], delta_bias=d["delta_bias"], out=y, h_final=hf, stream=stream)
+
+    total, per = time_launches(step, max(5, args.steps // 2), 2, stream)
+    ms = total / max(5, args.steps // 2)
+    nb = s6_bytes(s["batch"], s["d_inner"], s["seqlen"], s["d_state"], 2) + s["d_inner"] * (s["d_conv"] + 2) * 4
+    tok = s["batch"] * s["d_inner"] * s["seqlen"]
+    return {"workload": f"{wl.name}: batch {s['batch']}, d_inner {s['d_inner']}, seqlen {s['seqlen']}, "
+                        f"d_state {s['d_state']}, d_conv {s['d_conv']}, bf16",
+            "us": ms * 1e3, "GBs": nb / (ms * 1e-3) / 1e9, "hbm_frac": nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "tokens_ch_per_s": tok / (ms * 1e-3), "algorithmic_bytes": nb}
 
 
 def parity_sample(inp, y, hf, rows=32, seed=0):
@@ -390,7 +418,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="s6,decode,decode2,ssd")
+    ap.add_argument("--only", default="s6,s6fused,decode,decode2,ssd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
     args = ap.parse_args()
@@ -445,6 +473,11 @@ def main():
             log("[bench] s6: cpu baseline (the oracle on the same workload)")
             out["cpu_baseline"] = cpu_baseline(r["inp"])
         del r
+    if "s6fused" in parts:
+        try:
+            out["secondary_s6_fused_front_end"] = bench_s6fused(args)
+        except Exception as e:  # reported, not hidden
+            out["secondary_s6_fused_front_end"] = {"error": repr(e)}
     if "decode" in parts:
         try:
             out["secondary_decode"] = bench_decode(args)

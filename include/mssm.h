@@ -2,9 +2,11 @@
  * mssm.h -- C ABI of libmssm.so, the MI355X (gfx950) selective state-space
  * scan library.
  *
- * Four operations, each defined by the pages it cites:
+ * Five operations, each defined by the pages it cites:
  *
  *   mssm_selective_scan_fwd  the S6 selective scan over a whole sequence;
+ *   mssm_selective_scan_fused_fwd  the same scan with its input front end
+ *                            (causal conv1d + SiLU, softplus step) fused in;
  *   mssm_state_update        one decode token of the same recurrence;
  *   mssm_ssd_chunk_fwd       the Mamba-2 SSD (scalar transition per head),
  *                            computed chunk by chunk;
@@ -91,6 +93,42 @@ int mssm_selective_scan_fwd(const void* u, const void* delta, const float* A,
                             const void* z, const float* h0, void* y, float* h_final,
                             int64_t batch, int64_t d_inner, int64_t seqlen,
                             int64_t d_state, mssm_dtype dtype, void* stream);
+
+/*
+ * S6 selective scan with its front end fused in (forward).
+ *
+ * Defined by: "Mamba Architecture Details" page, "Hardware-Aware
+ * Implementation / CUDA Kernel Optimizations" -- discretisation, the
+ * recurrence and the 1-D convolution fused in one kernel; "Model
+ * Configuration" -- d_conv (4 in the configurations); "Mamba Block
+ * Structure" -- the causal convolution and SiLU that produce the SSM input;
+ * "Initialization Strategy" -- the step is a softplus of a projection plus
+ * a bias.  For every (b, d, t), with xx = concat(conv_init[b,d,:], x[b,d,:])
+ * (conv_init taken as zeros when NULL):
+ *
+ *   u[b,d,t]     = silu(sum_{k<d_conv} conv_w[d,k] * xx[b,d,t+k] + conv_b[d])
+ *   delta[b,d,t] = softplus(delta_raw[b,d,t] + delta_bias[d]),  softplus(v) = log(1 + e^v)
+ *
+ * then exactly mssm_selective_scan_fwd on (u, delta, A, Bm, Cm, Dskip, z, h0),
+ * the skip term using this u.  The last d_conv - 1 entries of x are the
+ * conv_init of a following call (together with h_final as its h0).
+ *
+ *   x, delta_raw (device) [batch, d_inner, seqlen] dtype
+ *   conv_w     (device) [d_inner, d_conv] float32
+ *   conv_b     (device) [d_inner] float32, NULL => 0
+ *   conv_init  (device) [batch, d_inner, d_conv - 1] dtype, NULL => zeros
+ *   delta_bias (device) [d_inner] float32, NULL => 0
+ *   the rest   as mssm_selective_scan_fwd
+ *
+ * Limits: 1 <= d_conv <= 4 and 1 <= d_state <= 64 (MSSM_ERR_UNSUPPORTED).
+ */
+int mssm_selective_scan_fused_fwd(const void* x, const float* conv_w, const float* conv_b,
+                                  const void* conv_init, const void* delta_raw,
+                                  const float* delta_bias, const float* A, const void* Bm,
+                                  const void* Cm, const float* Dskip, const void* z,
+                                  const float* h0, void* y, float* h_final, int64_t batch,
+                                  int64_t d_inner, int64_t seqlen, int64_t d_state,
+                                  int64_t d_conv, mssm_dtype dtype, void* stream);
 
 /*
  * Decode: one token of the same recurrence, state updated in place.

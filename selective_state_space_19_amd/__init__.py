@@ -10,7 +10,7 @@ from __future__ import annotations
 
 from ._lib import MSSM_BF16, MSSM_F32, MssmError, check, lib
 
-__all__ = ["selective_scan", "state_update", "ssd_chunk", "ssd_state_update", "ssd_workspace_size", "MssmError", "lib"]
+__all__ = ["selective_scan", "selective_scan_fused", "state_update", "ssd_chunk", "ssd_state_update", "ssd_workspace_size", "MssmError", "lib"]
 
 
 def _torch():
@@ -84,6 +84,49 @@ def selective_scan(u, delta, A, B, C, D=None, z=None, h0=None, *, return_final_s
     check(lib().mssm_selective_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                                         _ptr(h0), _ptr(y), _ptr(hf), bsz, dim, L, N, code,
                                         _stream(stream, dev)))
+    return (y, hf) if hf is not None else y
+
+
+def selective_scan_fused(x, conv_w, delta_raw, A, B, C, D=None, z=None, h0=None, *, conv_b=None, conv_init=None,
+                         delta_bias=None, return_final_state=False, out=None, h_final=None, stream=None):
+    """S6 scan with its front end: u = silu(causal conv1d(x; conv_w, conv_b,
+    history conv_init)), delta = softplus(delta_raw + delta_bias).  x,
+    delta_raw, z: [b, d, L]; conv_w: [d, K] float32 (K <= 4); conv_b,
+    delta_bias: [d] float32; conv_init: [b, d, K-1] (x's dtype); the rest as
+    selective_scan."""
+    torch = _torch()
+    dev = x.device
+    x = _dev(x, "x")
+    bsz, dim, L = x.shape
+    N = A.shape[-1]
+    dt = x.dtype
+    code = _dtype_code(x)
+    K = conv_w.shape[-1]
+    conv_w = _dev(conv_w, "conv_w", (dim, K), torch.float32, dev)
+    conv_b = _dev(conv_b, "conv_b", (dim,), torch.float32, dev)
+    conv_init = _dev(conv_init, "conv_init", (bsz, dim, K - 1), dt, dev)
+    delta_raw = _dev(delta_raw, "delta_raw", x.shape, dt, dev)
+    delta_bias = _dev(delta_bias, "delta_bias", (dim,), torch.float32, dev)
+    z = _dev(z, "z", x.shape, dt, dev)
+    B = _dev(B, "B", (bsz, N, L), dt, dev)
+    C = _dev(C, "C", (bsz, N, L), dt, dev)
+    A = _dev(A, "A", (dim, N), torch.float32, dev)
+    D = _dev(D, "D", (dim,), torch.float32, dev)
+    h0 = _dev(h0, "h0", (bsz, dim, N), torch.float32, dev)
+    y = out if out is not None else torch.empty_like(x)
+    _dev(y, "out", x.shape, dt, dev)
+    if not y.is_contiguous():
+        raise ValueError("out must be contiguous")
+    hf = None
+    if return_final_state or h_final is not None:
+        hf = h_final if h_final is not None else torch.empty((bsz, dim, N), dtype=torch.float32, device=dev)
+        _dev(hf, "h_final", (bsz, dim, N), torch.float32, dev)
+        if not hf.is_contiguous():
+            raise ValueError("h_final must be contiguous")
+    check(lib().mssm_selective_scan_fused_fwd(_ptr(x), _ptr(conv_w), _ptr(conv_b), _ptr(conv_init), _ptr(delta_raw),
+                                              _ptr(delta_bias), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                              _ptr(h0), _ptr(y), _ptr(hf), bsz, dim, L, N, K, code,
+                                              _stream(stream, dev)))
     return (y, hf) if hf is not None else y
 
 

@@ -10,6 +10,7 @@
 namespace mssm {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
 
 typedef __bf16 bf16x2_t __attribute__((__vector_size__(2 * sizeof(__bf16))));
 
@@ -36,6 +37,17 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ void lgkm_wait_all() {
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_sched_barrier(0);
+}
+
+// softplus(v) = log(1 + e^v) = max(v, 0) + log1p(e^-|v|).  log1p(w) for w in
+// (0, 1] is log(1 + w) * w / ((1 + w) - 1), which cancels the rounding of
+// 1 + w (exact when 1 + w rounds to 1: the result is then w).
+__device__ __forceinline__ float softplus_f(float v) {
+    const float w = fast_exp2(-fabsf(v) * kLog2e);
+    const float u = 1.0f + w;
+    const float d = u - 1.0f;
+    const float l1p = d == 0.0f ? w : __builtin_amdgcn_logf(u) * kLn2 * w * __builtin_amdgcn_rcpf(d);
+    return fmaxf(v, 0.0f) + l1p;
 }
 
 // silu(g) = g * sigmoid(g) = g / (1 + e^-g).

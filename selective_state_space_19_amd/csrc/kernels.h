@@ -21,6 +21,16 @@ struct S6Params {
     int32_t L, N;
 };
 
+// Front end of the scan: u = silu(causal depthwise conv1d(x)) with K taps
+// (K <= 4) and delta = softplus(delta_raw + delta_bias).
+struct S6FrontEnd {
+    const float* conv_w;      // [dim, K]
+    const float* conv_b;      // nullable, [dim]
+    const void* conv_init;    // nullable, [batch, dim, K - 1] (input dtype)
+    const float* delta_bias;  // nullable, [dim]
+    int32_t K;
+};
+
 struct SUParams {
     float* state;
     const void* u;
@@ -67,6 +77,7 @@ struct SSDUParams {
 
 // Each returns hipSuccess or the launch error; is_bf16 selects the storage type.
 hipError_t launch_s6_scan(const S6Params& p, bool is_bf16, hipStream_t stream);
+hipError_t launch_s6_scan_fused(const S6Params& p, const S6FrontEnd& fe, bool is_bf16, hipStream_t stream);
 hipError_t launch_state_update(const SUParams& p, bool is_bf16, hipStream_t stream);
 hipError_t launch_ssd(const SSDParams& p, hipStream_t stream);
 size_t ssd_workspace_bytes(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int64_t Q);

@@ -99,6 +99,49 @@ int mssm_selective_scan_fwd(const void* u, const void* delta, const float* A, co
     return launched(fn, mssm::launch_s6_scan(p, dtype == MSSM_BF16, s));
 }
 
+int mssm_selective_scan_fused_fwd(const void* x, const float* conv_w, const float* conv_b, const void* conv_init,
+                                  const void* delta_raw, const float* delta_bias, const float* A, const void* Bm,
+                                  const void* Cm, const float* Dskip, const void* z, const float* h0, void* y,
+                                  float* h_final, int64_t batch, int64_t d_inner, int64_t seqlen, int64_t d_state,
+                                  int64_t d_conv, mssm_dtype dtype, void* stream) {
+    static const char* fn = "mssm_selective_scan_fused_fwd";
+    g_err.clear();
+    if (dtype != MSSM_F32 && dtype != MSSM_BF16) return fail(MSSM_ERR_DTYPE, "%s: unknown dtype %d", fn, (int)dtype);
+    if (batch < 0 || d_inner < 0 || seqlen < 0 || d_state < 0 || d_conv < 0)
+        return fail(MSSM_ERR_SHAPE, "%s: negative dimension", fn);
+    if (d_state < 1 || d_state > 64) return fail(MSSM_ERR_UNSUPPORTED, "%s: d_state %lld not in [1, 64]", fn, (long long)d_state);
+    if (d_conv < 1 || d_conv > 4) return fail(MSSM_ERR_UNSUPPORTED, "%s: d_conv %lld not in [1, 4]", fn, (long long)d_conv);
+    if (seqlen > INT32_MAX) return fail(MSSM_ERR_UNSUPPORTED, "%s: seqlen %lld too large", fn, (long long)seqlen);
+    if (!prod_ok(batch, d_inner, seqlen, nullptr) || !prod_ok(batch, d_inner, d_state, nullptr))
+        return fail(MSSM_ERR_SHAPE, "%s: tensor too large", fn);
+    if (batch == 0 || d_inner == 0) return MSSM_OK;
+    CHECK_OPT(h0);
+    CHECK_OPT(h_final);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (seqlen == 0) {
+        if (!h_final) return MSSM_OK;
+        return launched(fn, mssm::launch_copy_or_zero(h_final, h0, batch * d_inner * d_state, s));
+    }
+    CHECK_PTR(x);
+    CHECK_PTR(conv_w);
+    CHECK_PTR(delta_raw);
+    CHECK_PTR(A);
+    CHECK_PTR(Bm);
+    CHECK_PTR(Cm);
+    CHECK_PTR(y);
+    CHECK_OPT(conv_b);
+    CHECK_OPT(conv_init);
+    CHECK_OPT(delta_bias);
+    CHECK_OPT(Dskip);
+    CHECK_OPT(z);
+    const int64_t blocks = ((d_inner + 63) / 64) * batch;
+    if (blocks > INT32_MAX) return fail(MSSM_ERR_UNSUPPORTED, "%s: batch*d_inner too large", fn);
+    mssm::S6Params p{x, delta_raw, Bm, Cm, z, A, Dskip, h0, y, h_final, batch, d_inner, (int32_t)seqlen,
+                     (int32_t)d_state};
+    mssm::S6FrontEnd fe{conv_w, conv_b, conv_init, delta_bias, (int32_t)d_conv};
+    return launched(fn, mssm::launch_s6_scan_fused(p, fe, dtype == MSSM_BF16, s));
+}
+
 int mssm_state_update(float* state, const void* u, const void* delta, const float* A, const void* Bm,
                       const void* Cm, const float* Dskip, const void* z, void* y, int64_t batch,
                       int64_t d_inner, int64_t d_state, mssm_dtype dtype, void* stream) {

@@ -48,12 +48,15 @@ namespace mssm {
 
 namespace {
 
-template <typename T, int NW, int NS, int TC, bool ALIGNED, bool FULLN, int RING>
+template <typename T, int NW, int NS, int TC, bool ALIGNED, bool FULLN, bool FUSED, int RING>
 __global__ __launch_bounds__(NW * 64) void s6_scan_kernel(
     const T* __restrict__ u_in, const T* __restrict__ dl_in, const T* __restrict__ B_in,
     const T* __restrict__ C_in, const T* __restrict__ z_in, const float* __restrict__ A_in,
     const float* __restrict__ D_in, const float* __restrict__ h0_in, T* __restrict__ y_out,
-    float* __restrict__ hT_out, int64_t dim, int L, int N) {
+    float* __restrict__ hT_out, int64_t dim, int L, int N, S6FrontEnd fe) {
+    // FUSED: u_in is x before the causal conv and dl_in the step before
+    // softplus; the row-mapping threads form u = silu(conv(x)) and
+    // delta = softplus(raw + bias) while staging.
     // Pointers are separate __restrict__ arguments so the compiler may fetch the
     // wave-uniform B / C words with scalar loads (it must know no store aliases them).
     constexpr int SEGS = NW;                       // row segments (threads per row)
@@ -101,6 +104,29 @@ __global__ __launch_bounds__(NW * 64) void s6_scan_kernel(
     const int toff = (tid % SEGS) * TPT;
     const bool rval = cr < nrows;
     const float dskip = (rval && D_in) ? D_in[d0 + cr] : 0.f;
+    // Front end (FUSED): this row's conv taps, right-aligned in a 4-tap
+    // window (w4[3] multiplies the current token); the 3 inputs before the
+    // current run (`carry`, used by the row's first segment); the biases.
+    float w4[4] = {0.f, 0.f, 0.f, 0.f}, carry[3] = {0.f, 0.f, 0.f}, cbias = 0.f, dbias = 0.f;
+    if constexpr (FUSED) {
+        const int64_t dr = d0 + (rval ? cr : 0);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {                      // tap k of the window is conv_w[k - (4 - K)]
+            const int i = k - (4 - fe.K);
+            w4[k] = i >= 0 ? fe.conv_w[dr * fe.K + i] : 0.f;
+        }
+        cbias = fe.conv_b ? fe.conv_b[dr] : 0.f;
+        dbias = fe.delta_bias ? fe.delta_bias[dr] : 0.f;
+        if (fe.conv_init) {
+            const T* ci = static_cast<const T*>(fe.conv_init) + (b * dim + dr) * (fe.K - 1);
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {                  // carry[k] is the input 3 - k tokens back
+                const int i = k - (4 - fe.K);
+                carry[k] = i >= 0 ? Elem<T>::load1(ci + i) : 0.f;
+            }
+        }
+    }
+    const int seg = tid % SEGS;
     const int64_t blk0 = (b * dim + d0) * (int64_t)L;            // first element of this block's rows
     const uint32_t blk_bytes = ALIGNED ? (uint32_t)nrows * (uint32_t)L * (uint32_t)sizeof(T) : 0u;
     const rsrc_t rs_u = make_rsrc(u_in + blk0, blk_bytes);
@@ -213,10 +239,47 @@ __global__ __launch_bounds__(NW * 64) void s6_scan_kernel(
                      uint32_t (&pu)[WPT], uint32_t (&pdl)[WPT], uint32_t (&pz)[WPT]) {
         const int t0 = ck * TC;
         // ---- stage (delta, delta*u) of this chunk in LDS -------------------
+        float uf[TPT];                           // u of this thread's run (FUSED: after the conv)
+        if constexpr (FUSED) {
+            static_assert(TPT >= 3, "a run holds the 3 inputs the next run's conv needs");
+            float xr[TPT];
 #pragma unroll
-        for (int j = 0; j < TPT; j += 2) {
-            const float e0 = Elem<T>::get(cdl, j), e1 = Elem<T>::get(cdl, j + 1);
-            s_dd[(toff + j) / 2][cr] = make_float4(e0, e0 * Elem<T>::get(cu, j), e1, e1 * Elem<T>::get(cu, j + 1));
+            for (int j = 0; j < TPT; ++j) xr[j] = Elem<T>::get(cu, j);
+            // the 3 inputs before this run: from the previous segment's lane, or
+            // (first segment) the carry from the previous chunk
+            const int lane = tid & 63;
+            float xp[3];
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                const float v = __shfl(xr[TPT - 3 + k], lane - 1, 64);
+                xp[k] = seg > 0 ? v : carry[k];
+            }
+#pragma unroll
+            for (int k = 0; k < 3; ++k) carry[k] = __shfl(xr[TPT - 3 + k], lane | (SEGS - 1), 64);
+#pragma unroll
+            for (int j = 0; j < TPT; ++j) {
+                float a = cbias;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int src = j - 3 + k;   // compile-time after unrolling
+                    a = fmaf(w4[k], src < 0 ? xp[src + 3] : xr[src < 0 ? 0 : src], a);
+                }
+                uf[j] = silu(a);
+            }
+#pragma unroll
+            for (int j = 0; j < TPT; j += 2) {
+                const float d0v = t0 + toff + j < L ? softplus_f(Elem<T>::get(cdl, j) + dbias) : 0.f;
+                const float d1v = t0 + toff + j + 1 < L ? softplus_f(Elem<T>::get(cdl, j + 1) + dbias) : 0.f;
+                s_dd[(toff + j) / 2][cr] = make_float4(d0v, d0v * uf[j], d1v, d1v * uf[j + 1]);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < TPT; ++j) uf[j] = Elem<T>::get(cu, j);
+#pragma unroll
+            for (int j = 0; j < TPT; j += 2) {
+                const float e0 = Elem<T>::get(cdl, j), e1 = Elem<T>::get(cdl, j + 1);
+                s_dd[(toff + j) / 2][cr] = make_float4(e0, e0 * uf[j], e1, e1 * uf[j + 1]);
+            }
         }
         if (ALIGNED || ck + RING - 1 < nchunks) load_chunk(ck + RING - 1, pu, pdl, pz);
         __syncthreads();
@@ -256,8 +319,8 @@ __global__ __launch_bounds__(NW * 64) void s6_scan_kernel(
                 acc.x += v.x;
                 acc.y += v.y;
             }
-            float o0 = fmaf(dskip, Elem<T>::get(cu, j), acc.x);
-            float o1 = fmaf(dskip, Elem<T>::get(cu, j + 1), acc.y);
+            float o0 = fmaf(dskip, uf[j], acc.x);
+            float o1 = fmaf(dskip, uf[j + 1], acc.y);
             if (z_in) {
                 o0 *= silu(Elem<T>::get(cz, j));
                 o1 *= silu(Elem<T>::get(cz, j + 1));
@@ -304,30 +367,34 @@ __global__ __launch_bounds__(NW * 64) void s6_scan_kernel(
 }
 
 template <typename T, int NW, int NS, int TC>
-hipError_t launch_cfg(const S6Params& p, hipStream_t stream) {
+hipError_t launch_cfg(const S6Params& p, const S6FrontEnd* fe, hipStream_t stream) {
     constexpr int RING = 8;
     const int64_t blocks = ((p.dim + 63) / 64) * p.batch;
     // The aligned path addresses a block's rows through 32-bit buffer
     // offsets, and reads B / C in whole 16-byte groups.
     const bool aligned = (p.L % 8 == 0) && int64_t(64) * p.L * int64_t(sizeof(T)) < (int64_t(1) << 31);
     const bool fulln = p.N == NW * NS;
-    auto kern = aligned ? (fulln ? s6_scan_kernel<T, NW, NS, TC, true, true, RING>
-                                 : s6_scan_kernel<T, NW, NS, TC, true, false, RING>)
-                        : s6_scan_kernel<T, NW, NS, TC, false, false, RING>;
+    auto kern = fe ? (aligned ? (fulln ? s6_scan_kernel<T, NW, NS, TC, true, true, true, RING>
+                                       : s6_scan_kernel<T, NW, NS, TC, true, false, true, RING>)
+                              : s6_scan_kernel<T, NW, NS, TC, false, false, true, RING>)
+                   : (aligned ? (fulln ? s6_scan_kernel<T, NW, NS, TC, true, true, false, RING>
+                                       : s6_scan_kernel<T, NW, NS, TC, true, false, false, RING>)
+                              : s6_scan_kernel<T, NW, NS, TC, false, false, false, RING>);
+    const S6FrontEnd none{};
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(NW * 64), 0, stream, static_cast<const T*>(p.u),
                        static_cast<const T*>(p.delta), static_cast<const T*>(p.Bm), static_cast<const T*>(p.Cm),
                        static_cast<const T*>(p.z), p.A, p.Dskip, p.h0, static_cast<T*>(p.y), p.h_final, p.dim,
-                       p.L, p.N);
+                       p.L, p.N, fe ? *fe : none);
     return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_t(const S6Params& p, hipStream_t stream) {
+hipError_t launch_t(const S6Params& p, const S6FrontEnd* fe, hipStream_t stream) {
     // 8 waves per 64 channels; NS = ceil(N / 8) states per lane.
-    if (p.N <= 8) return launch_cfg<T, 8, 1, 32>(p, stream);
-    if (p.N <= 16) return launch_cfg<T, 8, 2, 32>(p, stream);
-    if (p.N <= 32) return launch_cfg<T, 8, 4, 32>(p, stream);
-    return launch_cfg<T, 8, 8, 32>(p, stream);
+    if (p.N <= 8) return launch_cfg<T, 8, 1, 32>(p, fe, stream);
+    if (p.N <= 16) return launch_cfg<T, 8, 2, 32>(p, fe, stream);
+    if (p.N <= 32) return launch_cfg<T, 8, 4, 32>(p, fe, stream);
+    return launch_cfg<T, 8, 8, 32>(p, fe, stream);
 }
 
 __global__ void copy_or_zero_kernel(float* dst, const float* src, int64_t n) {
@@ -338,7 +405,11 @@ __global__ void copy_or_zero_kernel(float* dst, const float* src, int64_t n) {
 }  // namespace
 
 hipError_t launch_s6_scan(const S6Params& p, bool is_bf16, hipStream_t stream) {
-    return is_bf16 ? launch_t<uint16_t>(p, stream) : launch_t<float>(p, stream);
+    return is_bf16 ? launch_t<uint16_t>(p, nullptr, stream) : launch_t<float>(p, nullptr, stream);
+}
+
+hipError_t launch_s6_scan_fused(const S6Params& p, const S6FrontEnd& fe, bool is_bf16, hipStream_t stream) {
+    return is_bf16 ? launch_t<uint16_t>(p, &fe, stream) : launch_t<float>(p, &fe, stream);
 }
 
 hipError_t launch_copy_or_zero(float* dst, const float* src, int64_t n, hipStream_t stream) {

@@ -18,7 +18,8 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = _lib.header_functions()
-    assert set(names) == {"mssm_selective_scan_fwd", "mssm_state_update", "mssm_ssd_workspace_size",
+    assert set(names) == {"mssm_selective_scan_fwd", "mssm_selective_scan_fused_fwd", "mssm_state_update",
+                          "mssm_ssd_workspace_size",
                           "mssm_ssd_chunk_fwd", "mssm_ssd_state_update", "mssm_last_error", "mssm_version"}
     for n in names:
         assert hasattr(lib, n), n
@@ -118,3 +119,23 @@ def test_ssd_state_update_argument_errors(lib):
     assert _m2(lib, P=-1) == ERR_SHAPE
     assert _m2(lib, z=MISALIGNED) == ERR_ALIGN
     assert _m2(lib, b=0) == 0
+
+
+def _fused(lib, **kw):
+    a = dict(x=FAKE, w=FAKE, cb=None, ci=None, dr=FAKE, db=None, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, h0=None,
+             y=FAKE, hf=None, b=2, d=64, L=128, N=16, K=4, dtype=1)
+    a.update(kw)
+    return lib.mssm_selective_scan_fused_fwd(a["x"], a["w"], a["cb"], a["ci"], a["dr"], a["db"], a["A"], a["B"],
+                                             a["C"], a["D"], a["z"], a["h0"], a["y"], a["hf"], a["b"], a["d"],
+                                             a["L"], a["N"], a["K"], a["dtype"], None)
+
+
+def test_fused_scan_argument_errors(lib):
+    assert _fused(lib, w=None) == ERR_NULL
+    assert _fused(lib, dr=None) == ERR_NULL
+    assert _fused(lib, K=5) == ERR_UNSUP
+    assert _fused(lib, K=0) == ERR_UNSUP
+    assert _fused(lib, N=65) == ERR_UNSUP
+    assert _fused(lib, dtype=3) == ERR_DTYPE
+    assert _fused(lib, ci=MISALIGNED) == ERR_ALIGN
+    assert _fused(lib, b=0) == 0
