@@ -18,6 +18,8 @@ for what is computed and which passages of the pages it follows:
   ("Hardware-Aware Implementation / Parallel Algorithm", sequential mode).
 * Mamba-2 SSD -- Optimization Patterns page, section 2 "State Space Duality":
   the recurrence on (head, head channel) with a scalar A per head.
+* S6 backward -- the reverse-mode derivative of the scan ("State-Space
+  Model Optimization Patterns" page, section 4: the training pass).
 * Mamba-2 decode step -- one token of that recurrence with the state
   [b, H, P, N] updated in place ("Mamba - Selective State Space Models"
   page, "Workflow 3": the Mamba-2 block with headdim and d_state).
@@ -60,6 +62,8 @@ def _bind(lib):
     lib.oracle_state_update.restype = ctypes.c_int
     lib.oracle_ssd.argtypes = [d] * 10 + [L] * 6 + [ctypes.c_int]
     lib.oracle_ssd.restype = ctypes.c_int
+    lib.oracle_s6_scan_bwd.argtypes = [d] * 18 + [L] * 4 + [ctypes.c_int]
+    lib.oracle_s6_scan_bwd.restype = ctypes.c_int
     return lib
 
 
@@ -211,3 +215,31 @@ def s6_scan_fused(x, conv_w, conv_b, conv_init, delta_raw, delta_bias, A, B, C, 
     if delta_bias is not None:
         dr = dr + _f64(delta_bias)[None, :, None]
     return s6_scan(u, softplus(dr), A, B, C, D, z, h0, nthreads=nthreads, lib=lib)
+
+
+def s6_scan_bwd(u, delta, A, B, C, D=None, z=None, h0=None, dout=None, dhT=None, nthreads=None, lib=None):
+    """Reverse-mode derivative of s6_scan for the loss sum(dout * y) +
+    sum(dhT * h_final).  Shapes as s6_scan; dout: [b, d, L]; dhT: [b, d, N]
+    (zero if None).  Returns a dict of fp64 arrays du, ddelta [b, d, L],
+    dA [d, N], dB, dC [b, N, L], dD [d], dz [b, d, L] (if z), dh0
+    [b, d, N] (if h0)."""
+    u, delta, A, B, C, dout = map(_f64, (u, delta, A, B, C, dout))
+    D, z, h0, dhT = _f64(D), _f64(z), _f64(h0), _f64(dhT)
+    bsz, dim, L = u.shape
+    N = A.shape[1]
+    out = dict(du=np.empty((bsz, dim, L)), ddelta=np.empty((bsz, dim, L)), dA=np.empty((dim, N)),
+               dB=np.empty((bsz, N, L)), dC=np.empty((bsz, N, L)), dD=np.empty(dim))
+    dz = np.empty((bsz, dim, L)) if z is not None else None
+    dh0 = np.empty((bsz, dim, N)) if h0 is not None else None
+    lib = lib or load()
+    rc = lib.oracle_s6_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
+                                _ptr(dout), _ptr(dhT), _ptr(out["du"]), _ptr(out["ddelta"]), _ptr(out["dA"]),
+                                _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]), _ptr(dz), _ptr(dh0),
+                                bsz, dim, L, N, nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError("oracle_s6_scan_bwd failed")
+    if dz is not None:
+        out["dz"] = dz
+    if dh0 is not None:
+        out["dh0"] = dh0
+    return out

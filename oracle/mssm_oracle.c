@@ -266,3 +266,144 @@ int oracle_ssd(const double *x, const double *dt, const double *A,
     p.nchan = batch * nheads * headdim;
     return run(&p, nthreads);
 }
+
+/* ------------------------------------------------------------------------
+ * Backward of the S6 scan: the reverse-mode derivative of oracle_s6_scan
+ * (the training half of the recurrence; "State-Space Model Optimization
+ * Patterns" page, section 4 -- the backward pass recomputes the forward
+ * states instead of storing them; here the oracle simply keeps every state of
+ * one channel).  With g_t = dout_t * silu(z_t) (dout_t without a gate) and
+ * the adjoint lambda_t = dL/dh_t, taken backwards in time:
+ *     lambda_t  = (a_{t+1} lambda_{t+1} or dhT at t = L-1) + g_t C_t
+ *     dC_t     += g_t h_t                 (summed over channels)
+ *     dB_t     += lambda_t delta_t u_t    (summed over channels)
+ *     du_t      = g_t D + sum_n lambda_t delta_t B_t
+ *     ddelta_t  = sum_n lambda_t (A a_t h_{t-1} + u_t B_t)
+ *     dA       += lambda_t delta_t a_t h_{t-1}
+ *     dD       += g_t u_t
+ *     dz_t      = dout_t y_t silu'(z_t),  y_t = sum_n C_t h_t + D u_t
+ *     dh0       = a_0 lambda_0
+ * where a_t = exp(delta_t A) and h_{-1} = h0 (or 0).
+ * ------------------------------------------------------------------------ */
+typedef struct {
+    const double *u, *delta, *A, *Bm, *Cm, *Dskip, *z, *h0, *dout, *dhT;
+    double *du, *ddelta, *dz, *dh0;
+    double *dA, *dB, *dC, *dD;       /* per-thread partial sums (this thread's copy) */
+    long B, D, L, N;
+    long lo, hi;                      /* channel range [lo, hi) over (b, d) */
+} bwd_t;
+
+static void *bwd_worker(void *arg)
+{
+    bwd_t *w = (bwd_t *)arg;
+    const long D = w->D, L = w->L, N = w->N;
+    double *hs = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1) * (size_t)N);
+    double *lam = (double *)malloc(sizeof(double) * (size_t)N);
+    if (!hs || !lam) { free(hs); free(lam); return (void *)1; }
+    for (long ch = w->lo; ch < w->hi; ++ch) {
+        const long b = ch / D, d = ch % D;
+        const double *u = w->u + ch * L, *dl = w->delta + ch * L;
+        const double *z = w->z ? w->z + ch * L : NULL;
+        const double *dout = w->dout + ch * L;
+        const double *Bm = w->Bm + b * N * L, *Cm = w->Cm + b * N * L;
+        const double *A = w->A + d * N;
+        const double dsk = w->Dskip ? w->Dskip[d] : 0.0;
+        /* forward, keeping every state */
+        for (long n = 0; n < N; ++n) {
+            double h = w->h0 ? w->h0[ch * N + n] : 0.0;
+            for (long t = 0; t < L; ++t) {
+                h = exp(dl[t] * A[n]) * h + (dl[t] * u[t]) * Bm[n * L + t];
+                hs[t * N + n] = h;
+            }
+        }
+        /* backward */
+        for (long n = 0; n < N; ++n) lam[n] = w->dhT ? w->dhT[ch * N + n] : 0.0;
+        double dD = 0.0;
+        for (long t = L - 1; t >= 0; --t) {
+            double y = dsk * u[t];
+            for (long n = 0; n < N; ++n) y += Cm[n * L + t] * hs[t * N + n];
+            double g = dout[t];
+            if (z) {
+                const double zz = z[t], sg = 1.0 / (1.0 + exp(-zz));
+                w->dz[ch * L + t] = dout[t] * y * (sg * (1.0 + zz * (1.0 - sg)));
+                g = dout[t] * zz * sg;
+            } else if (w->dz) {
+                w->dz[ch * L + t] = 0.0;
+            }
+            dD += g * u[t];
+            double du = g * dsk, dd = 0.0;
+            for (long n = 0; n < N; ++n) {
+                const double lt = lam[n] + g * Cm[n * L + t];
+                const double a = exp(dl[t] * A[n]);
+                const double hp = t > 0 ? hs[(t - 1) * N + n] : (w->h0 ? w->h0[ch * N + n] : 0.0);
+                w->dC[b * N * L + n * L + t] += g * hs[t * N + n];
+                w->dB[b * N * L + n * L + t] += lt * dl[t] * u[t];
+                du += lt * dl[t] * Bm[n * L + t];
+                dd += lt * (A[n] * a * hp + u[t] * Bm[n * L + t]);
+                w->dA[d * N + n] += lt * dl[t] * a * hp;
+                lam[n] = a * lt;
+            }
+            w->du[ch * L + t] = du;
+            w->ddelta[ch * L + t] = dd;
+        }
+        w->dD[d] += dD;
+        if (w->dh0)
+            for (long n = 0; n < N; ++n) w->dh0[ch * N + n] = lam[n];
+    }
+    free(hs);
+    free(lam);
+    return NULL;
+}
+
+int oracle_s6_scan_bwd(const double *u, const double *delta, const double *A,
+                       const double *Bm, const double *Cm, const double *Dskip,
+                       const double *z, const double *h0, const double *dout,
+                       const double *dhT, double *du, double *ddelta, double *dA,
+                       double *dB, double *dC, double *dD, double *dz, double *dh0,
+                       long batch, long d_inner, long seqlen, long d_state, int nthreads)
+{
+    if (!u || !delta || !A || !Bm || !Cm || !dout || !du || !ddelta || !dA || !dB || !dC || !dD) return -1;
+    if (batch < 0 || d_inner < 0 || seqlen < 0 || d_state < 1) return -1;
+    const long nch = batch * d_inner, N = d_state, L = seqlen, D = d_inner;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 64) nthreads = 64;
+    if (nthreads > nch && nch > 0) nthreads = (int)nch;
+    const size_t nb = (size_t)batch * N * L, na = (size_t)D * N;
+    bwd_t w[64];
+    pthread_t th[64];
+    int started[64] = {0};
+    int rc = 0;
+    for (int i = 0; i < nthreads; ++i) {
+        bwd_t *x = &w[i];
+        x->u = u; x->delta = delta; x->A = A; x->Bm = Bm; x->Cm = Cm; x->Dskip = Dskip;
+        x->z = z; x->h0 = h0; x->dout = dout; x->dhT = dhT;
+        x->du = du; x->ddelta = ddelta; x->dz = dz; x->dh0 = dh0;
+        x->B = batch; x->D = D; x->L = L; x->N = N;
+        x->lo = nch * i / nthreads; x->hi = nch * (i + 1) / nthreads;
+        x->dB = (double *)calloc(nb ? nb : 1, sizeof(double));
+        x->dC = (double *)calloc(nb ? nb : 1, sizeof(double));
+        x->dA = (double *)calloc(na ? na : 1, sizeof(double));
+        x->dD = (double *)calloc(D ? D : 1, sizeof(double));
+        if (!x->dB || !x->dC || !x->dA || !x->dD) rc = -2;
+    }
+    for (int i = 0; i < nthreads && rc == 0; ++i)
+        started[i] = pthread_create(&th[i], NULL, bwd_worker, &w[i]) == 0;
+    for (int i = 0; i < nthreads && rc == 0; ++i) {
+        void *ret = NULL;
+        if (started[i]) pthread_join(th[i], &ret);
+        else ret = bwd_worker(&w[i]);
+        if (ret) rc = -2;
+    }
+    for (size_t k = 0; k < nb; ++k) { dB[k] = 0.0; dC[k] = 0.0; }
+    for (size_t k = 0; k < na; ++k) dA[k] = 0.0;
+    for (long k = 0; k < D; ++k) dD[k] = 0.0;
+    for (int i = 0; i < nthreads; ++i) {
+        if (rc == 0) {
+            for (size_t k = 0; k < nb; ++k) { dB[k] += w[i].dB[k]; dC[k] += w[i].dC[k]; }
+            for (size_t k = 0; k < na; ++k) dA[k] += w[i].dA[k];
+            for (long k = 0; k < D; ++k) dD[k] += w[i].dD[k];
+        }
+        free(w[i].dB); free(w[i].dC); free(w[i].dA); free(w[i].dD);
+    }
+    return rc;
+}

@@ -434,3 +434,53 @@ def test_fused_generator_matches_step_distribution():
     med = np.median(delta, axis=(0, 2))
     assert np.all(med > 5e-4) and np.all(med < 0.2)
     assert np.all(np.abs(inp["conv_w"]) <= 0.5) and inp["conv_init"].shape == (2, 64, 3)
+
+
+
+# ----------------------------------------------------------------------------
+# S6 backward: central finite differences of the forward oracle
+# ----------------------------------------------------------------------------
+def _loss(i, dout, dhT, lib):
+    y, hT = oracle.s6_scan(i["u"], i["delta"], i["A"], i["B"], i["C"], i["D"], i["z"], i["h0"], lib=lib)
+    return float(np.sum(dout * y) + np.sum(dhT * hT))
+
+
+@pytest.mark.parametrize("gate", [True, False])
+def test_backward_matches_finite_differences(oracle_lib, gate):
+    """Every gradient of the backward oracle equals the central difference
+    of the forward oracle's loss sum(dout * y) + sum(dhT * h_final)."""
+    rng = np.random.default_rng(41)
+    b, d, L, N = 2, 3, 6, 4
+    i = _rand_s6(rng, b, d, L, N, h0=True, z=gate, D=True)
+    dout = rng.standard_normal((b, d, L))
+    dhT = rng.standard_normal((b, d, N))
+    g = oracle.s6_scan_bwd(i["u"], i["delta"], i["A"], i["B"], i["C"], i["D"], i["z"], i["h0"], dout, dhT,
+                           lib=oracle_lib)
+    names = [("u", "du"), ("delta", "ddelta"), ("A", "dA"), ("B", "dB"), ("C", "dC"), ("D", "dD"), ("h0", "dh0")]
+    if gate:
+        names.append(("z", "dz"))
+    eps = 1e-6
+    for key, gkey in names:
+        base = i[key]
+        fd = np.empty_like(base)
+        for idx in np.ndindex(base.shape):
+            old = base[idx]
+            base[idx] = old + eps
+            lp = _loss(i, dout, dhT, oracle_lib)
+            base[idx] = old - eps
+            lm = _loss(i, dout, dhT, oracle_lib)
+            base[idx] = old
+            fd[idx] = (lp - lm) / (2 * eps)
+        np.testing.assert_allclose(g[gkey], fd, rtol=1e-6, atol=1e-7, err_msg=gkey)
+
+
+def test_backward_is_linear_in_dout(oracle_lib):
+    rng = np.random.default_rng(42)
+    i = _rand_s6(rng, 1, 4, 9, 3)
+    d1, d2 = rng.standard_normal((1, 4, 9)), rng.standard_normal((1, 4, 9))
+    args = (i["u"], i["delta"], i["A"], i["B"], i["C"], i["D"], i["z"], i["h0"])
+    g1 = oracle.s6_scan_bwd(*args, d1, lib=oracle_lib)
+    g2 = oracle.s6_scan_bwd(*args, d2, lib=oracle_lib)
+    g3 = oracle.s6_scan_bwd(*args, 2.0 * d1 - d2, lib=oracle_lib)
+    for k in ("du", "ddelta", "dA", "dB", "dC", "dD", "dz", "dh0"):
+        np.testing.assert_allclose(g3[k], 2.0 * g1[k] - g2[k], rtol=1e-12, atol=1e-12, err_msg=k)
