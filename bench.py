@@ -11,7 +11,7 @@ written once) divided by the time per step; also reported: tokens-ch/s
 fp64 CPU oracle timed on the same workload, and the other entry points
 (decode step at the Mamba-2.8B shape, Mamba-2 SSD) inside the same object.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--only s6,s6fused,decode,decode2,ssd,copy]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--only s6,s6fused,s6bwd,decode,decode2,ssd,copy]
 
 Prints exactly one JSON line on stdout; progress goes to stderr.  `--only`
 restricts the run (for profiling); `copy` times a plain 1 GiB device copy,
@@ -200,6 +200,40 @@ def bench_s6fused(args):
                         f"d_state {s['d_state']}, d_conv {s['d_conv']}, bf16",
             "us": ms * 1e3, "GBs": nb / (ms * 1e-3) / 1e9, "hbm_frac": nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "tokens_ch_per_s": tok / (ms * 1e-3), "algorithmic_bytes": nb}
+
+
+def bench_s6bwd(args):
+    """Backward of the scan at the headline layer shape (h0 and final-state
+    gradient included)."""
+    import torch
+    import selective_state_space_19_amd as mssm
+    from selective_state_space_19_amd import synth
+    wl = synth.WORKLOADS["s6_mamba1p4b_bf16"]
+    s = wl.shape
+    log("[bench] s6 backward: generating inputs")
+    inp = synth.s6_inputs(**s, dtype=wl.dtype, seed=wl.seed, init_state=True)
+    d = {k: to_dev(inp[k]) for k in ("u", "delta", "A", "B", "C", "D", "z", "h0")}
+    rng = np.random.default_rng(0)
+    dout = to_dev(synth.round_to(rng.standard_normal(inp["u"].shape), wl.dtype))
+    dhT = to_dev(rng.standard_normal(inp["h0"].shape).astype(np.float32))
+    ws = torch.empty(mssm.selective_scan_bwd_workspace_size(s["batch"], s["d_inner"], s["seqlen"], s["d_state"]),
+                     dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        mssm.selective_scan_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], dout, d["D"], d["z"], d["h0"], dhT,
+                                workspace=ws, stream=stream)
+
+    steps = max(3, args.steps // 4)
+    total, _ = time_launches(step, steps, 1, stream)
+    ms = total / steps
+    B, D, L, N = s["batch"], s["d_inner"], s["seqlen"], s["d_state"]
+    # read u, delta, z, dout (twice: forward sweep reads u, delta) ; write du, ddelta, dz; dB, dC; state checkpoints
+    nb = (6 + 3) * B * D * L * 2 + 2 * B * N * L * (2 + 4) + 2 * ws.numel()
+    return {"workload": f"{wl.name} backward: batch {B}, d_inner {D}, seqlen {L}, d_state {N}, bf16, "
+                        "gate, skip, h0 and final-state gradient",
+            "us": ms * 1e3, "tokens_ch_per_s": B * D * L / (ms * 1e-3), "bytes_moved_estimate": nb,
+            "GBs_estimate": nb / (ms * 1e-3) / 1e9, "workspace_bytes": ws.numel()}
 
 
 def parity_sample(inp, y, hf, rows=32, seed=0):
@@ -418,7 +452,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="s6,s6fused,decode,decode2,ssd")
+    ap.add_argument("--only", default="s6,s6fused,s6bwd,decode,decode2,ssd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
     args = ap.parse_args()
@@ -473,6 +507,11 @@ def main():
             log("[bench] s6: cpu baseline (the oracle on the same workload)")
             out["cpu_baseline"] = cpu_baseline(r["inp"])
         del r
+    if "s6bwd" in parts:
+        try:
+            out["secondary_s6_backward"] = bench_s6bwd(args)
+        except Exception as e:  # reported, not hidden
+            out["secondary_s6_backward"] = {"error": repr(e)}
     if "s6fused" in parts:
         try:
             out["secondary_s6_fused_front_end"] = bench_s6fused(args)

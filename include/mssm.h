@@ -2,11 +2,12 @@
  * mssm.h -- C ABI of libmssm.so, the MI355X (gfx950) selective state-space
  * scan library.
  *
- * Five operations, each defined by the pages it cites:
+ * Six operations, each defined by the pages it cites:
  *
  *   mssm_selective_scan_fwd  the S6 selective scan over a whole sequence;
  *   mssm_selective_scan_fused_fwd  the same scan with its input front end
  *                            (causal conv1d + SiLU, softplus step) fused in;
+ *   mssm_selective_scan_bwd  the gradients of that scan (training);
  *   mssm_state_update        one decode token of the same recurrence;
  *   mssm_ssd_chunk_fwd       the Mamba-2 SSD (scalar transition per head),
  *                            computed chunk by chunk;
@@ -129,6 +130,46 @@ int mssm_selective_scan_fused_fwd(const void* x, const float* conv_w, const floa
                                   const float* h0, void* y, float* h_final, int64_t batch,
                                   int64_t d_inner, int64_t seqlen, int64_t d_state,
                                   int64_t d_conv, mssm_dtype dtype, void* stream);
+
+/*
+ * Backward of the S6 scan: the gradients of the loss
+ *     sum(dout * y) + sum(dh_final * h_final)
+ * with respect to every input of mssm_selective_scan_fwd.
+ *
+ * Defined by: the recurrence of mssm_selective_scan_fwd (same pages), and
+ * "State-Space Model Optimization Patterns" page, section 4 -- the training
+ * pass recomputes the forward states rather than storing them.  With
+ * g = dout * silu(z) (dout without a gate), a_t = exp(delta_t A) and the
+ * adjoint lambda_t = dL/dh_t:
+ *   lambda_t = a_{t+1} lambda_{t+1} + g_t C_t   (dh_final at the last token, or 0)
+ *   du_t = g_t D + sum_n lambda_t delta_t B_t;  ddelta_t = sum_n lambda_t (A a_t h_{t-1} + u_t B_t)
+ *   dA = sum_{b,t} lambda_t delta_t a_t h_{t-1};  dB_t = sum_d lambda_t delta_t u_t;
+ *   dC_t = sum_d g_t h_t;  dD = sum_{b,t} g_t u_t;  dz_t = dout_t y_t silu'(z_t);  dh0 = a_0 lambda_0.
+ *
+ *   u, delta, A, Bm, Cm, Dskip, z, h0: as mssm_selective_scan_fwd
+ *   dout       (device) [batch, d_inner, seqlen] dtype, gradient of y
+ *   dh_final   (device) [batch, d_inner, d_state] float32, NULL => 0
+ *   du, ddelta (device) [batch, d_inner, seqlen] dtype, outputs
+ *   dA         (device) [d_inner, d_state] float32, output (summed over batch)
+ *   dB, dC     (device) [batch, d_state, seqlen] float32, outputs (summed over channels)
+ *   dD         (device) [d_inner] float32, NULL => not computed
+ *   dz         (device) [batch, d_inner, seqlen] dtype; required when z is given
+ *   dh0        (device) [batch, d_inner, d_state] float32, NULL => not written
+ *   workspace  (device) at least mssm_selective_scan_bwd_workspace_size(...)
+ *              bytes (the state at every 16-token chunk start); caller-owned
+ *
+ * dA, dB, dC and dD are accumulated with atomics, so their summation order
+ * (and last bits) can vary from call to call.  Limits: 1 <= d_state <= 64.
+ */
+size_t mssm_selective_scan_bwd_workspace_size(int64_t batch, int64_t d_inner, int64_t seqlen,
+                                              int64_t d_state);
+int mssm_selective_scan_bwd(const void* u, const void* delta, const float* A, const void* Bm,
+                            const void* Cm, const float* Dskip, const void* z, const float* h0,
+                            const void* dout, const float* dh_final, void* du, void* ddelta,
+                            float* dA, float* dB, float* dC, float* dD, void* dz, float* dh0,
+                            int64_t batch, int64_t d_inner, int64_t seqlen, int64_t d_state,
+                            void* workspace, size_t workspace_bytes, mssm_dtype dtype,
+                            void* stream);
 
 /*
  * Decode: one token of the same recurrence, state updated in place.

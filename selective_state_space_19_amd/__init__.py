@@ -10,7 +10,8 @@ from __future__ import annotations
 
 from ._lib import MSSM_BF16, MSSM_F32, MssmError, check, lib
 
-__all__ = ["selective_scan", "selective_scan_fused", "state_update", "ssd_chunk", "ssd_state_update", "ssd_workspace_size", "MssmError", "lib"]
+__all__ = ["selective_scan", "selective_scan_fused", "selective_scan_bwd", "selective_scan_bwd_workspace_size",
+           "state_update", "ssd_chunk", "ssd_state_update", "ssd_workspace_size", "MssmError", "lib"]
 
 
 def _torch():
@@ -128,6 +129,50 @@ def selective_scan_fused(x, conv_w, delta_raw, A, B, C, D=None, z=None, h0=None,
                                               _ptr(h0), _ptr(y), _ptr(hf), bsz, dim, L, N, K, code,
                                               _stream(stream, dev)))
     return (y, hf) if hf is not None else y
+
+
+def selective_scan_bwd_workspace_size(batch, d_inner, seqlen, d_state):
+    return int(lib().mssm_selective_scan_bwd_workspace_size(batch, d_inner, seqlen, d_state))
+
+
+def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, h0=None, dh_final=None, *, workspace=None,
+                       stream=None):
+    """Gradients of the S6 scan for the loss sum(dout * y) + sum(dh_final *
+    h_final).  Inputs as selective_scan; dout: [b, d, L] (u's dtype);
+    dh_final: [b, d, N] float32.  Returns a dict: du, ddelta (and dz if z)
+    [b, d, L] in u's dtype; dA [d, N], dB, dC [b, N, L], dD [d] (if D) and
+    dh0 [b, d, N] (if h0) in float32."""
+    torch = _torch()
+    dev = u.device
+    u = _dev(u, "u")
+    bsz, dim, L = u.shape
+    N = A.shape[-1]
+    dt = u.dtype
+    code = _dtype_code(u)
+    delta = _dev(delta, "delta", u.shape, dt, dev)
+    dout = _dev(dout, "dout", u.shape, dt, dev)
+    z = _dev(z, "z", u.shape, dt, dev)
+    B = _dev(B, "B", (bsz, N, L), dt, dev)
+    C = _dev(C, "C", (bsz, N, L), dt, dev)
+    A = _dev(A, "A", (dim, N), torch.float32, dev)
+    D = _dev(D, "D", (dim,), torch.float32, dev)
+    h0 = _dev(h0, "h0", (bsz, dim, N), torch.float32, dev)
+    dh_final = _dev(dh_final, "dh_final", (bsz, dim, N), torch.float32, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = {"du": torch.empty_like(u), "ddelta": torch.empty_like(u), "dA": torch.empty((dim, N), **f32),
+         "dB": torch.empty((bsz, N, L), **f32), "dC": torch.empty((bsz, N, L), **f32)}
+    g["dD"] = torch.empty((dim,), **f32) if D is not None else None
+    g["dz"] = torch.empty_like(u) if z is not None else None
+    g["dh0"] = torch.empty((bsz, dim, N), **f32) if h0 is not None else None
+    need = selective_scan_bwd_workspace_size(bsz, dim, L, N)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    check(lib().mssm_selective_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
+                                        _ptr(dout), _ptr(dh_final), _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]),
+                                        _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["dh0"]),
+                                        bsz, dim, L, N, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                        code, _stream(stream, dev)))
+    return {k: v for k, v in g.items() if v is not None}
 
 
 def state_update(state, u, delta, A, B, C, D=None, z=None, *, out=None, stream=None):

@@ -31,6 +31,16 @@ struct S6FrontEnd {
     int32_t K;
 };
 
+struct S6BwdParams {
+    const void *u, *delta, *Bm, *Cm, *z, *dout;   // [batch, dim, L] / [batch, N, L] (input dtype)
+    const float *A, *Dskip, *h0, *dhT;            // A [dim, N]; Dskip [dim]; h0, dhT [batch, dim, N]
+    void *du, *ddelta, *dz;                       // [batch, dim, L] (input dtype)
+    float *dA, *dB, *dC, *dD, *dh0;               // fp32: [dim, N], [batch, N, L] x 2, [dim], [batch, dim, N]
+    float* ws;                                    // chunk-start states
+    int64_t batch, dim;
+    int32_t L, N;
+};
+
 struct SUParams {
     float* state;
     const void* u;
@@ -79,6 +89,9 @@ struct SSDUParams {
 hipError_t launch_s6_scan(const S6Params& p, bool is_bf16, hipStream_t stream);
 hipError_t launch_s6_scan_fused(const S6Params& p, const S6FrontEnd& fe, bool is_bf16, hipStream_t stream);
 hipError_t launch_state_update(const SUParams& p, bool is_bf16, hipStream_t stream);
+// Backward of the scan; zeroes dA, dB, dC, dD and then accumulates into them.
+hipError_t launch_s6_scan_bwd(const S6BwdParams& p, bool is_bf16, hipStream_t stream);
+size_t s6_bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t L, int64_t N);
 hipError_t launch_ssd(const SSDParams& p, hipStream_t stream);
 size_t ssd_workspace_bytes(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int64_t Q);
 // Sizes the SSD kernels implement (headdim, d_state, chunk, 32-bit offsets).

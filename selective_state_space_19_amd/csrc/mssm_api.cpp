@@ -142,6 +142,58 @@ int mssm_selective_scan_fused_fwd(const void* x, const float* conv_w, const floa
     return launched(fn, mssm::launch_s6_scan_fused(p, fe, dtype == MSSM_BF16, s));
 }
 
+size_t mssm_selective_scan_bwd_workspace_size(int64_t batch, int64_t d_inner, int64_t seqlen, int64_t d_state) {
+    if (batch < 0 || d_inner < 0 || seqlen < 0 || d_state < 1 || d_state > 64) return 0;
+    if (!prod_ok(batch, d_inner, seqlen, nullptr) || !prod_ok(batch, d_inner, d_state, nullptr)) return 0;
+    return mssm::s6_bwd_workspace_bytes(batch, d_inner, seqlen, d_state);
+}
+
+int mssm_selective_scan_bwd(const void* u, const void* delta, const float* A, const void* Bm, const void* Cm,
+                            const float* Dskip, const void* z, const float* h0, const void* dout,
+                            const float* dh_final, void* du, void* ddelta, float* dA, float* dB, float* dC,
+                            float* dD, void* dz, float* dh0, int64_t batch, int64_t d_inner, int64_t seqlen,
+                            int64_t d_state, void* workspace, size_t workspace_bytes, mssm_dtype dtype,
+                            void* stream) {
+    static const char* fn = "mssm_selective_scan_bwd";
+    g_err.clear();
+    if (dtype != MSSM_F32 && dtype != MSSM_BF16) return fail(MSSM_ERR_DTYPE, "%s: unknown dtype %d", fn, (int)dtype);
+    if (batch < 0 || d_inner < 0 || seqlen < 0 || d_state < 0)
+        return fail(MSSM_ERR_SHAPE, "%s: negative dimension", fn);
+    if (d_state < 1 || d_state > 64) return fail(MSSM_ERR_UNSUPPORTED, "%s: d_state %lld not in [1, 64]", fn, (long long)d_state);
+    if (seqlen > INT32_MAX) return fail(MSSM_ERR_UNSUPPORTED, "%s: seqlen %lld too large", fn, (long long)seqlen);
+    if (!prod_ok(batch, d_inner, seqlen, nullptr) || !prod_ok(batch, d_inner, d_state, nullptr))
+        return fail(MSSM_ERR_SHAPE, "%s: tensor too large", fn);
+    if (batch == 0 || d_inner == 0) return MSSM_OK;
+    CHECK_PTR(u);
+    CHECK_PTR(delta);
+    CHECK_PTR(A);
+    CHECK_PTR(Bm);
+    CHECK_PTR(Cm);
+    CHECK_PTR(dout);
+    CHECK_PTR(du);
+    CHECK_PTR(ddelta);
+    CHECK_PTR(dA);
+    CHECK_PTR(dB);
+    CHECK_PTR(dC);
+    CHECK_OPT(Dskip);
+    CHECK_OPT(z);
+    CHECK_OPT(h0);
+    CHECK_OPT(dh_final);
+    CHECK_OPT(dD);
+    CHECK_OPT(dz);
+    CHECK_OPT(dh0);
+    if (z && !dz) return fail(MSSM_ERR_NULL, "%s: dz is NULL while z is given", fn);
+    const size_t need = mssm::s6_bwd_workspace_bytes(batch, d_inner, seqlen, d_state);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(MSSM_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace_bytes);
+    CHECK_OPT(workspace);
+    const int64_t blocks = ((d_inner + 63) / 64) * batch;
+    if (blocks > INT32_MAX) return fail(MSSM_ERR_UNSUPPORTED, "%s: batch*d_inner too large", fn);
+    mssm::S6BwdParams p{u, delta, Bm, Cm, z, dout, A, Dskip, h0, dh_final, du, ddelta, dz, dA, dB, dC, dD, dh0,
+                        static_cast<float*>(workspace), batch, d_inner, (int32_t)seqlen, (int32_t)d_state};
+    return launched(fn, mssm::launch_s6_scan_bwd(p, dtype == MSSM_BF16, static_cast<hipStream_t>(stream)));
+}
+
 int mssm_state_update(float* state, const void* u, const void* delta, const float* A, const void* Bm,
                       const void* Cm, const float* Dskip, const void* z, void* y, int64_t batch,
                       int64_t d_inner, int64_t d_state, mssm_dtype dtype, void* stream) {

@@ -18,7 +18,8 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = _lib.header_functions()
-    assert set(names) == {"mssm_selective_scan_fwd", "mssm_selective_scan_fused_fwd", "mssm_state_update",
+    assert set(names) == {"mssm_selective_scan_fwd", "mssm_selective_scan_fused_fwd", "mssm_selective_scan_bwd",
+                          "mssm_selective_scan_bwd_workspace_size", "mssm_state_update",
                           "mssm_ssd_workspace_size",
                           "mssm_ssd_chunk_fwd", "mssm_ssd_state_update", "mssm_last_error", "mssm_version"}
     for n in names:
@@ -139,3 +140,27 @@ def test_fused_scan_argument_errors(lib):
     assert _fused(lib, dtype=3) == ERR_DTYPE
     assert _fused(lib, ci=MISALIGNED) == ERR_ALIGN
     assert _fused(lib, b=0) == 0
+
+
+def _bwd(lib, **kw):
+    a = dict(u=FAKE, dl=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, h0=None, go=FAKE, dhT=None, du=FAKE, dd=FAKE,
+             dA=FAKE, dB=FAKE, dC=FAKE, dD=None, dz=None, dh0=None, b=2, d=64, L=128, N=16, ws=FAKE, wsb=1 << 40,
+             dtype=1)
+    a.update(kw)
+    return lib.mssm_selective_scan_bwd(a["u"], a["dl"], a["A"], a["B"], a["C"], a["D"], a["z"], a["h0"], a["go"],
+                                       a["dhT"], a["du"], a["dd"], a["dA"], a["dB"], a["dC"], a["dD"], a["dz"],
+                                       a["dh0"], a["b"], a["d"], a["L"], a["N"], a["ws"], a["wsb"], a["dtype"], None)
+
+
+def test_backward_argument_errors(lib):
+    assert _bwd(lib, go=None) == ERR_NULL
+    assert _bwd(lib, dB=None) == ERR_NULL
+    assert _bwd(lib, z=FAKE, dz=None) == ERR_NULL
+    assert _bwd(lib, N=65) == ERR_UNSUP
+    assert _bwd(lib, dtype=2) == ERR_DTYPE
+    assert _bwd(lib, dh0=MISALIGNED) == ERR_ALIGN
+    need = lib.mssm_selective_scan_bwd_workspace_size(2, 64, 128, 16)
+    assert need == 2 * 64 * 16 * (128 // 16) * 4
+    assert _bwd(lib, ws=None) == ERR_WS
+    assert _bwd(lib, wsb=need - 1) == ERR_WS
+    assert _bwd(lib, b=0) == 0
