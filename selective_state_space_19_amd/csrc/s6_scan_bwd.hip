@@ -49,7 +49,7 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-template <typename T, int NS>
+template <typename T, int NS, bool ALIGNED>
 __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
     constexpr int kTC = ChunkLen<NS>::value;
     constexpr int kTPT = kTC / kSegs;      // tokens per row thread
@@ -91,14 +91,41 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
         lam[s] = (ok && p.dhT) ? p.dhT[ch * N + n] : 0.f;
         dAacc[s] = 0.f;
     }
-    // B / C of state s at token t (0 past the end or for a state past N).
-    auto bval = [&](int s, int t) -> float {
-        const int n = w * NS + s;
-        return (n < N && t < L) ? Elem<T>::load1(B_in + (b * N + nst[s]) * (int64_t)L + t) : 0.f;
-    };
-    auto cvalf = [&](int s, int t) -> float {
-        const int n = w * NS + s;
-        return (n < N && t < L) ? Elem<T>::load1(C_in + (b * N + nst[s]) * (int64_t)L + t) : 0.f;
+    // B / C of this wave's states over one chunk (0 past the end or for a
+    // state past N).  ALIGNED (L % 8 == 0) and a whole chunk: one vector load
+    // per state row; otherwise element by element.
+    float Bf[NS][kTC], Cf[NS][kTC];
+    auto load_bc = [&](int t0) {
+        const bool vec = ALIGNED && t0 + kTC <= L;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const int n = w * NS + s;
+            const T* pb = B_in + (b * N + nst[s]) * (int64_t)L + t0;
+            const T* pc = C_in + (b * N + nst[s]) * (int64_t)L + t0;
+            if (vec) {
+                constexpr int NW4 = kTC * (int)sizeof(T) / 16;        // 16-byte words per chunk row
+                uint32_t wb[NW4 * 4], wc[NW4 * 4];
+#pragma unroll
+                for (int q = 0; q < NW4; ++q) {
+                    const uint4 x = reinterpret_cast<const uint4*>(pb)[q];
+                    const uint4 y = reinterpret_cast<const uint4*>(pc)[q];
+                    wb[4 * q] = x.x; wb[4 * q + 1] = x.y; wb[4 * q + 2] = x.z; wb[4 * q + 3] = x.w;
+                    wc[4 * q] = y.x; wc[4 * q + 1] = y.y; wc[4 * q + 2] = y.z; wc[4 * q + 3] = y.w;
+                }
+#pragma unroll
+                for (int k = 0; k < kTC; ++k) {
+                    Bf[s][k] = n < N ? Elem<T>::get(wb, k) : 0.f;
+                    Cf[s][k] = n < N ? Elem<T>::get(wc, k) : 0.f;
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < kTC; ++k) {
+                    const bool ok = n < N && t0 + k < L;
+                    Bf[s][k] = ok ? Elem<T>::load1(pb + (ok ? k : 0)) : 0.f;
+                    Cf[s][k] = ok ? Elem<T>::load1(pc + (ok ? k : 0)) : 0.f;
+                }
+            }
+        }
     };
     // checkpoint of state s at the start of chunk ck
     auto ckpt = [&](int ck, int s) -> float* {
@@ -128,12 +155,13 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
             for (int s = 0; s < NS; ++s)
                 if (w * NS + s < N) *ckpt(ck, s) = h[s];
         }
+        load_bc(t0);
         __syncthreads();
-#pragma unroll 4
+#pragma unroll
         for (int k = 0; k < kTC; ++k) {
             const float4 q = s_tk[k][cs];
 #pragma unroll
-            for (int s = 0; s < NS; ++s) h[s] = fmaf(fast_exp2(q.x * a2[s]), h[s], q.y * bval(s, t0 + k));
+            for (int s = 0; s < NS; ++s) h[s] = fmaf(fast_exp2(q.x * a2[s]), h[s], q.y * Bf[s][k]);
         }
         __syncthreads();
     }
@@ -157,6 +185,7 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
         float hc[NS];
 #pragma unroll
         for (int s = 0; s < NS; ++s) hc[s] = (cval && w * NS + s < N) ? *ckpt(ck, s) : 0.f;
+        load_bc(t0);
         __syncthreads();
 
         // recompute the chunk's states; per-wave partial outputs to LDS
@@ -171,9 +200,9 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
                 float yp = 0.f;
 #pragma unroll
                 for (int s = 0; s < NS; ++s) {
-                    hh[s] = fmaf(fast_exp2(q.x * a2[s]), hh[s], q.y * bval(s, t0 + k));
+                    hh[s] = fmaf(fast_exp2(q.x * a2[s]), hh[s], q.y * Bf[s][k]);
                     hs[k][s] = hh[s];
-                    yp = fmaf(cvalf(s, t0 + k), hh[s], yp);
+                    yp = fmaf(Cf[s][k], hh[s], yp);
                 }
                 s_y[w][k][cs] = yp;
             }
@@ -203,7 +232,7 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
             float dup = 0.f, ddp = 0.f;
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
-                const float bv = bval(s, t), cv = cvalf(s, t);
+                const float bv = Bf[s][k], cv = Cf[s][k];
                 const float lt = fmaf(q.w, cv, lam[s]);
                 const float hp = k > 0 ? hs[k > 0 ? k - 1 : 0][s] : hc[s];
                 const float a = fast_exp2(q.x * a2[s]);
@@ -274,7 +303,10 @@ hipError_t zero(float* a, int64_t n, hipStream_t stream) {
 template <typename T, int NS>
 hipError_t launch_ns(const S6BwdParams& p, hipStream_t stream) {
     const int64_t blocks = ((p.dim + 63) / 64) * p.batch;
-    hipLaunchKernelGGL((s6_scan_bwd_kernel<T, NS>), dim3((unsigned)blocks), dim3(kNW * 64), 0, stream, p);
+    if (p.L % 8 == 0)
+        hipLaunchKernelGGL((s6_scan_bwd_kernel<T, NS, true>), dim3((unsigned)blocks), dim3(kNW * 64), 0, stream, p);
+    else
+        hipLaunchKernelGGL((s6_scan_bwd_kernel<T, NS, false>), dim3((unsigned)blocks), dim3(kNW * 64), 0, stream, p);
     return hipGetLastError();
 }
 
