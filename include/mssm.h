@@ -156,10 +156,11 @@ int mssm_selective_scan_fused_fwd(const void* x, const float* conv_w, const floa
  *   dz         (device) [batch, d_inner, seqlen] dtype; required when z is given
  *   dh0        (device) [batch, d_inner, d_state] float32, NULL => not written
  *   workspace  (device) at least mssm_selective_scan_bwd_workspace_size(...)
- *              bytes (the state at every 16-token chunk start); caller-owned
+ *              bytes (the state at every chunk start, and per-block partial
+ *              sums of dB and dC); caller-owned, contents unspecified
  *
- * dA, dB, dC and dD are accumulated with atomics, so their summation order
- * (and last bits) can vary from call to call.  Limits: 1 <= d_state <= 64.
+ * dA and dD are accumulated with atomics, so their last bits can vary from
+ * call to call; the other outputs are deterministic.  Limits: 1 <= d_state <= 64.
  */
 size_t mssm_selective_scan_bwd_workspace_size(int64_t batch, int64_t d_inner, int64_t seqlen,
                                               int64_t d_state);

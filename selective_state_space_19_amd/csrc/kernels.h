@@ -37,6 +37,7 @@ struct S6BwdParams {
     void *du, *ddelta, *dz;                       // [batch, dim, L] (input dtype)
     float *dA, *dB, *dC, *dD, *dh0;               // fp32: [dim, N], [batch, N, L] x 2, [dim], [batch, dim, N]
     float* ws;                                    // chunk-start states
+    float* part;                                  // dB / dC partial sums per channel block
     int64_t batch, dim;
     int32_t L, N;
 };
@@ -89,9 +90,10 @@ struct SSDUParams {
 hipError_t launch_s6_scan(const S6Params& p, bool is_bf16, hipStream_t stream);
 hipError_t launch_s6_scan_fused(const S6Params& p, const S6FrontEnd& fe, bool is_bf16, hipStream_t stream);
 hipError_t launch_state_update(const SUParams& p, bool is_bf16, hipStream_t stream);
-// Backward of the scan; zeroes dA, dB, dC, dD and then accumulates into them.
+// Backward of the scan; zeroes dA and dD and then accumulates into them.
 hipError_t launch_s6_scan_bwd(const S6BwdParams& p, bool is_bf16, hipStream_t stream);
 size_t s6_bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t L, int64_t N);
+int64_t s6_bwd_ckpt_floats(int64_t batch, int64_t dim, int64_t L, int64_t N);  // offset of the partials
 hipError_t launch_ssd(const SSDParams& p, hipStream_t stream);
 size_t ssd_workspace_bytes(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int64_t Q);
 // Sizes the SSD kernels implement (headdim, d_state, chunk, 32-bit offsets).

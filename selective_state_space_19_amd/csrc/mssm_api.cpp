@@ -189,8 +189,10 @@ int mssm_selective_scan_bwd(const void* u, const void* delta, const float* A, co
     CHECK_OPT(workspace);
     const int64_t blocks = ((d_inner + 63) / 64) * batch;
     if (blocks > INT32_MAX) return fail(MSSM_ERR_UNSUPPORTED, "%s: batch*d_inner too large", fn);
+    float* ws = static_cast<float*>(workspace);
     mssm::S6BwdParams p{u, delta, Bm, Cm, z, dout, A, Dskip, h0, dh_final, du, ddelta, dz, dA, dB, dC, dD, dh0,
-                        static_cast<float*>(workspace), batch, d_inner, (int32_t)seqlen, (int32_t)d_state};
+                        ws, ws + mssm::s6_bwd_ckpt_floats(batch, d_inner, seqlen, d_state), batch, d_inner,
+                        (int32_t)seqlen, (int32_t)d_state};
     return launched(fn, mssm::launch_s6_scan_bwd(p, dtype == MSSM_BF16, static_cast<hipStream_t>(stream)));
 }
 

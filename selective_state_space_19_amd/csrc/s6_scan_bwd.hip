@@ -25,11 +25,13 @@
 //      chunk in LDS; recompute the chunk's TC states from its checkpoint into
 //      registers (the per-wave partial outputs go to LDS, from which the row
 //      threads form y and dz); then walk the chunk backwards, keeping lambda
-//      in registers.  dB and dC are summed over the wave's 64 channels
-//      (cross-lane butterfly) and added with one atomic per (state, token);
-//      du and ddelta are summed over the waves through LDS by the row threads.
+//      in registers.  dB and dC are summed over the wave's 64 channels (a
+//      transposing lane reduction that leaves one value per lane) and stored
+//      as this workgroup's partial sums; a second kernel adds the partials of
+//      all channel blocks (no atomics: dB and dC are deterministic).  du and
+//      ddelta are summed over the waves through LDS by the row threads.
 //   dA and dD are accumulated in registers and added with atomics at the end
-//   (the entry point zeroes dA, dB, dC, dD first).
+//   (the entry point zeroes them first).
 #include "common.h"
 #include "kernels.h"
 
@@ -43,11 +45,42 @@ constexpr int kSegs = 8;               // row threads per channel
 // Tokens per chunk: the chunk's states are held in registers (TC x NS).
 template <int NS> struct ChunkLen { static constexpr int value = NS <= 2 ? 16 : 8; };
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-    return v;
+// ---- sums over a wave's 64 lanes of many values at once -----------------------
+// A transposing reduction: each step takes two registers x, y and leaves one,
+// in which the lanes with a given lane bit 0 hold x summed with the partner
+// lane's x, and those with the bit 1 hold y summed likewise.  Step ST uses lane
+// bit 5 - ST: ST 0 and 1 are the gfx950 lane swaps across halves and rows (no
+// selects needed), ST 2..5 pair lanes inside a row of 16 with DPP (rotate by 8,
+// half-row mirror, quad permutes ^2 and ^1; any partner with the other bit
+// value works).  After all six steps a register's lane L holds the sum over all
+// 64 lanes of the value whose index has L as its top six bits.
+template <int ST>
+__device__ __forceinline__ float combine(float x, float y) {
+    if constexpr (ST == 0 || ST == 1) {
+        const auto r = ST == 0 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false)
+                               : __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+        return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    } else {
+        constexpr int CTRL = ST == 2 ? 0x128 : ST == 3 ? 0x141 : ST == 4 ? 0x4e : 0xb1;
+        const bool hi = (__lane_id() >> (5 - ST)) & 1;
+        const float keep = hi ? y : x, send = hi ? x : y;
+        return keep + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, send), CTRL, 0xf,
+                                                                          0xf, false));
+    }
 }
+
+// Steps ST, ST + 1, ... on v[0 .. SIZE) (pairs v[i], v[i + SIZE / 2]) until one
+// register is left or the six steps are done.
+template <int ST, int SIZE, int CAP>
+__device__ __forceinline__ void tree(float (&v)[CAP]) {
+    if constexpr (SIZE > 1 && ST < 6) {
+#pragma unroll
+        for (int i = 0; i < SIZE / 2; ++i) v[i] = combine<ST>(v[i], v[i + SIZE / 2]);
+        tree<ST + 1, SIZE / 2>(v);
+    }
+}
+
+constexpr int log2i(int n) { return n <= 1 ? 0 : 1 + log2i(n / 2); }
 
 template <typename T, int NS, bool ALIGNED>
 __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
@@ -69,6 +102,9 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
 
     const int tid = threadIdx.x;
     const int64_t nblk_d = (dim + 63) / 64;
+    constexpr int kNSP = NS < 2 ? 2 : NS;                 // states per wave in the dB / dC layout
+    constexpr int kVPW = 2 * kNSP * kTC;                  // dB / dC partials per wave and chunk
+    static_assert(kVPW == 64 || kVPW == 128, "reduction layout");
     const int64_t b = blockIdx.x / nblk_d;
     const int64_t d0 = (blockIdx.x % nblk_d) * 64;
     const int nrows = (int)((dim - d0) < 64 ? (dim - d0) : 64);
@@ -224,31 +260,45 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
             dDacc = fmaf(gg[j], uu[j], dDacc);
         }
 
-        // walk the chunk backwards
+        // walk the chunk backwards.  dB / dC of (state s, token k) summed over
+        // the wave's 64 channels: value index ((s 2 + c) kTC + k), c 0 for B
+        // and 1 for C; s runs to NSP = max(NS, 2), the padding states are 0.
+        // The (s, c) values of a token are reduced at once (tree steps 0 ..
+        // log2(2 NSP) - 1), leaving rk[k]; the tokens after the walk.
+        float rk[kTC];
 #pragma unroll
         for (int k = kTC - 1; k >= 0; --k) {
             const float4 q = s_tk[k][cs];
-            const int t = t0 + k;
             float dup = 0.f, ddp = 0.f;
+            float v[2 * kNSP];
+#pragma unroll
+            for (int s = NS; s < kNSP; ++s) v[2 * s] = v[2 * s + 1] = 0.f;
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
                 const float bv = Bf[s][k], cv = Cf[s][k];
                 const float lt = fmaf(q.w, cv, lam[s]);
                 const float hp = k > 0 ? hs[k > 0 ? k - 1 : 0][s] : hc[s];
                 const float a = fast_exp2(q.x * a2[s]);
-                const float dBp = wave_sum(lt * q.y);
-                const float dCp = wave_sum(q.w * hs[k][s]);
-                const int n = w * NS + s;
-                if (cs == 0 && n < N && t < L) {
-                    atomicAdd(p.dB + (b * N + n) * (int64_t)L + t, dBp);
-                    atomicAdd(p.dC + (b * N + n) * (int64_t)L + t, dCp);
-                }
+                v[2 * s] = lt * q.y;
+                v[2 * s + 1] = q.w * hs[k][s];
                 dup = fmaf(lt * q.x, bv, dup);
                 ddp = fmaf(lt, fmaf(Af[s] * a, hp, q.z * bv), ddp);
                 dAacc[s] = fmaf(lt * q.x * a, hp, dAacc[s]);
                 lam[s] = a * lt;
             }
+            tree<0, 2 * kNSP>(v);
+            rk[k] = v[0];
             s_p[w][k][cs] = make_float2(dup, ddp);
+        }
+        tree<log2i(2 * kNSP), kTC>(rk);
+        {
+            // this workgroup's partial sums for the chunk: lane L holds the
+            // values L R .. L R + R - 1 of the wave's kVPW
+            constexpr int R = kVPW / 64;
+            float* part = p.part + ((b * nblk_d + blockIdx.x % nblk_d) * nck + ck) * (int64_t)(kNW * kVPW) + w * kVPW +
+                          cs * R;
+            if constexpr (R == 1) part[0] = rk[0];
+            else *reinterpret_cast<float2*>(part) = make_float2(rk[0], rk[1]);
         }
         __syncthreads();
 
@@ -287,6 +337,35 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
     if (rval && seg == 0 && p.dD) atomicAdd(p.dD + d0 + cr, dDacc);
 }
 
+// dB, dC[b, n, t] = sum over the channel blocks of the partial sums.  Per
+// (batch, block, chunk) the partials are [wave][(s 2 + c) kTC + k] with
+// n = wave NS + s, c 0 for B and 1 for C.
+template <int NS>
+__global__ void s6_bwd_reduce_bc_kernel(S6BwdParams p) {
+    constexpr int kTC = ChunkLen<NS>::value;
+    constexpr int kNSP = NS < 2 ? 2 : NS;
+    constexpr int kVPW = 2 * kNSP * kTC;
+    constexpr int PER = kNW * kVPW;
+    const int64_t nblk = (p.dim + 63) / 64;
+    const int nck = (p.L + kTC - 1) / kTC;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (b, chunk, j)
+    if (i >= p.batch * nck * (int64_t)PER) return;
+    const int j = (int)(i % PER);
+    const int64_t bc = i / PER;
+    const int ck = (int)(bc % nck);
+    const int64_t b = bc / nck;
+    const int w = j / kVPW, idx = j % kVPW;
+    const int k = idx % kTC, sc = idx / kTC;
+    const int s = sc >> 1, c = sc & 1;
+    const int n = w * NS + s;
+    const int t = ck * kTC + k;
+    if (s >= NS || n >= p.N || t >= p.L) return;
+    float acc = 0.f;
+    const float* src = p.part + (b * nblk * nck + ck) * (int64_t)PER + j;
+    for (int64_t blk = 0; blk < nblk; ++blk) acc += src[blk * nck * (int64_t)PER];
+    (c ? p.dC : p.dB)[(b * p.N + n) * (int64_t)p.L + t] = acc;
+}
+
 __global__ void zero_kernel(float* a, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) a[i] = 0.f;
@@ -307,6 +386,13 @@ hipError_t launch_ns(const S6BwdParams& p, hipStream_t stream) {
         hipLaunchKernelGGL((s6_scan_bwd_kernel<T, NS, true>), dim3((unsigned)blocks), dim3(kNW * 64), 0, stream, p);
     else
         hipLaunchKernelGGL((s6_scan_bwd_kernel<T, NS, false>), dim3((unsigned)blocks), dim3(kNW * 64), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    constexpr int kTC = ChunkLen<NS>::value;
+    const int64_t n = p.batch * ((p.L + kTC - 1) / kTC) * (int64_t)(kNW * (NS < 2 ? 2 : NS) * kTC * 2);
+    const int64_t rblocks = (n + 255) / 256;
+    if (rblocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((s6_bwd_reduce_bc_kernel<NS>), dim3((unsigned)rblocks), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -320,17 +406,27 @@ hipError_t launch_t(const S6BwdParams& p, hipStream_t stream) {
 
 }  // namespace
 
-size_t s6_bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t L, int64_t N) {
-    const int tc = N <= 16 ? ChunkLen<2>::value : ChunkLen<4>::value;   // NS <= 2 iff N <= 16
+// Workspace: the chunk-start states [batch, chunk, N, dim], then the dB / dC
+// partial sums [batch, channel block, chunk, 8 NS states, TC tokens, 2].
+static int ns_of(int64_t N) { return N <= 8 ? 1 : N <= 16 ? 2 : N <= 32 ? 4 : 8; }
+
+int64_t s6_bwd_ckpt_floats(int64_t batch, int64_t dim, int64_t L, int64_t N) {
+    const int tc = ns_of(N) <= 2 ? ChunkLen<2>::value : ChunkLen<4>::value;
     const int64_t nck = (L + tc - 1) / tc;
-    return (size_t)(batch * nck * N * dim) * sizeof(float);
+    return (batch * nck * N * dim + 63) / 64 * 64;
+}
+
+size_t s6_bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t L, int64_t N) {
+    const int ns = ns_of(N);
+    const int tc = ns <= 2 ? ChunkLen<2>::value : ChunkLen<4>::value;
+    const int64_t nck = (L + tc - 1) / tc;
+    const int64_t part = batch * ((dim + 63) / 64) * nck * (int64_t)(kNW * (ns < 2 ? 2 : ns) * tc * 2);
+    return (size_t)(s6_bwd_ckpt_floats(batch, dim, L, N) + part) * sizeof(float);
 }
 
 hipError_t launch_s6_scan_bwd(const S6BwdParams& p, bool is_bf16, hipStream_t stream) {
     hipError_t e;
     if ((e = zero(p.dA, p.dim * p.N, stream)) != hipSuccess) return e;
-    if ((e = zero(p.dB, p.batch * p.N * (int64_t)p.L, stream)) != hipSuccess) return e;
-    if ((e = zero(p.dC, p.batch * p.N * (int64_t)p.L, stream)) != hipSuccess) return e;
     if ((e = zero(p.dD, p.dD ? p.dim : 0, stream)) != hipSuccess) return e;
     return is_bf16 ? launch_t<uint16_t>(p, stream) : launch_t<float>(p, stream);
 }

@@ -160,7 +160,9 @@ def test_backward_argument_errors(lib):
     assert _bwd(lib, dtype=2) == ERR_DTYPE
     assert _bwd(lib, dh0=MISALIGNED) == ERR_ALIGN
     need = lib.mssm_selective_scan_bwd_workspace_size(2, 64, 128, 16)
-    assert need == 2 * 64 * 16 * (128 // 16) * 4
+    ckpt = 2 * (128 // 16) * 16 * 64                    # chunk-start states
+    part = 2 * 1 * (128 // 16) * (8 * 2 * 16 * 2)       # dB / dC partials per channel block
+    assert need == (ckpt + part) * 4
     assert _bwd(lib, ws=None) == ERR_WS
     assert _bwd(lib, wsb=need - 1) == ERR_WS
     assert _bwd(lib, b=0) == 0
