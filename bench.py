@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "selective-scan effective HBM GB/s (% of peak) + B·L·D_inner tokens-ch/s"
 HBM_PEAK_GBS = 8000.0                  # MI355X HBM3E, 8 TB/s
+WARM_MS = 100.0                        # wall-clock warm-up before each secondary timing
 # fp32 VALU issue rate without packed math: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz.
 VALU_LANE_INSTR = 256 * 4 * 16 * 2.4e9
 # One S6 state element: v_mul (delta*A), v_exp, v_mul (delta*u*B), v_fma (h), v_fma (y):
@@ -121,15 +122,22 @@ def to_dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def time_launches(fn, steps, warmup, stream, wall=None):
-    """Warm up, then time `steps` calls with HIP events on `stream` (the
-    stream the kernels are launched on), bracketed by device synchronisation.
-    Returns (total ms, per-call ms); if `wall` is a list, the host wall-clock
-    ms of the same bracketed region is appended to it."""
+def time_launches(fn, steps, warmup, stream, wall=None, warm_ms=0.0):
+    """Warm up (`warmup` calls, then more until `warm_ms` of wall time has
+    passed: the GPU's clocks ramp up over tens of milliseconds of load), then
+    time `steps` calls with HIP events on `stream` (the stream the kernels are
+    launched on), bracketed by device synchronisation.  Returns (total ms,
+    per-call ms); if `wall` is a list, the host wall-clock ms of the same
+    bracketed region is appended to it."""
     import torch
+    t_w = time.perf_counter()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    while (time.perf_counter() - t_w) * 1e3 < warm_ms:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
     evs[0].record(stream)
@@ -192,7 +200,7 @@ def bench_s6fused(args):
         mssm.selective_scan_fused(d["x"], d["conv_w"], d["delta_raw"], d["A"], d["B"], d["C"], d["D"], d["z"],
                                   conv_b=d["conv_b"], delta_bias=d["delta_bias"], out=y, h_final=hf, stream=stream)
 
-    total, per = time_launches(step, max(5, args.steps // 2), 2, stream)
+    total, per = time_launches(step, max(5, args.steps // 2), 2, stream, warm_ms=WARM_MS)
     ms = total / max(5, args.steps // 2)
     nb = s6_bytes(s["batch"], s["d_inner"], s["seqlen"], s["d_state"], 2) + s["d_inner"] * (s["d_conv"] + 2) * 4
     tok = s["batch"] * s["d_inner"] * s["seqlen"]
@@ -225,7 +233,7 @@ def bench_s6bwd(args):
                                 workspace=ws, stream=stream)
 
     steps = max(3, args.steps // 4)
-    total, _ = time_launches(step, steps, 1, stream)
+    total, _ = time_launches(step, steps, 1, stream, warm_ms=WARM_MS)
     ms = total / steps
     B, D, L, N = s["batch"], s["d_inner"], s["seqlen"], s["d_state"]
     # read u, delta, z, dout (twice: forward sweep reads u, delta) ; write du, ddelta, dz; dB, dC; state checkpoints
@@ -313,7 +321,7 @@ def bench_decode(args):
     res = {"workload": f"{wl.name}: batch {bsz}, d_inner {dim}, d_state {N}, bf16, {steps} tokens",
            "bytes_per_step": nb, "traffic_bytes_per_launch": profiled_traffic("state_update_mamba2p8b_decode.md")}
     for label, rot in (("cold_16_buffers", True), ("hot_single_buffer", False)):
-        total, _ = time_launches(lambda: run_all(rot), 3, 1, stream)
+        total, _ = time_launches(lambda: run_all(rot), 3, 1, stream, warm_ms=WARM_MS)
         us = total / 3 / steps * 1e3
         res[label + "_launches"] = {"us_per_step": us, "GBs": nb / (us * 1e-6) / 1e9}
     # The same 256 tokens captured in one HIP graph (launch overhead removed).
@@ -330,7 +338,7 @@ def bench_decode(args):
                     t = dtk[i]
                     mssm.state_update(states[i % K] if rot else states[0], t["u"], t["delta"], A, t["B"], t["C"],
                                       D, t["z"], out=ys[i])
-            total, _ = time_launches(g.replay, 5, 2, torch.cuda.current_stream())
+            total, _ = time_launches(g.replay, 5, 2, torch.cuda.current_stream(), warm_ms=WARM_MS)
             us = total / 5 / steps * 1e3
             res[label + "_graph"] = {"us_per_step": us, "GBs": nb / (us * 1e-6) / 1e9,
                                      "hbm_frac": nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
@@ -373,7 +381,7 @@ def bench_decode2(args):
     res = {"workload": f"{wl.name}: batch {bsz}, {H} heads x {P}, d_state {N}, ngroups {G}, bf16, {steps} tokens",
            "bytes_per_step": nb, "traffic_bytes_per_launch": profiled_traffic("ssd_state_update_mamba2_decode.md")}
     for label, rot in (("cold_8_buffers", True), ("hot_single_buffer", False)):
-        total, _ = time_launches(lambda: run_all(rot, stream), 3, 1, stream)
+        total, _ = time_launches(lambda: run_all(rot, stream), 3, 1, stream, warm_ms=WARM_MS)
         us = total / 3 / steps * 1e3
         res[label + "_launches"] = {"us_per_step": us, "GBs": nb / (us * 1e-6) / 1e9}
     try:
@@ -386,7 +394,7 @@ def bench_decode2(args):
             torch.cuda.current_stream().wait_stream(side)
             with torch.cuda.graph(g):
                 run_all(rot)
-            total, _ = time_launches(g.replay, 5, 2, torch.cuda.current_stream())
+            total, _ = time_launches(g.replay, 5, 2, torch.cuda.current_stream(), warm_ms=WARM_MS)
             us = total / 5 / steps * 1e3
             res[label + "_graph"] = {"us_per_step": us, "GBs": nb / (us * 1e-6) / 1e9,
                                      "hbm_frac": nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
@@ -420,7 +428,7 @@ def bench_ssd(args):
         mssm.ssd_chunk(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], chunk=s["chunk"], out=y,
                        workspace=ws, stream=stream)
 
-    total, per = time_launches(step, 20, 3, stream)
+    total, per = time_launches(step, 20, 3, stream, warm_ms=WARM_MS)
     ms = total / 20
     nb = ssd_bytes(s["batch"], s["seqlen"], s["nheads"], s["headdim"], s["d_state"], s["ngroups"], 2)
     fl = ssd_flops(s["batch"], s["seqlen"], s["nheads"], s["headdim"], s["d_state"], s["ngroups"], s["chunk"])
@@ -450,8 +458,8 @@ def bench_copy(args):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--only", default="s6,s6fused,s6bwd,decode,decode2,ssd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")

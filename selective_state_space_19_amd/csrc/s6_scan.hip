@@ -15,32 +15,33 @@
 //   would add a second pass and a cross-lane combine per element).  The fp32
 //   state lives in registers for the whole sequence and reaches HBM only as
 //   h0 / h_final.
-// - Scan mapping: lanes are channels and waves are state groups.  A
-//   workgroup of NW = 8 waves owns 64 channels of one batch row; wave w owns
-//   the states [w*NS, (w+1)*NS).  B and C are shared by all channels, so
-//   within a wave they are uniform: they are fetched with scalar loads into
-//   SGPRs (bf16 unpacked on the scalar unit) and used as free scalar
-//   operands.  Eight waves of NS = 2 states put two waves on each SIMD, so
-//   one wave's scalar and LDS instructions issue beside the other's VALU work.
-// - Row mapping (loads, staging, epilogue): thread -> (row tid/8, segment
-//   tid%8), TPT consecutive tokens each, so one wave-level load or store
-//   covers 8 rows x 8 contiguous segments -- whole cache-line runs.  The
-//   row mapping stages (delta, delta*u) in LDS for the scan and, after it,
-//   sums the NW per-wave partial outputs sum_n C*h, adds D*u, gates with
-//   silu(z) and stores y; u and z stay in the registers they were loaded into.
-// - Time is processed in chunks of TC tokens; a register ring keeps the
-//   row loads of the next RING-1 chunks in flight; y is stored with the
-//   streaming (non-temporal) cache policy.  Inside a chunk, token
-//   groups (16 bytes of a B / C row) are software-pipelined: the next
-//   group's scalar B / C loads and LDS (delta, delta*u) loads are issued
-//   before the current group is computed, and waited for after it.
+// - A workgroup owns 64 channels of one batch row and has two roles:
+//   * 8 scan waves: lanes are channels, wave w owns the states
+//     [w*NS, (w+1)*NS).  B and C are shared by all channels, so within a
+//     wave they are uniform: they are fetched with scalar loads into SGPRs
+//     (bf16 unpacked on the scalar unit) and used as free scalar operands.
+//   * 4 row waves: lane = row (channel), row wave = a TPT-token segment of
+//     the chunk.  They stream u, delta, z through a register ring (the loads
+//     of the next RING-1 chunks in flight), stage (delta, delta*u) in LDS for
+//     the scan, and run the epilogue: the sum of the 8 per-wave partial
+//     outputs sum_n C*h, the D*u term, the silu(z) gate and the y store.
+//   Time is processed in chunks of TC tokens, the LDS buffers are doubled by
+//   chunk parity, and one barrier per chunk hands work between the roles:
+//   while the scan waves scan chunk k, the row waves finish chunk k-1 and
+//   stage chunk k+1.  Each SIMD holds two scan waves and one row wave, so
+//   the row work fills issue slots the scan leaves idle.
+// - Inside a chunk the scan runs token groups of 32 bytes of a B / C row,
+//   software-pipelined: the next group's scalar B / C loads and LDS
+//   (delta, delta*u) loads are issued before the current group is computed
+//   and waited for after it (scalar loads complete out of order, so every
+//   wait drains them all; a longer group gives each load more cover).
 // - exp(delta*A) is computed as exp2(delta * (A*log2 e)) with A*log2 e
 //   precomputed per lane.
-// - ALIGNED (L % 8 == 0; the common case) addresses rows through
-//   range-checked buffer resources: loads past the end read zero and stores
-//   there are dropped, so the hot loop has no bounds branches and every load
-//   is issued unconditionally.  Other lengths take the same arithmetic with
-//   element-wise bounds checks.
+// - ALIGNED (L a multiple of a group; the common case) addresses rows
+//   through range-checked buffer resources: loads past the end read zero and
+//   stores there are dropped, so the hot loops have no bounds branches and
+//   every load is issued unconditionally.  Other lengths take the same
+//   arithmetic with element-wise bounds checks.
 #include "common.h"
 #include "kernels.h"
 
@@ -48,353 +49,396 @@ namespace mssm {
 
 namespace {
 
-template <typename T, int NW, int NS, int TC, bool ALIGNED, bool FULLN, bool FUSED, int RING>
-__global__ __launch_bounds__(NW * 64) void s6_scan_kernel(
+struct alignas(16) Words8 { uint32_t w[8]; };   // bases are 16-byte aligned
+
+constexpr int kScanWaves = 8;     // waves running the recurrence
+constexpr int kRowWaves = 4;      // waves streaming rows: loads, staging, epilogue
+constexpr int kRing = 4;          // row-wave register ring: chunks of loads in flight + 1
+
+template <typename T, int NS, int TC, bool ALIGNED, bool FULLN, bool FUSED, int RING>
+__global__ __launch_bounds__((kScanWaves + kRowWaves) * 64) void s6_scan_kernel(
     const T* __restrict__ u_in, const T* __restrict__ dl_in, const T* __restrict__ B_in,
     const T* __restrict__ C_in, const T* __restrict__ z_in, const float* __restrict__ A_in,
     const float* __restrict__ D_in, const float* __restrict__ h0_in, T* __restrict__ y_out,
     float* __restrict__ hT_out, int64_t dim, int L, int N, S6FrontEnd fe) {
     // FUSED: u_in is x before the causal conv and dl_in the step before
-    // softplus; the row-mapping threads form u = silu(conv(x)) and
-    // delta = softplus(raw + bias) while staging.
+    // softplus; the row waves form u = silu(conv(x)) and delta =
+    // softplus(raw + bias) while staging.
     // Pointers are separate __restrict__ arguments so the compiler may fetch the
     // wave-uniform B / C words with scalar loads (it must know no store aliases them).
-    constexpr int SEGS = NW;                       // row segments (threads per row)
-    constexpr int TPT = TC / SEGS;                 // tokens per thread (row mapping)
+    constexpr int NW = kScanWaves;
+    constexpr int SEGS = kRowWaves;                // row threads per row (64 rows): one per row wave
+    constexpr int TPT = TC / SEGS;                 // tokens per row thread
     constexpr int WPT = TPT * sizeof(T) / 4;       // 32-bit words per thread run
-    constexpr int G = 16 / sizeof(T);              // tokens per scan group: 16 bytes of a B / C row
+    constexpr int PW = 4 * sizeof(T) / 4;          // words of the 4 tokens before a run (FUSED)
+    constexpr int G = 32 / sizeof(T);              // tokens per scan group: 32 bytes of a B / C row
     constexpr int NGRP = TC / G;
-    constexpr int BCW = 4;                         // words per B / C row per group
+    constexpr int BCW = 8;                         // words per B / C row per group
     constexpr int PR = TC / 2;                     // token pairs per chunk
-    constexpr int PAD = 1;                         // LDS row padding (bank spreading)
-    static_assert(TPT % 2 == 0 && (WPT == 2 || WPT == 4), "row runs are 8- or 16-byte vectors");
-    static_assert(TC % G == 0, "whole scan groups per chunk");
+    static_assert(TPT % 2 == 0 && (WPT == 2 || WPT == 4 || WPT == 8), "row runs are 8-, 16- or 32-byte vectors");
+    static_assert(TC % G == 0 && NGRP % 2 == 0, "whole scan groups per chunk, even count");
+    static_assert(RING >= 3 && RING % 2 == 0, "ring: stage, epilogue and reload use distinct slots");
 
-    __shared__ float4 s_dd[PR][64 + PAD];          // (delta_t, (delta*u)_t, delta_t+1, (delta*u)_t+1)
-    __shared__ float2 s_y[NW][PR][64 + PAD];       // per-wave partial outputs, token pairs
+    // Double-buffered by chunk parity.  Every access, from either role, has
+    // one token pair per instruction and the 64 channels on consecutive
+    // lanes, so the plain layout is free of bank conflicts.
+    __shared__ float4 s_dd[2][PR][64];             // (delta_t, (delta*u)_t, delta_t+1, (delta*u)_t+1)
+    __shared__ float2 s_y[2][NW][PR][64];          // per-scan-wave partial outputs, token pairs
 
     const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t nblk_d = (dim + 63) / 64;
     const int64_t b = blockIdx.x / nblk_d;
     const int64_t d0 = (blockIdx.x % nblk_d) * 64;
     const int nrows = (int)((dim - d0) < 64 ? (dim - d0) : 64);
+    const int nchunks = (L + TC - 1) / TC;
+    // Both roles run `nit` chunk iterations (a multiple of RING, so the row
+    // waves' ring slots are compile-time indices); chunks past the end read
+    // zeros (a zero step leaves h unchanged) and store nothing.
+    const int nit = (nchunks + RING - 1) / RING * RING;
 
-    // ---- scan mapping: lane = channel cs, wave = state group w --------------
-    const int cs = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const bool sval_d = cs < nrows;
-    const T* brow[NS];
-    const T* crow[NS];
-    bool sval[NS];
-    float h[NS], a2[NS];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        const int n = w * NS + s;
-        sval[s] = n < N;
-        const int64_t off = (b * N + (sval[s] ? n : 0)) * (int64_t)L;
-        brow[s] = B_in + off;
-        crow[s] = C_in + off;
-        const bool ok = sval_d && sval[s];
-        a2[s] = ok ? A_in[(d0 + cs) * N + n] * kLog2e : 0.f;
-        h[s] = (ok && h0_in) ? h0_in[(b * dim + d0 + cs) * N + n] : 0.f;
-    }
-
-    // ---- row mapping: thread -> (row cr, tokens [toff, toff + TPT)) ----------
-    const int cr = tid / SEGS;
-    const int toff = (tid % SEGS) * TPT;
-    const bool rval = cr < nrows;
-    const float dskip = (rval && D_in) ? D_in[d0 + cr] : 0.f;
-    // Front end (FUSED): this row's conv taps, right-aligned in a 4-tap
-    // window (w4[3] multiplies the current token); the 3 inputs before the
-    // current run (`carry`, used by the row's first segment); the biases.
-    float w4[4] = {0.f, 0.f, 0.f, 0.f}, carry[3] = {0.f, 0.f, 0.f}, cbias = 0.f, dbias = 0.f;
-    if constexpr (FUSED) {
-        const int64_t dr = d0 + (rval ? cr : 0);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {                      // tap k of the window is conv_w[k - (4 - K)]
-            const int i = k - (4 - fe.K);
-            w4[k] = i >= 0 ? fe.conv_w[dr * fe.K + i] : 0.f;
-        }
-        cbias = fe.conv_b ? fe.conv_b[dr] : 0.f;
-        dbias = fe.delta_bias ? fe.delta_bias[dr] : 0.f;
-        if (fe.conv_init) {
-            const T* ci = static_cast<const T*>(fe.conv_init) + (b * dim + dr) * (fe.K - 1);
-#pragma unroll
-            for (int k = 0; k < 3; ++k) {                  // carry[k] is the input 3 - k tokens back
-                const int i = k - (4 - fe.K);
-                carry[k] = i >= 0 ? Elem<T>::load1(ci + i) : 0.f;
-            }
-        }
-    }
-    const int seg = tid % SEGS;
-    const int64_t blk0 = (b * dim + d0) * (int64_t)L;            // first element of this block's rows
-    const uint32_t blk_bytes = ALIGNED ? (uint32_t)nrows * (uint32_t)L * (uint32_t)sizeof(T) : 0u;
-    const rsrc_t rs_u = make_rsrc(u_in + blk0, blk_bytes);
-    const rsrc_t rs_dl = make_rsrc(dl_in + blk0, blk_bytes);
-    const rsrc_t rs_z = make_rsrc(z_in ? z_in + blk0 : u_in + blk0, z_in ? blk_bytes : 0u);
-    const rsrc_t rs_y = make_rsrc(y_out + blk0, blk_bytes);
-    auto run_off = [&](int t) -> uint32_t {   // byte offset of this thread's run at token t
-        return (t < L) ? ((uint32_t)cr * (uint32_t)L + (uint32_t)t) * (uint32_t)sizeof(T) : kOutOfRange;
-    };
-    const int64_t rrow = (int64_t)(rval ? cr : 0) * L;
-    const T* u_row = u_in + blk0 + rrow;
-    const T* dl_row = dl_in + blk0 + rrow;
-    const T* z_row = z_in ? z_in + blk0 + rrow : nullptr;
-    T* y_row = y_out + blk0 + rrow;
-
-    // A ring of RING register sets holds the u / delta / z runs of the next
-    // RING-1 chunks, so several chunks of loads are in flight per CU.
-    uint32_t ru[RING][WPT], rdl[RING][WPT], rz[RING][WPT];
-#pragma unroll
-    for (int r = 0; r < RING; ++r)
-#pragma unroll
-        for (int i = 0; i < WPT; ++i) rz[r][i] = 0u;
-    auto load_chunk = [&](int ck, uint32_t (&wu)[WPT], uint32_t (&wdl)[WPT], uint32_t (&wz)[WPT]) {
-        const int t = ck * TC + toff;
-        if constexpr (ALIGNED) {
-            // Unconditional: without z, rs_z is empty and the load returns 0.
-            const uint32_t off = run_off(t);
-            buf_load<WPT>(rs_u, off, wu);
-            buf_load<WPT>(rs_dl, off, wdl);
-            buf_load<WPT>(rs_z, off, wz);
-        } else {
-            const int valid = rval ? (L - t) : 0;
-            load_run<T, TPT>(u_row + t, valid, false, wu);
-            load_run<T, TPT>(dl_row + t, valid, false, wdl);
-            if (z_row) load_run<T, TPT>(z_row + t, valid, false, wz);
-        }
-    };
-
-    // B / C words of one group, for NS states (scalar registers).  ALIGNED:
-    // a group is either inside the sequence or wholly past it; a group past
-    // it re-reads the last group (finite data times a zero step: no effect).
-    // A state past N gets C = 0, so it adds nothing to y.
-    auto load_bc = [&](int t, uint32_t (&bw)[NS][BCW], uint32_t (&cw)[NS][BCW]) {
+    if (wave < NW) {
+        // ================= scan role: lane = channel cs, wave = state group w =================
+        const int cs = tid & 63;
+        const int w = wave;
+        const bool sval_d = cs < nrows;
+        const T* brow[NS];
+        const T* crow[NS];
+        bool sval[NS];
+        float h[NS], a2[NS];
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-            if constexpr (ALIGNED) {
-                const int tc = t < L ? t : L - G;
-                const uint4 x = *reinterpret_cast<const uint4*>(brow[s] + tc);
-                const uint4 y = *reinterpret_cast<const uint4*>(crow[s] + tc);
-                // Raw words: a state past N is zeroed where C is used, after
-                // the group's wait, so these loads stay in flight meanwhile.
-                bw[s][0] = x.x; bw[s][1] = x.y; bw[s][2] = x.z; bw[s][3] = x.w;
-                cw[s][0] = y.x; cw[s][1] = y.y; cw[s][2] = y.z; cw[s][3] = y.w;
-            } else {
-                const int valid = sval[s] ? L - t : 0;
-                load_run<T, G>(brow[s] + t, valid, false, bw[s]);
-                load_run<T, G>(crow[s] + t, valid, false, cw[s]);
-            }
+            const int n = w * NS + s;
+            sval[s] = n < N;
+            const int64_t off = (b * N + (sval[s] ? n : 0)) * (int64_t)L;
+            brow[s] = B_in + off;
+            crow[s] = C_in + off;
+            const bool ok = sval_d && sval[s];
+            a2[s] = ok ? A_in[(d0 + cs) * N + n] * kLog2e : 0.f;
+            h[s] = (ok && h0_in) ? h0_in[(b * dim + d0 + cs) * N + n] : 0.f;
         }
-    };
 
-    uint32_t bw[2][NS][BCW], cw[2][NS][BCW];
-    float4 ddr[2][G / 2];
-    const int nchunks = (L + TC - 1) / TC;
-
-    // C of state s at token k of the group in buffer `buf`; 0 for a state
-    // past N (FULLN: every state of every wave is below N).
-    auto cval = [&](int buf, int s, int k) -> float {
-        const float c = Elem<T>::get(cw[buf][s], k);
-        if constexpr (ALIGNED && !FULLN) return sval[s] ? c : 0.f;
-        return c;
-    };
-    // One group of G tokens in buffer `buf`, all NS states.  The decay
-    // factors and input terms of the whole group are formed first (they do
-    // not depend on h), so each exp has independent work behind it; then the
-    // recurrence runs token by token.
-    auto group = [&](int buf, int gi) {
-        float dA[G][NS], bu[G][NS];
-#pragma unroll
-        for (int k = 0; k < G; k += 2) {
-            const float4 q = ddr[buf][k / 2];
+        // B / C words of one group, for NS states (scalar registers).  ALIGNED:
+        // a group is either inside the sequence or wholly past it; a group past
+        // it re-reads the last group (finite data times a zero step: no effect).
+        // A state past N gets C = 0, so it adds nothing to y.
+        auto load_bc = [&](int t, uint32_t (&bw)[NS][BCW], uint32_t (&cw)[NS][BCW]) {
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
-                dA[k][s] = fast_exp2(q.x * a2[s]);
-                dA[k + 1][s] = fast_exp2(q.z * a2[s]);
-                bu[k][s] = q.y * Elem<T>::get(bw[buf][s], k);
-                bu[k + 1][s] = q.w * Elem<T>::get(bw[buf][s], k + 1);
-            }
-        }
+                if constexpr (ALIGNED) {
+                    const int tc = t < L ? t : L - G;
+                    // Raw words (one 32-byte scalar load per row): a state past
+                    // N is zeroed where C is used, after the group's wait, so
+                    // these loads stay in flight meanwhile.
+                    const Words8 x = *reinterpret_cast<const Words8*>(brow[s] + tc);
+                    const Words8 y = *reinterpret_cast<const Words8*>(crow[s] + tc);
 #pragma unroll
-        for (int k = 0; k < G; k += 2) {
-            float y0 = 0.f, y1 = 0.f;
-#pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                h[s] = fmaf(dA[k][s], h[s], bu[k][s]);
-                y0 = fmaf(cval(buf, s, k), h[s], y0);
-            }
-#pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                h[s] = fmaf(dA[k + 1][s], h[s], bu[k + 1][s]);
-                y1 = fmaf(cval(buf, s, k + 1), h[s], y1);
-            }
-            s_y[w][gi * (G / 2) + k / 2][cs] = make_float2(y0, y1);
-        }
-    };
-
-    // One chunk: stage, scan, epilogue.  (cu, cdl, cz) hold this chunk's
-    // runs; (pu, pdl, pz) receive the prefetch of chunk ck + RING - 1.
-    auto chunk = [&](int ck, uint32_t (&cu)[WPT], uint32_t (&cdl)[WPT], uint32_t (&cz)[WPT],
-                     uint32_t (&pu)[WPT], uint32_t (&pdl)[WPT], uint32_t (&pz)[WPT]) {
-        const int t0 = ck * TC;
-        // ---- stage (delta, delta*u) of this chunk in LDS -------------------
-        float uf[TPT];                           // u of this thread's run (FUSED: after the conv)
-        if constexpr (FUSED) {
-            static_assert(TPT >= 3, "a run holds the 3 inputs the next run's conv needs");
-            float xr[TPT];
-#pragma unroll
-            for (int j = 0; j < TPT; ++j) xr[j] = Elem<T>::get(cu, j);
-            // the 3 inputs before this run: from the previous segment's lane, or
-            // (first segment) the carry from the previous chunk
-            const int lane = tid & 63;
-            float xp[3];
-#pragma unroll
-            for (int k = 0; k < 3; ++k) {
-                const float v = __shfl(xr[TPT - 3 + k], lane - 1, 64);
-                xp[k] = seg > 0 ? v : carry[k];
-            }
-#pragma unroll
-            for (int k = 0; k < 3; ++k) carry[k] = __shfl(xr[TPT - 3 + k], lane | (SEGS - 1), 64);
-#pragma unroll
-            for (int j = 0; j < TPT; ++j) {
-                float a = cbias;
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const int src = j - 3 + k;   // compile-time after unrolling
-                    a = fmaf(w4[k], src < 0 ? xp[src + 3] : xr[src < 0 ? 0 : src], a);
+                    for (int i = 0; i < BCW; ++i) {
+                        bw[s][i] = x.w[i];
+                        cw[s][i] = y.w[i];
+                    }
+                } else {
+                    const int valid = sval[s] ? L - t : 0;
+                    load_run<T, G>(brow[s] + t, valid, false, bw[s]);
+                    load_run<T, G>(crow[s] + t, valid, false, cw[s]);
                 }
-                uf[j] = silu(a);
             }
-#pragma unroll
-            for (int j = 0; j < TPT; j += 2) {
-                const float d0v = t0 + toff + j < L ? softplus_f(Elem<T>::get(cdl, j) + dbias) : 0.f;
-                const float d1v = t0 + toff + j + 1 < L ? softplus_f(Elem<T>::get(cdl, j + 1) + dbias) : 0.f;
-                s_dd[(toff + j) / 2][cr] = make_float4(d0v, d0v * uf[j], d1v, d1v * uf[j + 1]);
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < TPT; ++j) uf[j] = Elem<T>::get(cu, j);
-#pragma unroll
-            for (int j = 0; j < TPT; j += 2) {
-                const float e0 = Elem<T>::get(cdl, j), e1 = Elem<T>::get(cdl, j + 1);
-                s_dd[(toff + j) / 2][cr] = make_float4(e0, e0 * uf[j], e1, e1 * uf[j + 1]);
-            }
-        }
-        if (ALIGNED || ck + RING - 1 < nchunks) load_chunk(ck + RING - 1, pu, pdl, pz);
-        __syncthreads();
+        };
 
-        // ---- sequential scan: NGRP groups of G tokens, NS states per lane ---
+        uint32_t bw[2][NS][BCW], cw[2][NS][BCW];
+        float4 ddr[2][G / 2];
+
+        // C of state s at token k of the group in buffer `buf`; 0 for a state
+        // past N (FULLN: every state of every wave is below N).
+        auto cval = [&](int buf, int s, int k) -> float {
+            const float c = Elem<T>::get(cw[buf][s], k);
+            if constexpr (ALIGNED && !FULLN) return sval[s] ? c : 0.f;
+            return c;
+        };
+        // One group of G tokens in buffer `buf`, all NS states.  The decay
+        // factors and input terms of the whole group are formed first (they do
+        // not depend on h), so each exp has independent work behind it; then the
+        // recurrence runs token by token.
+        auto group = [&](int buf, int gi, int par) {
+            float dA[G][NS], bu[G][NS];
+#pragma unroll
+            for (int k = 0; k < G; k += 2) {
+                const float4 q = ddr[buf][k / 2];
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                    dA[k][s] = fast_exp2(q.x * a2[s]);
+                    dA[k + 1][s] = fast_exp2(q.z * a2[s]);
+                    bu[k][s] = q.y * Elem<T>::get(bw[buf][s], k);
+                    bu[k + 1][s] = q.w * Elem<T>::get(bw[buf][s], k + 1);
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < G; k += 2) {
+                float y0 = 0.f, y1 = 0.f;
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                    h[s] = fmaf(dA[k][s], h[s], bu[k][s]);
+                    y0 = fmaf(cval(buf, s, k), h[s], y0);
+                }
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                    h[s] = fmaf(dA[k + 1][s], h[s], bu[k + 1][s]);
+                    y1 = fmaf(cval(buf, s, k + 1), h[s], y1);
+                }
+                s_y[par][w][gi * (G / 2) + k / 2][cs] = make_float2(y0, y1);
+            }
+        };
+
         // Scalar and LDS loads share one wait counter and scalar loads
         // complete out of order, so any wait on it covers every load in
         // flight.  Hence: issue group gi+1's loads at the start of group gi,
         // compute group gi with no wait inside, and wait once at its end.
+        load_bc(0, bw[0], cw[0]);
+        for (int ck = 0; ck < nit; ++ck) {
+            const int t0 = ck * TC;
+            const int par = ck & 1;
+            __syncthreads();                       // chunk ck staged; its s_y buffer free
 #pragma unroll
-        for (int k = 0; k < G / 2; ++k) ddr[0][k] = s_dd[k][cs];
-        lgkm_wait_all();
-#pragma unroll
-        for (int gi = 0; gi < NGRP; ++gi) {
-            const int cur = gi & 1, nxt = cur ^ 1;
-            if (gi + 1 < NGRP) {
-                load_bc(t0 + (gi + 1) * G, bw[nxt], cw[nxt]);
-#pragma unroll
-                for (int k = 0; k < G / 2; ++k) ddr[nxt][k] = s_dd[(gi + 1) * (G / 2) + k][cs];
-            } else if (ALIGNED || ck + 1 < nchunks) {
-                load_bc(t0 + TC, bw[nxt], cw[nxt]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            group(cur, gi);
+            for (int k = 0; k < G / 2; ++k) ddr[0][k] = s_dd[par][k][cs];
             lgkm_wait_all();
-        }
-        __syncthreads();
-
-        // ---- epilogue: combine waves, skip term, gate, store -----------------
-        float out[TPT];
 #pragma unroll
-        for (int j = 0; j < TPT; j += 2) {
-            float2 acc = s_y[0][(toff + j) / 2][cr];
+            for (int gi = 0; gi < NGRP; ++gi) {
+                const int cur = gi & 1, nxt = cur ^ 1;
+                if (gi + 1 < NGRP) {
+                    load_bc(t0 + (gi + 1) * G, bw[nxt], cw[nxt]);
 #pragma unroll
-            for (int q = 1; q < NW; ++q) {
-                const float2 v = s_y[q][(toff + j) / 2][cr];
-                acc.x += v.x;
-                acc.y += v.y;
+                    for (int k = 0; k < G / 2; ++k) {
+                        ddr[nxt][k] = s_dd[par][(gi + 1) * (G / 2) + k][cs];
+                    }
+                } else {
+                    load_bc(t0 + TC, bw[nxt], cw[nxt]);
+                }
+                // The two scan waves of a SIMD (w and w + 4) take turns at the
+                // higher issue priority, group by group, so neither falls behind
+                // the other and idles at the next barrier.
+                if (((gi & 1) ^ (w >> 2)) & 1) __builtin_amdgcn_s_setprio(1);
+                else __builtin_amdgcn_s_setprio(0);
+                __builtin_amdgcn_sched_barrier(0);
+                group(cur, gi, par);
+                lgkm_wait_all();
             }
-            float o0 = fmaf(dskip, uf[j], acc.x);
-            float o1 = fmaf(dskip, uf[j + 1], acc.y);
-            if (z_in) {
-                o0 *= silu(Elem<T>::get(cz, j));
-                o1 *= silu(Elem<T>::get(cz, j + 1));
-            }
-            out[j] = o0;
-            out[j + 1] = o1;
         }
-        if constexpr (ALIGNED) {
-            uint32_t wy[WPT];
-            pack_words<T, TPT>(out, wy);
-            buf_store<WPT, kStream>(rs_y, run_off(t0 + toff), wy);
-        } else {
-            if (rval) store_run<T, TPT>(y_row + t0 + toff, L - t0 - toff, false, out);
-        }
-        // No barrier here: the epilogue reads only s_y, which the next chunk
-        // rewrites after its first barrier; the next staging step writes only
-        // s_dd, whose last readers finished before the barrier above.
-    };
+        __syncthreads();                           // last chunk's partials complete
 
+        if (hT_out && sval_d) {
 #pragma unroll
-    for (int r = 0; r < RING - 1; ++r)
-        if (ALIGNED || r < nchunks) load_chunk(r, ru[r], rdl[r], rz[r]);
-    load_bc(0, bw[0], cw[0]);
-    // ALIGNED: the chunk count is rounded up to a multiple of RING and every
-    // load / store is issued unconditionally (past the end they read zero or
-    // are dropped; a zero step leaves h exactly unchanged).  Straight-line
-    // code lets the compiler keep RING-1 chunks of loads in flight; a branch
-    // around a load would make its wait counting fall back to the worst path.
-    for (int ck0 = 0; ck0 < nchunks; ck0 += RING) {
+            for (int s = 0; s < NS; ++s) {
+                const int n = w * NS + s;
+                if (n < N) hT_out[(b * dim + d0 + cs) * N + n] = h[s];
+            }
+        }
+    } else {
+        // ================= row role: lane = row cr, row wave = tokens [toff, toff + TPT) =================
+        const int cr = tid & 63;
+        const int seg = wave - NW;
+        const int toff = seg * TPT;
+        const bool rval = cr < nrows;
+        const float dskip = (rval && D_in) ? D_in[d0 + cr] : 0.f;
+        // Front end (FUSED): this row's conv taps, right-aligned in a 4-tap
+        // window (w4[3] multiplies the current token); the 3 inputs before
+        // token 0 (`carry`, the conv history); the biases.
+        float w4[4] = {0.f, 0.f, 0.f, 0.f}, carry[3] = {0.f, 0.f, 0.f}, cbias = 0.f, dbias = 0.f;
+        if constexpr (FUSED) {
+            const int64_t dr = d0 + (rval ? cr : 0);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {                      // tap k of the window is conv_w[k - (4 - K)]
+                const int i = k - (4 - fe.K);
+                w4[k] = i >= 0 ? fe.conv_w[dr * fe.K + i] : 0.f;
+            }
+            cbias = fe.conv_b ? fe.conv_b[dr] : 0.f;
+            dbias = fe.delta_bias ? fe.delta_bias[dr] : 0.f;
+            if (fe.conv_init) {
+                const T* ci = static_cast<const T*>(fe.conv_init) + (b * dim + dr) * (fe.K - 1);
+#pragma unroll
+                for (int k = 0; k < 3; ++k) {                  // carry[k] is the input 3 - k tokens back
+                    const int i = k - (4 - fe.K);
+                    carry[k] = i >= 0 ? Elem<T>::load1(ci + i) : 0.f;
+                }
+            }
+        }
+        const int64_t blk0 = (b * dim + d0) * (int64_t)L;        // first element of this block's rows
+        const uint32_t blk_bytes = ALIGNED ? (uint32_t)nrows * (uint32_t)L * (uint32_t)sizeof(T) : 0u;
+        const rsrc_t rs_u = make_rsrc(u_in + blk0, blk_bytes);
+        const rsrc_t rs_dl = make_rsrc(dl_in + blk0, blk_bytes);
+        const rsrc_t rs_z = make_rsrc(z_in ? z_in + blk0 : u_in + blk0, z_in ? blk_bytes : 0u);
+        const rsrc_t rs_y = make_rsrc(y_out + blk0, blk_bytes);
+        auto run_off = [&](int t) -> uint32_t {   // byte offset of this thread's run at token t
+            return (uint32_t)t < (uint32_t)L ? ((uint32_t)cr * (uint32_t)L + (uint32_t)t) * (uint32_t)sizeof(T)
+                                             : kOutOfRange;
+        };
+        const int64_t rrow = (int64_t)(rval ? cr : 0) * L;
+        const T* u_row = u_in + blk0 + rrow;
+        const T* dl_row = dl_in + blk0 + rrow;
+        const T* z_row = z_in ? z_in + blk0 + rrow : nullptr;
+        T* y_row = y_out + blk0 + rrow;
+
+        // FUSED: rx holds the 4 inputs before each run (the conv window).
+        uint32_t ru[RING][WPT], rdl[RING][WPT], rz[RING][WPT], rx[RING][PW];
 #pragma unroll
         for (int r = 0; r < RING; ++r) {
-            const int pr = (r + RING - 1) % RING;
-            if (ALIGNED || ck0 + r < nchunks) chunk(ck0 + r, ru[r], rdl[r], rz[r], ru[pr], rdl[pr], rz[pr]);
-        }
-    }
-
-    if (hT_out && sval_d) {
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            const int n = w * NS + s;
-            if (n < N) hT_out[(b * dim + d0 + cs) * N + n] = h[s];
+            for (int i = 0; i < WPT; ++i) rz[r][i] = 0u;
+#pragma unroll
+            for (int i = 0; i < PW; ++i) rx[r][i] = 0u;
         }
+        auto load_chunk = [&](int ck, uint32_t (&wu)[WPT], uint32_t (&wdl)[WPT], uint32_t (&wz)[WPT],
+                              uint32_t (&wx)[PW]) {
+            const int t = ck * TC + toff;
+            if constexpr (ALIGNED) {
+                // Unconditional: without z, rs_z is empty and the load returns 0.
+                const uint32_t off = run_off(t);
+                buf_load<WPT>(rs_u, off, wu);
+                buf_load<WPT>(rs_dl, off, wdl);
+                buf_load<WPT>(rs_z, off, wz);
+                if constexpr (FUSED) buf_load<PW>(rs_u, run_off(t - 4), wx);   // t = 0: out of range, 0
+            } else {
+                const int valid = rval ? (L - t) : 0;
+                load_run<T, TPT>(u_row + t, valid, false, wu);
+                load_run<T, TPT>(dl_row + t, valid, false, wdl);
+                if (z_row) load_run<T, TPT>(z_row + t, valid, false, wz);
+                if constexpr (FUSED) {
+                    const int vp = (rval && t >= 4) ? L - (t - 4) : 0;
+                    load_run<T, 4>(u_row + (t >= 4 ? t - 4 : 0), vp, false, wx);
+                }
+            }
+        };
+
+        // Stage chunk ck: (delta, delta*u) to LDS; keep u (FUSED: after the
+        // conv) for the epilogue.
+        auto stage = [&](int ck, const uint32_t (&cu)[WPT], const uint32_t (&cdl)[WPT], const uint32_t (&cx)[PW],
+                         float (&uk)[TPT]) {
+            const int t0 = ck * TC;
+            const int par = ck & 1;
+            if constexpr (FUSED) {
+                float xr[TPT];
+#pragma unroll
+                for (int j = 0; j < TPT; ++j) xr[j] = Elem<T>::get(cu, j);
+                // the 3 inputs before this run: loaded with it, or (token 0) the history
+                const bool first = t0 + toff == 0;
+                float xp[3];
+#pragma unroll
+                for (int k = 0; k < 3; ++k) xp[k] = first ? carry[k] : Elem<T>::get(cx, k + 1);
+#pragma unroll
+                for (int j = 0; j < TPT; ++j) {
+                    float a = cbias;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const int src = j - 3 + k;   // compile-time after unrolling
+                        a = fmaf(w4[k], src < 0 ? xp[src + 3] : xr[src < 0 ? 0 : src], a);
+                    }
+                    uk[j] = silu(a);
+                }
+#pragma unroll
+                for (int j = 0; j < TPT; j += 2) {
+                    const float d0v = t0 + toff + j < L ? softplus_f(Elem<T>::get(cdl, j) + dbias) : 0.f;
+                    const float d1v = t0 + toff + j + 1 < L ? softplus_f(Elem<T>::get(cdl, j + 1) + dbias) : 0.f;
+                    s_dd[par][(toff + j) / 2][cr] = make_float4(d0v, d0v * uk[j], d1v, d1v * uk[j + 1]);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < TPT; ++j) uk[j] = Elem<T>::get(cu, j);
+#pragma unroll
+                for (int j = 0; j < TPT; j += 2) {
+                    const float e0 = Elem<T>::get(cdl, j), e1 = Elem<T>::get(cdl, j + 1);
+                    s_dd[par][(toff + j) / 2][cr] = make_float4(e0, e0 * uk[j], e1, e1 * uk[j + 1]);
+                }
+            }
+        };
+
+        // Epilogue of chunk ck: combine the scan waves' partials, skip term,
+        // gate, store.  Chunk -1 (the first iteration) reads an unused buffer
+        // and stores nothing (its offsets are out of range).
+        auto epilogue = [&](int ck, const uint32_t (&cz)[WPT], const float (&uk)[TPT]) {
+            const int t0 = ck * TC;
+            const int par = ck & 1;
+            float out[TPT];
+#pragma unroll
+            for (int j = 0; j < TPT; j += 2) {
+                const int pair = (toff + j) / 2;
+                float2 acc = s_y[par][0][pair][cr];
+#pragma unroll
+                for (int q = 1; q < NW; ++q) {
+                    const float2 v = s_y[par][q][pair][cr];
+                    acc.x += v.x;
+                    acc.y += v.y;
+                }
+                float o0 = fmaf(dskip, uk[j], acc.x);
+                float o1 = fmaf(dskip, uk[j + 1], acc.y);
+                if (z_in) {
+                    o0 *= silu(Elem<T>::get(cz, j));
+                    o1 *= silu(Elem<T>::get(cz, j + 1));
+                }
+                out[j] = o0;
+                out[j + 1] = o1;
+            }
+            if constexpr (ALIGNED) {
+                uint32_t wy[WPT];
+                pack_words<T, TPT>(out, wy);
+                buf_store<WPT, kCached>(rs_y, run_off(t0 + toff), wy);
+            } else {
+                const int t = t0 + toff;
+                if (rval && t >= 0) store_run<T, TPT>(y_row + t, L - t, false, out);
+            }
+        };
+
+        float uk[2][TPT];                          // kept u of the chunks of each parity
+#pragma unroll
+        for (int j = 0; j < TPT; ++j) uk[0][j] = uk[1][j] = 0.f;
+#pragma unroll
+        for (int r = 0; r < RING - 1; ++r) load_chunk(r, ru[r], rdl[r], rz[r], rx[r]);
+        stage(0, ru[0], rdl[0], rx[0], uk[0]);
+        // Iteration ck: the scan waves scan chunk ck; here the epilogue of
+        // chunk ck-1, the staging of chunk ck+1 and the loads of chunk
+        // ck+RING-1 (into the slot the epilogue just released).
+        for (int ck0 = 0; ck0 < nit; ck0 += RING) {
+#pragma unroll
+            for (int r = 0; r < RING; ++r) {
+                const int ck = ck0 + r;
+                const int sp = (r + RING - 1) % RING, sn = (r + 1) % RING;
+                __syncthreads();
+                epilogue(ck - 1, rz[sp], uk[(r + 1) & 1]);
+                stage(ck + 1, ru[sn], rdl[sn], rx[sn], uk[(r + 1) & 1]);
+                load_chunk(ck + RING - 1, ru[sp], rdl[sp], rz[sp], rx[sp]);
+            }
+        }
+        __syncthreads();
+        epilogue(nit - 1, rz[RING - 1], uk[1]);
     }
 }
 
-template <typename T, int NW, int NS, int TC>
+template <typename T, int NS, int TC>
 hipError_t launch_cfg(const S6Params& p, const S6FrontEnd* fe, hipStream_t stream) {
-    constexpr int RING = 8;
     const int64_t blocks = ((p.dim + 63) / 64) * p.batch;
     // The aligned path addresses a block's rows through 32-bit buffer
-    // offsets, and reads B / C in whole 16-byte groups.
-    const bool aligned = (p.L % 8 == 0) && int64_t(64) * p.L * int64_t(sizeof(T)) < (int64_t(1) << 31);
-    const bool fulln = p.N == NW * NS;
-    auto kern = fe ? (aligned ? (fulln ? s6_scan_kernel<T, NW, NS, TC, true, true, true, RING>
-                                       : s6_scan_kernel<T, NW, NS, TC, true, false, true, RING>)
-                              : s6_scan_kernel<T, NW, NS, TC, false, false, true, RING>)
-                   : (aligned ? (fulln ? s6_scan_kernel<T, NW, NS, TC, true, true, false, RING>
-                                       : s6_scan_kernel<T, NW, NS, TC, true, false, false, RING>)
-                              : s6_scan_kernel<T, NW, NS, TC, false, false, false, RING>);
+    // offsets, and reads B / C in whole 32-byte groups.
+    const bool aligned = (p.L % (32 / int(sizeof(T))) == 0) && int64_t(64) * p.L * int64_t(sizeof(T)) < (int64_t(1) << 31);
+    const bool fulln = p.N == kScanWaves * NS;
+    auto kern = fe ? (aligned ? (fulln ? s6_scan_kernel<T, NS, TC, true, true, true, kRing>
+                                       : s6_scan_kernel<T, NS, TC, true, false, true, kRing>)
+                              : s6_scan_kernel<T, NS, TC, false, false, true, kRing>)
+                   : (aligned ? (fulln ? s6_scan_kernel<T, NS, TC, true, true, false, kRing>
+                                       : s6_scan_kernel<T, NS, TC, true, false, false, kRing>)
+                              : s6_scan_kernel<T, NS, TC, false, false, false, kRing>);
     const S6FrontEnd none{};
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(NW * 64), 0, stream, static_cast<const T*>(p.u),
-                       static_cast<const T*>(p.delta), static_cast<const T*>(p.Bm), static_cast<const T*>(p.Cm),
-                       static_cast<const T*>(p.z), p.A, p.Dskip, p.h0, static_cast<T*>(p.y), p.h_final, p.dim,
-                       p.L, p.N, fe ? *fe : none);
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3((kScanWaves + kRowWaves) * 64), 0, stream,
+                       static_cast<const T*>(p.u), static_cast<const T*>(p.delta), static_cast<const T*>(p.Bm),
+                       static_cast<const T*>(p.Cm), static_cast<const T*>(p.z), p.A, p.Dskip, p.h0,
+                       static_cast<T*>(p.y), p.h_final, p.dim, p.L, p.N, fe ? *fe : none);
     return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_t(const S6Params& p, const S6FrontEnd* fe, hipStream_t stream) {
-    // 8 waves per 64 channels; NS = ceil(N / 8) states per lane.
-    if (p.N <= 8) return launch_cfg<T, 8, 1, 32>(p, fe, stream);
-    if (p.N <= 16) return launch_cfg<T, 8, 2, 32>(p, fe, stream);
-    if (p.N <= 32) return launch_cfg<T, 8, 4, 32>(p, fe, stream);
-    return launch_cfg<T, 8, 8, 32>(p, fe, stream);
+    // 8 scan waves per 64 channels; NS = ceil(N / 8) states per lane.
+    if (p.N <= 8) return launch_cfg<T, 1, 32>(p, fe, stream);
+    if (p.N <= 16) return launch_cfg<T, 2, 32>(p, fe, stream);
+    if (p.N <= 32) return launch_cfg<T, 4, 32>(p, fe, stream);
+    return launch_cfg<T, 8, 32>(p, fe, stream);
 }
 
 __global__ void copy_or_zero_kernel(float* dst, const float* src, int64_t n) {

@@ -58,6 +58,12 @@ CASES = [
     (1, 130, 1000, 16, "bf16", True, False, True),
     (1, 64, 257, 64, "bf16", False, True, True),
     (2, 192, 333, 12, "bf16", True, True, False),
+    # bf16 lengths that are whole 16-token groups (range-checked group loads)
+    (2, 64, 32, 8, "bf16", True, True, True),
+    (2, 100, 208, 16, "bf16", True, True, True),
+    (1, 130, 1024, 16, "bf16", True, False, True),
+    (2, 192, 336, 12, "bf16", True, True, False),
+    (1, 64, 272, 64, "bf16", False, True, True),
 ]
 
 

@@ -56,6 +56,10 @@ CASES = [
     (2, 100, 200, 16, 4, "bf16", True, True, True, True),
     (1, 130, 1000, 16, 4, "bf16", True, False, True, False),
     (2, 192, 333, 12, 3, "bf16", True, True, False, True),
+    # bf16 lengths that are whole 16-token groups (range-checked group loads)
+    (2, 100, 208, 16, 4, "bf16", True, True, True, True),
+    (1, 64, 528, 64, 4, "bf16", False, True, True, True),
+    (2, 192, 336, 12, 3, "bf16", True, True, False, True),
 ]
 
 
