@@ -207,7 +207,8 @@ def bench_s6fused(args):
     return {"workload": f"{wl.name}: batch {s['batch']}, d_inner {s['d_inner']}, seqlen {s['seqlen']}, "
                         f"d_state {s['d_state']}, d_conv {s['d_conv']}, bf16",
             "us": ms * 1e3, "GBs": nb / (ms * 1e-3) / 1e9, "hbm_frac": nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "tokens_ch_per_s": tok / (ms * 1e-3), "algorithmic_bytes": nb}
+            "tokens_ch_per_s": tok / (ms * 1e-3), "algorithmic_bytes": nb,
+            "traffic_bytes_per_launch": profiled_traffic("s6_scan_fused_mamba1p4b_bf16.md")}
 
 
 def bench_s6bwd(args):
@@ -241,7 +242,9 @@ def bench_s6bwd(args):
     return {"workload": f"{wl.name} backward: batch {B}, d_inner {D}, seqlen {L}, d_state {N}, bf16, "
                         "gate, skip, h0 and final-state gradient",
             "us": ms * 1e3, "tokens_ch_per_s": B * D * L / (ms * 1e-3), "bytes_moved_estimate": nb,
-            "GBs_estimate": nb / (ms * 1e-3) / 1e9, "workspace_bytes": ws.numel()}
+            "GBs_estimate": nb / (ms * 1e-3) / 1e9, "workspace_bytes": ws.numel(),
+            "traffic_bytes_per_call": {"s6_scan_bwd_kernel": profiled_traffic("s6_scan_bwd_mamba1p4b_bf16.md"),
+                                       "s6_bwd_reduce_bc_kernel": profiled_traffic("s6_bwd_reduce_bc_mamba1p4b_bf16.md")}}
 
 
 def parity_sample(inp, y, hf, rows=32, seed=0):

@@ -20,11 +20,13 @@
 //     [w*NS, (w+1)*NS).  B and C are shared by all channels, so within a
 //     wave they are uniform: they are fetched with scalar loads into SGPRs
 //     (bf16 unpacked on the scalar unit) and used as free scalar operands.
-//   * 4 row waves: lane = row (channel), row wave = a TPT-token segment of
-//     the chunk.  They stream u, delta, z through a register ring (the loads
-//     of the next RING-1 chunks in flight), stage (delta, delta*u) in LDS for
-//     the scan, and run the epilogue: the sum of the 8 per-wave partial
-//     outputs sum_n C*h, the D*u term, the silu(z) gate and the y store.
+//   * 4 row waves: thread = (row, TPT-token segment of the chunk), a row's
+//     segments on consecutive lanes, so each load or store instruction moves
+//     whole 64-byte row runs.  They stream u, delta, z through a register
+//     ring (the loads of the next RING-1 chunks in flight), stage
+//     (delta, delta*u) in LDS for the scan, and run the epilogue: the sum of
+//     the 8 per-wave partial outputs sum_n C*h, the D*u term, the silu(z)
+//     gate and the y store (streaming cache policy).
 //   Time is processed in chunks of TC tokens, the LDS buffers are doubled by
 //   chunk parity, and one barrier per chunk hands work between the roles:
 //   while the scan waves scan chunk k, the row waves finish chunk k-1 and
@@ -67,23 +69,25 @@ __global__ __launch_bounds__((kScanWaves + kRowWaves) * 64) void s6_scan_kernel(
     // Pointers are separate __restrict__ arguments so the compiler may fetch the
     // wave-uniform B / C words with scalar loads (it must know no store aliases them).
     constexpr int NW = kScanWaves;
-    constexpr int SEGS = kRowWaves;                // row threads per row (64 rows): one per row wave
+    constexpr int SEGS = kRowWaves;                // row threads per row (64 rows x SEGS = the row waves)
     constexpr int TPT = TC / SEGS;                 // tokens per row thread
     constexpr int WPT = TPT * sizeof(T) / 4;       // 32-bit words per thread run
-    constexpr int PW = 4 * sizeof(T) / 4;          // words of the 4 tokens before a run (FUSED)
     constexpr int G = 32 / sizeof(T);              // tokens per scan group: 32 bytes of a B / C row
     constexpr int NGRP = TC / G;
     constexpr int BCW = 8;                         // words per B / C row per group
     constexpr int PR = TC / 2;                     // token pairs per chunk
-    static_assert(TPT % 2 == 0 && (WPT == 2 || WPT == 4 || WPT == 8), "row runs are 8-, 16- or 32-byte vectors");
+    constexpr int QR = TC / 4;                     // token quads per chunk
+    static_assert(TPT % 4 == 0 && (WPT == 2 || WPT == 4 || WPT == 8), "row runs are 8-, 16- or 32-byte vectors");
     static_assert(TC % G == 0 && NGRP % 2 == 0, "whole scan groups per chunk, even count");
     static_assert(RING >= 3 && RING % 2 == 0, "ring: stage, epilogue and reload use distinct slots");
 
-    // Double-buffered by chunk parity.  Every access, from either role, has
-    // one token pair per instruction and the 64 channels on consecutive
-    // lanes, so the plain layout is free of bank conflicts.
+    // Double-buffered by chunk parity, 16 bytes per (channel, token pair or
+    // quad).  The scan waves access one pair / quad per instruction with the
+    // 64 channels on consecutive lanes; each quarter-wave of a row wave covers
+    // 16 channels of one pair / quad.  Both are free of bank conflicts with
+    // the plain layout, and the scan side needs no address arithmetic.
     __shared__ float4 s_dd[2][PR][64];             // (delta_t, (delta*u)_t, delta_t+1, (delta*u)_t+1)
-    __shared__ float2 s_y[2][NW][PR][64];          // per-scan-wave partial outputs, token pairs
+    __shared__ float4 s_y[2][NW][QR][64];          // per-scan-wave partial outputs, token quads
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -173,19 +177,16 @@ __global__ __launch_bounds__((kScanWaves + kRowWaves) * 64) void s6_scan_kernel(
                 }
             }
 #pragma unroll
-            for (int k = 0; k < G; k += 2) {
-                float y0 = 0.f, y1 = 0.f;
+            for (int k = 0; k < G; k += 4) {
+                float yv[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int s = 0; s < NS; ++s) {
-                    h[s] = fmaf(dA[k][s], h[s], bu[k][s]);
-                    y0 = fmaf(cval(buf, s, k), h[s], y0);
-                }
+                for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-                for (int s = 0; s < NS; ++s) {
-                    h[s] = fmaf(dA[k + 1][s], h[s], bu[k + 1][s]);
-                    y1 = fmaf(cval(buf, s, k + 1), h[s], y1);
-                }
-                s_y[par][w][gi * (G / 2) + k / 2][cs] = make_float2(y0, y1);
+                    for (int s = 0; s < NS; ++s) {
+                        h[s] = fmaf(dA[k + kk][s], h[s], bu[k + kk][s]);
+                        yv[kk] = fmaf(cval(buf, s, k + kk), h[s], yv[kk]);
+                    }
+                s_y[par][w][gi * (G / 4) + k / 4][cs] = make_float4(yv[0], yv[1], yv[2], yv[3]);
             }
         };
 
@@ -233,15 +234,20 @@ __global__ __launch_bounds__((kScanWaves + kRowWaves) * 64) void s6_scan_kernel(
             }
         }
     } else {
-        // ================= row role: lane = row cr, row wave = tokens [toff, toff + TPT) =================
-        const int cr = tid & 63;
-        const int seg = wave - NW;
+        // ================= row role: thread -> (row cr, tokens [toff, toff + TPT)) =================
+        // Row wave v owns rows 16v .. 16v+15; lane l takes row 16v + (l & 15)
+        // and segment l >> 4, so one load or store instruction moves 16 rows
+        // x TC contiguous tokens.
+        static_assert(SEGS * 16 == 64, "a row wave holds 16 rows x SEGS segments");
+        const int rt = tid - NW * 64;
+        const int cr = 16 * (rt >> 6) + (rt & 15);
+        const int seg = (rt >> 4) & (SEGS - 1);
         const int toff = seg * TPT;
         const bool rval = cr < nrows;
         const float dskip = (rval && D_in) ? D_in[d0 + cr] : 0.f;
         // Front end (FUSED): this row's conv taps, right-aligned in a 4-tap
-        // window (w4[3] multiplies the current token); the 3 inputs before
-        // token 0 (`carry`, the conv history); the biases.
+        // window (w4[3] multiplies the current token); the 3 inputs before the
+        // current run (`carry`, used by the row's first segment); the biases.
         float w4[4] = {0.f, 0.f, 0.f, 0.f}, carry[3] = {0.f, 0.f, 0.f}, cbias = 0.f, dbias = 0.f;
         if constexpr (FUSED) {
             const int64_t dr = d0 + (rval ? cr : 0);
@@ -277,17 +283,12 @@ __global__ __launch_bounds__((kScanWaves + kRowWaves) * 64) void s6_scan_kernel(
         const T* z_row = z_in ? z_in + blk0 + rrow : nullptr;
         T* y_row = y_out + blk0 + rrow;
 
-        // FUSED: rx holds the 4 inputs before each run (the conv window).
-        uint32_t ru[RING][WPT], rdl[RING][WPT], rz[RING][WPT], rx[RING][PW];
+        uint32_t ru[RING][WPT], rdl[RING][WPT], rz[RING][WPT];
 #pragma unroll
-        for (int r = 0; r < RING; ++r) {
+        for (int r = 0; r < RING; ++r)
 #pragma unroll
             for (int i = 0; i < WPT; ++i) rz[r][i] = 0u;
-#pragma unroll
-            for (int i = 0; i < PW; ++i) rx[r][i] = 0u;
-        }
-        auto load_chunk = [&](int ck, uint32_t (&wu)[WPT], uint32_t (&wdl)[WPT], uint32_t (&wz)[WPT],
-                              uint32_t (&wx)[PW]) {
+        auto load_chunk = [&](int ck, uint32_t (&wu)[WPT], uint32_t (&wdl)[WPT], uint32_t (&wz)[WPT]) {
             const int t = ck * TC + toff;
             if constexpr (ALIGNED) {
                 // Unconditional: without z, rs_z is empty and the load returns 0.
@@ -295,34 +296,35 @@ __global__ __launch_bounds__((kScanWaves + kRowWaves) * 64) void s6_scan_kernel(
                 buf_load<WPT>(rs_u, off, wu);
                 buf_load<WPT>(rs_dl, off, wdl);
                 buf_load<WPT>(rs_z, off, wz);
-                if constexpr (FUSED) buf_load<PW>(rs_u, run_off(t - 4), wx);   // t = 0: out of range, 0
             } else {
                 const int valid = rval ? (L - t) : 0;
                 load_run<T, TPT>(u_row + t, valid, false, wu);
                 load_run<T, TPT>(dl_row + t, valid, false, wdl);
                 if (z_row) load_run<T, TPT>(z_row + t, valid, false, wz);
-                if constexpr (FUSED) {
-                    const int vp = (rval && t >= 4) ? L - (t - 4) : 0;
-                    load_run<T, 4>(u_row + (t >= 4 ? t - 4 : 0), vp, false, wx);
-                }
             }
         };
 
         // Stage chunk ck: (delta, delta*u) to LDS; keep u (FUSED: after the
         // conv) for the epilogue.
-        auto stage = [&](int ck, const uint32_t (&cu)[WPT], const uint32_t (&cdl)[WPT], const uint32_t (&cx)[PW],
-                         float (&uk)[TPT]) {
+        auto stage = [&](int ck, const uint32_t (&cu)[WPT], const uint32_t (&cdl)[WPT], float (&uk)[TPT]) {
             const int t0 = ck * TC;
             const int par = ck & 1;
             if constexpr (FUSED) {
+                static_assert(TPT >= 3, "a run holds the 3 inputs the next run's conv needs");
                 float xr[TPT];
 #pragma unroll
                 for (int j = 0; j < TPT; ++j) xr[j] = Elem<T>::get(cu, j);
-                // the 3 inputs before this run: loaded with it, or (token 0) the history
-                const bool first = t0 + toff == 0;
+                // the 3 inputs before this run: from the previous segment's lane, or
+                // (first segment) the carry from the previous chunk
+                const int lane = tid & 63;
                 float xp[3];
 #pragma unroll
-                for (int k = 0; k < 3; ++k) xp[k] = first ? carry[k] : Elem<T>::get(cx, k + 1);
+                for (int k = 0; k < 3; ++k) {
+                    const float v = __shfl(xr[TPT - 3 + k], lane - 16, 64);
+                    xp[k] = seg > 0 ? v : carry[k];
+                }
+#pragma unroll
+                for (int k = 0; k < 3; ++k) carry[k] = __shfl(xr[TPT - 3 + k], (lane & 15) + 16 * (SEGS - 1), 64);
 #pragma unroll
                 for (int j = 0; j < TPT; ++j) {
                     float a = cbias;
@@ -358,28 +360,29 @@ __global__ __launch_bounds__((kScanWaves + kRowWaves) * 64) void s6_scan_kernel(
             const int par = ck & 1;
             float out[TPT];
 #pragma unroll
-            for (int j = 0; j < TPT; j += 2) {
-                const int pair = (toff + j) / 2;
-                float2 acc = s_y[par][0][pair][cr];
+            for (int j = 0; j < TPT; j += 4) {
+                const int quad = (toff + j) / 4;
+                float4 acc = s_y[par][0][quad][cr];
 #pragma unroll
                 for (int q = 1; q < NW; ++q) {
-                    const float2 v = s_y[par][q][pair][cr];
+                    const float4 v = s_y[par][q][quad][cr];
                     acc.x += v.x;
                     acc.y += v.y;
+                    acc.z += v.z;
+                    acc.w += v.w;
                 }
-                float o0 = fmaf(dskip, uk[j], acc.x);
-                float o1 = fmaf(dskip, uk[j + 1], acc.y);
-                if (z_in) {
-                    o0 *= silu(Elem<T>::get(cz, j));
-                    o1 *= silu(Elem<T>::get(cz, j + 1));
+                const float a4[4] = {acc.x, acc.y, acc.z, acc.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float o = fmaf(dskip, uk[j + i], a4[i]);
+                    if (z_in) o *= silu(Elem<T>::get(cz, j + i));
+                    out[j + i] = o;
                 }
-                out[j] = o0;
-                out[j + 1] = o1;
             }
             if constexpr (ALIGNED) {
                 uint32_t wy[WPT];
                 pack_words<T, TPT>(out, wy);
-                buf_store<WPT, kCached>(rs_y, run_off(t0 + toff), wy);
+                buf_store<WPT, kStream>(rs_y, run_off(t0 + toff), wy);
             } else {
                 const int t = t0 + toff;
                 if (rval && t >= 0) store_run<T, TPT>(y_row + t, L - t, false, out);
@@ -390,8 +393,8 @@ __global__ __launch_bounds__((kScanWaves + kRowWaves) * 64) void s6_scan_kernel(
 #pragma unroll
         for (int j = 0; j < TPT; ++j) uk[0][j] = uk[1][j] = 0.f;
 #pragma unroll
-        for (int r = 0; r < RING - 1; ++r) load_chunk(r, ru[r], rdl[r], rz[r], rx[r]);
-        stage(0, ru[0], rdl[0], rx[0], uk[0]);
+        for (int r = 0; r < RING - 1; ++r) load_chunk(r, ru[r], rdl[r], rz[r]);
+        stage(0, ru[0], rdl[0], uk[0]);
         // Iteration ck: the scan waves scan chunk ck; here the epilogue of
         // chunk ck-1, the staging of chunk ck+1 and the loads of chunk
         // ck+RING-1 (into the slot the epilogue just released).
@@ -402,8 +405,8 @@ __global__ __launch_bounds__((kScanWaves + kRowWaves) * 64) void s6_scan_kernel(
                 const int sp = (r + RING - 1) % RING, sn = (r + 1) % RING;
                 __syncthreads();
                 epilogue(ck - 1, rz[sp], uk[(r + 1) & 1]);
-                stage(ck + 1, ru[sn], rdl[sn], rx[sn], uk[(r + 1) & 1]);
-                load_chunk(ck + RING - 1, ru[sp], rdl[sp], rz[sp], rx[sp]);
+                stage(ck + 1, ru[sn], rdl[sn], uk[(r + 1) & 1]);
+                load_chunk(ck + RING - 1, ru[sp], rdl[sp], rz[sp]);
             }
         }
         __syncthreads();
