@@ -58,6 +58,8 @@ def _bind(lib):
     L = ctypes.c_long
     lib.oracle_s6_scan.argtypes = [d] * 10 + [L] * 4 + [ctypes.c_int]
     lib.oracle_s6_scan.restype = ctypes.c_int
+    lib.oracle_s6_scan_zoh.argtypes = [d] * 10 + [L] * 4 + [ctypes.c_int]
+    lib.oracle_s6_scan_zoh.restype = ctypes.c_int
     lib.oracle_state_update.argtypes = [d] * 9 + [L] * 3 + [ctypes.c_int]
     lib.oracle_state_update.restype = ctypes.c_int
     lib.oracle_ssd.argtypes = [d] * 10 + [L] * 6 + [ctypes.c_int]
@@ -98,9 +100,11 @@ def _ptr(a):
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
 
 
-def s6_scan(u, delta, A, B, C, D=None, z=None, h0=None, nthreads=None, lib=None):
+def s6_scan(u, delta, A, B, C, D=None, z=None, h0=None, nthreads=None, lib=None, zoh=False):
     """Selective scan.  u, delta, z: [b, d, L]; A: [d, N]; B, C: [b, N, L];
-    D: [d]; h0: [b, d, N].  Returns (y [b, d, L], h_final [b, d, N]) in fp64."""
+    D: [d]; h0: [b, d, N].  Returns (y [b, d, L], h_final [b, d, N]) in fp64.
+    zoh: zero-order-hold input term (exp(delta A) - 1) / A * B instead of the
+    Euler delta * B (the Optimization Patterns page, section 7)."""
     u, delta, A, B, C = map(_f64, (u, delta, A, B, C))
     D, z, h0 = _f64(D), _f64(z), _f64(h0)
     bsz, dim, L = u.shape
@@ -113,9 +117,10 @@ def s6_scan(u, delta, A, B, C, D=None, z=None, h0=None, nthreads=None, lib=None)
     y = np.empty((bsz, dim, L), np.float64)
     hT = np.empty((bsz, dim, N), np.float64)
     lib = lib or load()
-    rc = lib.oracle_s6_scan(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
-                            _ptr(z), _ptr(h0), _ptr(y), _ptr(hT), bsz, dim, L, N,
-                            nthreads or default_threads())
+    fn = lib.oracle_s6_scan_zoh if zoh else lib.oracle_s6_scan
+    rc = fn(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+            _ptr(z), _ptr(h0), _ptr(y), _ptr(hT), bsz, dim, L, N,
+            nthreads or default_threads())
     if rc != 0:
         raise RuntimeError("oracle_s6_scan failed")
     return y, hT

@@ -31,6 +31,10 @@
  *   Reading adopted where the pages differ: the input term is the Euler form
  *   delta*B*x of the architecture page (the Optimization Patterns page's
  *   section 7 prints the zero-order-hold form (A_bar - I) A^-1 B instead).
+ *   The zero-order-hold form is offered as a variant (oracle_s6_scan_zoh):
+ *   with a diagonal A it is, per state, B_bar = (exp(delta*A) - 1) / A * B,
+ *   computed with expm1 (no cancellation for small delta*A) and taken as its
+ *   limit delta * B when A = 0.
  *
  * Per channel, in this order, for t = 0 .. L-1:
  *       d = delta[t]; x = u[t]; acc = 0
@@ -64,6 +68,7 @@ typedef struct {
     const double *A;            /* A[n] at A[n * s_a] (s_a = 0: scalar A) */
     long s_a;
     double dskip;
+    int zoh;                    /* input term: 0 Euler delta*B*x, 1 zero-order hold */
     double *y;                  /* y[t] at y[t * s_x] */
     const double *h0;           /* h0[n] at h0[n * s_h], may be NULL */
     double *hT;                 /* final state, h[n] at hT[n * s_h], may be NULL */
@@ -79,8 +84,11 @@ static void run_channel(const chan_t *c, long L, long N, double *h)
         const double x = c->u[t * c->s_x];
         double acc = 0.0;
         for (long n = 0; n < N; ++n) {
-            const double dA = exp(d * c->A[n * c->s_a]);
-            const double dBu = (d * x) * c->Bm[n * c->s_bn + t * c->s_bt];
+            const double a = c->A[n * c->s_a];
+            const double dA = exp(d * a);
+            /* Euler: delta*x*B.  ZOH: (exp(delta*a) - 1)/a * x*B, limit delta*x*B at a = 0. */
+            const double k = c->zoh ? (a != 0.0 ? expm1(d * a) / a : d) : d;
+            const double dBu = (k * x) * c->Bm[n * c->s_bn + t * c->s_bt];
             h[n] = dA * h[n] + dBu;
             acc += c->Cm[n * c->s_bn + t * c->s_bt] * h[n];
         }
@@ -112,6 +120,7 @@ typedef struct {
     long D;              /* S6: d_inner */
     long H, P, G;        /* SSD: heads, head dim, groups */
     long nchan;
+    int zoh;             /* S6: zero-order-hold input term */
 } prob_t;
 
 static void make_view(const prob_t *p, long ch, chan_t *c)
@@ -132,6 +141,7 @@ static void make_view(const prob_t *p, long ch, chan_t *c)
         c->A = p->A + d * p->N;
         c->s_a = 1;
         c->dskip = p->Dskip ? p->Dskip[d] : 0.0;
+        c->zoh = p->zoh;
         c->h0 = p->h0 ? p->h0 + (b * p->D + d) * p->N : NULL;
         c->hT = p->hT ? p->hT + (b * p->D + d) * p->N : NULL;
         c->s_h = 1;
@@ -155,6 +165,7 @@ static void make_view(const prob_t *p, long ch, chan_t *c)
         c->A = p->A + h;
         c->s_a = 0;
         c->dskip = p->Dskip ? p->Dskip[h] : 0.0;
+        c->zoh = 0;
         c->h0 = p->h0 ? p->h0 + ((b * p->H + h) * p->P + q) * p->N : NULL;
         c->hT = p->hT ? p->hT + ((b * p->H + h) * p->P + q) * p->N : NULL;
         c->s_h = 1;
@@ -217,11 +228,11 @@ static int run(const prob_t *p, int nthreads)
  * Nullable: Dskip (=> 0), z (=> no gate), h0 (=> zeros), hT (=> not written).
  * Return 0 on success, -1 on bad arguments or allocation failure.
  * ------------------------------------------------------------------------- */
-int oracle_s6_scan(const double *u, const double *delta, const double *A,
-                   const double *Bm, const double *Cm, const double *Dskip,
-                   const double *z, const double *h0, double *y, double *hT,
-                   long batch, long d_inner, long seqlen, long d_state,
-                   int nthreads)
+static int s6_common(const double *u, const double *delta, const double *A,
+                     const double *Bm, const double *Cm, const double *Dskip,
+                     const double *z, const double *h0, double *y, double *hT,
+                     long batch, long d_inner, long seqlen, long d_state,
+                     int zoh, int nthreads)
 {
     if (!u || !delta || !A || !Bm || !Cm || !y) return -1;
     if (batch < 0 || d_inner < 0 || seqlen < 0 || d_state < 1) return -1;
@@ -231,7 +242,29 @@ int oracle_s6_scan(const double *u, const double *delta, const double *A,
     p.z = z; p.h0 = h0; p.y = y; p.hT = hT;
     p.batch = batch; p.L = seqlen; p.N = d_state; p.D = d_inner;
     p.nchan = batch * d_inner;
+    p.zoh = zoh;
     return run(&p, nthreads);
+}
+
+int oracle_s6_scan(const double *u, const double *delta, const double *A,
+                   const double *Bm, const double *Cm, const double *Dskip,
+                   const double *z, const double *h0, double *y, double *hT,
+                   long batch, long d_inner, long seqlen, long d_state,
+                   int nthreads)
+{
+    return s6_common(u, delta, A, Bm, Cm, Dskip, z, h0, y, hT, batch, d_inner,
+                     seqlen, d_state, 0, nthreads);
+}
+
+/* The same scan with the zero-order-hold input term (see the header). */
+int oracle_s6_scan_zoh(const double *u, const double *delta, const double *A,
+                       const double *Bm, const double *Cm, const double *Dskip,
+                       const double *z, const double *h0, double *y, double *hT,
+                       long batch, long d_inner, long seqlen, long d_state,
+                       int nthreads)
+{
+    return s6_common(u, delta, A, Bm, Cm, Dskip, z, h0, y, hT, batch, d_inner,
+                     seqlen, d_state, 1, nthreads);
 }
 
 /* One decode step: the loop body with L = 1, state read from and written

@@ -19,12 +19,15 @@ MUTANTS = {
     "output_reads_old_state": (
         "h[n] = dA * h[n] + dBu;\n            acc += c->Cm[n * c->s_bn + t * c->s_bt] * h[n];",
         "acc += c->Cm[n * c->s_bn + t * c->s_bt] * h[n];\n            h[n] = dA * h[n] + dBu;"),
-    "exp_sign": ("exp(d * c->A[n * c->s_a])", "exp(-d * c->A[n * c->s_a])"),
-    "B_and_C_swapped": ("(d * x) * c->Bm[", "(d * x) * c->Cm["),
+    "exp_sign": ("const double dA = exp(d * a);", "const double dA = exp(-d * a);"),
+    "B_and_C_swapped": ("(k * x) * c->Bm[", "(k * x) * c->Cm["),
     "gate_sign": ("o *= g / (1.0 + exp(-g));", "o *= g / (1.0 + exp(g));"),
     "initial_state_ignored": ("c->h0 ? c->h0[n * c->s_h] : 0.0", "0.0"),
     "ssd_dt_stride": ("c->s_d = p->H;", "c->s_d = 1;"),
-    "step_dropped_from_input": ("(d * x) * c->Bm[", "x * c->Bm["),
+    "step_dropped_from_input": ("expm1(d * a) / a : d) : d;", "expm1(d * a) / a : d) : 1.0;"),
+    "zoh_gain_is_euler": ("expm1(d * a) / a : d) : d;", "d : d) : d;"),
+    "zoh_gain_sign": ("expm1(d * a) / a", "expm1(-d * a) / a"),
+    "zoh_gain_without_minus_one": ("expm1(d * a) / a", "exp(d * a) / a"),
     "ssd_group_map": ("const long g = h / (p->H / p->G);", "const long g = h % p->G;"),
     "final_state_index": ("c->hT[n * c->s_h] = h[n];", "c->hT[n * c->s_h] = h[0];"),
     "ssd_h0_ignores_head_channel": (
@@ -69,6 +72,18 @@ def _pins(lib):
     yq, hq = ssd_quadratic(**sd)
     if normwise_err(y, yq) > 1e-11 or normwise_err(hT, hq) > 1e-11:
         failed.append("ssd_quadratic")
+    # zero-order hold: L held steps equal the exact solution over L*delta
+    d, L, N = 2, 13, 3
+    a = -rng.uniform(0.1, 3.0, (d, N))
+    dl, u0, bn = rng.uniform(0.05, 0.4, d), rng.standard_normal(d), rng.standard_normal(N)
+    h0 = rng.standard_normal((1, d, N))
+    _, hT = oracle.s6_scan(np.repeat(u0[None, :, None], L, 2), np.repeat(dl[None, :, None], L, 2), a,
+                           np.repeat(bn[None, :, None], L, 2), rng.standard_normal((1, N, L)), h0=h0,
+                           lib=lib, zoh=True)
+    T = L * dl[:, None]
+    exact = np.exp(a * T) * h0[0] + np.expm1(a * T) / a * bn[None, :] * u0[:, None]
+    if not np.allclose(hT[0], exact, 1e-11, 1e-13):
+        failed.append("zoh_exact_solution")
     return failed
 
 

@@ -484,3 +484,71 @@ def test_backward_is_linear_in_dout(oracle_lib):
     g3 = oracle.s6_scan_bwd(*args, 2.0 * d1 - d2, lib=oracle_lib)
     for k in ("du", "ddelta", "dA", "dB", "dC", "dD", "dz", "dh0"):
         np.testing.assert_allclose(g3[k], 2.0 * g1[k] - g2[k], rtol=1e-12, atol=1e-12, err_msg=k)
+
+
+# ---- zero-order hold ----------------------------------------------------------
+# [ZOH] Optimization Patterns page, section 7: B_bar = (A_bar - I) A^-1 B, with
+# A_bar = exp(delta A); for a diagonal A this is (exp(delta a) - 1) / a * B per
+# state.  It is the exact discretisation of dh/dt = a h + B u for an input held
+# constant over the step.
+
+def test_zoh_constant_input_is_exact_ode_solution(oracle_lib):
+    """Under a constant step, input and B, L zero-order-hold steps compose to
+    the exact solution of dh/dt = a h + B u over the whole interval L*delta:
+    e^{aT} h0 + (e^{aT} - 1)/a B u (T B u at a = 0).  The Euler form does not."""
+    rng = np.random.default_rng(41)
+    b, d, L, N = 1, 3, 37, 4
+    A = np.array([[0.0, -1e-9, -0.7, -3.0], [-0.05, -1.3, -2.0, -0.4], [-5.0, -0.01, 0.0, -1.0]])
+    dl = np.array([0.02, 0.13, 0.4])                       # per channel, constant in t
+    u0 = np.array([0.7, -1.1, 0.3])
+    Bn = rng.standard_normal(N)                            # per state, constant in t
+    delta = np.repeat(dl[None, :, None], L, axis=2)
+    u = np.repeat(u0[None, :, None], L, axis=2)
+    B = np.repeat(Bn[None, :, None], L, axis=2)
+    C = rng.standard_normal((b, N, L))
+    h0 = rng.standard_normal((b, d, N))
+    _, hT = oracle.s6_scan(u, delta, A, B, C, h0=h0, lib=oracle_lib, zoh=True)
+    T = L * dl[:, None]
+    safe = np.where(A != 0, A, 1.0)
+    gain = np.where(A != 0, np.expm1(A * T) / safe, T)
+    exact = np.exp(A * T) * h0[0] + gain * Bn[None, :] * u0[:, None]
+    np.testing.assert_allclose(hT[0], exact, rtol=1e-12, atol=1e-14)
+    _, hE = oracle.s6_scan(u, delta, A, B, C, h0=h0, lib=oracle_lib)
+    assert np.abs(hE[0] - exact).max() > 1e-2
+
+
+def test_zoh_matches_ode_integration(oracle_lib):
+    """With every input held over its step, the zero-order-hold scan samples
+    the continuous system dh/dt = a h + B(t) u(t) exactly: compare y and the
+    final state with a high-accuracy numerical integration (scipy DOP853)."""
+    from scipy.integrate import solve_ivp
+    rng = np.random.default_rng(43)
+    b, d, L, N = 1, 2, 12, 3
+    inp = _rand_s6(rng, b, d, L, N)
+    inp["delta"] = rng.uniform(0.05, 0.6, (b, d, L))
+    y, hT = oracle.s6_scan(**inp, lib=oracle_lib, zoh=True)
+    for ch in range(d):
+        a = inp["A"][ch]
+        h = inp["h0"][0, ch].copy()
+        for t in range(L):
+            bt, ut = inp["B"][0, :, t], inp["u"][0, ch, t]
+            sol = solve_ivp(lambda _, x: a * x + bt * ut, (0.0, inp["delta"][0, ch, t]), h,
+                            method="DOP853", rtol=1e-12, atol=1e-14)
+            h = sol.y[:, -1]
+            o = (inp["C"][0, :, t] @ h + inp["D"][ch] * ut) * silu(inp["z"][0, ch, t])
+            assert abs(o - y[0, ch, t]) <= 1e-9 * (1.0 + abs(o))
+        np.testing.assert_allclose(hT[0, ch], h, rtol=1e-9, atol=1e-11)
+
+
+def test_zoh_at_zero_A_is_euler_and_continuous_near_it(oracle_lib):
+    """At a = 0 the hold gain's limit is delta, so both forms coincide bit for
+    bit; a tiny nonzero a stays within rounding of it."""
+    rng = np.random.default_rng(47)
+    inp = _rand_s6(rng, 2, 3, 20, 4)
+    inp["A"] = np.zeros_like(inp["A"])
+    yz, hz = oracle.s6_scan(**inp, lib=oracle_lib, zoh=True)
+    ye, he = oracle.s6_scan(**inp, lib=oracle_lib)
+    assert np.array_equal(yz, ye) and np.array_equal(hz, he)
+    inp["A"] = np.full_like(inp["A"], -1e-10)
+    yt, _ = oracle.s6_scan(**inp, lib=oracle_lib, zoh=True)
+    assert normwise_err(yt, ye) < 1e-9
