@@ -211,6 +211,35 @@ def bench_s6fused(args):
             "traffic_bytes_per_launch": profiled_traffic("s6_scan_fused_mamba1p4b_bf16.md")}
 
 
+def bench_s6zoh(args):
+    """The scan with the zero-order-hold input term, same layer shape as the headline."""
+    import torch
+    import selective_state_space_19_amd as mssm
+    from selective_state_space_19_amd import synth
+    wl = synth.WORKLOADS["s6_mamba1p4b_bf16"]
+    s = wl.shape
+    log("[bench] s6 zoh: generating inputs")
+    inp = synth.s6_inputs(**s, dtype=wl.dtype, seed=wl.seed)
+    d = {k: to_dev(inp[k]) for k in ("u", "delta", "A", "B", "C", "D", "z", "h0")}
+    y = torch.empty_like(d["u"])
+    hf = torch.empty((s["batch"], s["d_inner"], s["d_state"]), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        mssm.selective_scan(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["h0"],
+                            out=y, h_final=hf, stream=stream, zoh=True)
+
+    steps = max(5, args.steps // 2)
+    total, _ = time_launches(step, steps, 2, stream, warm_ms=WARM_MS)
+    ms = total / steps
+    nb = s6_bytes(s["batch"], s["d_inner"], s["seqlen"], s["d_state"], 2)
+    tok = s["batch"] * s["d_inner"] * s["seqlen"]
+    return {"workload": f"{wl.name} with the zero-order-hold input term: batch {s['batch']}, d_inner {s['d_inner']}, "
+                        f"seqlen {s['seqlen']}, d_state {s['d_state']}, bf16",
+            "us": ms * 1e3, "GBs": nb / (ms * 1e-3) / 1e9, "hbm_frac": nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "tokens_ch_per_s": tok / (ms * 1e-3), "algorithmic_bytes": nb}
+
+
 def bench_s6bwd(args):
     """Backward of the scan at the headline layer shape (h0 and final-state
     gradient included)."""
@@ -463,7 +492,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--only", default="s6,s6fused,s6bwd,decode,decode2,ssd")
+    ap.add_argument("--only", default="s6,s6fused,s6zoh,s6bwd,decode,decode2,ssd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
     args = ap.parse_args()
@@ -523,6 +552,11 @@ def main():
             out["secondary_s6_backward"] = bench_s6bwd(args)
         except Exception as e:  # reported, not hidden
             out["secondary_s6_backward"] = {"error": repr(e)}
+    if "s6zoh" in parts:
+        try:
+            out["secondary_s6_zoh"] = bench_s6zoh(args)
+        except Exception as e:  # reported, not hidden
+            out["secondary_s6_zoh"] = {"error": repr(e)}
     if "s6fused" in parts:
         try:
             out["secondary_s6_fused_front_end"] = bench_s6fused(args)

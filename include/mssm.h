@@ -2,9 +2,11 @@
  * mssm.h -- C ABI of libmssm.so, the MI355X (gfx950) selective state-space
  * scan library.
  *
- * Six operations, each defined by the pages it cites:
+ * Seven operations, each defined by the pages it cites:
  *
  *   mssm_selective_scan_fwd  the S6 selective scan over a whole sequence;
+ *   mssm_selective_scan_zoh_fwd  the same scan with the zero-order-hold
+ *                            input term;
  *   mssm_selective_scan_fused_fwd  the same scan with its input front end
  *                            (causal conv1d + SiLU, softplus step) fused in;
  *   mssm_selective_scan_bwd  the gradients of that scan (training);
@@ -94,6 +96,27 @@ int mssm_selective_scan_fwd(const void* u, const void* delta, const float* A,
                             const void* z, const float* h0, void* y, float* h_final,
                             int64_t batch, int64_t d_inner, int64_t seqlen,
                             int64_t d_state, mssm_dtype dtype, void* stream);
+
+/*
+ * S6 selective scan with the zero-order-hold input term (forward).
+ *
+ * Defined by: the "State-Space Model Optimization Patterns" page, section 7,
+ * which discretises B as (A_bar - I) A^-1 B with A_bar = exp(delta A); with a
+ * diagonal A that is, per state, (exp(delta A[d,n]) - 1) / A[d,n] * B, the
+ * exact discretisation of dh/dt = A h + B u for an input held over the step.
+ * Everything else is mssm_selective_scan_fwd:
+ *
+ *   h[n] <- exp(delta*A[d,n]) * h[n] + (exp(delta*A[d,n]) - 1) / A[d,n] * u * B[b,n,t]
+ *
+ * with the term's limit delta * u * B at A[d,n] = 0 (computed without
+ * cancellation for small delta*A).  Arguments, layouts, limits and errors are
+ * those of mssm_selective_scan_fwd.
+ */
+int mssm_selective_scan_zoh_fwd(const void* u, const void* delta, const float* A,
+                                const void* Bm, const void* Cm, const float* Dskip,
+                                const void* z, const float* h0, void* y, float* h_final,
+                                int64_t batch, int64_t d_inner, int64_t seqlen,
+                                int64_t d_state, mssm_dtype dtype, void* stream);
 
 /*
  * S6 selective scan with its front end fused in (forward).

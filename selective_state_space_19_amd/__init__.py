@@ -54,10 +54,12 @@ def _stream(stream, device):
 
 
 def selective_scan(u, delta, A, B, C, D=None, z=None, h0=None, *, return_final_state=False,
-                   out=None, h_final=None, stream=None):
+                   out=None, h_final=None, stream=None, zoh=False):
     """S6 scan.  u, delta, z: [b, d, L]; B, C: [b, N, L] (float32 or bfloat16,
     all the same); A: [d, N] float32; D: [d] float32; h0: [b, d, N] float32.
-    Returns y [b, d, L] (u's dtype), and h_final [b, d, N] float32 if asked."""
+    Returns y [b, d, L] (u's dtype), and h_final [b, d, N] float32 if asked.
+    zoh: the zero-order-hold input term (exp(delta A) - 1) / A * B instead of
+    the Euler delta * B."""
     torch = _torch()
     dev = u.device
     u = _dev(u, "u")
@@ -82,9 +84,9 @@ def selective_scan(u, delta, A, B, C, D=None, z=None, h0=None, *, return_final_s
         _dev(hf, "h_final", (bsz, dim, N), torch.float32, dev)
         if not hf.is_contiguous():
             raise ValueError("h_final must be contiguous")
-    check(lib().mssm_selective_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                                        _ptr(h0), _ptr(y), _ptr(hf), bsz, dim, L, N, code,
-                                        _stream(stream, dev)))
+    fn = lib().mssm_selective_scan_zoh_fwd if zoh else lib().mssm_selective_scan_fwd
+    check(fn(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(hf),
+             bsz, dim, L, N, code, _stream(stream, dev)))
     return (y, hf) if hf is not None else y
 
 

@@ -39,6 +39,8 @@ _vp, _fp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ct
 def _bind(lib):
     lib.mssm_selective_scan_fwd.argtypes = [_vp] * 10 + [_i64] * 4 + [_i32, _vp]
     lib.mssm_selective_scan_fwd.restype = _i32
+    lib.mssm_selective_scan_zoh_fwd.argtypes = [_vp] * 10 + [_i64] * 4 + [_i32, _vp]
+    lib.mssm_selective_scan_zoh_fwd.restype = _i32
     lib.mssm_selective_scan_fused_fwd.argtypes = [_vp] * 14 + [_i64] * 5 + [_i32, _vp]
     lib.mssm_selective_scan_fused_fwd.restype = _i32
     lib.mssm_selective_scan_bwd_workspace_size.argtypes = [_i64] * 4

@@ -87,7 +87,7 @@ struct SSDUParams {
 };
 
 // Each returns hipSuccess or the launch error; is_bf16 selects the storage type.
-hipError_t launch_s6_scan(const S6Params& p, bool is_bf16, hipStream_t stream);
+hipError_t launch_s6_scan(const S6Params& p, bool is_bf16, bool zoh, hipStream_t stream);   // zoh: hold input term
 hipError_t launch_s6_scan_fused(const S6Params& p, const S6FrontEnd& fe, bool is_bf16, hipStream_t stream);
 hipError_t launch_state_update(const SUParams& p, bool is_bf16, hipStream_t stream);
 // Backward of the scan; zeroes dA and dD and then accumulates into them.

@@ -64,11 +64,10 @@ const char* mssm_last_error(void) { return g_err.c_str(); }
 
 int mssm_version(void) { return 100; }
 
-int mssm_selective_scan_fwd(const void* u, const void* delta, const float* A, const void* Bm,
-                            const void* Cm, const float* Dskip, const void* z, const float* h0,
-                            void* y, float* h_final, int64_t batch, int64_t d_inner, int64_t seqlen,
-                            int64_t d_state, mssm_dtype dtype, void* stream) {
-    static const char* fn = "mssm_selective_scan_fwd";
+static int scan_fwd(const char* fn, bool zoh, const void* u, const void* delta, const float* A, const void* Bm,
+                    const void* Cm, const float* Dskip, const void* z, const float* h0, void* y, float* h_final,
+                    int64_t batch, int64_t d_inner, int64_t seqlen, int64_t d_state, mssm_dtype dtype,
+                    void* stream) {
     g_err.clear();
     if (dtype != MSSM_F32 && dtype != MSSM_BF16) return fail(MSSM_ERR_DTYPE, "%s: unknown dtype %d", fn, (int)dtype);
     if (batch < 0 || d_inner < 0 || seqlen < 0 || d_state < 0)
@@ -96,7 +95,23 @@ int mssm_selective_scan_fwd(const void* u, const void* delta, const float* A, co
     const int64_t blocks = ((d_inner + 63) / 64) * batch;
     if (blocks > INT32_MAX) return fail(MSSM_ERR_UNSUPPORTED, "%s: batch*d_inner too large", fn);
     mssm::S6Params p{u, delta, Bm, Cm, z, A, Dskip, h0, y, h_final, batch, d_inner, (int32_t)seqlen, (int32_t)d_state};
-    return launched(fn, mssm::launch_s6_scan(p, dtype == MSSM_BF16, s));
+    return launched(fn, mssm::launch_s6_scan(p, dtype == MSSM_BF16, zoh, s));
+}
+
+int mssm_selective_scan_fwd(const void* u, const void* delta, const float* A, const void* Bm,
+                            const void* Cm, const float* Dskip, const void* z, const float* h0,
+                            void* y, float* h_final, int64_t batch, int64_t d_inner, int64_t seqlen,
+                            int64_t d_state, mssm_dtype dtype, void* stream) {
+    return scan_fwd("mssm_selective_scan_fwd", false, u, delta, A, Bm, Cm, Dskip, z, h0, y, h_final, batch,
+                    d_inner, seqlen, d_state, dtype, stream);
+}
+
+int mssm_selective_scan_zoh_fwd(const void* u, const void* delta, const float* A, const void* Bm,
+                                const void* Cm, const float* Dskip, const void* z, const float* h0,
+                                void* y, float* h_final, int64_t batch, int64_t d_inner, int64_t seqlen,
+                                int64_t d_state, mssm_dtype dtype, void* stream) {
+    return scan_fwd("mssm_selective_scan_zoh_fwd", true, u, delta, A, Bm, Cm, Dskip, z, h0, y, h_final, batch,
+                    d_inner, seqlen, d_state, dtype, stream);
 }
 
 int mssm_selective_scan_fused_fwd(const void* x, const float* conv_w, const float* conv_b, const void* conv_init,

@@ -53,11 +53,23 @@ namespace {
 
 struct alignas(16) Words8 { uint32_t w[8]; };   // bases are 16-byte aligned
 
+// The zero-order-hold gain expm1(x) / x of x = delta*A, given e = exp(x)
+// (so the hold input term is delta*u*B times this): for |x| < 1/4 the
+// Taylor series through x^5/720 (truncation under 5e-8 relative), otherwise
+// (e - 1) / x, where e - 1 costs at most a few units in e's last place.  At
+// x = 0 the series gives exactly 1, the Euler term.
+__device__ __forceinline__ float zoh_gain(float x, float e) {
+    const float p = fmaf(x, fmaf(x, fmaf(x, fmaf(x, fmaf(x, 1.f / 720.f, 1.f / 120.f), 1.f / 24.f), 1.f / 6.f), 0.5f),
+                         1.f);
+    const float r = (e - 1.f) * __builtin_amdgcn_rcpf(x);
+    return fabsf(x) < 0.25f ? p : r;
+}
+
 constexpr int kScanWaves = 8;     // waves running the recurrence
 constexpr int kRowWaves = 4;      // waves streaming rows: loads, staging, epilogue
 constexpr int kRing = 4;          // row-wave register ring: chunks of loads in flight + 1
 
-template <typename T, int NS, int TC, bool ALIGNED, bool FULLN, bool FUSED, int RING>
+template <typename T, int NS, int TC, bool ALIGNED, bool FULLN, bool FUSED, bool ZOH, int RING>
 __global__ __launch_bounds__((kScanWaves + kRowWaves) * 64) void s6_scan_kernel(
     const T* __restrict__ u_in, const T* __restrict__ dl_in, const T* __restrict__ B_in,
     const T* __restrict__ C_in, const T* __restrict__ z_in, const float* __restrict__ A_in,
@@ -65,7 +77,9 @@ __global__ __launch_bounds__((kScanWaves + kRowWaves) * 64) void s6_scan_kernel(
     float* __restrict__ hT_out, int64_t dim, int L, int N, S6FrontEnd fe) {
     // FUSED: u_in is x before the causal conv and dl_in the step before
     // softplus; the row waves form u = silu(conv(x)) and delta =
-    // softplus(raw + bias) while staging.
+    // softplus(raw + bias) while staging.  ZOH: the input term is the
+    // zero-order hold (exp(delta*A) - 1) / A * u * B instead of delta * u * B
+    // ("State-Space Model Optimization Patterns" page, section 7).
     // Pointers are separate __restrict__ arguments so the compiler may fetch the
     // wave-uniform B / C words with scalar loads (it must know no store aliases them).
     constexpr int NW = kScanWaves;
@@ -109,7 +123,7 @@ __global__ __launch_bounds__((kScanWaves + kRowWaves) * 64) void s6_scan_kernel(
         const T* brow[NS];
         const T* crow[NS];
         bool sval[NS];
-        float h[NS], a2[NS];
+        float h[NS], a2[NS], af[NS];
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             const int n = w * NS + s;
@@ -118,7 +132,8 @@ __global__ __launch_bounds__((kScanWaves + kRowWaves) * 64) void s6_scan_kernel(
             brow[s] = B_in + off;
             crow[s] = C_in + off;
             const bool ok = sval_d && sval[s];
-            a2[s] = ok ? A_in[(d0 + cs) * N + n] * kLog2e : 0.f;
+            af[s] = ok ? A_in[(d0 + cs) * N + n] : 0.f;
+            a2[s] = af[s] * kLog2e;
             h[s] = (ok && h0_in) ? h0_in[(b * dim + d0 + cs) * N + n] : 0.f;
         }
 
@@ -172,8 +187,13 @@ __global__ __launch_bounds__((kScanWaves + kRowWaves) * 64) void s6_scan_kernel(
                 for (int s = 0; s < NS; ++s) {
                     dA[k][s] = fast_exp2(q.x * a2[s]);
                     dA[k + 1][s] = fast_exp2(q.z * a2[s]);
-                    bu[k][s] = q.y * Elem<T>::get(bw[buf][s], k);
-                    bu[k + 1][s] = q.w * Elem<T>::get(bw[buf][s], k + 1);
+                    if constexpr (ZOH) {
+                        bu[k][s] = (q.y * zoh_gain(q.x * af[s], dA[k][s])) * Elem<T>::get(bw[buf][s], k);
+                        bu[k + 1][s] = (q.w * zoh_gain(q.z * af[s], dA[k + 1][s])) * Elem<T>::get(bw[buf][s], k + 1);
+                    } else {
+                        bu[k][s] = q.y * Elem<T>::get(bw[buf][s], k);
+                        bu[k + 1][s] = q.w * Elem<T>::get(bw[buf][s], k + 1);
+                    }
                 }
             }
 #pragma unroll
@@ -415,18 +435,22 @@ __global__ __launch_bounds__((kScanWaves + kRowWaves) * 64) void s6_scan_kernel(
 }
 
 template <typename T, int NS, int TC>
-hipError_t launch_cfg(const S6Params& p, const S6FrontEnd* fe, hipStream_t stream) {
+hipError_t launch_cfg(const S6Params& p, const S6FrontEnd* fe, bool zoh, hipStream_t stream) {
     const int64_t blocks = ((p.dim + 63) / 64) * p.batch;
     // The aligned path addresses a block's rows through 32-bit buffer
     // offsets, and reads B / C in whole 32-byte groups.
     const bool aligned = (p.L % (32 / int(sizeof(T))) == 0) && int64_t(64) * p.L * int64_t(sizeof(T)) < (int64_t(1) << 31);
     const bool fulln = p.N == kScanWaves * NS;
-    auto kern = fe ? (aligned ? (fulln ? s6_scan_kernel<T, NS, TC, true, true, true, kRing>
-                                       : s6_scan_kernel<T, NS, TC, true, false, true, kRing>)
-                              : s6_scan_kernel<T, NS, TC, false, false, true, kRing>)
-                   : (aligned ? (fulln ? s6_scan_kernel<T, NS, TC, true, true, false, kRing>
-                                       : s6_scan_kernel<T, NS, TC, true, false, false, kRing>)
-                              : s6_scan_kernel<T, NS, TC, false, false, false, kRing>);
+    // The hold form is built for the plain scan only (the fused front end is Euler).
+    auto kern = fe ? (aligned ? (fulln ? s6_scan_kernel<T, NS, TC, true, true, true, false, kRing>
+                                       : s6_scan_kernel<T, NS, TC, true, false, true, false, kRing>)
+                              : s6_scan_kernel<T, NS, TC, false, false, true, false, kRing>)
+            : zoh ? (aligned ? (fulln ? s6_scan_kernel<T, NS, TC, true, true, false, true, kRing>
+                                      : s6_scan_kernel<T, NS, TC, true, false, false, true, kRing>)
+                             : s6_scan_kernel<T, NS, TC, false, false, false, true, kRing>)
+                  : (aligned ? (fulln ? s6_scan_kernel<T, NS, TC, true, true, false, false, kRing>
+                                      : s6_scan_kernel<T, NS, TC, true, false, false, false, kRing>)
+                             : s6_scan_kernel<T, NS, TC, false, false, false, false, kRing>);
     const S6FrontEnd none{};
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3((kScanWaves + kRowWaves) * 64), 0, stream,
                        static_cast<const T*>(p.u), static_cast<const T*>(p.delta), static_cast<const T*>(p.Bm),
@@ -436,12 +460,12 @@ hipError_t launch_cfg(const S6Params& p, const S6FrontEnd* fe, hipStream_t strea
 }
 
 template <typename T>
-hipError_t launch_t(const S6Params& p, const S6FrontEnd* fe, hipStream_t stream) {
+hipError_t launch_t(const S6Params& p, const S6FrontEnd* fe, bool zoh, hipStream_t stream) {
     // 8 scan waves per 64 channels; NS = ceil(N / 8) states per lane.
-    if (p.N <= 8) return launch_cfg<T, 1, 32>(p, fe, stream);
-    if (p.N <= 16) return launch_cfg<T, 2, 32>(p, fe, stream);
-    if (p.N <= 32) return launch_cfg<T, 4, 32>(p, fe, stream);
-    return launch_cfg<T, 8, 32>(p, fe, stream);
+    if (p.N <= 8) return launch_cfg<T, 1, 32>(p, fe, zoh, stream);
+    if (p.N <= 16) return launch_cfg<T, 2, 32>(p, fe, zoh, stream);
+    if (p.N <= 32) return launch_cfg<T, 4, 32>(p, fe, zoh, stream);
+    return launch_cfg<T, 8, 32>(p, fe, zoh, stream);
 }
 
 __global__ void copy_or_zero_kernel(float* dst, const float* src, int64_t n) {
@@ -451,12 +475,12 @@ __global__ void copy_or_zero_kernel(float* dst, const float* src, int64_t n) {
 
 }  // namespace
 
-hipError_t launch_s6_scan(const S6Params& p, bool is_bf16, hipStream_t stream) {
-    return is_bf16 ? launch_t<uint16_t>(p, nullptr, stream) : launch_t<float>(p, nullptr, stream);
+hipError_t launch_s6_scan(const S6Params& p, bool is_bf16, bool zoh, hipStream_t stream) {
+    return is_bf16 ? launch_t<uint16_t>(p, nullptr, zoh, stream) : launch_t<float>(p, nullptr, zoh, stream);
 }
 
 hipError_t launch_s6_scan_fused(const S6Params& p, const S6FrontEnd& fe, bool is_bf16, hipStream_t stream) {
-    return is_bf16 ? launch_t<uint16_t>(p, &fe, stream) : launch_t<float>(p, &fe, stream);
+    return is_bf16 ? launch_t<uint16_t>(p, &fe, false, stream) : launch_t<float>(p, &fe, false, stream);
 }
 
 hipError_t launch_copy_or_zero(float* dst, const float* src, int64_t n, hipStream_t stream) {

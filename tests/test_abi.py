@@ -1,6 +1,7 @@
 """The C ABI library loads, exports what include/mssm.h declares, and rejects
 bad arguments on the host -- no GPU needed (no call here reaches a launch)."""
 import ctypes
+import functools
 
 import pytest
 
@@ -18,7 +19,8 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = _lib.header_functions()
-    assert set(names) == {"mssm_selective_scan_fwd", "mssm_selective_scan_fused_fwd", "mssm_selective_scan_bwd",
+    assert set(names) == {"mssm_selective_scan_fwd", "mssm_selective_scan_zoh_fwd",
+                          "mssm_selective_scan_fused_fwd", "mssm_selective_scan_bwd",
                           "mssm_selective_scan_bwd_workspace_size", "mssm_state_update",
                           "mssm_ssd_workspace_size",
                           "mssm_ssd_chunk_fwd", "mssm_ssd_state_update", "mssm_last_error", "mssm_version"}
@@ -31,17 +33,21 @@ def test_version(lib):
     assert lib.mssm_version() >= 100
 
 
-def _scan(lib, **kw):
+def _scan_any(lib, zoh=False, **kw):
     a = dict(u=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, h0=None, y=FAKE, hf=None,
              b=2, d=64, L=128, N=16, dtype=0)
     a.update(kw)
-    return lib.mssm_selective_scan_fwd(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["h0"],
-                                       a["y"], a["hf"], a["b"], a["d"], a["L"], a["N"], a["dtype"], None)
+    fn = lib.mssm_selective_scan_zoh_fwd if zoh else lib.mssm_selective_scan_fwd
+    return fn(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["h0"],
+              a["y"], a["hf"], a["b"], a["d"], a["L"], a["N"], a["dtype"], None)
 
 
-def test_scan_argument_errors(lib):
+@pytest.mark.parametrize("zoh", [False, True])
+def test_scan_argument_errors(lib, zoh):
+    _scan = functools.partial(_scan_any, zoh=zoh)
     assert _scan(lib, u=None) == ERR_NULL
     assert b"u is NULL" in lib.mssm_last_error()
+    assert (b"zoh" in lib.mssm_last_error()) == zoh
     assert _scan(lib, y=None) == ERR_NULL
     assert _scan(lib, dtype=7) == ERR_DTYPE
     assert _scan(lib, L=-1) == ERR_SHAPE
