@@ -237,7 +237,8 @@ def bench_s6zoh(args):
     return {"workload": f"{wl.name} with the zero-order-hold input term: batch {s['batch']}, d_inner {s['d_inner']}, "
                         f"seqlen {s['seqlen']}, d_state {s['d_state']}, bf16",
             "us": ms * 1e3, "GBs": nb / (ms * 1e-3) / 1e9, "hbm_frac": nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "tokens_ch_per_s": tok / (ms * 1e-3), "algorithmic_bytes": nb}
+            "tokens_ch_per_s": tok / (ms * 1e-3), "algorithmic_bytes": nb,
+            "traffic_bytes_per_launch": profiled_traffic("s6_scan_zoh_mamba1p4b_bf16.md")}
 
 
 def bench_s6bwd(args):
