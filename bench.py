@@ -463,9 +463,15 @@ def bench_ssd(args):
 
     total, per = time_launches(step, 20, 3, stream, warm_ms=WARM_MS)
     ms = total / 20
+    # The chunk length is a tile size: the result is the same up to rounding.
+    # The same call with 64-token chunks, for comparison (not the workload).
+    y64 = torch.empty_like(y)
+    total64, _ = time_launches(lambda: mssm.ssd_chunk(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], chunk=64,
+                                                      out=y64, workspace=ws, stream=stream), 20, 3, stream)
     nb = ssd_bytes(s["batch"], s["seqlen"], s["nheads"], s["headdim"], s["d_state"], s["ngroups"], 2)
     fl = ssd_flops(s["batch"], s["seqlen"], s["nheads"], s["headdim"], s["d_state"], s["ngroups"], s["chunk"])
     return dict(workload=f"{wl.name}: batch 4, seqlen 4096, 32 heads x 64, d_state 128, ngroups 1, chunk 256, bf16",
+                us_same_call_chunk64=total64 / 20 * 1e3,
                 us=ms * 1e3, GBs=nb / (ms * 1e-3) / 1e9, hbm_frac=nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                 mfma_TFLOPs=fl / (ms * 1e-3) / 1e12, mfma_frac=fl / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                 tokens_ch_per_s=s["batch"] * s["seqlen"] * s["nheads"] * s["headdim"] / (ms * 1e-3),
