@@ -14,9 +14,11 @@
 //     dA += lambda_t delta_t a_t h_{t-1},  dD += g_t u_t
 //     dz_t = dout_t y_t silu'(z_t),  dh0 = a_0 lambda_0.
 //
-// Design (same mapping as the forward kernel): a workgroup of 8 waves owns 64
-// channels of one batch row; lane = channel, wave w = states
-// [w NS, (w+1) NS); B and C are wave-uniform (scalar operands).
+// Design: a workgroup of 8 waves owns 64 channels of one batch row; lane =
+// channel, wave w = states [w NS, (w+1) NS).  Row threads (8 per channel)
+// load u, delta, dout, z and the whole block's B / C rows of a chunk one
+// chunk ahead, so their memory latency hides behind the current chunk; B / C
+// reach the waves through LDS (uniform reads).
 //   1. Forward sweep over the whole sequence in chunks of TC tokens (16, or 8
 //      when a lane holds more than 2 states), writing
 //      the state at every chunk start to the workspace (one fp32 per
@@ -82,13 +84,18 @@ __device__ __forceinline__ void tree(float (&v)[CAP]) {
 
 constexpr int log2i(int n) { return n <= 1 ? 0 : 1 + log2i(n / 2); }
 
-template <typename T, int NS, bool ALIGNED>
+// An element of type T widened to float (bf16: the upper half of a float).
+__device__ __forceinline__ float widen(float v) { return v; }
+__device__ __forceinline__ float widen(uint16_t v) { return __uint_as_float(uint32_t(v) << 16); }
+
+template <typename T, int NS>
 __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
     constexpr int kTC = ChunkLen<NS>::value;
     constexpr int kTPT = kTC / kSegs;      // tokens per row thread
     __shared__ float4 s_tk[kTC][64 + 1];          // (delta, delta*u, u, g) per token and channel
     __shared__ float s_y[kNW][kTC][64 + 1];       // per-wave partial sum_n C h
     __shared__ float2 s_p[kNW][kTC][64 + 1];      // per-wave partial (du, ddelta)
+    __shared__ __align__(16) float s_bc[2][kNW * NS][kTC];   // the chunk's B (0) and C (1) rows
 
     const T* u_in = static_cast<const T*>(p.u);
     const T* dl_in = static_cast<const T*>(p.delta);
@@ -128,44 +135,58 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
         dAacc[s] = 0.f;
     }
     // B / C of this wave's states over one chunk (0 past the end or for a
-    // state past N).  ALIGNED (L % 8 == 0) and a whole chunk: one vector load
-    // per state row; otherwise element by element.
+    // state past N), read from LDS after the barrier.  The block's B / C
+    // elements of a chunk are fetched by all threads one chunk ahead (raw,
+    // clamped addresses; kBPT per thread) and written to s_bc when staging.
     float Bf[NS][kTC], Cf[NS][kTC];
-    auto load_bc = [&](int t0) {
-        const bool vec = ALIGNED && t0 + kTC <= L;
+    constexpr int kNP = kNW * NS;                              // states, padded
+    constexpr int kBCE = 2 * kNP * kTC;                        // B / C elements per chunk
+    constexpr int kBPT = (kBCE + kNW * 64 - 1) / (kNW * 64);   // per thread
+    auto bc_index = [&](int i, int& m, int& n, int& k) {
+        m = i / (kNP * kTC);
+        n = (i / kTC) % kNP;
+        k = i % kTC;
+    };
+    auto fetch_bc = [&](int ck, T (&r)[kBPT]) {
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            const int n = w * NS + s;
-            const T* pb = B_in + (b * N + nst[s]) * (int64_t)L + t0;
-            const T* pc = C_in + (b * N + nst[s]) * (int64_t)L + t0;
-            if (vec) {
-                constexpr int NW4 = kTC * (int)sizeof(T) / 16;        // 16-byte words per chunk row
-                uint32_t wb[NW4 * 4], wc[NW4 * 4];
+        for (int q = 0; q < kBPT; ++q) {
+            const int i = tid + q * kNW * 64;
+            int m, n, k;
+            bc_index(i < kBCE ? i : 0, m, n, k);
+            const int t = ck * kTC + k;
+            r[q] = (m ? C_in : B_in)[(b * N + (n < N ? n : N - 1)) * (int64_t)L + (t < L ? t : L - 1)];
+        }
+    };
+    auto stage_bc = [&](int ck, const T (&r)[kBPT]) {
 #pragma unroll
-                for (int q = 0; q < NW4; ++q) {
-                    const uint4 x = reinterpret_cast<const uint4*>(pb)[q];
-                    const uint4 y = reinterpret_cast<const uint4*>(pc)[q];
-                    wb[4 * q] = x.x; wb[4 * q + 1] = x.y; wb[4 * q + 2] = x.z; wb[4 * q + 3] = x.w;
-                    wc[4 * q] = y.x; wc[4 * q + 1] = y.y; wc[4 * q + 2] = y.z; wc[4 * q + 3] = y.w;
-                }
-#pragma unroll
-                for (int k = 0; k < kTC; ++k) {
-                    Bf[s][k] = n < N ? Elem<T>::get(wb, k) : 0.f;
-                    Cf[s][k] = n < N ? Elem<T>::get(wc, k) : 0.f;
-                }
-            } else {
-#pragma unroll
-                for (int k = 0; k < kTC; ++k) {
-                    const bool ok = n < N && t0 + k < L;
-                    Bf[s][k] = ok ? Elem<T>::load1(pb + (ok ? k : 0)) : 0.f;
-                    Cf[s][k] = ok ? Elem<T>::load1(pc + (ok ? k : 0)) : 0.f;
-                }
+        for (int q = 0; q < kBPT; ++q) {
+            const int i = tid + q * kNW * 64;
+            if (i < kBCE) {
+                int m, n, k;
+                bc_index(i, m, n, k);
+                const float v = widen(r[q]);
+                s_bc[m][n][k] = (n < N && ck * kTC + k < L) ? v : 0.f;
             }
         }
     };
-    // checkpoint of state s at the start of chunk ck
+    auto read_bc = [&]() {
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int k = 0; k < kTC; k += 4) {
+                const float4 x = *reinterpret_cast<const float4*>(&s_bc[0][w * NS + s][k]);
+                const float4 y = *reinterpret_cast<const float4*>(&s_bc[1][w * NS + s][k]);
+                Bf[s][k] = x.x; Bf[s][k + 1] = x.y; Bf[s][k + 2] = x.z; Bf[s][k + 3] = x.w;
+                Cf[s][k] = y.x; Cf[s][k + 1] = y.y; Cf[s][k + 2] = y.z; Cf[s][k + 3] = y.w;
+            }
+    };
+    // checkpoint of state s at the start of chunk ck (a lane or state past the
+    // end reads a valid element in place of its own: clamped, never used)
     auto ckpt = [&](int ck, int s) -> float* {
         return p.ws + ((b * nck + ck) * (int64_t)N + w * NS + s) * dim + d0 + cs;
+    };
+    auto ckpt_in = [&](int ck, int s) -> const float* {
+        return p.ws + ((b * nck + ck) * (int64_t)N + nst[s]) * dim + d0 + (cval ? cs : 0);
     };
 
     // ---- row mapping: thread -> (row cr, tokens [toff, toff + kTPT)) ----------
@@ -175,24 +196,50 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
     const bool rval = cr < nrows;
     const int64_t rrow = (b * dim + d0 + (rval ? cr : 0)) * (int64_t)L;   // first element of this row
     const float dskip = (rval && p.Dskip) ? p.Dskip[d0 + cr] : 0.f;
-    auto ld = [&](const T* base, int t) -> float { return (rval && t < L) ? Elem<T>::load1(base + rrow + t) : 0.f; };
+    // Row loads issued a chunk ahead: unconditional (clamped address) and
+    // left untouched until the next chunk uses them (touching a loaded value
+    // waits for it); `rv` then replaces a value past the end by 0.
+    // The raw element is kept (a conversion would be a use) and widened by
+    // `rv`.  Without z, u's row is read in its place and ignored.
+    auto ld = [&](const T* base, int t) -> T { return base[rrow + (t < L ? t : L - 1)]; };
+    auto rv = [&](T raw, int t) -> float { return (rval && t < L) ? widen(raw) : 0.f; };
+    const T* zl_in = z_in ? z_in : u_in;
 
     // ================= 1. forward sweep: chunk-start checkpoints =================
-    for (int ck = 0; ck < nck; ++ck) {
-        const int t0 = ck * kTC;
+    // (delta, u) of the next chunk are loaded while this one is scanned.
+    T f_dl[kTPT], f_u[kTPT], f_bc[kBPT];
+    auto fetch_fwd = [&](int ck) {
 #pragma unroll
         for (int j = 0; j < kTPT; ++j) {
-            const int t = t0 + toff + j;
-            const float dl = ld(dl_in, t), uu = ld(u_in, t);
-            s_tk[toff + j][cr] = make_float4(dl, dl * uu, 0.f, 0.f);
+            const int t = ck * kTC + toff + j;
+            f_dl[j] = ld(dl_in, t);
+            f_u[j] = ld(u_in, t);
         }
+        fetch_bc(ck, f_bc);
+    };
+    if (nck > 0) fetch_fwd(0);
+    for (int ck = 0; ck < nck; ++ck) {
+        const int t0 = ck * kTC;
+        float dlv[kTPT], uv[kTPT];
+        T bcv[kBPT];
+#pragma unroll
+        for (int j = 0; j < kTPT; ++j) {
+            dlv[j] = rv(f_dl[j], t0 + toff + j);
+            uv[j] = rv(f_u[j], t0 + toff + j);
+        }
+#pragma unroll
+        for (int q = 0; q < kBPT; ++q) bcv[q] = f_bc[q];
+        if (ck + 1 < nck) fetch_fwd(ck + 1);
+        stage_bc(ck, bcv);
+#pragma unroll
+        for (int j = 0; j < kTPT; ++j) s_tk[toff + j][cr] = make_float4(dlv[j], dlv[j] * uv[j], 0.f, 0.f);
         if (cval) {
 #pragma unroll
             for (int s = 0; s < NS; ++s)
                 if (w * NS + s < N) *ckpt(ck, s) = h[s];
         }
-        load_bc(t0);
         __syncthreads();
+        read_bc();
 #pragma unroll
         for (int k = 0; k < kTC; ++k) {
             const float4 q = s_tk[k][cs];
@@ -203,29 +250,57 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
     }
 
     // ================= 2. backward sweep, last chunk first =======================
+    // The row data and the chunk-start states of the next chunk (ck - 1) are
+    // loaded while this one is processed.
     float dDacc = 0.f;
+    T b_dl[kTPT], b_u[kTPT], b_go[kTPT], b_z[kTPT], b_bc[kBPT];
+    float b_hc[NS];
+    auto fetch_bwd = [&](int ck) {
+#pragma unroll
+        for (int j = 0; j < kTPT; ++j) {
+            const int t = ck * kTC + toff + j;
+            b_dl[j] = ld(dl_in, t);
+            b_u[j] = ld(u_in, t);
+            b_go[j] = ld(go_in, t);
+            b_z[j] = ld(zl_in, t);
+        }
+#pragma unroll
+        for (int s = 0; s < NS; ++s) b_hc[s] = *ckpt_in(ck, s);
+        fetch_bc(ck, b_bc);
+    };
+    if (nck > 0) fetch_bwd(nck - 1);
     for (int ck = nck - 1; ck >= 0; --ck) {
         const int t0 = ck * kTC;
         // stage (delta, delta*u, u, g) -- the row thread keeps its own tokens
-        float uu[kTPT], zz[kTPT], go[kTPT], gg[kTPT];
+        float uu[kTPT], zz[kTPT], go[kTPT], gg[kTPT], dlv[kTPT], hc[NS];
 #pragma unroll
         for (int j = 0; j < kTPT; ++j) {
             const int t = t0 + toff + j;
-            const float dl = ld(dl_in, t);
-            uu[j] = ld(u_in, t);
-            go[j] = ld(go_in, t);
-            zz[j] = z_in ? ld(z_in, t) : 0.f;
-            gg[j] = z_in ? go[j] * silu(zz[j]) : go[j];
-            s_tk[toff + j][cr] = make_float4(dl, dl * uu[j], uu[j], gg[j]);
+            dlv[j] = rv(b_dl[j], t);
+            uu[j] = rv(b_u[j], t);
+            go[j] = rv(b_go[j], t);
+            zz[j] = z_in ? rv(b_z[j], t) : 0.f;
         }
-        float hc[NS];
 #pragma unroll
-        for (int s = 0; s < NS; ++s) hc[s] = (cval && w * NS + s < N) ? *ckpt(ck, s) : 0.f;
-        load_bc(t0);
+        for (int s = 0; s < NS; ++s) hc[s] = (cval && w * NS + s < N) ? b_hc[s] : 0.f;
+        T bcv[kBPT];
+#pragma unroll
+        for (int q = 0; q < kBPT; ++q) bcv[q] = b_bc[q];
+        if (ck > 0) fetch_bwd(ck - 1);
+        stage_bc(ck, bcv);
+#pragma unroll
+        for (int j = 0; j < kTPT; ++j) {
+            gg[j] = z_in ? go[j] * silu(zz[j]) : go[j];
+            s_tk[toff + j][cr] = make_float4(dlv[j], dlv[j] * uu[j], uu[j], gg[j]);
+        }
         __syncthreads();
+        read_bc();
 
-        // recompute the chunk's states; per-wave partial outputs to LDS
-        float hs[kTC][NS];
+        // recompute the chunk's states and decay factors (the factors are kept
+        // for the walk when registers allow: NS <= 4); per-wave partial
+        // outputs to LDS
+        constexpr bool kKeepA = NS <= 4;
+        float hs[kTC][NS], as[kKeepA ? kTC : 1][NS];
         {
             float hh[NS];
 #pragma unroll
@@ -236,7 +311,9 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
                 float yp = 0.f;
 #pragma unroll
                 for (int s = 0; s < NS; ++s) {
-                    hh[s] = fmaf(fast_exp2(q.x * a2[s]), hh[s], q.y * Bf[s][k]);
+                    const float e = fast_exp2(q.x * a2[s]);
+                    if constexpr (kKeepA) as[k][s] = e;
+                    hh[s] = fmaf(e, hh[s], q.y * Bf[s][k]);
                     hs[k][s] = hh[s];
                     yp = fmaf(Cf[s][k], hh[s], yp);
                 }
@@ -278,7 +355,9 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
                 const float bv = Bf[s][k], cv = Cf[s][k];
                 const float lt = fmaf(q.w, cv, lam[s]);
                 const float hp = k > 0 ? hs[k > 0 ? k - 1 : 0][s] : hc[s];
-                const float a = fast_exp2(q.x * a2[s]);
+                float a;
+                if constexpr (kKeepA) a = as[k][s];
+                else a = fast_exp2(q.x * a2[s]);
                 v[2 * s] = lt * q.y;
                 v[2 * s + 1] = q.w * hs[k][s];
                 dup = fmaf(lt * q.x, bv, dup);
@@ -382,10 +461,7 @@ hipError_t zero(float* a, int64_t n, hipStream_t stream) {
 template <typename T, int NS>
 hipError_t launch_ns(const S6BwdParams& p, hipStream_t stream) {
     const int64_t blocks = ((p.dim + 63) / 64) * p.batch;
-    if (p.L % 8 == 0)
-        hipLaunchKernelGGL((s6_scan_bwd_kernel<T, NS, true>), dim3((unsigned)blocks), dim3(kNW * 64), 0, stream, p);
-    else
-        hipLaunchKernelGGL((s6_scan_bwd_kernel<T, NS, false>), dim3((unsigned)blocks), dim3(kNW * 64), 0, stream, p);
+    hipLaunchKernelGGL((s6_scan_bwd_kernel<T, NS>), dim3((unsigned)blocks), dim3(kNW * 64), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     constexpr int kTC = ChunkLen<NS>::value;
