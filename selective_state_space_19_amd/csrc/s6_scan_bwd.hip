@@ -95,7 +95,8 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
     __shared__ float4 s_tk[kTC][64 + 1];          // (delta, delta*u, u, g) per token and channel
     __shared__ float s_y[kNW][kTC][64 + 1];       // per-wave partial sum_n C h
     __shared__ float2 s_p[kNW][kTC][64 + 1];      // per-wave partial (du, ddelta)
-    __shared__ __align__(16) float s_bc[2][kNW * NS][kTC];   // the chunk's B (0) and C (1) rows
+    __shared__ __align__(16) float s_bc[2][2][kNW * NS][kTC];   // [buffer][B 0 / C 1][state][token]
+    __shared__ float2 s_fw[2][kTC][64 + 1];       // forward sweep: (delta, delta*u), double-buffered
 
     const T* u_in = static_cast<const T*>(p.u);
     const T* dl_in = static_cast<const T*>(p.delta);
@@ -157,7 +158,7 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
             r[q] = (m ? C_in : B_in)[(b * N + (n < N ? n : N - 1)) * (int64_t)L + (t < L ? t : L - 1)];
         }
     };
-    auto stage_bc = [&](int ck, const T (&r)[kBPT]) {
+    auto stage_bc = [&](int ck, const T (&r)[kBPT], int buf) {
 #pragma unroll
         for (int q = 0; q < kBPT; ++q) {
             const int i = tid + q * kNW * 64;
@@ -165,17 +166,17 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
                 int m, n, k;
                 bc_index(i, m, n, k);
                 const float v = widen(r[q]);
-                s_bc[m][n][k] = (n < N && ck * kTC + k < L) ? v : 0.f;
+                s_bc[buf][m][n][k] = (n < N && ck * kTC + k < L) ? v : 0.f;
             }
         }
     };
-    auto read_bc = [&]() {
+    auto read_bc = [&](int buf) {
 #pragma unroll
         for (int s = 0; s < NS; ++s)
 #pragma unroll
             for (int k = 0; k < kTC; k += 4) {
-                const float4 x = *reinterpret_cast<const float4*>(&s_bc[0][w * NS + s][k]);
-                const float4 y = *reinterpret_cast<const float4*>(&s_bc[1][w * NS + s][k]);
+                const float4 x = *reinterpret_cast<const float4*>(&s_bc[buf][0][w * NS + s][k]);
+                const float4 y = *reinterpret_cast<const float4*>(&s_bc[buf][1][w * NS + s][k]);
                 Bf[s][k] = x.x; Bf[s][k + 1] = x.y; Bf[s][k + 2] = x.z; Bf[s][k + 3] = x.w;
                 Cf[s][k] = y.x; Cf[s][k + 1] = y.y; Cf[s][k + 2] = y.z; Cf[s][k + 3] = y.w;
             }
@@ -217,37 +218,45 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
         }
         fetch_bc(ck, f_bc);
     };
-    if (nck > 0) fetch_fwd(0);
-    for (int ck = 0; ck < nck; ++ck) {
-        const int t0 = ck * kTC;
+    // Staging of chunk ck into buffer ck & 1 (and the fetch of chunk ck + 1);
+    // chunk ck + 1 is staged right after chunk ck is scanned, so one barrier
+    // per chunk suffices.
+    auto stage_fwd = [&](int ck) {
         float dlv[kTPT], uv[kTPT];
         T bcv[kBPT];
 #pragma unroll
         for (int j = 0; j < kTPT; ++j) {
-            dlv[j] = rv(f_dl[j], t0 + toff + j);
-            uv[j] = rv(f_u[j], t0 + toff + j);
+            dlv[j] = rv(f_dl[j], ck * kTC + toff + j);
+            uv[j] = rv(f_u[j], ck * kTC + toff + j);
         }
 #pragma unroll
         for (int q = 0; q < kBPT; ++q) bcv[q] = f_bc[q];
         if (ck + 1 < nck) fetch_fwd(ck + 1);
-        stage_bc(ck, bcv);
+        stage_bc(ck, bcv, ck & 1);
 #pragma unroll
-        for (int j = 0; j < kTPT; ++j) s_tk[toff + j][cr] = make_float4(dlv[j], dlv[j] * uv[j], 0.f, 0.f);
+        for (int j = 0; j < kTPT; ++j) s_fw[ck & 1][toff + j][cr] = make_float2(dlv[j], dlv[j] * uv[j]);
+    };
+    if (nck > 0) {
+        fetch_fwd(0);
+        stage_fwd(0);
+    }
+    for (int ck = 0; ck < nck; ++ck) {
         if (cval) {
 #pragma unroll
             for (int s = 0; s < NS; ++s)
                 if (w * NS + s < N) *ckpt(ck, s) = h[s];
         }
-        __syncthreads();
-        read_bc();
+        __syncthreads();                          // chunk ck staged; buffer (ck + 1) & 1 free
+        read_bc(ck & 1);
 #pragma unroll
         for (int k = 0; k < kTC; ++k) {
-            const float4 q = s_tk[k][cs];
+            const float2 q = s_fw[ck & 1][k][cs];
 #pragma unroll
             for (int s = 0; s < NS; ++s) h[s] = fmaf(fast_exp2(q.x * a2[s]), h[s], q.y * Bf[s][k]);
         }
-        __syncthreads();
+        if (ck + 1 < nck) stage_fwd(ck + 1);
     }
+    __syncthreads();                              // the backward sweep reuses the B / C buffers
 
     // ================= 2. backward sweep, last chunk first =======================
     // The row data and the chunk-start states of the next chunk (ck - 1) are
@@ -287,14 +296,14 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
 #pragma unroll
         for (int q = 0; q < kBPT; ++q) bcv[q] = b_bc[q];
         if (ck > 0) fetch_bwd(ck - 1);
-        stage_bc(ck, bcv);
+        stage_bc(ck, bcv, 0);
 #pragma unroll
         for (int j = 0; j < kTPT; ++j) {
             gg[j] = z_in ? go[j] * silu(zz[j]) : go[j];
             s_tk[toff + j][cr] = make_float4(dlv[j], dlv[j] * uu[j], uu[j], gg[j]);
         }
         __syncthreads();
-        read_bc();
+        read_bc(0);
 
         // recompute the chunk's states and decay factors (the factors are kept
         // for the walk when registers allow: NS <= 4); per-wave partial
