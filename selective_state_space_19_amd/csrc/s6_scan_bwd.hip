@@ -34,6 +34,8 @@
 //      ddelta are summed over the waves through LDS by the row threads.
 //   dA and dD are accumulated in registers and added with atomics at the end
 //   (the entry point zeroes them first).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -88,7 +90,10 @@ constexpr int log2i(int n) { return n <= 1 ? 0 : 1 + log2i(n / 2); }
 __device__ __forceinline__ float widen(float v) { return v; }
 __device__ __forceinline__ float widen(uint16_t v) { return __uint_as_float(uint32_t(v) << 16); }
 
-template <typename T, int NS>
+// BUF (L even, a block's rows addressable with 32-bit offsets): each row
+// thread reads its two tokens with one buffer load per array; offsets past the
+// sequence or past the block's rows read zero.  Otherwise element loads.
+template <typename T, int NS, bool BUF>
 __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
     constexpr int kTC = ChunkLen<NS>::value;
     constexpr int kTPT = kTC / kSegs;      // tokens per row thread
@@ -197,25 +202,53 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
     const bool rval = cr < nrows;
     const int64_t rrow = (b * dim + d0 + (rval ? cr : 0)) * (int64_t)L;   // first element of this row
     const float dskip = (rval && p.Dskip) ? p.Dskip[d0 + cr] : 0.f;
-    // Row loads issued a chunk ahead: unconditional (clamped address) and
-    // left untouched until the next chunk uses them (touching a loaded value
-    // waits for it); `rv` then replaces a value past the end by 0.
-    // The raw element is kept (a conversion would be a use) and widened by
-    // `rv`.  Without z, u's row is read in its place and ignored.
-    auto ld = [&](const T* base, int t) -> T { return base[rrow + (t < L ? t : L - 1)]; };
-    auto rv = [&](T raw, int t) -> float { return (rval && t < L) ? widen(raw) : 0.f; };
+    // Row loads issued a chunk ahead: unconditional and left untouched until
+    // the next chunk uses them (touching a loaded value waits for it).  A
+    // thread's kTPT (1 or 2) tokens are kept raw as one Pair and widened by
+    // `rv`, which also gives 0 past the end.  Without z, u's row is read in
+    // its place and ignored.
+    static_assert(kTPT == 1 || kTPT == 2, "one or two tokens per row thread");
+    using Pair = typename std::conditional<sizeof(T) == 2 || kTPT == 1, uint32_t, uint2>::type;
     const T* zl_in = z_in ? z_in : u_in;
+    const int64_t blk0 = (b * dim + d0) * (int64_t)L;
+    const uint32_t blk_bytes = BUF ? (uint32_t)nrows * (uint32_t)L * (uint32_t)sizeof(T) : 0u;
+    const rsrc_t rs_dl = make_rsrc(dl_in + blk0, blk_bytes), rs_u = make_rsrc(u_in + blk0, blk_bytes);
+    const rsrc_t rs_go = make_rsrc(go_in + blk0, blk_bytes), rs_z = make_rsrc(zl_in + blk0, blk_bytes);
+    auto ld = [&](const T* base, rsrc_t rs, int t) -> Pair {       // tokens t, t + 1 (t even)
+        if constexpr (BUF) {
+            const uint32_t off = off_if(t < L, ((uint32_t)cr * (uint32_t)L + (uint32_t)t) * (uint32_t)sizeof(T));
+            if constexpr (sizeof(T) * kTPT == 2) return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0);
+            else if constexpr (sizeof(T) * kTPT == 4) return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
+            else return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0));
+        } else {
+            const T e0 = base[rrow + (t < L ? t : L - 1)];
+            if constexpr (kTPT == 1) {
+                if constexpr (sizeof(T) == 2) return (uint32_t)e0;
+                else return __float_as_uint(e0);
+            } else {
+                const T e1 = base[rrow + (t + 1 < L ? t + 1 : L - 1)];
+                if constexpr (sizeof(T) == 2) return (uint32_t)e0 | ((uint32_t)e1 << 16);
+                else return make_uint2(__float_as_uint(e0), __float_as_uint(e1));
+            }
+        }
+    };
+    auto rv = [&](Pair raw, int j, int t) -> float {
+        float v;
+        if constexpr (sizeof(T) == 2) v = __uint_as_float(j ? (raw & 0xffff0000u) : (raw << 16));
+        else if constexpr (kTPT == 1) v = __uint_as_float(raw);
+        else v = __uint_as_float(j ? raw.y : raw.x);
+        if constexpr (BUF) return v;
+        else return (rval && t < L) ? v : 0.f;
+    };
 
     // ================= 1. forward sweep: chunk-start checkpoints =================
     // (delta, u) of the next chunk are loaded while this one is scanned.
-    T f_dl[kTPT], f_u[kTPT], f_bc[kBPT];
+    Pair f_dl, f_u;
+    T f_bc[kBPT];
     auto fetch_fwd = [&](int ck) {
-#pragma unroll
-        for (int j = 0; j < kTPT; ++j) {
-            const int t = ck * kTC + toff + j;
-            f_dl[j] = ld(dl_in, t);
-            f_u[j] = ld(u_in, t);
-        }
+        const int t = ck * kTC + toff;
+        f_dl = ld(dl_in, rs_dl, t);
+        f_u = ld(u_in, rs_u, t);
         fetch_bc(ck, f_bc);
     };
     // Staging of chunk ck into buffer ck & 1 (and the fetch of chunk ck + 1);
@@ -226,8 +259,8 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
         T bcv[kBPT];
 #pragma unroll
         for (int j = 0; j < kTPT; ++j) {
-            dlv[j] = rv(f_dl[j], ck * kTC + toff + j);
-            uv[j] = rv(f_u[j], ck * kTC + toff + j);
+            dlv[j] = rv(f_dl, j, ck * kTC + toff + j);
+            uv[j] = rv(f_u, j, ck * kTC + toff + j);
         }
 #pragma unroll
         for (int q = 0; q < kBPT; ++q) bcv[q] = f_bc[q];
@@ -262,17 +295,15 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
     // The row data and the chunk-start states of the next chunk (ck - 1) are
     // loaded while this one is processed.
     float dDacc = 0.f;
-    T b_dl[kTPT], b_u[kTPT], b_go[kTPT], b_z[kTPT], b_bc[kBPT];
+    Pair b_dl, b_u, b_go, b_z;
+    T b_bc[kBPT];
     float b_hc[NS];
     auto fetch_bwd = [&](int ck) {
-#pragma unroll
-        for (int j = 0; j < kTPT; ++j) {
-            const int t = ck * kTC + toff + j;
-            b_dl[j] = ld(dl_in, t);
-            b_u[j] = ld(u_in, t);
-            b_go[j] = ld(go_in, t);
-            b_z[j] = ld(zl_in, t);
-        }
+        const int t = ck * kTC + toff;
+        b_dl = ld(dl_in, rs_dl, t);
+        b_u = ld(u_in, rs_u, t);
+        b_go = ld(go_in, rs_go, t);
+        b_z = ld(zl_in, rs_z, t);
 #pragma unroll
         for (int s = 0; s < NS; ++s) b_hc[s] = *ckpt_in(ck, s);
         fetch_bc(ck, b_bc);
@@ -285,10 +316,10 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
 #pragma unroll
         for (int j = 0; j < kTPT; ++j) {
             const int t = t0 + toff + j;
-            dlv[j] = rv(b_dl[j], t);
-            uu[j] = rv(b_u[j], t);
-            go[j] = rv(b_go[j], t);
-            zz[j] = z_in ? rv(b_z[j], t) : 0.f;
+            dlv[j] = rv(b_dl, j, t);
+            uu[j] = rv(b_u, j, t);
+            go[j] = rv(b_go, j, t);
+            zz[j] = z_in ? rv(b_z, j, t) : 0.f;
         }
 #pragma unroll
         for (int s = 0; s < NS; ++s) hc[s] = (cval && w * NS + s < N) ? b_hc[s] : 0.f;
@@ -470,7 +501,11 @@ hipError_t zero(float* a, int64_t n, hipStream_t stream) {
 template <typename T, int NS>
 hipError_t launch_ns(const S6BwdParams& p, hipStream_t stream) {
     const int64_t blocks = ((p.dim + 63) / 64) * p.batch;
-    hipLaunchKernelGGL((s6_scan_bwd_kernel<T, NS>), dim3((unsigned)blocks), dim3(kNW * 64), 0, stream, p);
+    const bool buf = p.L % 2 == 0 && int64_t(64) * p.L * int64_t(sizeof(T)) < (int64_t(1) << 31);
+    if (buf)
+        hipLaunchKernelGGL((s6_scan_bwd_kernel<T, NS, true>), dim3((unsigned)blocks), dim3(kNW * 64), 0, stream, p);
+    else
+        hipLaunchKernelGGL((s6_scan_bwd_kernel<T, NS, false>), dim3((unsigned)blocks), dim3(kNW * 64), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     constexpr int kTC = ChunkLen<NS>::value;

@@ -51,6 +51,9 @@ CASES = [
     (2, 100, 200, 16, "bf16", True, True, True, True),
     (1, 130, 301, 16, "bf16", True, False, True, False),
     (2, 64, 96, 8, "bf16", False, True, False, True),
+    # odd lengths with 8-token chunks (one token per row thread)
+    (1, 70, 77, 32, "f32", True, True, True, True),
+    (2, 64, 33, 64, "bf16", True, True, False, True),
 ]
 
 
