@@ -86,6 +86,8 @@ __device__ __forceinline__ void tree(float (&v)[CAP]) {
 
 constexpr int log2i(int n) { return n <= 1 ? 0 : 1 + log2i(n / 2); }
 
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
 // An element of type T widened to float (bf16: the upper half of a float).
 __device__ __forceinline__ float widen(float v) { return v; }
 __device__ __forceinline__ float widen(uint16_t v) { return __uint_as_float(uint32_t(v) << 16); }
@@ -232,6 +234,26 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
             }
         }
     };
+    // Store the thread's kTPT values of one output row (BUF: one buffer store;
+    // offsets past the sequence or the block's rows are dropped).
+    auto st = [&](T* base, int t, const float (&v)[kTPT]) {
+        if constexpr (BUF) {
+            const rsrc_t rs = make_rsrc(base + blk0, blk_bytes);
+            const uint32_t off = off_if(t < L, ((uint32_t)cr * (uint32_t)L + (uint32_t)t) * (uint32_t)sizeof(T));
+            if constexpr (sizeof(T) == 2 && kTPT == 1)
+                __builtin_amdgcn_raw_buffer_store_b16(to_bf16(v[0]), rs, off, 0, 0);
+            else if constexpr (sizeof(T) == 2)
+                __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(v[0], v[1]), rs, off, 0, 0);
+            else if constexpr (kTPT == 1)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[0]), rs, off, 0, 0);
+            else
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{__float_as_uint(v[0]), __float_as_uint(v[1])}, rs, off, 0, 0);
+        } else {
+#pragma unroll
+            for (int j = 0; j < kTPT; ++j)
+                if (rval && t + j < L) Elem<T>::store1(base + rrow + t + j, v[j]);
+        }
+    };
     auto rv = [&](Pair raw, int j, int t) -> float {
         float v;
         if constexpr (sizeof(T) == 2) v = __uint_as_float(j ? (raw & 0xffff0000u) : (raw << 16));
@@ -363,19 +385,18 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
         __syncthreads();
 
         // row threads: y, dz, dD
+        float dzv[kTPT];
 #pragma unroll
         for (int j = 0; j < kTPT; ++j) {
-            const int t = t0 + toff + j;
             float y = dskip * uu[j];
 #pragma unroll
             for (int q = 0; q < kNW; ++q) y += s_y[q][toff + j][cr];
-            if (z_in && rval && t < L) {
-                const float e = fast_exp2(-zz[j] * kLog2e);
-                const float sg = __builtin_amdgcn_rcpf(1.f + e);
-                Elem<T>::store1(static_cast<T*>(p.dz) + rrow + t, go[j] * y * (sg * (1.f + zz[j] * (1.f - sg))));
-            }
+            const float e = fast_exp2(-zz[j] * kLog2e);
+            const float sg = __builtin_amdgcn_rcpf(1.f + e);
+            dzv[j] = go[j] * y * (sg * (1.f + zz[j] * (1.f - sg)));
             dDacc = fmaf(gg[j], uu[j], dDacc);
         }
+        if (z_in) st(static_cast<T*>(p.dz), t0 + toff, dzv);
 
         // walk the chunk backwards.  dB / dC of (state s, token k) summed over
         // the wave's 64 channels: value index ((s 2 + c) kTC + k), c 0 for B
@@ -422,21 +443,20 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
         __syncthreads();
 
         // row threads: du, ddelta
+        float duv[kTPT], ddv[kTPT];
 #pragma unroll
         for (int j = 0; j < kTPT; ++j) {
-            const int t = t0 + toff + j;
-            float du = gg[j] * dskip, dd = 0.f;
+            duv[j] = gg[j] * dskip;
+            ddv[j] = 0.f;
 #pragma unroll
             for (int q = 0; q < kNW; ++q) {
                 const float2 v = s_p[q][toff + j][cr];
-                du += v.x;
-                dd += v.y;
-            }
-            if (rval && t < L) {
-                Elem<T>::store1(static_cast<T*>(p.du) + rrow + t, du);
-                Elem<T>::store1(static_cast<T*>(p.ddelta) + rrow + t, dd);
+                duv[j] += v.x;
+                ddv[j] += v.y;
             }
         }
+        st(static_cast<T*>(p.du), t0 + toff, duv);
+        st(static_cast<T*>(p.ddelta), t0 + toff, ddv);
     }
 
     // ---- ends: dh0, dA, dD -------------------------------------------------------
