@@ -151,7 +151,10 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(const uint16_t* __restric
 //     off the output waves' path.  Every LDS buffer a chunk is read from is
 //     double-buffered by chunk parity: one barrier per chunk.
 // ---------------------------------------------------------------------------
-template <int Q, int N>
+// HASZ: a gate z is given.  Loads for the chunk after the last read zeros
+// through zero-size buffer resources (no branches around loads, which would
+// make the compiler's wait counting fall back to waiting for everything).
+template <int Q, int N, bool HASZ>
 __global__ __launch_bounds__(512) void ssd_main_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ DT, const float* __restrict__ Ah,
     const uint16_t* __restrict__ Cm, const float* __restrict__ Dh, const uint16_t* __restrict__ Z,
@@ -222,7 +225,8 @@ __global__ __launch_bounds__(512) void ssd_main_kernel(
         uint32_t zz[2][8];
         auto load_g = [&](int cc, int rb) {
             const int I = wr + 4 * rb;
-            const rsrc_t rG = make_rsrc(Gw + (((int64_t)b * nc + cc) * G + g) * Q * Q, gbytes);
+            const rsrc_t rG = make_rsrc(Gw + (((int64_t)b * nc + (cc < nc ? cc : 0)) * G + g) * Q * Q,
+                                        cc < nc ? gbytes : 0u);
             const uint32_t gb = ((uint32_t)(16 * I + m) * Q + 8 * kg) * 2u;
             const uint32_t glast = off_if(jhi != 0, gb + 64u * (2 * rb + 1));
 #pragma unroll
@@ -235,7 +239,7 @@ __global__ __launch_bounds__(512) void ssd_main_kernel(
             const uint32_t cb = off_if(t < L, (uint32_t)t * crow + (uint32_t)g * N * 2u + 16u * kg);
 #pragma unroll
             for (int nk = 0; nk < NKB; ++nk) ca[sl][nk] = gload128(rC, cb + 64u * nk);
-            if (Z) {
+            if constexpr (HASZ) {
                 const int I = wr + 4 * rb;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -271,11 +275,13 @@ __global__ __launch_bounds__(512) void ssd_main_kernel(
                 const float si0 = s_s[pb][i0];
 #pragma unroll
                 for (int J = 0; J <= 2 * rb; ++J) {
+                    // J = 2 rb is off-diagonal only for the waves with jhi = 1;
+                    // the others scale its tile by 0 (no branch)
                     if (J < Jd) {
-                        const u32x4_t a = scale_bf16x8(gt[J], fast_exp2(si0 - send(pb, J)));
+                    const u32x4_t a = scale_bf16x8(gt[J], fast_exp2(si0 - send(pb, J)));
 #pragma unroll
-                        for (int pt = 0; pt < 2; ++pt)
-                            off_[pt] = mfma16(a, lds128(&xsT[pb][16 * pt + m][16 * J + 4 * kg]), off_[pt]);
+                    for (int pt = 0; pt < 2; ++pt)
+                        off_[pt] = mfma16(a, lds128(&xsT[pb][16 * pt + m][16 * J + 4 * kg]), off_[pt]);
                     }
                 }
                 // diagonal token block: mask built element by element, dt folded in, plain x
@@ -312,11 +318,11 @@ __global__ __launch_bounds__(512) void ssd_main_kernel(
                     for (int pt = 0; pt < 2; ++pt)
                         yo[pt] = mfma16(ca[sl][nk], lds128(&Hb[pb][16 * pt + m][16 * nk + 4 * kg]), yo[pt]);
                 // this row block's G tiles for the next chunk
-                if (c + 1 < nc) load_g(c + 1, rb);
+                load_g(c + 1, rb);
                 // Next chunk's row block 0 goes to slot 0; with one row block
                 // per wave that slot still holds the gate values read below.
                 if constexpr (RBW > 1)
-                    if (rb + 1 == RBW && c + 1 < nc) load_cz(c + 1, 0, 0);
+                    if (rb + 1 == RBW) load_cz(c + 1, 0, 0);
                 // combine, skip, gate; the tile goes through LDS so that each
                 // lane stores 8 consecutive head channels of one token (16 bytes).
                 uint16_t* yt16 = reinterpret_cast<uint16_t*>(&ytile[wr][0][0]);
@@ -331,7 +337,7 @@ __global__ __launch_bounds__(512) void ssd_main_kernel(
                         const uint32_t xw = xT[pb][16 * pt + m][i >> 1];
                         const float xv = __uint_as_float((i & 1) ? (xw & 0xffff0000u) : (xw << 16));
                         float yv = al * off_[pt][r] + dg[pt][r] + ei * yo[pt][r] + dskip * xv;
-                        if (Z) yv *= silu(__uint_as_float(zz[sl][2 * r + pt] << 16));
+                        if constexpr (HASZ) yv *= silu(__uint_as_float(zz[sl][2 * r + pt] << 16));
                         yt16[(4 * kg + r) * kPW + 16 * pt + m] = to_bf16(yv);
                     }
                 }
@@ -349,7 +355,7 @@ __global__ __launch_bounds__(512) void ssd_main_kernel(
                 __builtin_amdgcn_wave_barrier();
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
                 if constexpr (RBW == 1)
-                    if (c + 1 < nc) load_cz(c + 1, 0, 0);
+                    load_cz(c + 1, 0, 0);
             }
             __syncthreads();
         }
@@ -396,7 +402,8 @@ __global__ __launch_bounds__(512) void ssd_main_kernel(
         constexpr int BSL = NBW < 2 ? NBW : 2;
         u32x4_t ba[BSL][KB];
         auto load_bt = [&](int cc, int k) {
-            const rsrc_t rBT = make_rsrc(BTw + (((int64_t)b * nc + cc) * G + g) * N * Q, btbytes);
+            const rsrc_t rBT = make_rsrc(BTw + (((int64_t)b * nc + (cc < nc ? cc : 0)) * G + g) * N * Q,
+                                         cc < nc ? btbytes : 0u);
             const int nb = wr + 4 * k;
             const uint32_t base = off_if(nb < NB, ((uint32_t)(16 * nb + m) * Q + 8 * kg) * 2u);
 #pragma unroll
@@ -519,12 +526,11 @@ __global__ __launch_bounds__(512) void ssd_main_kernel(
                 }
                 if (k + BSL < NBW) load_bt(c, k + BSL);
             }
-            if (c + 1 < nc) {
-                load_bt_ahead(c + 1);
-                write_hb(pb ^ 1);
-                s_end = stage_store(pb ^ 1);
-                if (c + 2 < nc) stage_load(c + 2);
-            }
+            // the next chunk (past the last one: zeros, results unused)
+            load_bt_ahead(c + 1);
+            write_hb(pb ^ 1);
+            s_end = stage_store(pb ^ 1);
+            stage_load(c + 2);
             __syncthreads();
         }
         if (hT) {
@@ -547,6 +553,7 @@ __global__ __launch_bounds__(512) void ssd_main_kernel(
 
 template <int Q, int N>
 hipError_t launch_qn(const SSDParams& p, hipStream_t stream) {
+    auto kern = p.z ? ssd_main_kernel<Q, N, true> : ssd_main_kernel<Q, N, false>;
     const int nc = (p.L + Q - 1) / Q;
     uint16_t* Gw = static_cast<uint16_t*>(p.workspace);
     uint16_t* BTw = Gw + (int64_t)p.batch * nc * p.G * Q * Q;
@@ -556,7 +563,7 @@ hipError_t launch_qn(const SSDParams& p, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t blocks = p.batch * p.H * 2;
-    hipLaunchKernelGGL((ssd_main_kernel<Q, N>), dim3((unsigned)blocks), dim3(512), 0, stream,
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(512), 0, stream,
                        static_cast<const uint16_t*>(p.x), static_cast<const uint16_t*>(p.dt), p.A,
                        static_cast<const uint16_t*>(p.Cm), p.Dskip, static_cast<const uint16_t*>(p.z), p.h0,
                        static_cast<uint16_t*>(p.y), p.h_final, Gw, BTw, p.L, p.H, p.G, nc);
