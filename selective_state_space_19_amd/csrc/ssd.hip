@@ -227,7 +227,10 @@ __global__ __launch_bounds__(512) void ssd_main_kernel(
             const int I = wr + 4 * rb;
             const rsrc_t rG = make_rsrc(Gw + (((int64_t)b * nc + (cc < nc ? cc : 0)) * G + g) * Q * Q,
                                         cc < nc ? gbytes : 0u);
-            const uint32_t gb = ((uint32_t)(16 * I + m) * Q + 8 * kg) * 2u;
+            // recomputed per call (volatile asm): the tile offsets then go in
+            // the loads' immediate field instead of 20 registers held across chunks
+            uint32_t gb = ((uint32_t)(16 * I + m) * Q + 8 * kg) * 2u;
+            asm volatile("" : "+v"(gb));
             const uint32_t glast = off_if(jhi != 0, gb + 64u * (2 * rb + 1));
 #pragma unroll
             for (int J = 0; J <= 2 * rb + 1; ++J)
@@ -269,31 +272,55 @@ __global__ __launch_bounds__(512) void ssd_main_kernel(
                 f32x4_t off_[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
                 f32x4_t dg[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
                 f32x4_t yo[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+                // Every LDS operand is read one step ahead of the MFMAs that
+                // use it (the sched_barriers keep the compiler from sinking the
+                // reads back next to their use, which would expose each read's
+                // latency in turn).
+                const float si0 = s_s[pb][i0];
+                float se[2 * RBW];
+#pragma unroll
+                for (int J = 0; J <= 2 * rb; ++J) se[J] = send(pb, J);
+                u32x4_t xb[2][2];
+#pragma unroll
+                for (int pt = 0; pt < 2; ++pt) xb[0][pt] = lds128(&xsT[pb][16 * pt + m][4 * kg]);
                 // off-diagonal token blocks J < Jd: the G tile is scaled by the
                 // decay from the end of block J to the first row of block I
                 // (<= 1), so the MFMAs accumulate back to back.
-                const float si0 = s_s[pb][i0];
 #pragma unroll
                 for (int J = 0; J <= 2 * rb; ++J) {
-                    // J = 2 rb is off-diagonal only for the waves with jhi = 1;
-                    // the others scale its tile by 0 (no branch)
-                    if (J < Jd) {
-                    const u32x4_t a = scale_bf16x8(gt[J], fast_exp2(si0 - send(pb, J)));
+                    if (J < 2 * rb) {
 #pragma unroll
-                    for (int pt = 0; pt < 2; ++pt)
-                        off_[pt] = mfma16(a, lds128(&xsT[pb][16 * pt + m][16 * J + 4 * kg]), off_[pt]);
+                        for (int pt = 0; pt < 2; ++pt)
+                            xb[(J + 1) & 1][pt] = lds128(&xsT[pb][16 * pt + m][16 * (J + 1) + 4 * kg]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (J < Jd) {                // J = 2 rb: off-diagonal for jhi = 1 only
+                        const u32x4_t a = scale_bf16x8(gt[J], fast_exp2(si0 - se[J]));
+#pragma unroll
+                        for (int pt = 0; pt < 2; ++pt) off_[pt] = mfma16(a, xb[J & 1][pt], off_[pt]);
                     }
                 }
+                // operands of the diagonal block and of C H_in^T
+                const int i = i0 + m;
+                const float si = s_s[pb][i];
+                const int j0 = 32 * Jd + 8 * kg;
+                const float4 d0 = *reinterpret_cast<const float4*>(&s_dt[pb][j0]);
+                const float4 d1 = *reinterpret_cast<const float4*>(&s_dt[pb][j0 + 4]);
+                const float4 q0 = *reinterpret_cast<const float4*>(&s_s[pb][j0]);
+                const float4 q1 = *reinterpret_cast<const float4*>(&s_s[pb][j0 + 4]);
+                u32x4_t xd[2], hb[2][2];
+                uint2 xr[2];                     // x of this lane's output rows (skip term)
+#pragma unroll
+                for (int pt = 0; pt < 2; ++pt) {
+                    xd[pt] = lds128(&xT[pb][16 * pt + m][16 * Jd + 4 * kg]);
+                    hb[0][pt] = lds128(&Hb[pb][16 * pt + m][4 * kg]);
+                    xr[pt] = *reinterpret_cast<const uint2*>(&xT[pb][16 * pt + m][(i0 + 4 * kg) >> 1]);
+                }
+                const float4 sr = *reinterpret_cast<const float4*>(&s_s[pb][i0 + 4 * kg]);
+                __builtin_amdgcn_sched_barrier(0);
                 // diagonal token block: mask built element by element, dt folded in, plain x
                 {
-                    const int i = i0 + m;
-                    const float si = s_s[pb][i];
                     const u32x4_t gv = jhi ? gt[2 * rb + 1] : gt[2 * rb];
-                    const int j0 = 32 * Jd + 8 * kg;
-                    const float4 d0 = *reinterpret_cast<const float4*>(&s_dt[pb][j0]);
-                    const float4 d1 = *reinterpret_cast<const float4*>(&s_dt[pb][j0 + 4]);
-                    const float4 q0 = *reinterpret_cast<const float4*>(&s_s[pb][j0]);
-                    const float4 q1 = *reinterpret_cast<const float4*>(&s_s[pb][j0 + 4]);
                     const float dj[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
                     const float sj[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
                     uint32_t av[4];
@@ -308,15 +335,20 @@ __global__ __launch_bounds__(512) void ssd_main_kernel(
                     }
                     const u32x4_t a = {av[0], av[1], av[2], av[3]};
 #pragma unroll
-                    for (int pt = 0; pt < 2; ++pt)
-                        dg[pt] = mfma16(a, lds128(&xT[pb][16 * pt + m][16 * Jd + 4 * kg]), dg[pt]);
+                    for (int pt = 0; pt < 2; ++pt) dg[pt] = mfma16(a, xd[pt], dg[pt]);
                 }
                 // carried-in state: C rows times H_in^T
 #pragma unroll
-                for (int nk = 0; nk < NKB; ++nk)
+                for (int nk = 0; nk < NKB; ++nk) {
+                    if (nk + 1 < NKB) {
 #pragma unroll
-                    for (int pt = 0; pt < 2; ++pt)
-                        yo[pt] = mfma16(ca[sl][nk], lds128(&Hb[pb][16 * pt + m][16 * nk + 4 * kg]), yo[pt]);
+                        for (int pt = 0; pt < 2; ++pt)
+                            hb[(nk + 1) & 1][pt] = lds128(&Hb[pb][16 * pt + m][16 * (nk + 1) + 4 * kg]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int pt = 0; pt < 2; ++pt) yo[pt] = mfma16(ca[sl][nk], hb[nk & 1][pt], yo[pt]);
+                }
                 // this row block's G tiles for the next chunk
                 load_g(c + 1, rb);
                 // Next chunk's row block 0 goes to slot 0; with one row block
@@ -326,16 +358,15 @@ __global__ __launch_bounds__(512) void ssd_main_kernel(
                 // combine, skip, gate; the tile goes through LDS so that each
                 // lane stores 8 consecutive head channels of one token (16 bytes).
                 uint16_t* yt16 = reinterpret_cast<uint16_t*>(&ytile[wr][0][0]);
+                const float srv[4] = {sr.x, sr.y, sr.z, sr.w};
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int i = i0 + 4 * kg + r;
-                    const float si = s_s[pb][i];
-                    const float al = fast_exp2(si - si0);
-                    const float ei = fast_exp2(si);
+                    const float al = fast_exp2(srv[r] - si0);
+                    const float ei = fast_exp2(srv[r]);
 #pragma unroll
                     for (int pt = 0; pt < 2; ++pt) {
-                        const uint32_t xw = xT[pb][16 * pt + m][i >> 1];
-                        const float xv = __uint_as_float((i & 1) ? (xw & 0xffff0000u) : (xw << 16));
+                        const uint32_t xw = (r >> 1) ? xr[pt].y : xr[pt].x;
+                        const float xv = __uint_as_float((r & 1) ? (xw & 0xffff0000u) : (xw << 16));
                         float yv = al * off_[pt][r] + dg[pt][r] + ei * yo[pt][r] + dskip * xv;
                         if constexpr (HASZ) yv *= silu(__uint_as_float(zz[sl][2 * r + pt] << 16));
                         yt16[(4 * kg + r) * kPW + 16 * pt + m] = to_bf16(yv);
@@ -512,19 +543,36 @@ __global__ __launch_bounds__(512) void ssd_main_kernel(
             const int pb = c & 1;
             // H_out = e^(s_end) H_in + B^T (w o X), w_j = dt_j e^(s_end - s_j) <= 1
             const float dec = fast_exp2(s_end);
+            // state blocks in pairs (the held B^T slots); each x tile read
+            // from LDS one token block ahead serves both blocks of the pair
 #pragma unroll
-            for (int k = 0; k < NBW; ++k) {
-                if (wr + 4 * k < NB) {
+            for (int k0 = 0; k0 < NBW; k0 += BSL) {
 #pragma unroll
-                    for (int pt = 0; pt < 2; ++pt) {
-                        accH[k][pt] *= dec;
+                for (int k = k0; k < k0 + BSL; ++k)
 #pragma unroll
-                        for (int J = 0; J < KB; ++J)
-                            accH[k][pt] = mfma16(ba[k % BSL][J], lds128(&xwT[pb][16 * pt + m][16 * J + 4 * kg]),
-                                                 accH[k][pt]);
+                    for (int pt = 0; pt < 2; ++pt) accH[k][pt] *= dec;
+                u32x4_t xw[2][2];
+#pragma unroll
+                for (int pt = 0; pt < 2; ++pt) xw[0][pt] = lds128(&xwT[pb][16 * pt + m][4 * kg]);
+#pragma unroll
+                for (int J = 0; J < KB; ++J) {
+                    if (J + 1 < KB) {
+#pragma unroll
+                        for (int pt = 0; pt < 2; ++pt)
+                            xw[(J + 1) & 1][pt] = lds128(&xwT[pb][16 * pt + m][16 * (J + 1) + 4 * kg]);
                     }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int k = k0; k < k0 + BSL; ++k)
+                        if (wr + 4 * k < NB) {
+#pragma unroll
+                            for (int pt = 0; pt < 2; ++pt)
+                                accH[k][pt] = mfma16(ba[k % BSL][J], xw[J & 1][pt], accH[k][pt]);
+                        }
                 }
-                if (k + BSL < NBW) load_bt(c, k + BSL);
+#pragma unroll
+                for (int k = k0; k < k0 + BSL; ++k)
+                    if (k + BSL < NBW) load_bt(c, k + BSL);
             }
             // the next chunk (past the last one: zeros, results unused)
             load_bt_ahead(c + 1);
