@@ -62,6 +62,23 @@ __device__ __forceinline__ u32x4_t scale_bf16x8(const u32x4_t v, float f) {
 __device__ __forceinline__ u32x4_t gload128(rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
+// Per-lane offset plus a wave-uniform one (a tile's place in its array).
+__device__ __forceinline__ u32x4_t gload128s(rsrc_t r, uint32_t off, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0);
+}
+
+// Workspace layout.  G, B^T and a copy of C are stored as MFMA operand
+// tiles: a tile is 16 rows x 32 columns of bf16 (1 KB), and the 16 bytes
+// lane l = 16 kg + m of a wave needs (row m, columns 8 kg .. 8 kg + 7) sit at
+// byte 16 l.  One load instruction then reads 1 KB of consecutive bytes: the
+// row-major form had consecutive lanes 256-512 bytes apart, so the vector
+// L1 looked up one line per lane -- four times the lookups -- and those
+// lookups, not HBM, limited the main kernel.
+//   G   : tile (I, J)  = rows 16 I.., columns (tokens j) 32 J..   index I * (Q/32) + J
+//   B^T : tile (nb, J) = rows (states) 16 nb.., columns (tokens) 32 J..   index nb * (Q/32) + J
+//   C   : tile (I, nk) = rows (tokens) 16 I.., columns (states) 32 nk..   index I * (N/32) + nk
+// per (b, chunk, group), in that order: Q*Q, N*Q and Q*N bf16.
+constexpr uint32_t kTileBytes = 1024;
 
 // ---------------------------------------------------------------------------
 // Prep: G = C B^T (causal blocks, bf16) and B^T for one (b, chunk, group) and
@@ -71,9 +88,11 @@ template <int Q, int N>
 __global__ __launch_bounds__(256) void ssd_prep_kernel(const uint16_t* __restrict__ Bm,
                                                        const uint16_t* __restrict__ Cm,
                                                        uint16_t* __restrict__ Gw, uint16_t* __restrict__ BTw,
-                                                       int L, int G, int nc) {
+                                                       uint16_t* __restrict__ Cw, int L, int G, int nc) {
     constexpr int QB = Q / 64;
+    constexpr int KB = Q / 32;
     __shared__ uint32_t sB[64][(N + 8) / 2];     // 64 tokens x N, bf16 pairs along n
+    __shared__ __align__(16) uint32_t sT[4][16][20];   // per wave: one 16 x 32 G tile (bf16 pairs, padded)
 
     const int q4 = blockIdx.x % QB;
     const int bcg = blockIdx.x / QB;             // (b * nc + c) * G + g
@@ -94,13 +113,19 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(const uint16_t* __restric
     // ---- G rows of row-block I: the causal extent is 32 * (I/2 + 1) columns ---
     // The C tiles of the row block are loaded once; B tiles one column tile ahead.
     const int I = q4 * 4 + w;
-    uint16_t* Gout = Gw + (int64_t)bcg * Q * Q;
+    char* Gout = reinterpret_cast<char*>(Gw + (int64_t)bcg * Q * Q) + ((uint32_t)I * KB * 64 + lane) * 16u;
     const int ncol = 32 * (I / 2 + 1);
     u32x4_t ct[N / 32], bt[2][N / 32];
 #pragma unroll
     for (int nk = 0; nk < N / 32; ++nk) {
         ct[nk] = gload128(rC, tok(16 * I + m, 32 * nk + 8 * kg));
         bt[0][nk] = gload128(rB, tok(m, 32 * nk + 8 * kg));
+    }
+    // the copy of C, as operand tiles (rows past the sequence end are zero)
+    {
+        char* Cout = reinterpret_cast<char*>(Cw + (int64_t)bcg * Q * N) + ((uint32_t)I * (N / 32) * 64 + lane) * 16u;
+#pragma unroll
+        for (int nk = 0; nk < N / 32; ++nk) *reinterpret_cast<u32x4_t*>(Cout + nk * kTileBytes) = ct[nk];
     }
     for (int jt = 0; jt < ncol / 16; jt += 2) {
 #pragma unroll
@@ -113,9 +138,20 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(const uint16_t* __restric
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int nk = 0; nk < N / 32; ++nk) acc = mfma16(ct[nk], bt[u][nk], acc);
+            // lane holds rows 4 kg + r, column 16 u + m of the 16 x 32 tile
+            uint16_t* t16 = reinterpret_cast<uint16_t*>(&sT[w][0][0]);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Gout[(16 * I + 4 * kg + r) * Q + 16 * j + m] = to_bf16(acc[r]);
+            for (int r = 0; r < 4; ++r) t16[(4 * kg + r) * 40 + 16 * u + m] = to_bf16(acc[r]);
         }
+        // the tile, re-read in operand order: lane (kg, m) takes row m, columns 8 kg ..
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&sT[w][m][4 * kg]);
+        *reinterpret_cast<u32x4_t*>(Gout + (jt / 2) * kTileBytes) = v;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 
     // ---- B^T for this quarter's 64 tokens -------------------------------------
@@ -125,19 +161,23 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(const uint16_t* __restric
         *reinterpret_cast<u32x4_t*>(&sB[tl][4 * n8]) = v;
     }
     __syncthreads();
-    uint16_t* BTout = BTw + (int64_t)bcg * N * Q;
+    // operand tiles (nb, J) for this quarter's token blocks J = 2 q4, 2 q4 + 1:
+    // lane l = 16 kg + m holds state 16 nb + m, tokens 32 J + 8 kg .. + 7
+    char* BTout = reinterpret_cast<char*>(BTw + (int64_t)bcg * N * Q);
     const uint16_t* sB16 = reinterpret_cast<const uint16_t*>(&sB[0][0]);
     constexpr int SBS = N + 8;                   // sB row stride in bf16
-    for (int idx = tid; idx < N * 8; idx += 256) {
-        const int n = idx / 8, tg = idx % 8;
+    for (int idx = tid; idx < (N / 16) * 2 * 64; idx += 256) {
+        const int l = idx & 63, jj = (idx >> 6) & 1, nb = idx >> 7;
+        const int n = 16 * nb + (l & 15), tl0 = 32 * jj + 8 * (l >> 4);
         uint32_t wv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const uint32_t lo = sB16[(8 * tg + 2 * e) * SBS + n];
-            const uint32_t hi = sB16[(8 * tg + 2 * e + 1) * SBS + n];
+            const uint32_t lo = sB16[(tl0 + 2 * e) * SBS + n];
+            const uint32_t hi = sB16[(tl0 + 2 * e + 1) * SBS + n];
             wv[e] = lo | (hi << 16);
         }
-        *reinterpret_cast<uint4*>(BTout + (int64_t)n * Q + 64 * q4 + 8 * tg) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+        const uint32_t tile = (uint32_t)nb * KB + 2 * q4 + jj;
+        *reinterpret_cast<uint4*>(BTout + tile * kTileBytes + 16u * l) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
     }
 }
 
@@ -157,9 +197,10 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(const uint16_t* __restric
 template <int Q, int N, bool HASZ>
 __global__ __launch_bounds__(512) void ssd_main_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ DT, const float* __restrict__ Ah,
-    const uint16_t* __restrict__ Cm, const float* __restrict__ Dh, const uint16_t* __restrict__ Z,
+    const float* __restrict__ Dh, const uint16_t* __restrict__ Z,
     const float* __restrict__ h0, uint16_t* __restrict__ Y, float* __restrict__ hT,
-    const uint16_t* __restrict__ Gw, const uint16_t* __restrict__ BTw, int L, int H, int G, int nc) {
+    const uint16_t* __restrict__ Gw, const uint16_t* __restrict__ BTw, const uint16_t* __restrict__ Cw,
+    int L, int H, int G, int nc) {
     constexpr int RB = Q / 16;                   // row blocks (16 tokens)
     constexpr int RBW = RB / 4;                  // row blocks per output wave
     constexpr int KB = Q / 32;                   // token blocks (32 tokens, one MFMA K step)
@@ -207,9 +248,8 @@ __global__ __launch_bounds__(512) void ssd_main_kernel(
         const float dskip = Dh ? Dh[h] : 0.f;
         const rsrc_t rY = make_rsrc(Y + b * (int64_t)L * H * kP, (uint32_t)L * xrow);
         const rsrc_t rZ = make_rsrc(Z ? Z + b * (int64_t)L * H * kP : X, Z ? (uint32_t)L * xrow : 0u);
-        const uint32_t crow = (uint32_t)G * N * 2u;
-        const rsrc_t rC = make_rsrc(Cm + b * (int64_t)L * G * N, (uint32_t)L * crow);
         const uint32_t gbytes = (uint32_t)Q * Q * 2u;
+        const uint32_t cbytes = (uint32_t)Q * N * 2u;
         const int jhi = wr >> 1;                 // row block I = wr + 4 rb lies in token block 2 rb + jhi
 
         // G tiles: every row block has its own registers (row block rb needs
@@ -227,21 +267,19 @@ __global__ __launch_bounds__(512) void ssd_main_kernel(
             const int I = wr + 4 * rb;
             const rsrc_t rG = make_rsrc(Gw + (((int64_t)b * nc + (cc < nc ? cc : 0)) * G + g) * Q * Q,
                                         cc < nc ? gbytes : 0u);
-            // recomputed per call (volatile asm): the tile offsets then go in
-            // the loads' immediate field instead of 20 registers held across chunks
-            uint32_t gb = ((uint32_t)(16 * I + m) * Q + 8 * kg) * 2u;
-            asm volatile("" : "+v"(gb));
-            const uint32_t glast = off_if(jhi != 0, gb + 64u * (2 * rb + 1));
+            const uint32_t gb = ((uint32_t)I * KB * 64 + lane) * 16u;
+            const uint32_t glast = off_if(jhi != 0, gb);
 #pragma unroll
             for (int J = 0; J <= 2 * rb + 1; ++J)
-                ga[rb * (rb + 1) + J] = gload128(rG, J <= 2 * rb ? gb + 64u * J : glast);
+                ga[rb * (rb + 1) + J] = gload128s(rG, J <= 2 * rb ? gb : glast, (uint32_t)J * kTileBytes);
         };
         auto load_cz = [&](int cc, int rb, int sl) {
             const int I = wr + 4 * rb;
-            const int t = cc * Q + 16 * I + m;
-            const uint32_t cb = off_if(t < L, (uint32_t)t * crow + (uint32_t)g * N * 2u + 16u * kg);
+            const rsrc_t rC = make_rsrc(Cw + (((int64_t)b * nc + (cc < nc ? cc : 0)) * G + g) * Q * N,
+                                        cc < nc ? cbytes : 0u);
+            const uint32_t cb = ((uint32_t)I * NKB * 64 + lane) * 16u;
 #pragma unroll
-            for (int nk = 0; nk < NKB; ++nk) ca[sl][nk] = gload128(rC, cb + 64u * nk);
+            for (int nk = 0; nk < NKB; ++nk) ca[sl][nk] = gload128s(rC, cb, (uint32_t)nk * kTileBytes);
             if constexpr (HASZ) {
                 const int I = wr + 4 * rb;
 #pragma unroll
@@ -436,9 +474,9 @@ __global__ __launch_bounds__(512) void ssd_main_kernel(
             const rsrc_t rBT = make_rsrc(BTw + (((int64_t)b * nc + (cc < nc ? cc : 0)) * G + g) * N * Q,
                                          cc < nc ? btbytes : 0u);
             const int nb = wr + 4 * k;
-            const uint32_t base = off_if(nb < NB, ((uint32_t)(16 * nb + m) * Q + 8 * kg) * 2u);
+            const uint32_t base = off_if(nb < NB, ((uint32_t)nb * KB * 64 + lane) * 16u);
 #pragma unroll
-            for (int J = 0; J < KB; ++J) ba[k % BSL][J] = gload128(rBT, base + 64u * J);
+            for (int J = 0; J < KB; ++J) ba[k % BSL][J] = gload128s(rBT, base, (uint32_t)J * kTileBytes);
         };
         auto load_bt_ahead = [&](int cc) {
 #pragma unroll
@@ -605,16 +643,18 @@ hipError_t launch_qn(const SSDParams& p, hipStream_t stream) {
     const int nc = (p.L + Q - 1) / Q;
     uint16_t* Gw = static_cast<uint16_t*>(p.workspace);
     uint16_t* BTw = Gw + (int64_t)p.batch * nc * p.G * Q * Q;
+    uint16_t* Cw = BTw + (int64_t)p.batch * nc * p.G * N * Q;
     const int64_t prep_blocks = p.batch * nc * p.G * (Q / 64);
     hipLaunchKernelGGL((ssd_prep_kernel<Q, N>), dim3((unsigned)prep_blocks), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(p.Bm), static_cast<const uint16_t*>(p.Cm), Gw, BTw, p.L, p.G, nc);
+                       static_cast<const uint16_t*>(p.Bm), static_cast<const uint16_t*>(p.Cm), Gw, BTw, Cw, p.L, p.G,
+                       nc);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t blocks = p.batch * p.H * 2;
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(512), 0, stream,
                        static_cast<const uint16_t*>(p.x), static_cast<const uint16_t*>(p.dt), p.A,
-                       static_cast<const uint16_t*>(p.Cm), p.Dskip, static_cast<const uint16_t*>(p.z), p.h0,
-                       static_cast<uint16_t*>(p.y), p.h_final, Gw, BTw, p.L, p.H, p.G, nc);
+                       p.Dskip, static_cast<const uint16_t*>(p.z), p.h0,
+                       static_cast<uint16_t*>(p.y), p.h_final, Gw, BTw, Cw, p.L, p.H, p.G, nc);
     return hipGetLastError();
 }
 
@@ -636,7 +676,7 @@ size_t ssd_workspace_bytes(int64_t batch, int64_t L, int64_t H, int64_t P, int64
     (void)P;
     if (Q <= 0) return 0;
     const int64_t nc = (L + Q - 1) / Q;
-    return (size_t)(batch * nc * G * Q * (Q + N) * 2);
+    return (size_t)(batch * nc * G * Q * (Q + 2 * N) * 2);     // G, B^T and C tiles
 }
 
 bool ssd_supported(int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int64_t Q) {
