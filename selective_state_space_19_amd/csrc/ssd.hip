@@ -321,9 +321,12 @@ __global__ __launch_bounds__(512) void ssd_main_kernel(
                 u32x4_t xb[2][2];
 #pragma unroll
                 for (int pt = 0; pt < 2; ++pt) xb[0][pt] = lds128(&xsT[pb][16 * pt + m][4 * kg]);
-                // off-diagonal token blocks J < Jd: the G tile is scaled by the
-                // decay from the end of block J to the first row of block I
-                // (<= 1), so the MFMAs accumulate back to back.
+                // off-diagonal token blocks J < Jd: each block's product G_IJ xs_J
+                // goes to a fresh accumulator and is added scaled by the decay
+                // from the end of block J to the first row of block I (<= 1),
+                // one block behind, so the adds never wait on an MFMA.
+                f32x4_t tq[2][2];
+                const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int J = 0; J <= 2 * rb; ++J) {
                     if (J < 2 * rb) {
@@ -333,10 +336,19 @@ __global__ __launch_bounds__(512) void ssd_main_kernel(
                     }
                     __builtin_amdgcn_sched_barrier(0);
                     if (J < Jd) {                // J = 2 rb: off-diagonal for jhi = 1 only
-                        const u32x4_t a = scale_bf16x8(gt[J], fast_exp2(si0 - se[J]));
 #pragma unroll
-                        for (int pt = 0; pt < 2; ++pt) off_[pt] = mfma16(a, xb[J & 1][pt], off_[pt]);
+                        for (int pt = 0; pt < 2; ++pt) tq[J & 1][pt] = mfma16(gt[J], xb[J & 1][pt], zero4);
                     }
+                    if (J > 0) {
+                        const float f = fast_exp2(si0 - se[J - 1]);
+#pragma unroll
+                        for (int pt = 0; pt < 2; ++pt) off_[pt] += f * tq[(J - 1) & 1][pt];
+                    }
+                }
+                if (jhi) {
+                    const float f = fast_exp2(si0 - se[2 * rb]);
+#pragma unroll
+                    for (int pt = 0; pt < 2; ++pt) off_[pt] += f * tq[(2 * rb) & 1][pt];
                 }
                 // operands of the diagonal block and of C H_in^T
                 const int i = i0 + m;
@@ -358,7 +370,11 @@ __global__ __launch_bounds__(512) void ssd_main_kernel(
                 __builtin_amdgcn_sched_barrier(0);
                 // diagonal token block: mask built element by element, dt folded in, plain x
                 {
-                    const u32x4_t gv = jhi ? gt[2 * rb + 1] : gt[2 * rb];
+                    // the two candidate tiles pass through an empty asm, so the
+                    // choice stays a select: an index into `ga` would put it in scratch
+                    u32x4_t g0 = gt[2 * rb], g1 = gt[2 * rb + 1];
+                    asm("" : "+v"(g0), "+v"(g1));
+                    const u32x4_t gv = jhi ? g1 : g0;
                     const float dj[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
                     const float sj[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
                     uint32_t av[4];
