@@ -81,103 +81,130 @@ __device__ __forceinline__ u32x4_t gload128s(rsrc_t r, uint32_t off, uint32_t so
 constexpr uint32_t kTileBytes = 1024;
 
 // ---------------------------------------------------------------------------
-// Prep: G = C B^T (causal blocks, bf16) and B^T for one (b, chunk, group) and
-// one quarter of the chunk's rows.  grid = B * nc * G * (Q / 64), 256 threads.
+// Prep: the operand tiles of one (b, chunk, group) and one 32-token block rp
+// of the chunk: G = C B^T for rows 32 rp .. 32 rp + 31 and the causal column
+// blocks J <= rp, B^T for token block rp, and the copy of C for those rows.
+// grid = B * nc * G * (Q / 32), 256 threads.  B rows 0 .. 32 rp + 31 are
+// staged in LDS with coalesced loads (16-byte pieces XOR-swizzled by row, so
+// fragment reads of 16 consecutive rows hit distinct banks without padding:
+// two workgroups fit on a CU at N = 128); every tile leaves as one 1 KB
+// store per wave.
 // ---------------------------------------------------------------------------
 template <int Q, int N>
 __global__ __launch_bounds__(256) void ssd_prep_kernel(const uint16_t* __restrict__ Bm,
                                                        const uint16_t* __restrict__ Cm,
                                                        uint16_t* __restrict__ Gw, uint16_t* __restrict__ BTw,
                                                        uint16_t* __restrict__ Cw, int L, int G, int nc) {
-    constexpr int QB = Q / 64;
-    constexpr int KB = Q / 32;
-    __shared__ uint32_t sB[64][(N + 8) / 2];     // 64 tokens x N, bf16 pairs along n
-    __shared__ __align__(16) uint32_t sT[4][16][20];   // per wave: one 16 x 32 G tile (bf16 pairs, padded)
+    constexpr int KB = Q / 32, NKB = N / 32, NB = N / 16;
+    constexpr int CPR = N / 8;                   // 16-byte pieces per row
+    constexpr int SWZ = (CPR < 16 ? CPR : 16) - 1;
+    constexpr int NLD = Q * CPR / 256;           // staging loads per thread
+    __shared__ __align__(16) u32x4_t sB[Q][CPR];
+    __shared__ __align__(16) uint32_t sT[4][16][20];   // per wave: one 16 x 32 tile (bf16 pairs, padded)
+    auto piece = [](int r, int q) { return q ^ (r & SWZ); };
 
-    const int q4 = blockIdx.x % QB;
-    const int bcg = blockIdx.x / QB;             // (b * nc + c) * G + g
+    const int rp = blockIdx.x % KB;
+    const int bcg = blockIdx.x / KB;             // (b * nc + c) * G + g
     const int g = bcg % G;
     const int c = (bcg / G) % nc;
     const int64_t b = (bcg / G) / nc;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int kg = lane >> 4, m = lane & 15;
 
     const uint32_t rowbytes = (uint32_t)G * N * 2u;
     const rsrc_t rB = make_rsrc(Bm + b * (int64_t)L * G * N, (uint32_t)L * rowbytes);
     const rsrc_t rC = make_rsrc(Cm + b * (int64_t)L * G * N, (uint32_t)L * rowbytes);
-    auto tok = [&](int tl, int n) -> uint32_t {  // byte offset of (chunk token tl, state n)
+    auto tok = [&](int tl, int n, bool ok) -> uint32_t {  // byte offset of (chunk token tl, state n)
         const int t = c * Q + tl;
-        return off_if(t < L, (uint32_t)t * rowbytes + ((uint32_t)g * N + n) * 2u);
+        return off_if(ok && t < L, (uint32_t)t * rowbytes + ((uint32_t)g * N + n) * 2u);
     };
 
-    // ---- G rows of row-block I: the causal extent is 32 * (I/2 + 1) columns ---
-    // The C tiles of the row block are loaded once; B tiles one column tile ahead.
-    const int I = q4 * 4 + w;
-    char* Gout = reinterpret_cast<char*>(Gw + (int64_t)bcg * Q * Q) + ((uint32_t)I * KB * 64 + lane) * 16u;
-    const int ncol = 32 * (I / 2 + 1);
-    u32x4_t ct[N / 32], bt[2][N / 32];
+    // C fragments of rows 32 rp + 16 il + m (rows past the sequence end read as 0)
+    u32x4_t ca[2][NKB];
 #pragma unroll
-    for (int nk = 0; nk < N / 32; ++nk) {
-        ct[nk] = gload128(rC, tok(16 * I + m, 32 * nk + 8 * kg));
-        bt[0][nk] = gload128(rB, tok(m, 32 * nk + 8 * kg));
-    }
-    // the copy of C, as operand tiles (rows past the sequence end are zero)
+    for (int il = 0; il < 2; ++il)
+#pragma unroll
+        for (int nk = 0; nk < NKB; ++nk) ca[il][nk] = gload128(rC, tok(32 * rp + 16 * il + m, 32 * nk + 8 * kg, true));
+    // B rows 0 .. 32 (rp + 1) - 1, every load in flight at once
     {
-        char* Cout = reinterpret_cast<char*>(Cw + (int64_t)bcg * Q * N) + ((uint32_t)I * (N / 32) * 64 + lane) * 16u;
+        const int nB = 32 * (rp + 1) * CPR;
+        u32x4_t v[NLD];
 #pragma unroll
-        for (int nk = 0; nk < N / 32; ++nk) *reinterpret_cast<u32x4_t*>(Cout + nk * kTileBytes) = ct[nk];
-    }
-    for (int jt = 0; jt < ncol / 16; jt += 2) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {            // two column tiles per step: static buffer index
-            const int j = jt + u;
-            if (j + 1 < ncol / 16) {
-#pragma unroll
-                for (int nk = 0; nk < N / 32; ++nk) bt[u ^ 1][nk] = gload128(rB, tok(16 * (j + 1) + m, 32 * nk + 8 * kg));
-            }
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int nk = 0; nk < N / 32; ++nk) acc = mfma16(ct[nk], bt[u][nk], acc);
-            // lane holds rows 4 kg + r, column 16 u + m of the 16 x 32 tile
-            uint16_t* t16 = reinterpret_cast<uint16_t*>(&sT[w][0][0]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) t16[(4 * kg + r) * 40 + 16 * u + m] = to_bf16(acc[r]);
+        for (int k = 0; k < NLD; ++k) {
+            const int idx = 256 * k + tid;
+            v[k] = gload128(rB, tok(idx / CPR, 8 * (idx % CPR), idx < nB));
         }
-        // the tile, re-read in operand order: lane (kg, m) takes row m, columns 8 kg ..
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&sT[w][m][4 * kg]);
-        *reinterpret_cast<u32x4_t*>(Gout + (jt / 2) * kTileBytes) = v;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int k = 0; k < NLD; ++k) {
+            const int idx = 256 * k + tid, r = idx / CPR;
+            sB[r][piece(r, idx % CPR)] = v[k];
+        }
+    }
+    // the copy of C: tiles (2 rp + il, nk), spread over the waves
+    char* Cout = reinterpret_cast<char*>(Cw + (int64_t)bcg * Q * N) + 16u * lane;
+#pragma unroll
+    for (int il = 0; il < 2; ++il)
+#pragma unroll
+        for (int nk = 0; nk < NKB; ++nk)
+            if ((il * NKB + nk) % 4 == w)
+                *reinterpret_cast<u32x4_t*>(Cout + (uint32_t)((2 * rp + il) * NKB + nk) * kTileBytes) = ca[il][nk];
+    __syncthreads();
+
+    // ---- G tiles (2 rp + il, J), J = w, w + 4, .. <= rp ----
+    char* Gout = reinterpret_cast<char*>(Gw + (int64_t)bcg * Q * Q) + 16u * lane;
+    uint16_t* t16 = reinterpret_cast<uint16_t*>(&sT[w][0][0]);
+    for (int J = w; J <= rp; J += 4) {
+        f32x4_t acc[2][2] = {};
+#pragma unroll
+        for (int nk = 0; nk < NKB; ++nk)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int r = 32 * J + 16 * u + m;
+                const u32x4_t bv = sB[r][piece(r, 4 * nk + kg)];
+#pragma unroll
+                for (int il = 0; il < 2; ++il) acc[il][u] = mfma16(ca[il][nk], bv, acc[il][u]);
+            }
+#pragma unroll
+        for (int il = 0; il < 2; ++il) {
+            // lane holds rows 4 kg + r, column 16 u + m; re-read in operand order
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) t16[(4 * kg + r) * 40 + 16 * u + m] = to_bf16(acc[il][u][r]);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&sT[w][m][4 * kg]);
+            *reinterpret_cast<u32x4_t*>(Gout + (uint32_t)((2 * rp + il) * KB + J) * kTileBytes) = v;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
     }
 
-    // ---- B^T for this quarter's 64 tokens -------------------------------------
-    for (int idx = tid; idx < 64 * (N / 8); idx += 256) {
-        const int tl = idx / (N / 8), n8 = idx % (N / 8);
-        const u32x4_t v = gload128(rB, tok(64 * q4 + tl, 8 * n8));
-        *reinterpret_cast<u32x4_t*>(&sB[tl][4 * n8]) = v;
-    }
-    __syncthreads();
-    // operand tiles (nb, J) for this quarter's token blocks J = 2 q4, 2 q4 + 1:
-    // lane l = 16 kg + m holds state 16 nb + m, tokens 32 J + 8 kg .. + 7
-    char* BTout = reinterpret_cast<char*>(BTw + (int64_t)bcg * N * Q);
-    const uint16_t* sB16 = reinterpret_cast<const uint16_t*>(&sB[0][0]);
-    constexpr int SBS = N + 8;                   // sB row stride in bf16
-    for (int idx = tid; idx < (N / 16) * 2 * 64; idx += 256) {
-        const int l = idx & 63, jj = (idx >> 6) & 1, nb = idx >> 7;
-        const int n = 16 * nb + (l & 15), tl0 = 32 * jj + 8 * (l >> 4);
-        uint32_t wv[4];
+    // ---- B^T tiles (nb, rp): state 16 nb + m, tokens 32 rp + 8 kg .. + 7 ----
+    char* BTout = reinterpret_cast<char*>(BTw + (int64_t)bcg * N * Q) + 16u * lane;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint32_t lo = sB16[(tl0 + 2 * e) * SBS + n];
-            const uint32_t hi = sB16[(tl0 + 2 * e + 1) * SBS + n];
-            wv[e] = lo | (hi << 16);
+    for (int nb0 = 0; nb0 < NB; nb0 += 4) {
+        const int nb = nb0 + w;
+        if (nb < NB) {
+            const int n = 16 * nb + m, r0 = 32 * rp + 8 * kg;
+            uint32_t wv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                uint32_t h[2];
+#pragma unroll
+                for (int o = 0; o < 2; ++o) {
+                    const int r = r0 + 2 * e + o;
+                    const uint16_t* row = reinterpret_cast<const uint16_t*>(&sB[r][0]);
+                    h[o] = row[8 * piece(r, n >> 3) + (n & 7)];
+                }
+                wv[e] = h[0] | (h[1] << 16);
+            }
+            *reinterpret_cast<uint4*>(BTout + (uint32_t)(nb * KB + rp) * kTileBytes) =
+                make_uint4(wv[0], wv[1], wv[2], wv[3]);
         }
-        const uint32_t tile = (uint32_t)nb * KB + 2 * q4 + jj;
-        *reinterpret_cast<uint4*>(BTout + tile * kTileBytes + 16u * l) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
     }
 }
 
@@ -660,7 +687,7 @@ hipError_t launch_qn(const SSDParams& p, hipStream_t stream) {
     uint16_t* Gw = static_cast<uint16_t*>(p.workspace);
     uint16_t* BTw = Gw + (int64_t)p.batch * nc * p.G * Q * Q;
     uint16_t* Cw = BTw + (int64_t)p.batch * nc * p.G * N * Q;
-    const int64_t prep_blocks = p.batch * nc * p.G * (Q / 64);
+    const int64_t prep_blocks = p.batch * nc * p.G * (Q / 32);
     hipLaunchKernelGGL((ssd_prep_kernel<Q, N>), dim3((unsigned)prep_blocks), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(p.Bm), static_cast<const uint16_t*>(p.Cm), Gw, BTw, Cw, p.L, p.G,
                        nc);
