@@ -33,6 +33,8 @@
 //   the middle one is applied to the accumulator per block (Horner form).  The
 //   state update uses the same staged x and per-block factors.  Only the
 //   diagonal 16 x 32 blocks build the mask element by element.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -51,6 +53,14 @@ __device__ __forceinline__ f32x4_t mfma16(const u32x4_t a, const u32x4_t b, f32x
                                                    c, 0, 0, 0);
 }
 __device__ __forceinline__ u32x4_t lds128(const uint32_t* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+// f(integral_constant<int, i>) for i = B .. E - 1, unrolled at compile time.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
 // Eight packed bf16 values times f, rounded back to bf16.
 __device__ __forceinline__ u32x4_t scale_bf16x8(const u32x4_t v, float f) {
     u32x4_t o;
@@ -229,7 +239,8 @@ __global__ __launch_bounds__(512) void ssd_main_kernel(
     const uint16_t* __restrict__ Gw, const uint16_t* __restrict__ BTw, const uint16_t* __restrict__ Cw,
     int L, int H, int G, int nc) {
     constexpr int RB = Q / 16;                   // row blocks (16 tokens)
-    constexpr int RBW = RB / 4;                  // row blocks per output wave
+    constexpr int RBW = RB / 4;                  // rounds of row blocks (4 row blocks each)
+    constexpr int SRB = RBW > 1 ? 1 : 0;         // rounds the state waves take (the cheapest one)
     constexpr int KB = Q / 32;                   // token blocks (32 tokens, one MFMA K step)
     constexpr int NB = N / 16;                   // state blocks (16 states)
     constexpr int NKB = N / 32;                  // 32-state K steps
@@ -245,7 +256,7 @@ __global__ __launch_bounds__(512) void ssd_main_kernel(
     __shared__ __align__(16) uint32_t xsT[2][kPW][XS];   // (dt * e^(s_blockend - s) * x)^T
     __shared__ __align__(16) uint32_t xwT[2][kPW][XS];   // (dt * e^(s_chunkend - s) * x)^T
     __shared__ __align__(16) uint32_t Hb[2][kPW][HS];    // carried-in state, bf16 pairs along n
-    __shared__ __align__(16) uint32_t ytile[4][16][kPW / 2];  // per output wave: one 16 x 32 bf16 output tile
+    __shared__ __align__(16) uint32_t ytile[8][16][kPW / 2];  // per wave: one 16 x 32 bf16 output tile
 
     // Blocks are dispatched round-robin over the 8 XCDs; number them so that
     // consecutive ids (the heads of one batch row) share an XCD and its L2,
@@ -270,205 +281,225 @@ __global__ __launch_bounds__(512) void ssd_main_kernel(
     const uint32_t chan0 = ((uint32_t)h * kP + kPW * ph) * 2u;  // byte offset of this half-head in a token row
     auto send = [&](int pb, int J) { return s_s[pb][32 * J + 31]; };   // s at the end of token block J
 
+    const float dskip = Dh ? Dh[h] : 0.f;
+    const rsrc_t rY = make_rsrc(Y + b * (int64_t)L * H * kP, (uint32_t)L * xrow);
+    const rsrc_t rZ = make_rsrc(Z ? Z + b * (int64_t)L * H * kP : X, Z ? (uint32_t)L * xrow : 0u);
+    const uint32_t gbytes = (uint32_t)Q * Q * 2u;
+    const uint32_t cbytes = (uint32_t)Q * N * 2u;
+    const int jhi = wr >> 1;                 // row block I = wr + 4 rb lies in token block 2 rb + jhi
+
+    // G tiles: every row block has its own registers (row block rb needs
+    // G tiles J <= 2 rb + 1, at offset rb (rb + 1) in `ga`), and a row
+    // block's tiles for the next chunk are requested as soon as its MFMAs
+    // have read them, a whole chunk ahead of use.  C tiles and gate values
+    // are double-buffered one row block ahead.  Tiles a row block does not
+    // need are read at an out-of-range offset (no traffic, value 0), so
+    // every load is unconditional.
+    constexpr int NGA = RBW * (RBW + 1);
+    u32x4_t ga[NGA];
+    u32x4_t ca[2][NKB];
+    uint32_t zz[2][8];
+    auto load_g = [&](int cc, int rb) {
+        const int I = wr + 4 * rb;
+        const rsrc_t rG = make_rsrc(Gw + (((int64_t)b * nc + (cc < nc ? cc : 0)) * G + g) * Q * Q,
+                                    cc < nc ? gbytes : 0u);
+        const uint32_t gb = ((uint32_t)I * KB * 64 + lane) * 16u;
+        const uint32_t glast = off_if(jhi != 0, gb);
+#pragma unroll
+        for (int J = 0; J <= 2 * rb + 1; ++J)
+            ga[rb * (rb + 1) + J] = gload128s(rG, J <= 2 * rb ? gb : glast, (uint32_t)J * kTileBytes);
+    };
+    auto load_c = [&](int cc, int rb, int sl) {
+        const int I = wr + 4 * rb;
+        const rsrc_t rC = make_rsrc(Cw + (((int64_t)b * nc + (cc < nc ? cc : 0)) * G + g) * Q * N,
+                                    cc < nc ? cbytes : 0u);
+        const uint32_t cb = ((uint32_t)I * NKB * 64 + lane) * 16u;
+#pragma unroll
+        for (int nk = 0; nk < NKB; ++nk) ca[sl][nk] = gload128s(rC, cb, (uint32_t)nk * kTileBytes);
+    };
+    auto load_z = [&](int cc, int rb, int sl) {
+        if constexpr (HASZ) {
+            const int I = wr + 4 * rb;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int tr = cc * Q + 16 * I + 4 * kg + r;
+                const uint32_t zb = off_if(tr < L, (uint32_t)tr * xrow + chan0 + 2u * m);
+#pragma unroll
+                for (int pt = 0; pt < 2; ++pt)
+                    zz[sl][2 * r + pt] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rZ, zb + 32u * pt, 0, 0);
+            }
+        }
+    };
+
+    // One 16-row block I = wr + 4 rb of chunk c: off-diagonal and diagonal
+    // token blocks, C H_in^T, then `mid` (the caller's loads for later row
+    // blocks), then combine, skip, gate and store through LDS tile `yt`.
+    auto row_block = [&](auto rbc, auto slc, int c, int pb, int yt, auto mid) {
+        constexpr int rb = decltype(rbc)::value;
+        constexpr int sl = decltype(slc)::value;
+        const int I = wr + 4 * rb;
+        const int i0 = 16 * I;
+        const int Jd = 2 * rb + jhi;     // the token block holding row block I
+        const u32x4_t* gt = &ga[rb * (rb + 1)];
+        f32x4_t off_[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        f32x4_t dg[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        f32x4_t yo[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        // Every LDS operand is read one step ahead of the MFMAs that
+        // use it (the sched_barriers keep the compiler from sinking the
+        // reads back next to their use, which would expose each read's
+        // latency in turn).
+        const float si0 = s_s[pb][i0];
+        float se[2 * RBW];
+#pragma unroll
+        for (int J = 0; J <= 2 * rb; ++J) se[J] = send(pb, J);
+        u32x4_t xb[2][2];
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt) xb[0][pt] = lds128(&xsT[pb][16 * pt + m][4 * kg]);
+        // off-diagonal token blocks J < Jd: each block's product G_IJ xs_J
+        // goes to a fresh accumulator and is added scaled by the decay
+        // from the end of block J to the first row of block I (<= 1),
+        // one block behind, so the adds never wait on an MFMA.
+        f32x4_t tq[2][2];
+        const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int J = 0; J <= 2 * rb; ++J) {
+            if (J < 2 * rb) {
+#pragma unroll
+                for (int pt = 0; pt < 2; ++pt)
+                    xb[(J + 1) & 1][pt] = lds128(&xsT[pb][16 * pt + m][16 * (J + 1) + 4 * kg]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (J < Jd) {                // J = 2 rb: off-diagonal for jhi = 1 only
+#pragma unroll
+                for (int pt = 0; pt < 2; ++pt) tq[J & 1][pt] = mfma16(gt[J], xb[J & 1][pt], zero4);
+            }
+            if (J > 0) {
+                const float f = fast_exp2(si0 - se[J - 1]);
+#pragma unroll
+                for (int pt = 0; pt < 2; ++pt) off_[pt] += f * tq[(J - 1) & 1][pt];
+            }
+        }
+        if (jhi) {
+            const float f = fast_exp2(si0 - se[2 * rb]);
+#pragma unroll
+            for (int pt = 0; pt < 2; ++pt) off_[pt] += f * tq[(2 * rb) & 1][pt];
+        }
+        // operands of the diagonal block and of C H_in^T
+        const int i = i0 + m;
+        const float si = s_s[pb][i];
+        const int j0 = 32 * Jd + 8 * kg;
+        const float4 d0 = *reinterpret_cast<const float4*>(&s_dt[pb][j0]);
+        const float4 d1 = *reinterpret_cast<const float4*>(&s_dt[pb][j0 + 4]);
+        const float4 q0 = *reinterpret_cast<const float4*>(&s_s[pb][j0]);
+        const float4 q1 = *reinterpret_cast<const float4*>(&s_s[pb][j0 + 4]);
+        u32x4_t xd[2], hb[2][2];
+        uint2 xr[2];                     // x of this lane's output rows (skip term)
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt) {
+            xd[pt] = lds128(&xT[pb][16 * pt + m][16 * Jd + 4 * kg]);
+            hb[0][pt] = lds128(&Hb[pb][16 * pt + m][4 * kg]);
+            xr[pt] = *reinterpret_cast<const uint2*>(&xT[pb][16 * pt + m][(i0 + 4 * kg) >> 1]);
+        }
+        const float4 sr = *reinterpret_cast<const float4*>(&s_s[pb][i0 + 4 * kg]);
+        __builtin_amdgcn_sched_barrier(0);
+        // diagonal token block: mask built element by element, dt folded in, plain x
+        {
+            // the two candidate tiles pass through an empty asm, so the
+            // choice stays a select: an index into `ga` would put it in scratch
+            u32x4_t g0 = gt[2 * rb], g1 = gt[2 * rb + 1];
+            asm("" : "+v"(g0), "+v"(g1));
+            const u32x4_t gv = jhi ? g1 : g0;
+            const float dj[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+            const float sj[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+            uint32_t av[4];
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                const uint32_t gw = gv[e / 2];
+                float v0 = __uint_as_float(gw << 16) * dj[e] * fast_exp2(si - sj[e]);
+                float v1 = __uint_as_float(gw & 0xffff0000u) * dj[e + 1] * fast_exp2(si - sj[e + 1]);
+                keep_select(v0);
+                keep_select(v1);
+                av[e / 2] = pack_bf16x2(j0 + e <= i ? v0 : 0.f, j0 + e + 1 <= i ? v1 : 0.f);
+            }
+            const u32x4_t a = {av[0], av[1], av[2], av[3]};
+#pragma unroll
+            for (int pt = 0; pt < 2; ++pt) dg[pt] = mfma16(a, xd[pt], dg[pt]);
+        }
+        // carried-in state: C rows times H_in^T
+#pragma unroll
+        for (int nk = 0; nk < NKB; ++nk) {
+            if (nk + 1 < NKB) {
+#pragma unroll
+                for (int pt = 0; pt < 2; ++pt)
+                    hb[(nk + 1) & 1][pt] = lds128(&Hb[pb][16 * pt + m][16 * (nk + 1) + 4 * kg]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int pt = 0; pt < 2; ++pt) yo[pt] = mfma16(ca[sl][nk], hb[nk & 1][pt], yo[pt]);
+        }
+        mid();
+        // combine, skip, gate; the tile goes through LDS so that each
+        // lane stores 8 consecutive head channels of one token (16 bytes).
+        uint16_t* yt16 = reinterpret_cast<uint16_t*>(&ytile[yt][0][0]);
+        const float srv[4] = {sr.x, sr.y, sr.z, sr.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float al = fast_exp2(srv[r] - si0);
+            const float ei = fast_exp2(srv[r]);
+#pragma unroll
+            for (int pt = 0; pt < 2; ++pt) {
+                const uint32_t xw = (r >> 1) ? xr[pt].y : xr[pt].x;
+                const float xv = __uint_as_float((r & 1) ? (xw & 0xffff0000u) : (xw << 16));
+                float yv = al * off_[pt][r] + dg[pt][r] + ei * yo[pt][r] + dskip * xv;
+                if constexpr (HASZ) yv *= silu(__uint_as_float(zz[sl][2 * r + pt] << 16));
+                yt16[(4 * kg + r) * kPW + 16 * pt + m] = to_bf16(yv);
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        {
+            const int tr = lane >> 2, cg = lane & 3;          // token row, 8-channel group
+            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&ytile[yt][tr][4 * cg]);
+            const int t = c * Q + i0 + tr;
+            __builtin_amdgcn_raw_buffer_store_b128(v, rY, off_if(t < L, (uint32_t)t * xrow + chan0 + 16u * cg),
+                                                   0, kCached);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+
     if (w < 4) {
         // ======================= output waves ======================================
-        const float dskip = Dh ? Dh[h] : 0.f;
-        const rsrc_t rY = make_rsrc(Y + b * (int64_t)L * H * kP, (uint32_t)L * xrow);
-        const rsrc_t rZ = make_rsrc(Z ? Z + b * (int64_t)L * H * kP : X, Z ? (uint32_t)L * xrow : 0u);
-        const uint32_t gbytes = (uint32_t)Q * Q * 2u;
-        const uint32_t cbytes = (uint32_t)Q * N * 2u;
-        const int jhi = wr >> 1;                 // row block I = wr + 4 rb lies in token block 2 rb + jhi
-
-        // G tiles: every row block has its own registers (row block rb needs
-        // G tiles J <= 2 rb + 1, at offset rb (rb + 1) in `ga`), and a row
-        // block's tiles for the next chunk are requested as soon as its MFMAs
-        // have read them, a whole chunk ahead of use.  C tiles and gate values
-        // are double-buffered one row block ahead.  Tiles a row block does not
-        // need are read at an out-of-range offset (no traffic, value 0), so
-        // every load is unconditional.
-        constexpr int NGA = RBW * (RBW + 1);
-        u32x4_t ga[NGA];
-        u32x4_t ca[2][NKB];
-        uint32_t zz[2][8];
-        auto load_g = [&](int cc, int rb) {
-            const int I = wr + 4 * rb;
-            const rsrc_t rG = make_rsrc(Gw + (((int64_t)b * nc + (cc < nc ? cc : 0)) * G + g) * Q * Q,
-                                        cc < nc ? gbytes : 0u);
-            const uint32_t gb = ((uint32_t)I * KB * 64 + lane) * 16u;
-            const uint32_t glast = off_if(jhi != 0, gb);
+        // Row blocks SRB .. RBW - 1 (with more than one per wave the state
+        // waves take the first round).  C tiles and gate values alternate
+        // between two slots; the next chunk's first row block goes to slot 0
+        // once the last row block has read its own.
+        constexpr int NRO = RBW - SRB;
 #pragma unroll
-            for (int J = 0; J <= 2 * rb + 1; ++J)
-                ga[rb * (rb + 1) + J] = gload128s(rG, J <= 2 * rb ? gb : glast, (uint32_t)J * kTileBytes);
-        };
-        auto load_cz = [&](int cc, int rb, int sl) {
-            const int I = wr + 4 * rb;
-            const rsrc_t rC = make_rsrc(Cw + (((int64_t)b * nc + (cc < nc ? cc : 0)) * G + g) * Q * N,
-                                        cc < nc ? cbytes : 0u);
-            const uint32_t cb = ((uint32_t)I * NKB * 64 + lane) * 16u;
-#pragma unroll
-            for (int nk = 0; nk < NKB; ++nk) ca[sl][nk] = gload128s(rC, cb, (uint32_t)nk * kTileBytes);
-            if constexpr (HASZ) {
-                const int I = wr + 4 * rb;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int tr = cc * Q + 16 * I + 4 * kg + r;
-                    const uint32_t zb = off_if(tr < L, (uint32_t)tr * xrow + chan0 + 2u * m);
-#pragma unroll
-                    for (int pt = 0; pt < 2; ++pt)
-                        zz[sl][2 * r + pt] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rZ, zb + 32u * pt, 0, 0);
-                }
-            }
-        };
-
-#pragma unroll
-        for (int rb = 0; rb < RBW; ++rb) load_g(0, rb);
-        load_cz(0, 0, 0);
+        for (int rb = SRB; rb < RBW; ++rb) load_g(0, rb);
+        load_c(0, SRB, 0);
+        load_z(0, SRB, 0);
         __syncthreads();                         // chunk 0 staged, carried-in state written
         for (int c = 0; c < nc; ++c) {
             const int pb = c & 1;
-#pragma unroll
-            for (int rb = 0; rb < RBW; ++rb) {
-                const int sl = rb & 1;
-                if (rb + 1 < RBW) load_cz(c, rb + 1, sl ^ 1);
-                const int I = wr + 4 * rb;
-                const int i0 = 16 * I;
-                const int Jd = 2 * rb + jhi;     // the token block holding row block I
-                const u32x4_t* gt = &ga[rb * (rb + 1)];
-                f32x4_t off_[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-                f32x4_t dg[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-                f32x4_t yo[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-                // Every LDS operand is read one step ahead of the MFMAs that
-                // use it (the sched_barriers keep the compiler from sinking the
-                // reads back next to their use, which would expose each read's
-                // latency in turn).
-                const float si0 = s_s[pb][i0];
-                float se[2 * RBW];
-#pragma unroll
-                for (int J = 0; J <= 2 * rb; ++J) se[J] = send(pb, J);
-                u32x4_t xb[2][2];
-#pragma unroll
-                for (int pt = 0; pt < 2; ++pt) xb[0][pt] = lds128(&xsT[pb][16 * pt + m][4 * kg]);
-                // off-diagonal token blocks J < Jd: each block's product G_IJ xs_J
-                // goes to a fresh accumulator and is added scaled by the decay
-                // from the end of block J to the first row of block I (<= 1),
-                // one block behind, so the adds never wait on an MFMA.
-                f32x4_t tq[2][2];
-                const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int J = 0; J <= 2 * rb; ++J) {
-                    if (J < 2 * rb) {
-#pragma unroll
-                        for (int pt = 0; pt < 2; ++pt)
-                            xb[(J + 1) & 1][pt] = lds128(&xsT[pb][16 * pt + m][16 * (J + 1) + 4 * kg]);
+            static_for<SRB, RBW>([&](auto rbc) {
+                constexpr int rb = decltype(rbc)::value;
+                constexpr int sl = (rb - SRB) & 1;
+                if constexpr (rb + 1 < RBW) {
+                    load_c(c, rb + 1, sl ^ 1);
+                    load_z(c, rb + 1, sl ^ 1);
+                }
+                row_block(rbc, std::integral_constant<int, sl>{}, c, pb, wr, [&] {
+                    load_g(c + 1, rb);           // this row block's G tiles for the next chunk
+                    if constexpr (rb + 1 == RBW) {
+                        load_c(c + 1, SRB, 0);
+                        if constexpr (NRO % 2 == 0) load_z(c + 1, SRB, 0);
                     }
-                    __builtin_amdgcn_sched_barrier(0);
-                    if (J < Jd) {                // J = 2 rb: off-diagonal for jhi = 1 only
-#pragma unroll
-                        for (int pt = 0; pt < 2; ++pt) tq[J & 1][pt] = mfma16(gt[J], xb[J & 1][pt], zero4);
-                    }
-                    if (J > 0) {
-                        const float f = fast_exp2(si0 - se[J - 1]);
-#pragma unroll
-                        for (int pt = 0; pt < 2; ++pt) off_[pt] += f * tq[(J - 1) & 1][pt];
-                    }
-                }
-                if (jhi) {
-                    const float f = fast_exp2(si0 - se[2 * rb]);
-#pragma unroll
-                    for (int pt = 0; pt < 2; ++pt) off_[pt] += f * tq[(2 * rb) & 1][pt];
-                }
-                // operands of the diagonal block and of C H_in^T
-                const int i = i0 + m;
-                const float si = s_s[pb][i];
-                const int j0 = 32 * Jd + 8 * kg;
-                const float4 d0 = *reinterpret_cast<const float4*>(&s_dt[pb][j0]);
-                const float4 d1 = *reinterpret_cast<const float4*>(&s_dt[pb][j0 + 4]);
-                const float4 q0 = *reinterpret_cast<const float4*>(&s_s[pb][j0]);
-                const float4 q1 = *reinterpret_cast<const float4*>(&s_s[pb][j0 + 4]);
-                u32x4_t xd[2], hb[2][2];
-                uint2 xr[2];                     // x of this lane's output rows (skip term)
-#pragma unroll
-                for (int pt = 0; pt < 2; ++pt) {
-                    xd[pt] = lds128(&xT[pb][16 * pt + m][16 * Jd + 4 * kg]);
-                    hb[0][pt] = lds128(&Hb[pb][16 * pt + m][4 * kg]);
-                    xr[pt] = *reinterpret_cast<const uint2*>(&xT[pb][16 * pt + m][(i0 + 4 * kg) >> 1]);
-                }
-                const float4 sr = *reinterpret_cast<const float4*>(&s_s[pb][i0 + 4 * kg]);
-                __builtin_amdgcn_sched_barrier(0);
-                // diagonal token block: mask built element by element, dt folded in, plain x
-                {
-                    // the two candidate tiles pass through an empty asm, so the
-                    // choice stays a select: an index into `ga` would put it in scratch
-                    u32x4_t g0 = gt[2 * rb], g1 = gt[2 * rb + 1];
-                    asm("" : "+v"(g0), "+v"(g1));
-                    const u32x4_t gv = jhi ? g1 : g0;
-                    const float dj[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-                    const float sj[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-                    uint32_t av[4];
-#pragma unroll
-                    for (int e = 0; e < 8; e += 2) {
-                        const uint32_t gw = gv[e / 2];
-                        float v0 = __uint_as_float(gw << 16) * dj[e] * fast_exp2(si - sj[e]);
-                        float v1 = __uint_as_float(gw & 0xffff0000u) * dj[e + 1] * fast_exp2(si - sj[e + 1]);
-                        keep_select(v0);
-                        keep_select(v1);
-                        av[e / 2] = pack_bf16x2(j0 + e <= i ? v0 : 0.f, j0 + e + 1 <= i ? v1 : 0.f);
-                    }
-                    const u32x4_t a = {av[0], av[1], av[2], av[3]};
-#pragma unroll
-                    for (int pt = 0; pt < 2; ++pt) dg[pt] = mfma16(a, xd[pt], dg[pt]);
-                }
-                // carried-in state: C rows times H_in^T
-#pragma unroll
-                for (int nk = 0; nk < NKB; ++nk) {
-                    if (nk + 1 < NKB) {
-#pragma unroll
-                        for (int pt = 0; pt < 2; ++pt)
-                            hb[(nk + 1) & 1][pt] = lds128(&Hb[pb][16 * pt + m][16 * (nk + 1) + 4 * kg]);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                    for (int pt = 0; pt < 2; ++pt) yo[pt] = mfma16(ca[sl][nk], hb[nk & 1][pt], yo[pt]);
-                }
-                // this row block's G tiles for the next chunk
-                load_g(c + 1, rb);
-                // Next chunk's row block 0 goes to slot 0; with one row block
-                // per wave that slot still holds the gate values read below.
-                if constexpr (RBW > 1)
-                    if (rb + 1 == RBW) load_cz(c + 1, 0, 0);
-                // combine, skip, gate; the tile goes through LDS so that each
-                // lane stores 8 consecutive head channels of one token (16 bytes).
-                uint16_t* yt16 = reinterpret_cast<uint16_t*>(&ytile[wr][0][0]);
-                const float srv[4] = {sr.x, sr.y, sr.z, sr.w};
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float al = fast_exp2(srv[r] - si0);
-                    const float ei = fast_exp2(srv[r]);
-#pragma unroll
-                    for (int pt = 0; pt < 2; ++pt) {
-                        const uint32_t xw = (r >> 1) ? xr[pt].y : xr[pt].x;
-                        const float xv = __uint_as_float((r & 1) ? (xw & 0xffff0000u) : (xw << 16));
-                        float yv = al * off_[pt][r] + dg[pt][r] + ei * yo[pt][r] + dskip * xv;
-                        if constexpr (HASZ) yv *= silu(__uint_as_float(zz[sl][2 * r + pt] << 16));
-                        yt16[(4 * kg + r) * kPW + 16 * pt + m] = to_bf16(yv);
-                    }
-                }
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-                {
-                    const int tr = lane >> 2, cg = lane & 3;          // token row, 8-channel group
-                    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&ytile[wr][tr][4 * cg]);
-                    const int t = c * Q + i0 + tr;
-                    __builtin_amdgcn_raw_buffer_store_b128(v, rY, off_if(t < L, (uint32_t)t * xrow + chan0 + 16u * cg),
-                                                           0, kCached);
-                }
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-                if constexpr (RBW == 1)
-                    load_cz(c + 1, 0, 0);
-            }
+                });
+                if constexpr (rb + 1 == RBW && NRO % 2 == 1) load_z(c + 1, SRB, 0);
+            });
             __syncthreads();
         }
     } else {
@@ -616,6 +647,11 @@ __global__ __launch_bounds__(512) void ssd_main_kernel(
 
         stage_load(0);
         load_bt_ahead(0);
+        if constexpr (SRB > 0) {                 // the first round of row blocks: I = wr
+            load_g(0, 0);
+            load_c(0, 0, 0);
+            load_z(0, 0, 0);
+        }
         write_hb(0);
         float s_end = stage_store(0);
         if (nc > 1) stage_load(1);
@@ -654,6 +690,14 @@ __global__ __launch_bounds__(512) void ssd_main_kernel(
 #pragma unroll
                 for (int k = k0; k < k0 + BSL; ++k)
                     if (k + BSL < NBW) load_bt(c, k + BSL);
+            }
+            // row block I = wr of this chunk, while the MFMAs above drain
+            if constexpr (SRB > 0) {
+                row_block(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, c, pb, 4 + wr, [&] {
+                    load_g(c + 1, 0);
+                    load_c(c + 1, 0, 0);
+                });
+                load_z(c + 1, 0, 0);
             }
             // the next chunk (past the last one: zeros, results unused)
             load_bt_ahead(c + 1);
