@@ -47,6 +47,12 @@ CASES = [
     (1, 1, 2, 64, 2, 64, True, True, True),
     (1, 777, 8, 128, 4, 128, True, True, False),
     (2, 1024, 4, 32, 1, 256, False, True, True),
+    # gate at chunk 256 (three rounds of row blocks on the output waves, one
+    # on the state waves), and the other d_state values at chunk 128 / 256
+    (1, 600, 4, 128, 1, 256, True, True, True),
+    (1, 300, 2, 64, 1, 256, True, False, False),
+    (1, 200, 2, 256, 2, 128, True, True, True),
+    (1, 130, 2, 32, 1, 128, False, True, True),
 ]
 
 
