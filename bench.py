@@ -266,12 +266,29 @@ def bench_s6bwd(args):
     steps = max(3, args.steps // 4)
     total, _ = time_launches(step, steps, 1, stream, warm_ms=WARM_MS)
     ms = total / steps
+    # The training pair: the forward that keeps the chunk-start states in the
+    # workspace, and the backward that starts from them.
+    y = torch.empty_like(d["u"])
+
+    def fwd_save():
+        mssm.selective_scan(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], d["h0"], out=y,
+                            save_workspace=ws, stream=stream)
+
+    def bwd_saved():
+        mssm.selective_scan_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], dout, d["D"], d["z"], d["h0"], dhT,
+                                workspace=ws, saved=True, stream=stream)
+
+    fwd_save()
+    total_s, _ = time_launches(bwd_saved, steps, 1, stream, warm_ms=WARM_MS)
+    total_f, _ = time_launches(fwd_save, steps, 1, stream, warm_ms=WARM_MS)
     B, D, L, N = s["batch"], s["d_inner"], s["seqlen"], s["d_state"]
     # read u, delta, z, dout (twice: forward sweep reads u, delta) ; write du, ddelta, dz; dB, dC; state checkpoints
     nb = (6 + 3) * B * D * L * 2 + 2 * B * N * L * (2 + 4) + 2 * ws.numel()
     return {"workload": f"{wl.name} backward: batch {B}, d_inner {D}, seqlen {L}, d_state {N}, bf16, "
                         "gate, skip, h0 and final-state gradient",
-            "us": ms * 1e3, "tokens_ch_per_s": B * D * L / (ms * 1e-3), "bytes_moved_estimate": nb,
+            "us": ms * 1e3, "us_from_saved_states": total_s / steps * 1e3,
+            "us_forward_saving_states": total_f / steps * 1e3,
+            "tokens_ch_per_s": B * D * L / (ms * 1e-3), "bytes_moved_estimate": nb,
             "GBs_estimate": nb / (ms * 1e-3) / 1e9, "workspace_bytes": ws.numel(),
             "traffic_bytes_per_call": {"s6_scan_bwd_kernel": profiled_traffic("s6_scan_bwd_mamba1p4b_bf16.md"),
                                        "s6_bwd_reduce_bc_kernel": profiled_traffic("s6_bwd_reduce_bc_mamba1p4b_bf16.md")}}

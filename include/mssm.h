@@ -4,12 +4,16 @@
  *
  * Seven operations, each defined by the pages it cites:
  *
- *   mssm_selective_scan_fwd  the S6 selective scan over a whole sequence;
+ *   mssm_selective_scan_fwd  the S6 selective scan over a whole sequence
+ *                            (mssm_selective_scan_fwd_save: the same, also
+ *                            keeping the states the backward starts from);
  *   mssm_selective_scan_zoh_fwd  the same scan with the zero-order-hold
  *                            input term;
  *   mssm_selective_scan_fused_fwd  the same scan with its input front end
  *                            (causal conv1d + SiLU, softplus step) fused in;
- *   mssm_selective_scan_bwd  the gradients of that scan (training);
+ *   mssm_selective_scan_bwd  the gradients of that scan (training;
+ *                            mssm_selective_scan_bwd_saved: from the states
+ *                            mssm_selective_scan_fwd_save kept);
  *   mssm_state_update        one decode token of the same recurrence;
  *   mssm_ssd_chunk_fwd       the Mamba-2 SSD (scalar transition per head),
  *                            computed chunk by chunk;
@@ -194,6 +198,45 @@ int mssm_selective_scan_bwd(const void* u, const void* delta, const float* A, co
                             int64_t batch, int64_t d_inner, int64_t seqlen, int64_t d_state,
                             void* workspace, size_t workspace_bytes, mssm_dtype dtype,
                             void* stream);
+
+/*
+ * The training pair: a forward scan that keeps the states the backward starts
+ * its chunks from, and the backward that uses them instead of re-running the
+ * recurrence over the whole sequence first.
+ *
+ * Defined by: the same recurrence and gradients as mssm_selective_scan_fwd and
+ * mssm_selective_scan_bwd; "State-Space Model Optimization Patterns" page,
+ * section 4 -- the forward saves states at chunk boundaries and the backward
+ * recomputes within each chunk from them.
+ *
+ * mssm_selective_scan_fwd_save takes the arguments of mssm_selective_scan_fwd
+ * plus `workspace` / `workspace_bytes`: a (device) buffer of at least
+ * mssm_selective_scan_bwd_workspace_size(batch, d_inner, seqlen, d_state)
+ * bytes, 16-byte aligned, owned by the caller.  It writes y and h_final
+ * exactly as mssm_selective_scan_fwd does (bit for bit), and the state at
+ * every backward chunk start into the front of the workspace.
+ *
+ * mssm_selective_scan_bwd_saved takes the arguments of mssm_selective_scan_bwd
+ * and returns the same gradients (bit for bit, dA and dD up to the order of
+ * their atomic sums), provided its `workspace` still holds what
+ * mssm_selective_scan_fwd_save wrote there for the same u, delta, A, Bm, h0
+ * and sizes.  Anything else in the workspace gives wrong gradients; this is
+ * not checked.  Errors and limits: as the two calls they mirror.
+ */
+int mssm_selective_scan_fwd_save(const void* u, const void* delta, const float* A,
+                                 const void* Bm, const void* Cm, const float* Dskip,
+                                 const void* z, const float* h0, void* y, float* h_final,
+                                 int64_t batch, int64_t d_inner, int64_t seqlen,
+                                 int64_t d_state, void* workspace, size_t workspace_bytes,
+                                 mssm_dtype dtype, void* stream);
+int mssm_selective_scan_bwd_saved(const void* u, const void* delta, const float* A,
+                                  const void* Bm, const void* Cm, const float* Dskip,
+                                  const void* z, const float* h0, const void* dout,
+                                  const float* dh_final, void* du, void* ddelta, float* dA,
+                                  float* dB, float* dC, float* dD, void* dz, float* dh0,
+                                  int64_t batch, int64_t d_inner, int64_t seqlen,
+                                  int64_t d_state, void* workspace, size_t workspace_bytes,
+                                  mssm_dtype dtype, void* stream);
 
 /*
  * Decode: one token of the same recurrence, state updated in place.

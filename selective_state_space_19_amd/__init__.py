@@ -54,12 +54,14 @@ def _stream(stream, device):
 
 
 def selective_scan(u, delta, A, B, C, D=None, z=None, h0=None, *, return_final_state=False,
-                   out=None, h_final=None, stream=None, zoh=False):
+                   out=None, h_final=None, stream=None, zoh=False, save_workspace=None):
     """S6 scan.  u, delta, z: [b, d, L]; B, C: [b, N, L] (float32 or bfloat16,
     all the same); A: [d, N] float32; D: [d] float32; h0: [b, d, N] float32.
     Returns y [b, d, L] (u's dtype), and h_final [b, d, N] float32 if asked.
     zoh: the zero-order-hold input term (exp(delta A) - 1) / A * B instead of
-    the Euler delta * B."""
+    the Euler delta * B.  save_workspace: a GPU buffer of at least
+    selective_scan_bwd_workspace_size(b, d, L, N) bytes that also receives the
+    states selective_scan_bwd(..., workspace=it, saved=True) starts from."""
     torch = _torch()
     dev = u.device
     u = _dev(u, "u")
@@ -84,9 +86,17 @@ def selective_scan(u, delta, A, B, C, D=None, z=None, h0=None, *, return_final_s
         _dev(hf, "h_final", (bsz, dim, N), torch.float32, dev)
         if not hf.is_contiguous():
             raise ValueError("h_final must be contiguous")
-    fn = lib().mssm_selective_scan_zoh_fwd if zoh else lib().mssm_selective_scan_fwd
-    check(fn(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(hf),
-             bsz, dim, L, N, code, _stream(stream, dev)))
+    if save_workspace is not None:
+        if zoh:
+            raise ValueError("save_workspace is for the Euler scan (the backward pass is of that scan)")
+        ws = _dev(save_workspace, "save_workspace", device=dev)
+        check(lib().mssm_selective_scan_fwd_save(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                                 _ptr(h0), _ptr(y), _ptr(hf), bsz, dim, L, N, _ptr(ws),
+                                                 ws.numel() * ws.element_size(), code, _stream(stream, dev)))
+    else:
+        fn = lib().mssm_selective_scan_zoh_fwd if zoh else lib().mssm_selective_scan_fwd
+        check(fn(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(hf),
+                 bsz, dim, L, N, code, _stream(stream, dev)))
     return (y, hf) if hf is not None else y
 
 
@@ -138,12 +148,13 @@ def selective_scan_bwd_workspace_size(batch, d_inner, seqlen, d_state):
 
 
 def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, h0=None, dh_final=None, *, workspace=None,
-                       stream=None):
+                       saved=False, stream=None):
     """Gradients of the S6 scan for the loss sum(dout * y) + sum(dh_final *
     h_final).  Inputs as selective_scan; dout: [b, d, L] (u's dtype);
     dh_final: [b, d, N] float32.  Returns a dict: du, ddelta (and dz if z)
     [b, d, L] in u's dtype; dA [d, N], dB, dC [b, N, L], dD [d] (if D) and
-    dh0 [b, d, N] (if h0) in float32."""
+    dh0 [b, d, N] (if h0) in float32.  saved: `workspace` holds the states
+    that selective_scan(..., save_workspace=workspace) kept for these inputs."""
     torch = _torch()
     dev = u.device
     u = _dev(u, "u")
@@ -168,12 +179,14 @@ def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, h0=None, dh_fina
     g["dh0"] = torch.empty((bsz, dim, N), **f32) if h0 is not None else None
     need = selective_scan_bwd_workspace_size(bsz, dim, L, N)
     if workspace is None:
+        if saved:
+            raise ValueError("saved=True needs the workspace the forward call filled")
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    check(lib().mssm_selective_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
-                                        _ptr(dout), _ptr(dh_final), _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]),
-                                        _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["dh0"]),
-                                        bsz, dim, L, N, _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                        code, _stream(stream, dev)))
+    fn = lib().mssm_selective_scan_bwd_saved if saved else lib().mssm_selective_scan_bwd
+    check(fn(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(dout),
+             _ptr(dh_final), _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
+             _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["dh0"]), bsz, dim, L, N, _ptr(workspace),
+             workspace.numel() * workspace.element_size(), code, _stream(stream, dev)))
     return {k: v for k, v in g.items() if v is not None}
 
 

@@ -47,6 +47,10 @@ def _bind(lib):
     lib.mssm_selective_scan_bwd_workspace_size.restype = _sz
     lib.mssm_selective_scan_bwd.argtypes = [_vp] * 18 + [_i64] * 4 + [_vp, _sz, _i32, _vp]
     lib.mssm_selective_scan_bwd.restype = _i32
+    lib.mssm_selective_scan_fwd_save.argtypes = [_vp] * 10 + [_i64] * 4 + [_vp, _sz, _i32, _vp]
+    lib.mssm_selective_scan_fwd_save.restype = _i32
+    lib.mssm_selective_scan_bwd_saved.argtypes = [_vp] * 18 + [_i64] * 4 + [_vp, _sz, _i32, _vp]
+    lib.mssm_selective_scan_bwd_saved.restype = _i32
     lib.mssm_state_update.argtypes = [_vp] * 9 + [_i64] * 3 + [_i32, _vp]
     lib.mssm_state_update.restype = _i32
     lib.mssm_ssd_state_update.argtypes = [_vp] * 9 + [_i64] * 5 + [_i32, _vp]

@@ -19,6 +19,7 @@ struct S6Params {
     float* h_final;       // nullable
     int64_t batch, dim;
     int32_t L, N;
+    float* ckpt;          // nullable: the states at every backward-chunk start, in the backward's workspace layout
 };
 
 // Front end of the scan: u = silu(causal depthwise conv1d(x)) with K taps
@@ -40,6 +41,7 @@ struct S6BwdParams {
     float* part;                                  // dB / dC partial sums per channel block
     int64_t batch, dim;
     int32_t L, N;
+    int32_t saved;                                // ws already holds the chunk-start states (from the forward)
 };
 
 struct SUParams {

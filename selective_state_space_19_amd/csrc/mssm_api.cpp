@@ -64,10 +64,12 @@ const char* mssm_last_error(void) { return g_err.c_str(); }
 
 int mssm_version(void) { return 100; }
 
-static int scan_fwd(const char* fn, bool zoh, const void* u, const void* delta, const float* A, const void* Bm,
-                    const void* Cm, const float* Dskip, const void* z, const float* h0, void* y, float* h_final,
-                    int64_t batch, int64_t d_inner, int64_t seqlen, int64_t d_state, mssm_dtype dtype,
-                    void* stream) {
+// save: the chunk-start states for mssm_selective_scan_bwd_saved go to the
+// start of `workspace` (the backward's own workspace, of its size).
+static int scan_fwd(const char* fn, bool zoh, bool save, const void* u, const void* delta, const float* A,
+                    const void* Bm, const void* Cm, const float* Dskip, const void* z, const float* h0, void* y,
+                    float* h_final, int64_t batch, int64_t d_inner, int64_t seqlen, int64_t d_state,
+                    void* workspace, size_t workspace_bytes, mssm_dtype dtype, void* stream) {
     g_err.clear();
     if (dtype != MSSM_F32 && dtype != MSSM_BF16) return fail(MSSM_ERR_DTYPE, "%s: unknown dtype %d", fn, (int)dtype);
     if (batch < 0 || d_inner < 0 || seqlen < 0 || d_state < 0)
@@ -94,7 +96,16 @@ static int scan_fwd(const char* fn, bool zoh, const void* u, const void* delta, 
     CHECK_OPT(z);
     const int64_t blocks = ((d_inner + 63) / 64) * batch;
     if (blocks > INT32_MAX) return fail(MSSM_ERR_UNSUPPORTED, "%s: batch*d_inner too large", fn);
-    mssm::S6Params p{u, delta, Bm, Cm, z, A, Dskip, h0, y, h_final, batch, d_inner, (int32_t)seqlen, (int32_t)d_state};
+    float* ckpt = nullptr;
+    if (save) {
+        const size_t need = mssm::s6_bwd_workspace_bytes(batch, d_inner, seqlen, d_state);
+        if (!workspace || workspace_bytes < need)
+            return fail(MSSM_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace_bytes);
+        CHECK_OPT(workspace);
+        ckpt = static_cast<float*>(workspace);
+    }
+    mssm::S6Params p{u, delta, Bm, Cm, z, A, Dskip, h0, y, h_final, batch, d_inner, (int32_t)seqlen, (int32_t)d_state,
+                     ckpt};
     return launched(fn, mssm::launch_s6_scan(p, dtype == MSSM_BF16, zoh, s));
 }
 
@@ -102,16 +113,25 @@ int mssm_selective_scan_fwd(const void* u, const void* delta, const float* A, co
                             const void* Cm, const float* Dskip, const void* z, const float* h0,
                             void* y, float* h_final, int64_t batch, int64_t d_inner, int64_t seqlen,
                             int64_t d_state, mssm_dtype dtype, void* stream) {
-    return scan_fwd("mssm_selective_scan_fwd", false, u, delta, A, Bm, Cm, Dskip, z, h0, y, h_final, batch,
-                    d_inner, seqlen, d_state, dtype, stream);
+    return scan_fwd("mssm_selective_scan_fwd", false, false, u, delta, A, Bm, Cm, Dskip, z, h0, y, h_final, batch,
+                    d_inner, seqlen, d_state, nullptr, 0, dtype, stream);
+}
+
+int mssm_selective_scan_fwd_save(const void* u, const void* delta, const float* A, const void* Bm,
+                                 const void* Cm, const float* Dskip, const void* z, const float* h0,
+                                 void* y, float* h_final, int64_t batch, int64_t d_inner, int64_t seqlen,
+                                 int64_t d_state, void* workspace, size_t workspace_bytes, mssm_dtype dtype,
+                                 void* stream) {
+    return scan_fwd("mssm_selective_scan_fwd_save", false, true, u, delta, A, Bm, Cm, Dskip, z, h0, y, h_final,
+                    batch, d_inner, seqlen, d_state, workspace, workspace_bytes, dtype, stream);
 }
 
 int mssm_selective_scan_zoh_fwd(const void* u, const void* delta, const float* A, const void* Bm,
                                 const void* Cm, const float* Dskip, const void* z, const float* h0,
                                 void* y, float* h_final, int64_t batch, int64_t d_inner, int64_t seqlen,
                                 int64_t d_state, mssm_dtype dtype, void* stream) {
-    return scan_fwd("mssm_selective_scan_zoh_fwd", true, u, delta, A, Bm, Cm, Dskip, z, h0, y, h_final, batch,
-                    d_inner, seqlen, d_state, dtype, stream);
+    return scan_fwd("mssm_selective_scan_zoh_fwd", true, false, u, delta, A, Bm, Cm, Dskip, z, h0, y, h_final,
+                    batch, d_inner, seqlen, d_state, nullptr, 0, dtype, stream);
 }
 
 int mssm_selective_scan_fused_fwd(const void* x, const float* conv_w, const float* conv_b, const void* conv_init,
@@ -163,13 +183,13 @@ size_t mssm_selective_scan_bwd_workspace_size(int64_t batch, int64_t d_inner, in
     return mssm::s6_bwd_workspace_bytes(batch, d_inner, seqlen, d_state);
 }
 
-int mssm_selective_scan_bwd(const void* u, const void* delta, const float* A, const void* Bm, const void* Cm,
-                            const float* Dskip, const void* z, const float* h0, const void* dout,
-                            const float* dh_final, void* du, void* ddelta, float* dA, float* dB, float* dC,
-                            float* dD, void* dz, float* dh0, int64_t batch, int64_t d_inner, int64_t seqlen,
-                            int64_t d_state, void* workspace, size_t workspace_bytes, mssm_dtype dtype,
-                            void* stream) {
-    static const char* fn = "mssm_selective_scan_bwd";
+// saved: the workspace already holds the chunk-start states written by
+// mssm_selective_scan_fwd_save, so the kernel skips its forward sweep.
+static int scan_bwd(const char* fn, bool saved, const void* u, const void* delta, const float* A, const void* Bm,
+                    const void* Cm, const float* Dskip, const void* z, const float* h0, const void* dout,
+                    const float* dh_final, void* du, void* ddelta, float* dA, float* dB, float* dC, float* dD,
+                    void* dz, float* dh0, int64_t batch, int64_t d_inner, int64_t seqlen, int64_t d_state,
+                    void* workspace, size_t workspace_bytes, mssm_dtype dtype, void* stream) {
     g_err.clear();
     if (dtype != MSSM_F32 && dtype != MSSM_BF16) return fail(MSSM_ERR_DTYPE, "%s: unknown dtype %d", fn, (int)dtype);
     if (batch < 0 || d_inner < 0 || seqlen < 0 || d_state < 0)
@@ -207,8 +227,30 @@ int mssm_selective_scan_bwd(const void* u, const void* delta, const float* A, co
     float* ws = static_cast<float*>(workspace);
     mssm::S6BwdParams p{u, delta, Bm, Cm, z, dout, A, Dskip, h0, dh_final, du, ddelta, dz, dA, dB, dC, dD, dh0,
                         ws, ws + mssm::s6_bwd_ckpt_floats(batch, d_inner, seqlen, d_state), batch, d_inner,
-                        (int32_t)seqlen, (int32_t)d_state};
+                        (int32_t)seqlen, (int32_t)d_state, saved ? 1 : 0};
     return launched(fn, mssm::launch_s6_scan_bwd(p, dtype == MSSM_BF16, static_cast<hipStream_t>(stream)));
+}
+
+int mssm_selective_scan_bwd(const void* u, const void* delta, const float* A, const void* Bm, const void* Cm,
+                            const float* Dskip, const void* z, const float* h0, const void* dout,
+                            const float* dh_final, void* du, void* ddelta, float* dA, float* dB, float* dC,
+                            float* dD, void* dz, float* dh0, int64_t batch, int64_t d_inner, int64_t seqlen,
+                            int64_t d_state, void* workspace, size_t workspace_bytes, mssm_dtype dtype,
+                            void* stream) {
+    return scan_bwd("mssm_selective_scan_bwd", false, u, delta, A, Bm, Cm, Dskip, z, h0, dout, dh_final, du, ddelta,
+                    dA, dB, dC, dD, dz, dh0, batch, d_inner, seqlen, d_state, workspace, workspace_bytes, dtype,
+                    stream);
+}
+
+int mssm_selective_scan_bwd_saved(const void* u, const void* delta, const float* A, const void* Bm,
+                                  const void* Cm, const float* Dskip, const void* z, const float* h0,
+                                  const void* dout, const float* dh_final, void* du, void* ddelta, float* dA,
+                                  float* dB, float* dC, float* dD, void* dz, float* dh0, int64_t batch,
+                                  int64_t d_inner, int64_t seqlen, int64_t d_state, void* workspace,
+                                  size_t workspace_bytes, mssm_dtype dtype, void* stream) {
+    return scan_bwd("mssm_selective_scan_bwd_saved", true, u, delta, A, Bm, Cm, Dskip, z, h0, dout, dh_final, du,
+                    ddelta, dA, dB, dC, dD, dz, dh0, batch, d_inner, seqlen, d_state, workspace, workspace_bytes,
+                    dtype, stream);
 }
 
 int mssm_state_update(float* state, const void* u, const void* delta, const float* A, const void* Bm,

@@ -69,17 +69,25 @@ constexpr int kScanWaves = 8;     // waves running the recurrence
 constexpr int kRowWaves = 4;      // waves streaming rows: loads, staging, epilogue
 constexpr int kRing = 4;          // row-wave register ring: chunks of loads in flight + 1
 
-template <typename T, int NS, int TC, bool ALIGNED, bool FULLN, bool FUSED, bool ZOH, int RING>
+// Tokens between the saved states the backward pass starts its chunks from
+// (its chunk length: 16 with up to 2 states per lane, else 8).
+template <int NS> constexpr int kCkptLen = NS <= 2 ? 16 : 8;
+
+template <typename T, int NS, int TC, bool ALIGNED, bool FULLN, bool FUSED, bool ZOH, bool CKPT, int RING>
 __global__ __launch_bounds__((kScanWaves + kRowWaves) * 64) void s6_scan_kernel(
     const T* __restrict__ u_in, const T* __restrict__ dl_in, const T* __restrict__ B_in,
     const T* __restrict__ C_in, const T* __restrict__ z_in, const float* __restrict__ A_in,
     const float* __restrict__ D_in, const float* __restrict__ h0_in, T* __restrict__ y_out,
-    float* __restrict__ hT_out, int64_t dim, int L, int N, S6FrontEnd fe) {
+    float* __restrict__ hT_out, int64_t dim, int L, int N, S6FrontEnd fe, float* __restrict__ ck_out) {
     // FUSED: u_in is x before the causal conv and dl_in the step before
     // softplus; the row waves form u = silu(conv(x)) and delta =
     // softplus(raw + bias) while staging.  ZOH: the input term is the
     // zero-order hold (exp(delta*A) - 1) / A * u * B instead of delta * u * B
-    // ("State-Space Model Optimization Patterns" page, section 7).
+    // ("State-Space Model Optimization Patterns" page, section 7).  CKPT: the
+    // scan waves also store the state at every kCkptLen-th token (before it
+    // is applied) for the backward pass, which then need not re-run the
+    // recurrence to find its chunk starts ("State-Space Model Optimization
+    // Patterns" page, section 4: recompute within chunks from saved states).
     // Pointers are separate __restrict__ arguments so the compiler may fetch the
     // wave-uniform B / C words with scalar loads (it must know no store aliases them).
     constexpr int NW = kScanWaves;
@@ -178,7 +186,7 @@ __global__ __launch_bounds__((kScanWaves + kRowWaves) * 64) void s6_scan_kernel(
         // factors and input terms of the whole group are formed first (they do
         // not depend on h), so each exp has independent work behind it; then the
         // recurrence runs token by token.
-        auto group = [&](int buf, int gi, int par) {
+        auto group = [&](int buf, int gi, int par, int tg) {
             float dA[G][NS], bu[G][NS];
 #pragma unroll
             for (int k = 0; k < G; k += 2) {
@@ -200,12 +208,25 @@ __global__ __launch_bounds__((kScanWaves + kRowWaves) * 64) void s6_scan_kernel(
             for (int k = 0; k < G; k += 4) {
                 float yv[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
+                for (int kk = 0; kk < 4; ++kk) {
+                    if constexpr (CKPT) {
+                        // the state entering token tg + k + kk, if a backward chunk starts there
+                        constexpr int CK = kCkptLen<NS>;
+                        const int t = tg + k + kk;
+                        if ((t % CK) == 0 && t < L && sval_d) {
+                            const int nckb = (L + CK - 1) / CK;
+#pragma unroll
+                            for (int s = 0; s < NS; ++s)
+                                if (sval[s])
+                                    ck_out[((b * nckb + t / CK) * N + w * NS + s) * dim + d0 + cs] = h[s];
+                        }
+                    }
 #pragma unroll
                     for (int s = 0; s < NS; ++s) {
                         h[s] = fmaf(dA[k + kk][s], h[s], bu[k + kk][s]);
                         yv[kk] = fmaf(cval(buf, s, k + kk), h[s], yv[kk]);
                     }
+                }
                 s_y[par][w][gi * (G / 4) + k / 4][cs] = make_float4(yv[0], yv[1], yv[2], yv[3]);
             }
         };
@@ -240,7 +261,7 @@ __global__ __launch_bounds__((kScanWaves + kRowWaves) * 64) void s6_scan_kernel(
                 if (((gi & 1) ^ (w >> 2)) & 1) __builtin_amdgcn_s_setprio(1);
                 else __builtin_amdgcn_s_setprio(0);
                 __builtin_amdgcn_sched_barrier(0);
-                group(cur, gi, par);
+                group(cur, gi, par, t0 + gi * G);
                 lgkm_wait_all();
             }
         }
@@ -441,21 +462,25 @@ hipError_t launch_cfg(const S6Params& p, const S6FrontEnd* fe, bool zoh, hipStre
     // offsets, and reads B / C in whole 32-byte groups.
     const bool aligned = (p.L % (32 / int(sizeof(T))) == 0) && int64_t(64) * p.L * int64_t(sizeof(T)) < (int64_t(1) << 31);
     const bool fulln = p.N == kScanWaves * NS;
-    // The hold form is built for the plain scan only (the fused front end is Euler).
-    auto kern = fe ? (aligned ? (fulln ? s6_scan_kernel<T, NS, TC, true, true, true, false, kRing>
-                                       : s6_scan_kernel<T, NS, TC, true, false, true, false, kRing>)
-                              : s6_scan_kernel<T, NS, TC, false, false, true, false, kRing>)
-            : zoh ? (aligned ? (fulln ? s6_scan_kernel<T, NS, TC, true, true, false, true, kRing>
-                                      : s6_scan_kernel<T, NS, TC, true, false, false, true, kRing>)
-                             : s6_scan_kernel<T, NS, TC, false, false, false, true, kRing>)
-                  : (aligned ? (fulln ? s6_scan_kernel<T, NS, TC, true, true, false, false, kRing>
-                                      : s6_scan_kernel<T, NS, TC, true, false, false, false, kRing>)
-                             : s6_scan_kernel<T, NS, TC, false, false, false, false, kRing>);
+    // The hold form and the saved states are built for the plain scan only
+    // (the fused front end is Euler; the backward pass is of the plain scan).
+    auto kern = fe ? (aligned ? (fulln ? s6_scan_kernel<T, NS, TC, true, true, true, false, false, kRing>
+                                       : s6_scan_kernel<T, NS, TC, true, false, true, false, false, kRing>)
+                              : s6_scan_kernel<T, NS, TC, false, false, true, false, false, kRing>)
+            : zoh ? (aligned ? (fulln ? s6_scan_kernel<T, NS, TC, true, true, false, true, false, kRing>
+                                      : s6_scan_kernel<T, NS, TC, true, false, false, true, false, kRing>)
+                             : s6_scan_kernel<T, NS, TC, false, false, false, true, false, kRing>)
+            : p.ckpt ? (aligned ? (fulln ? s6_scan_kernel<T, NS, TC, true, true, false, false, true, kRing>
+                                         : s6_scan_kernel<T, NS, TC, true, false, false, false, true, kRing>)
+                                : s6_scan_kernel<T, NS, TC, false, false, false, false, true, kRing>)
+                  : (aligned ? (fulln ? s6_scan_kernel<T, NS, TC, true, true, false, false, false, kRing>
+                                      : s6_scan_kernel<T, NS, TC, true, false, false, false, false, kRing>)
+                             : s6_scan_kernel<T, NS, TC, false, false, false, false, false, kRing>);
     const S6FrontEnd none{};
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3((kScanWaves + kRowWaves) * 64), 0, stream,
                        static_cast<const T*>(p.u), static_cast<const T*>(p.delta), static_cast<const T*>(p.Bm),
                        static_cast<const T*>(p.Cm), static_cast<const T*>(p.z), p.A, p.Dskip, p.h0,
-                       static_cast<T*>(p.y), p.h_final, p.dim, p.L, p.N, fe ? *fe : none);
+                       static_cast<T*>(p.y), p.h_final, p.dim, p.L, p.N, fe ? *fe : none, p.ckpt);
     return hipGetLastError();
 }
 

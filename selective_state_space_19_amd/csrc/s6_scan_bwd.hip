@@ -22,7 +22,8 @@
 //   1. Forward sweep over the whole sequence in chunks of TC tokens (16, or 8
 //      when a lane holds more than 2 states), writing
 //      the state at every chunk start to the workspace (one fp32 per
-//      channel, state and chunk).
+//      channel, state and chunk).  Skipped (p.saved) when the forward scan
+//      has already stored those states there.
 //   2. Backward sweep, last chunk first: stage (delta, delta*u, u, g) of the
 //      chunk in LDS; recompute the chunk's TC states from its checkpoint into
 //      registers (the per-wave partial outputs go to LDS, from which the row
@@ -291,11 +292,13 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
 #pragma unroll
         for (int j = 0; j < kTPT; ++j) s_fw[ck & 1][toff + j][cr] = make_float2(dlv[j], dlv[j] * uv[j]);
     };
-    if (nck > 0) {
+    // (skipped when the forward pass saved the chunk-start states: p.saved)
+    const int nck_fwd = p.saved ? 0 : nck;
+    if (nck_fwd > 0) {
         fetch_fwd(0);
         stage_fwd(0);
     }
-    for (int ck = 0; ck < nck; ++ck) {
+    for (int ck = 0; ck < nck_fwd; ++ck) {
         if (cval) {
 #pragma unroll
             for (int s = 0; s < NS; ++s)
@@ -309,7 +312,7 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
 #pragma unroll
             for (int s = 0; s < NS; ++s) h[s] = fmaf(fast_exp2(q.x * a2[s]), h[s], q.y * Bf[s][k]);
         }
-        if (ck + 1 < nck) stage_fwd(ck + 1);
+        if (ck + 1 < nck_fwd) stage_fwd(ck + 1);
     }
     __syncthreads();                              // the backward sweep reuses the B / C buffers
 

@@ -21,6 +21,7 @@ def test_exports_every_declared_function(lib):
     names = _lib.header_functions()
     assert set(names) == {"mssm_selective_scan_fwd", "mssm_selective_scan_zoh_fwd",
                           "mssm_selective_scan_fused_fwd", "mssm_selective_scan_bwd",
+                          "mssm_selective_scan_fwd_save", "mssm_selective_scan_bwd_saved",
                           "mssm_selective_scan_bwd_workspace_size", "mssm_state_update",
                           "mssm_ssd_workspace_size",
                           "mssm_ssd_chunk_fwd", "mssm_ssd_state_update", "mssm_last_error", "mssm_version"}
@@ -57,6 +58,25 @@ def test_scan_argument_errors(lib, zoh):
     assert _scan(lib, z=MISALIGNED) == ERR_ALIGN
     assert _scan(lib, b=1 << 40, d=1 << 40) == ERR_SHAPE
     assert _scan(lib, b=0) == 0           # nothing to do, nothing launched
+
+
+def test_scan_save_argument_errors(lib):
+    a = dict(u=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, h0=None, y=FAKE, hf=None,
+             b=2, d=64, L=128, N=16, dtype=1)
+    need = lib.mssm_selective_scan_bwd_workspace_size(2, 64, 128, 16)
+
+    def save(ws, wsb, **kw):
+        v = dict(a, **kw)
+        return lib.mssm_selective_scan_fwd_save(v["u"], v["delta"], v["A"], v["B"], v["C"], v["D"], v["z"], v["h0"],
+                                                v["y"], v["hf"], v["b"], v["d"], v["L"], v["N"], ws, wsb,
+                                                v["dtype"], None)
+    assert save(None, need) == ERR_WS
+    assert b"workspace" in lib.mssm_last_error()
+    assert save(FAKE, need - 1) == ERR_WS
+    assert save(MISALIGNED, need) == ERR_ALIGN
+    assert save(FAKE, need, u=None) == ERR_NULL
+    assert save(FAKE, need, N=65) == ERR_UNSUP
+    assert save(FAKE, need, b=0) == 0
 
 
 def _su(lib, **kw):
@@ -148,18 +168,22 @@ def test_fused_scan_argument_errors(lib):
     assert _fused(lib, b=0) == 0
 
 
-def _bwd(lib, **kw):
+def _bwd_any(lib, saved=False, **kw):
     a = dict(u=FAKE, dl=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, h0=None, go=FAKE, dhT=None, du=FAKE, dd=FAKE,
              dA=FAKE, dB=FAKE, dC=FAKE, dD=None, dz=None, dh0=None, b=2, d=64, L=128, N=16, ws=FAKE, wsb=1 << 40,
              dtype=1)
     a.update(kw)
-    return lib.mssm_selective_scan_bwd(a["u"], a["dl"], a["A"], a["B"], a["C"], a["D"], a["z"], a["h0"], a["go"],
-                                       a["dhT"], a["du"], a["dd"], a["dA"], a["dB"], a["dC"], a["dD"], a["dz"],
-                                       a["dh0"], a["b"], a["d"], a["L"], a["N"], a["ws"], a["wsb"], a["dtype"], None)
+    fn = lib.mssm_selective_scan_bwd_saved if saved else lib.mssm_selective_scan_bwd
+    return fn(a["u"], a["dl"], a["A"], a["B"], a["C"], a["D"], a["z"], a["h0"], a["go"], a["dhT"], a["du"], a["dd"],
+              a["dA"], a["dB"], a["dC"], a["dD"], a["dz"], a["dh0"], a["b"], a["d"], a["L"], a["N"], a["ws"], a["wsb"],
+              a["dtype"], None)
 
 
-def test_backward_argument_errors(lib):
+@pytest.mark.parametrize("saved", [False, True])
+def test_backward_argument_errors(lib, saved):
+    _bwd = functools.partial(_bwd_any, saved=saved)
     assert _bwd(lib, go=None) == ERR_NULL
+    assert (b"saved" in lib.mssm_last_error()) == saved
     assert _bwd(lib, dB=None) == ERR_NULL
     assert _bwd(lib, z=FAKE, dz=None) == ERR_NULL
     assert _bwd(lib, N=65) == ERR_UNSUP

@@ -106,3 +106,76 @@ def test_mamba1p4b_backward_sampled():
     say("  1.4B bwd sampled: " + ", ".join(f"{k} {v:.2e}" for k, v in sorted(errs.items())))
     for k, v in errs.items():
         assert v <= TOL[w.dtype], f"{k} normwise error {v}"
+
+
+# ---- the training pair: forward that keeps the chunk-start states, backward from them ----
+
+SAVE_CASES = [
+    # (batch, d_inner, L, N, dtype, gate, skip, h0, dhT)
+    (1, 1, 1, 1, "f32", True, True, True, True),          # one state per lane, one token
+    (2, 100, 65, 16, "f32", True, True, True, True),      # 2 per lane, L past a 16-token chunk
+    (1, 70, 130, 17, "bf16", True, True, True, False),    # 4 per lane: 8-token chunks; ragged L
+    (1, 128, 40, 64, "f32", True, True, True, True),      # 8 per lane
+    (2, 64, 256, 16, "bf16", False, True, False, True),   # whole 16-token groups, no h0
+    (1, 64, 96, 32, "bf16", True, False, True, True),     # 8-token chunks inside 16-token groups
+]
+
+
+def _both(inp, seed):
+    """Plain forward + backward, and the saving forward + the backward from the
+    saved states, on the same inputs."""
+    import torch
+    dt = inp["dtype"]
+    b, d, L = inp["u"].shape
+    N = inp["A"].shape[1]
+    rng = np.random.default_rng(seed)
+    dout = synth.round_to(rng.standard_normal((b, d, L)), dt)
+    dhT = rng.standard_normal((b, d, N)).astype(np.float32)
+    args = [dev(inp[k]) for k in ("u", "delta", "A", "B", "C")]
+    kw = dict(D=dev(inp["D"]), z=dev(inp["z"]), h0=dev(inp["h0"]))
+    ws = torch.empty(max(mssm.selective_scan_bwd_workspace_size(b, d, L, N), 1), dtype=torch.uint8, device="cuda")
+    say(f"  saved pair: u{inp['u'].shape} N{N} {dt}")
+    y0, h0f = mssm.selective_scan(*args, **kw, return_final_state=True)
+    y1, h1f = mssm.selective_scan(*args, **kw, return_final_state=True, save_workspace=ws)
+    gd, go = dev(dout), dev(dhT)
+    g0 = mssm.selective_scan_bwd(*args, gd, **kw, dh_final=go)
+    g1 = mssm.selective_scan_bwd(*args, gd, **kw, dh_final=go, workspace=ws, saved=True)
+    torch.cuda.synchronize()
+    return (y0, h0f, g0), (y1, h1f, g1), dout, dhT
+
+
+@pytest.mark.parametrize("case", SAVE_CASES, ids=lambda c: "b{}_d{}_L{}_N{}_{}_z{}_D{}_h{}_g{}".format(*c))
+def test_saved_pair_matches(case):
+    """The saving forward writes the same y and h_final bit for bit; the
+    backward from the saved states gives the same gradients (dA and dD, summed
+    with atomics, to rounding) and matches the oracle."""
+    import torch
+    b, d, L, N, dt, gate, skip, h0, _ = case
+    inp = synth.s6_inputs(b, d, L, N, dtype=dt, seed=5000 + d + L + N, gate=gate, skip=skip, init_state=h0)
+    (y0, hf0, g0), (y1, hf1, g1), dout, dhT = _both(inp, seed=L + N + 1)
+    assert torch.equal(y0, y1) and torch.equal(hf0, hf1)
+    for k in g0:
+        if k in ("dA", "dD"):
+            assert normwise(host(g1[k]), host(g0[k])) <= 1e-6, k
+        else:
+            assert torch.equal(g0[k], g1[k]), k
+    w = lambda a: None if a is None else synth.widen(a, dt)  # noqa: E731
+    o = oracle.s6_scan_bwd(w(inp["u"]), w(inp["delta"]), inp["A"], w(inp["B"]), w(inp["C"]), inp["D"], w(inp["z"]),
+                           inp["h0"], w(dout), dhT)
+    _compare(g1, o, TOL[dt], "saved " + "x".join(map(str, case)))
+
+
+def test_mamba1p4b_saved_pair_matches():
+    """At the Mamba-1.4B layer shape (the launch configuration the benchmark
+    times): the saving forward and the backward from its states against the
+    plain calls."""
+    import torch
+    w = synth.WORKLOADS["s6_mamba1p4b_bf16"]
+    inp = synth.s6_inputs(**w.shape, dtype=w.dtype, seed=w.seed, init_state=True)
+    (y0, hf0, g0), (y1, hf1, g1), _, _ = _both(inp, seed=11)
+    assert torch.equal(y0, y1) and torch.equal(hf0, hf1)
+    for k in g0:
+        if k in ("dA", "dD"):
+            assert normwise(host(g1[k]), host(g0[k])) <= 1e-6, k
+        else:
+            assert torch.equal(g0[k], g1[k]), k
