@@ -221,7 +221,10 @@ int mssm_selective_scan_bwd(const void* u, const void* delta, const float* A, co
  * their atomic sums), provided its `workspace` still holds what
  * mssm_selective_scan_fwd_save wrote there for the same u, delta, A, Bm, h0
  * and sizes.  Anything else in the workspace gives wrong gradients; this is
- * not checked.  Errors and limits: as the two calls they mirror.
+ * not checked.  Errors and limits: as the two calls they mirror; in addition
+ * the saved states of one batch row (4 * d_state * d_inner * seqlen / 16
+ * bytes, / 8 when d_state > 16) must stay below 2 GiB
+ * (MSSM_ERR_UNSUPPORTED).
  */
 int mssm_selective_scan_fwd_save(const void* u, const void* delta, const float* A,
                                  const void* Bm, const void* Cm, const float* Dskip,

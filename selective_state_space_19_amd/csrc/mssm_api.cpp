@@ -102,6 +102,8 @@ static int scan_fwd(const char* fn, bool zoh, bool save, const void* u, const vo
         if (!workspace || workspace_bytes < need)
             return fail(MSSM_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace_bytes);
         CHECK_OPT(workspace);
+        if (mssm::s6_bwd_ckpt_floats(1, d_inner, seqlen, d_state) * 4 >= (int64_t(1) << 31))
+            return fail(MSSM_ERR_UNSUPPORTED, "%s: saved states of one batch row exceed 2 GiB", fn);
         ckpt = static_cast<float*>(workspace);
     }
     mssm::S6Params p{u, delta, Bm, Cm, z, A, Dskip, h0, y, h_final, batch, d_inner, (int32_t)seqlen, (int32_t)d_state,

@@ -174,6 +174,11 @@ __global__ __launch_bounds__((kScanWaves + kRowWaves) * 64) void s6_scan_kernel(
 
         uint32_t bw[2][NS][BCW], cw[2][NS][BCW];
         float4 ddr[2][G / 2];
+        // CKPT: this batch row's saved states, [chunk, N, dim] fp32 (the host
+        // keeps them under 2 GiB); a lane's own offset, out of range if idle
+        const int64_t ck_row = CKPT ? (int64_t)((L + kCkptLen<NS> - 1) / kCkptLen<NS>) * N * dim : 0;
+        const rsrc_t rck = make_rsrc(CKPT ? ck_out + b * ck_row : h0_in, (uint32_t)(ck_row * 4));
+        const uint32_t ck_lane = sval_d ? (uint32_t)cs * 4u : kOutOfRange;
 
         // C of state s at token k of the group in buffer `buf`; 0 for a state
         // past N (FULLN: every state of every wave is below N).
@@ -210,15 +215,19 @@ __global__ __launch_bounds__((kScanWaves + kRowWaves) * 64) void s6_scan_kernel(
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
                     if constexpr (CKPT) {
-                        // the state entering token tg + k + kk, if a backward chunk starts there
+                        // the state entering token tg + k + kk, if a backward chunk starts
+                        // there (a compile-time test: tg is a multiple of G); no branch,
+                        // stores past the sequence or for idle lanes are dropped
                         constexpr int CK = kCkptLen<NS>;
                         const int t = tg + k + kk;
-                        if ((t % CK) == 0 && t < L && sval_d) {
-                            const int nckb = (L + CK - 1) / CK;
+                        if ((t % CK) == 0) {
 #pragma unroll
-                            for (int s = 0; s < NS; ++s)
-                                if (sval[s])
-                                    ck_out[((b * nckb + t / CK) * N + w * NS + s) * dim + d0 + cs] = h[s];
+                            for (int s = 0; s < NS; ++s) {
+                                const uint32_t so = ((uint32_t)((t / CK) * N + w * NS + s) * (uint32_t)dim +
+                                                     (uint32_t)d0) * 4u;
+                                __builtin_amdgcn_raw_buffer_store_b32(
+                                    __float_as_uint(h[s]), rck, off_if(t < L && sval[s], ck_lane), so, 0);
+                            }
                         }
                     }
 #pragma unroll
