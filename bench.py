@@ -291,7 +291,10 @@ def bench_s6bwd(args):
             "tokens_ch_per_s": B * D * L / (ms * 1e-3), "bytes_moved_estimate": nb,
             "GBs_estimate": nb / (ms * 1e-3) / 1e9, "workspace_bytes": ws.numel(),
             "traffic_bytes_per_call": {"s6_scan_bwd_kernel": profiled_traffic("s6_scan_bwd_mamba1p4b_bf16.md"),
-                                       "s6_bwd_reduce_bc_kernel": profiled_traffic("s6_bwd_reduce_bc_mamba1p4b_bf16.md")}}
+                                       "s6_bwd_reduce_bc_kernel": profiled_traffic("s6_bwd_reduce_bc_mamba1p4b_bf16.md")},
+            "traffic_bytes_saved_pair": {
+                "s6_scan_kernel saving states": profiled_traffic("s6_scan_fwd_save_mamba1p4b_bf16.md"),
+                "s6_scan_bwd_kernel from saved states": profiled_traffic("s6_scan_bwd_saved_mamba1p4b_bf16.md")}}
 
 
 def parity_sample(inp, y, hf, rows=32, seed=0):

@@ -22,7 +22,7 @@
 //   1. Forward sweep over the whole sequence in chunks of TC tokens (16, or 8
 //      when a lane holds more than 2 states), writing
 //      the state at every chunk start to the workspace (one fp32 per
-//      channel, state and chunk).  Skipped (p.saved) when the forward scan
+//      channel, state and chunk).  Left out (SAVED) when the forward scan
 //      has already stored those states there.
 //   2. Backward sweep, last chunk first: stage (delta, delta*u, u, g) of the
 //      chunk in LDS; recompute the chunk's TC states from its checkpoint into
@@ -96,7 +96,9 @@ __device__ __forceinline__ float widen(uint16_t v) { return __uint_as_float(uint
 // BUF (L even, a block's rows addressable with 32-bit offsets): each row
 // thread reads its two tokens with one buffer load per array; offsets past the
 // sequence or past the block's rows read zero.  Otherwise element loads.
-template <typename T, int NS, bool BUF>
+// SAVED: the workspace already holds the chunk-start states (written by the
+// forward scan), so the forward sweep is left out.
+template <typename T, int NS, bool BUF, bool SAVED>
 __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
     constexpr int kTC = ChunkLen<NS>::value;
     constexpr int kTPT = kTC / kSegs;      // tokens per row thread
@@ -292,8 +294,8 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
 #pragma unroll
         for (int j = 0; j < kTPT; ++j) s_fw[ck & 1][toff + j][cr] = make_float2(dlv[j], dlv[j] * uv[j]);
     };
-    // (skipped when the forward pass saved the chunk-start states: p.saved)
-    const int nck_fwd = p.saved ? 0 : nck;
+    // (left out when the forward pass saved the chunk-start states)
+    const int nck_fwd = SAVED ? 0 : nck;
     if (nck_fwd > 0) {
         fetch_fwd(0);
         stage_fwd(0);
@@ -525,10 +527,9 @@ template <typename T, int NS>
 hipError_t launch_ns(const S6BwdParams& p, hipStream_t stream) {
     const int64_t blocks = ((p.dim + 63) / 64) * p.batch;
     const bool buf = p.L % 2 == 0 && int64_t(64) * p.L * int64_t(sizeof(T)) < (int64_t(1) << 31);
-    if (buf)
-        hipLaunchKernelGGL((s6_scan_bwd_kernel<T, NS, true>), dim3((unsigned)blocks), dim3(kNW * 64), 0, stream, p);
-    else
-        hipLaunchKernelGGL((s6_scan_bwd_kernel<T, NS, false>), dim3((unsigned)blocks), dim3(kNW * 64), 0, stream, p);
+    auto kern = p.saved ? (buf ? s6_scan_bwd_kernel<T, NS, true, true> : s6_scan_bwd_kernel<T, NS, false, true>)
+                        : (buf ? s6_scan_bwd_kernel<T, NS, true, false> : s6_scan_bwd_kernel<T, NS, false, false>);
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kNW * 64), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     constexpr int kTC = ChunkLen<NS>::value;
