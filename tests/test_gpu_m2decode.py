@@ -88,6 +88,33 @@ def test_decode_equals_ssd_kernel():
     assert normwise(host(st), host(h_ssd)) <= TOL["bf16"]
 
 
+def test_prefill_then_decode_matches_oracle():
+    """Prefill -> decode: the chunked SSD over the first L1 tokens (chunk 256,
+    from h0) hands its h_final to L2 decode steps; their outputs and the last
+    state match the fp64 oracle run over all L1 + L2 tokens."""
+    import torch
+    b, L1, L2, H, P, N, G = 2, 300, 6, 4, 64, 128, 1
+    inp = synth.ssd_inputs(b, L1 + L2, H, P, N, G, dtype="bf16", seed=81, gate=True, init_state=True)
+    pre = {k: (None if inp[k] is None else
+               (np.ascontiguousarray(inp[k][:, :L1]) if k in ("x", "dt", "B", "C", "z") else inp[k]))
+           for k in ("x", "dt", "A", "B", "C", "D", "z", "h0")}
+    say(f"  prefill {L1} tokens (chunk 256) + {L2} decode steps: b{b} H{H} P{P} N{N}")
+    _, st = mssm.ssd_chunk(*(dev(pre[k]) for k in ("x", "dt", "A", "B", "C", "D", "z", "h0")), chunk=256,
+                           return_final_state=True)
+    ys = []
+    for t in range(L1, L1 + L2):
+        ys.append(mssm.ssd_state_update(st, *(dev(np.ascontiguousarray(inp[k][:, t])) for k in ("x", "dt")),
+                                        dev(inp["A"]), *(dev(np.ascontiguousarray(inp[k][:, t])) for k in ("B", "C")),
+                                        dev(inp["D"]), dev(np.ascontiguousarray(inp["z"][:, t]))))
+    torch.cuda.synchronize()
+    yo, ho = oracle.ssd(*(synth.widen(inp[k], "bf16") if inp[k] is not None and inp[k].dtype == np.uint16
+                          else inp[k] for k in ("x", "dt", "A", "B", "C", "D", "z", "h0")))
+    ey = normwise(np.stack([host(y) for y in ys], axis=1), yo[:, L1:])
+    es = normwise(host(st), ho)
+    say(f"  prefill + decode: y err {ey:.3e}, final state err {es:.3e}")
+    assert ey <= TOL["bf16"] and es <= TOL["bf16"]
+
+
 def test_errors_and_noop():
     import torch
     init = synth.mamba2_decode_initial(1, 2, 4, 48, seed=1)
