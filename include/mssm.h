@@ -187,7 +187,8 @@ int mssm_selective_scan_fused_fwd(const void* x, const float* conv_w, const floa
  *              sums of dB and dC); caller-owned, contents unspecified
  *
  * dA and dD are accumulated with atomics, so their last bits can vary from
- * call to call; the other outputs are deterministic.  Limits: 1 <= d_state <= 64.
+ * call to call; the other outputs are deterministic.  With seqlen = 0, dh0
+ * receives dh_final (or zeros) and dA, dD zeros.  Limits: 1 <= d_state <= 64.
  */
 size_t mssm_selective_scan_bwd_workspace_size(int64_t batch, int64_t d_inner, int64_t seqlen,
                                               int64_t d_state);

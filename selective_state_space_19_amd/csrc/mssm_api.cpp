@@ -201,6 +201,19 @@ static int scan_bwd(const char* fn, bool saved, const void* u, const void* delta
     if (!prod_ok(batch, d_inner, seqlen, nullptr) || !prod_ok(batch, d_inner, d_state, nullptr))
         return fail(MSSM_ERR_SHAPE, "%s: tensor too large", fn);
     if (batch == 0 || d_inner == 0) return MSSM_OK;
+    if (seqlen == 0) {
+        // h_final = h0: dh0 = dh_final; no step, so dA = dD = 0.  The
+        // per-token tensors are empty and not touched.
+        CHECK_PTR(dA);
+        CHECK_OPT(dD);
+        CHECK_OPT(dh0);
+        CHECK_OPT(dh_final);
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        hipError_t e = mssm::launch_copy_or_zero(dA, nullptr, d_inner * d_state, s);
+        if (e == hipSuccess && dD) e = mssm::launch_copy_or_zero(dD, nullptr, d_inner, s);
+        if (e == hipSuccess && dh0) e = mssm::launch_copy_or_zero(dh0, dh_final, batch * d_inner * d_state, s);
+        return launched(fn, e);
+    }
     CHECK_PTR(u);
     CHECK_PTR(delta);
     CHECK_PTR(A);

@@ -179,3 +179,20 @@ def test_mamba1p4b_saved_pair_matches():
             assert normwise(host(g1[k]), host(g0[k])) <= 1e-6, k
         else:
             assert torch.equal(g0[k], g1[k]), k
+
+
+@pytest.mark.parametrize("saved", [False, True])
+def test_zero_length_backward(saved):
+    """seqlen 0: h_final = h0, so dh0 = dh_final, and dA, dD are zero."""
+    import torch
+    inp = synth.s6_inputs(2, 40, 0, 16, dtype="bf16", seed=4, init_state=True)
+    dhT = np.random.default_rng(2).standard_normal((2, 40, 16)).astype(np.float32)
+    args = [dev(inp[k]) for k in ("u", "delta", "A", "B", "C")]
+    dout = torch.empty_like(args[0])
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    g = mssm.selective_scan_bwd(*args, dout, D=dev(inp["D"]), z=dev(inp["z"]), h0=dev(inp["h0"]), dh_final=dev(dhT),
+                                workspace=ws, saved=saved)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(g["dh0"]), dhT)
+    assert not host(g["dA"]).any() and not host(g["dD"]).any()
+    assert g["du"].numel() == 0 and g["dB"].numel() == 0
