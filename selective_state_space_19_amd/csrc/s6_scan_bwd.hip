@@ -424,11 +424,13 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
                 float a;
                 if constexpr (kKeepA) a = as[k][s];
                 else a = fast_exp2(q.x * a2[s]);
+                const float ah = a * hp;              // a_t h_{t-1}, shared by ddelta and dA
+                const float ltx = lt * q.x;           // lambda_t delta_t
                 v[2 * s] = lt * q.y;
                 v[2 * s + 1] = q.w * hs[k][s];
-                dup = fmaf(lt * q.x, bv, dup);
-                ddp = fmaf(lt, fmaf(Af[s] * a, hp, q.z * bv), ddp);
-                dAacc[s] = fmaf(lt * q.x * a, hp, dAacc[s]);
+                dup = fmaf(ltx, bv, dup);
+                ddp = fmaf(lt, fmaf(Af[s], ah, q.z * bv), ddp);
+                dAacc[s] = fmaf(ltx, ah, dAacc[s]);
                 lam[s] = a * lt;
             }
             tree<0, 2 * kNSP>(v);
