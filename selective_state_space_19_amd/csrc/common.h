@@ -39,15 +39,16 @@ __device__ __forceinline__ void lgkm_wait_all() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// softplus(v) = log(1 + e^v) = max(v, 0) + log1p(e^-|v|).  log1p(w) for w in
-// (0, 1] is log(1 + w) * w / ((1 + w) - 1), which cancels the rounding of
-// 1 + w (exact when 1 + w rounds to 1: the result is then w).
+// softplus(v) = log(1 + e^v) = max(v, 0) + log1p(w), w = e^-|v| in (0, 1].
+// With u = 1 + w rounded to float and c = w - (u - 1) its rounding error
+// (|c| <= 2^-24), log1p(w) = log(u) + log(1 + c / u).  The last term is c / u
+// to first order; c (1 - w) stands in for it with an error below 2^-24 w^2,
+// so no division is needed (when u rounds to 1 the result is w - w^2).
 __device__ __forceinline__ float softplus_f(float v) {
     const float w = fast_exp2(-fabsf(v) * kLog2e);
     const float u = 1.0f + w;
-    const float d = u - 1.0f;
-    const float l1p = d == 0.0f ? w : __builtin_amdgcn_logf(u) * kLn2 * w * __builtin_amdgcn_rcpf(d);
-    return fmaxf(v, 0.0f) + l1p;
+    const float c = w - (u - 1.0f);
+    return fmaxf(v, 0.0f) + fmaf(__builtin_amdgcn_logf(u), kLn2, fmaf(-c, w, c));
 }
 
 // silu(g) = g * sigmoid(g) = g / (1 + e^-g).
