@@ -55,6 +55,11 @@ extern "C" {
 
 typedef enum { MSSM_F32 = 0, MSSM_BF16 = 1 } mssm_dtype;
 
+/* Longest sequence the S6 entry points (forward, fused, zero-order hold,
+ * backward) accept: 2^31 - 2^16 tokens, so that token indices rounded up to
+ * whole chunks stay within 32-bit signed integers. */
+#define MSSM_MAX_SEQLEN 2147418112LL
+
 enum {
     MSSM_OK = 0,
     MSSM_ERR_NULL = -1,         /* a required pointer is NULL                 */
@@ -92,8 +97,9 @@ enum {
  *   y          (device) [batch, d_inner, seqlen]  dtype, output
  *   h_final    (device) [batch, d_inner, d_state] float32, NULL => not written
  *
- * Limits: 1 <= d_state <= 64 (MSSM_ERR_UNSUPPORTED otherwise); batch,
- * d_inner, seqlen >= 0; batch*d_inner*seqlen < 2^62.
+ * Limits: 1 <= d_state <= 64 and seqlen <= MSSM_MAX_SEQLEN
+ * (MSSM_ERR_UNSUPPORTED otherwise); batch, d_inner, seqlen >= 0;
+ * batch*d_inner*seqlen < 2^62.
  */
 int mssm_selective_scan_fwd(const void* u, const void* delta, const float* A,
                             const void* Bm, const void* Cm, const float* Dskip,
@@ -148,7 +154,8 @@ int mssm_selective_scan_zoh_fwd(const void* u, const void* delta, const float* A
  *   delta_bias (device) [d_inner] float32, NULL => 0
  *   the rest   as mssm_selective_scan_fwd
  *
- * Limits: 1 <= d_conv <= 4 and 1 <= d_state <= 64 (MSSM_ERR_UNSUPPORTED).
+ * Limits: 1 <= d_conv <= 4, 1 <= d_state <= 64 and seqlen <= MSSM_MAX_SEQLEN
+ * (MSSM_ERR_UNSUPPORTED).
  */
 int mssm_selective_scan_fused_fwd(const void* x, const float* conv_w, const float* conv_b,
                                   const void* conv_init, const void* delta_raw,
@@ -188,7 +195,8 @@ int mssm_selective_scan_fused_fwd(const void* x, const float* conv_w, const floa
  *
  * dA and dD are accumulated with atomics, so their last bits can vary from
  * call to call; the other outputs are deterministic.  With seqlen = 0, dh0
- * receives dh_final (or zeros) and dA, dD zeros.  Limits: 1 <= d_state <= 64.
+ * receives dh_final (or zeros) and dA, dD zeros.  Limits: 1 <= d_state <= 64
+ * and seqlen <= MSSM_MAX_SEQLEN.
  */
 size_t mssm_selective_scan_bwd_workspace_size(int64_t batch, int64_t d_inner, int64_t seqlen,
                                               int64_t d_state);

@@ -75,7 +75,8 @@ static int scan_fwd(const char* fn, bool zoh, bool save, const void* u, const vo
     if (batch < 0 || d_inner < 0 || seqlen < 0 || d_state < 0)
         return fail(MSSM_ERR_SHAPE, "%s: negative dimension", fn);
     if (d_state < 1 || d_state > 64) return fail(MSSM_ERR_UNSUPPORTED, "%s: d_state %lld not in [1, 64]", fn, (long long)d_state);
-    if (seqlen > INT32_MAX) return fail(MSSM_ERR_UNSUPPORTED, "%s: seqlen %lld too large", fn, (long long)seqlen);
+    if (seqlen > MSSM_MAX_SEQLEN)
+        return fail(MSSM_ERR_UNSUPPORTED, "%s: seqlen %lld above %lld", fn, (long long)seqlen, MSSM_MAX_SEQLEN);
     if (!prod_ok(batch, d_inner, seqlen, nullptr) || !prod_ok(batch, d_inner, d_state, nullptr))
         return fail(MSSM_ERR_SHAPE, "%s: tensor too large", fn);
     if (batch == 0 || d_inner == 0) return MSSM_OK;
@@ -148,7 +149,8 @@ int mssm_selective_scan_fused_fwd(const void* x, const float* conv_w, const floa
         return fail(MSSM_ERR_SHAPE, "%s: negative dimension", fn);
     if (d_state < 1 || d_state > 64) return fail(MSSM_ERR_UNSUPPORTED, "%s: d_state %lld not in [1, 64]", fn, (long long)d_state);
     if (d_conv < 1 || d_conv > 4) return fail(MSSM_ERR_UNSUPPORTED, "%s: d_conv %lld not in [1, 4]", fn, (long long)d_conv);
-    if (seqlen > INT32_MAX) return fail(MSSM_ERR_UNSUPPORTED, "%s: seqlen %lld too large", fn, (long long)seqlen);
+    if (seqlen > MSSM_MAX_SEQLEN)
+        return fail(MSSM_ERR_UNSUPPORTED, "%s: seqlen %lld above %lld", fn, (long long)seqlen, MSSM_MAX_SEQLEN);
     if (!prod_ok(batch, d_inner, seqlen, nullptr) || !prod_ok(batch, d_inner, d_state, nullptr))
         return fail(MSSM_ERR_SHAPE, "%s: tensor too large", fn);
     if (batch == 0 || d_inner == 0) return MSSM_OK;
@@ -197,7 +199,8 @@ static int scan_bwd(const char* fn, bool saved, const void* u, const void* delta
     if (batch < 0 || d_inner < 0 || seqlen < 0 || d_state < 0)
         return fail(MSSM_ERR_SHAPE, "%s: negative dimension", fn);
     if (d_state < 1 || d_state > 64) return fail(MSSM_ERR_UNSUPPORTED, "%s: d_state %lld not in [1, 64]", fn, (long long)d_state);
-    if (seqlen > INT32_MAX) return fail(MSSM_ERR_UNSUPPORTED, "%s: seqlen %lld too large", fn, (long long)seqlen);
+    if (seqlen > MSSM_MAX_SEQLEN)
+        return fail(MSSM_ERR_UNSUPPORTED, "%s: seqlen %lld above %lld", fn, (long long)seqlen, MSSM_MAX_SEQLEN);
     if (!prod_ok(batch, d_inner, seqlen, nullptr) || !prod_ok(batch, d_inner, d_state, nullptr))
         return fail(MSSM_ERR_SHAPE, "%s: tensor too large", fn);
     if (batch == 0 || d_inner == 0) return MSSM_OK;
