@@ -83,6 +83,16 @@ def _delta(rng, dt_inv, shape):
     return _softplus(0.5 * rng.standard_normal(shape) + dt_inv)
 
 
+def periodic_window(a, axis: int, start: int, length: int) -> np.ndarray:
+    """Tokens start .. start+length-1 of the sequence that repeats `a` along
+    `axis` (a holds one period).  Used to build sequences far longer than
+    can be generated or checked whole, from one seeded period."""
+    if a is None:
+        return None
+    idx = (start + np.arange(length)) % a.shape[axis]
+    return np.take(a, idx, axis=axis)
+
+
 # --------------------------------------------------------------------------
 # S6 selective scan inputs
 # --------------------------------------------------------------------------
