@@ -44,15 +44,16 @@ def _tile(a, axis, L):
     return out
 
 
-def _period_shift_err(y, axis, chunk):
-    """max |y[t + PERIOD] - y[t]| / max |y| over t >= BURN, along `axis`, in
-    slices of `chunk` tokens per batch row."""
-    L = y.shape[axis]
+def _period_shift_err(y, axis, chunk, stop=None):
+    """max |y[t + PERIOD] - y[t]| / max |y| over BURN <= t < stop - PERIOD
+    (stop: the length by default), along `axis`, in slices of `chunk` tokens
+    per batch row."""
+    stop = y.shape[axis] if stop is None else stop
     num = den = 0.0
     for b in range(y.shape[0]):
         yb = y[b]
-        for s in range(BURN, L - PERIOD, chunk):
-            n = min(chunk, L - PERIOD - s)
+        for s in range(BURN, stop - PERIOD, chunk):
+            n = min(chunk, stop - PERIOD - s)
             later = yb.narrow(axis - 1, s + PERIOD, n).float()
             now = yb.narrow(axis - 1, s, n).float()
             num = max(num, float((later - now).abs().max()))
@@ -115,6 +116,88 @@ def test_s6_longest_sequences(case):
     assert bool(torch.isfinite(y).all()) and bool(torch.isfinite(hf).all())
     assert e_start <= tol and e_end <= tol and e_hf <= tol
     assert e_per <= 2 * tol
+
+
+# --------------------------------------------------------------------------
+# S6 backward: the same switch from buffer to element addressing; and the
+# longest sequence the saving forward takes (its states of one batch row just
+# under 2 GiB).  A gradient at token t depends on the states before t and on
+# dout after t, and both memories fade, so the windows are checked against
+# the oracle run BURN tokens past them (start) or before them (end), and the
+# period shift over the tokens BURN away from both ends.  dA and dD sum over
+# the whole sequence: checked finite here, against the oracle at the other
+# sizes.
+# --------------------------------------------------------------------------
+BWD_CASES = [
+    # (dtype, L, saved pair too)
+    ("bf16", (1 << 24) - 16, False),
+    ("bf16", 1 << 24, False),
+    ("f32", (1 << 23) - 8, False),
+    ("f32", 1 << 23, False),
+    ("bf16", (1 << 23) - 16, True),
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: f"{c[0]}_L{c[1]}" + ("_saved" if c[2] else ""))
+def test_s6_backward_longest_sequences(case):
+    import torch
+    dt, L, saved = case
+    bsz, d, N = 2, 64, 16
+    per = synth.s6_inputs(bsz, d, PERIOD, N, dtype=dt, seed=4444, init_state=True)
+    rng = np.random.default_rng(4445)
+    dout = synth.round_to(rng.standard_normal((bsz, d, PERIOD)), dt)
+    dhT = rng.standard_normal((bsz, d, N)).astype(np.float32)
+    dl = synth.widen(per["delta"], dt)
+    rate = (BURN // PERIOD) * dl.sum(axis=2) * np.abs(per["A"]).min(axis=1)[None, :]
+    assert rate.min() >= 40.0, rate.min()
+
+    say(f"  s6 backward longest: {dt} b{bsz} d{d} L{L} N{N} saved pair {saved}")
+    args = [_tile(per[k], 2, L) for k in ("u", "delta")] + [dev(per["A"])] + \
+           [_tile(per[k], 2, L) for k in ("B", "C")]
+    kw = dict(D=dev(per["D"]), z=_tile(per["z"], 2, L), h0=dev(per["h0"]))
+    gd, go = _tile(dout, 2, L), dev(dhT)
+    g = mssm.selective_scan_bwd(*args, gd, **kw, dh_final=go)
+    torch.cuda.synchronize()
+    if saved:
+        ws = torch.empty(mssm.selective_scan_bwd_workspace_size(bsz, d, L, N), dtype=torch.uint8, device="cuda")
+        y0, hf0 = mssm.selective_scan(*args, **kw, return_final_state=True)
+        y1, hf1 = mssm.selective_scan(*args, **kw, return_final_state=True, save_workspace=ws)
+        g1 = mssm.selective_scan_bwd(*args, gd, **kw, dh_final=go, workspace=ws, saved=True)
+        torch.cuda.synchronize()
+        assert torch.equal(y0, y1) and torch.equal(hf0, hf1)
+        for k in g:
+            if k in ("dA", "dD"):
+                assert normwise(host(g1[k]), host(g[k])) <= 1e-6, k
+            else:
+                assert torch.equal(g[k], g1[k]), k
+        del ws, y0, y1, hf0, hf1, g1
+    del args, kw, gd
+    tol = TOL[dt]
+    w = lambda a: None if a is None else synth.widen(a, dt)  # noqa: E731
+
+    def window(start, n, h0, dh):
+        sub = {k: synth.periodic_window(per[k], 2, start, n) for k in ("u", "delta", "B", "C", "z")}
+        return oracle.s6_scan_bwd(w(sub["u"]), w(sub["delta"]), per["A"], w(sub["B"]), w(sub["C"]), per["D"],
+                                  w(sub["z"]), per["h0"] if h0 else None,
+                                  w(synth.periodic_window(dout, 2, start, n)), dh)
+
+    errs = {}
+    o = window(0, WIN + BURN, True, None)
+    for k in ("du", "ddelta", "dz", "dB", "dC"):
+        errs[k + " start"] = normwise(host(g[k][:, :, :WIN]), o[k][:, :, :WIN])
+    errs["dh0"] = normwise(host(g["dh0"]), o["dh0"])
+    o = window(L - BURN - WIN, BURN + WIN, False, dhT)
+    for k in ("du", "ddelta", "dz", "dB", "dC"):
+        errs[k + " end"] = normwise(host(g[k][:, :, L - WIN:]), o[k][:, :, BURN:])
+    shift = {k: _period_shift_err(g[k], 2, 1 << 22, stop=L - BURN) for k in ("du", "ddelta", "dz", "dB", "dC")}
+    say(f"  s6 backward {dt} L{L}: " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()) +
+        "; period shift " + ", ".join(f"{k} {v:.2e}" for k, v in shift.items()) + f" (tol {tol})")
+    for k, v in g.items():
+        assert bool(torch.isfinite(v).all()), k
+    for k, v in errs.items():
+        assert v <= tol, k
+    for k, v in shift.items():
+        assert v <= 2 * tol, k
 
 
 # --------------------------------------------------------------------------
