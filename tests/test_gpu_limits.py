@@ -67,43 +67,63 @@ def _period_shift_err(y, axis, chunk, stop=None):
 # pointers.
 # --------------------------------------------------------------------------
 S6_CASES = [
-    # (dtype, L)
-    ("bf16", (1 << 24) - 16),     # the longest aligned sequence: 64 L 2 = 2^31 - 2048
-    ("bf16", 1 << 24),            # the first one past it
-    ("f32", (1 << 23) - 8),
-    ("f32", 1 << 23),
+    # (variant, dtype, L)
+    ("plain", "bf16", (1 << 24) - 16),     # the longest aligned sequence: 64 L 2 = 2^31 - 2048
+    ("plain", "bf16", 1 << 24),            # the first one past it
+    ("plain", "f32", (1 << 23) - 8),
+    ("plain", "f32", 1 << 23),
+    ("zoh", "bf16", (1 << 24) - 16),
+    ("zoh", "bf16", 1 << 24),
+    ("fused", "bf16", (1 << 24) - 16),
+    ("fused", "bf16", 1 << 24),
 ]
 
 
-@pytest.mark.parametrize("case", S6_CASES, ids=lambda c: f"{c[0]}_L{c[1]}")
+@pytest.mark.parametrize("case", S6_CASES, ids=lambda c: f"{c[0]}_{c[1]}_L{c[2]}")
 def test_s6_longest_sequences(case):
     import torch
-    dt, L = case
+    variant, dt, L = case
     bsz, d, N = 2, 64, 16
-    per = synth.s6_inputs(bsz, d, PERIOD, N, dtype=dt, seed=4242, init_state=True)
+    w = lambda a: synth.widen(a, dt)  # noqa: E731
+    if variant == "fused":
+        per = synth.s6_fused_inputs(bsz, d, PERIOD, N, d_conv=4, dtype=dt, seed=4242, init_state=True,
+                                    conv_history=True)
+        dl = oracle.softplus(w(per["delta_raw"]) + per["delta_bias"][None, :, None])
+        seq = ("x", "delta_raw", "z")
+    else:
+        per = synth.s6_inputs(bsz, d, PERIOD, N, dtype=dt, seed=4242, init_state=True)
+        dl = w(per["delta"])
+        seq = ("u", "delta", "z")
     # every state decays by e^-40 or more over BURN tokens
-    dl = synth.widen(per["delta"], dt)
     rate = (BURN // PERIOD) * dl.sum(axis=2) * np.abs(per["A"]).min(axis=1)[None, :]
     assert rate.min() >= 40.0, rate.min()
 
-    say(f"  s6 longest: {dt} b{bsz} d{d} L{L} N{N}")
-    args = [_tile(per[k], 2, L) for k in ("u", "delta")] + [dev(per["A"])] + \
-           [_tile(per[k], 2, L) for k in ("B", "C")] + [dev(per["D"]), _tile(per["z"], 2, L), dev(per["h0"])]
-    y, hf = mssm.selective_scan(*args, return_final_state=True)
+    say(f"  s6 longest: {variant} {dt} b{bsz} d{d} L{L} N{N}")
+    t = {k: _tile(per[k], 2, L) for k in seq + ("B", "C")}
+    if variant == "fused":
+        y, hf = mssm.selective_scan_fused(t["x"], dev(per["conv_w"]), t["delta_raw"], dev(per["A"]), t["B"], t["C"],
+                                          dev(per["D"]), t["z"], dev(per["h0"]), conv_b=dev(per["conv_b"]),
+                                          conv_init=dev(per["conv_init"]), delta_bias=dev(per["delta_bias"]),
+                                          return_final_state=True)
+    else:
+        y, hf = mssm.selective_scan(t["u"], t["delta"], dev(per["A"]), t["B"], t["C"], dev(per["D"]), t["z"],
+                                    dev(per["h0"]), return_final_state=True, zoh=variant == "zoh")
     torch.cuda.synchronize()
-    del args
+    del t
     tol = TOL[dt]
     ds = [0, 63]
 
-    def window(start, n, h0):
-        sub = dict(dtype=dt)
-        for k in ("u", "delta", "z"):
-            sub[k] = synth.periodic_window(per[k][:, ds], 2, start, n)
-        for k in ("B", "C"):
-            sub[k] = synth.periodic_window(per[k], 2, start, n)
-        sub["A"], sub["D"] = per["A"][ds], per["D"][ds]
-        sub["h0"] = per["h0"][:, ds] if h0 else None
-        return oracle.s6_scan(*(synth.widen(sub[k], dt) for k in ("u", "delta", "A", "B", "C", "D", "z", "h0")))
+    def window(start, n, first):
+        sub = {k: w(synth.periodic_window(per[k][:, ds], 2, start, n)) for k in seq}
+        B, C = (w(synth.periodic_window(per[k], 2, start, n)) for k in ("B", "C"))
+        h0 = per["h0"][:, ds] if first else None
+        if variant == "fused":
+            # the conv's history: the caller's before the sequence, else the inputs before the window
+            hist = per["conv_init"][:, ds] if first else synth.periodic_window(per["x"][:, ds], 2, start - 3, 3)
+            return oracle.s6_scan_fused(sub["x"], per["conv_w"][ds], per["conv_b"][ds], w(hist), sub["delta_raw"],
+                                        per["delta_bias"][ds], per["A"][ds], B, C, per["D"][ds], sub["z"], h0)
+        return oracle.s6_scan(sub["u"], sub["delta"], per["A"][ds], B, C, per["D"][ds], sub["z"], h0,
+                              zoh=variant == "zoh")
 
     yo, _ = window(0, WIN, True)
     e_start = normwise(host(y[:, ds, :WIN]), yo)
@@ -111,7 +131,7 @@ def test_s6_longest_sequences(case):
     e_end = normwise(host(y[:, ds, L - PERIOD:]), yo[:, :, BURN:])
     e_hf = normwise(host(hf[:, ds]), ho)
     e_per = _period_shift_err(y, 2, 1 << 22)
-    say(f"  s6 {dt} L{L}: start {e_start:.3e} end {e_end:.3e} h_final {e_hf:.3e} "
+    say(f"  s6 {variant} {dt} L{L}: start {e_start:.3e} end {e_end:.3e} h_final {e_hf:.3e} "
         f"period shift {e_per:.3e} (tol {tol})")
     assert bool(torch.isfinite(y).all()) and bool(torch.isfinite(hf).all())
     assert e_start <= tol and e_end <= tol and e_hf <= tol
