@@ -47,6 +47,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kP = 64;     // head dim handled by this kernel
 constexpr int kPW = 32;    // head channels per workgroup (half of kP)
+constexpr float kDiagSpan = 64.f;   // largest decay (log2 units) over a token block for the factored diagonal
 
 __device__ __forceinline__ f32x4_t mfma16(const u32x4_t a, const u32x4_t b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
@@ -388,42 +389,63 @@ __global__ __launch_bounds__(512) void ssd_main_kernel(
         const int i = i0 + m;
         const float si = s_s[pb][i];
         const int j0 = 32 * Jd + 8 * kg;
+        // Diagonal block, usual case: exp(s_i - s_j) = exp(s_i - s_e) exp(s_e - s_j)
+        // with s_e the end of token block Jd.  The second factor (with dt) is
+        // already in the staged xs, the first scales the accumulator row, and
+        // the mask is a select on G.  Both factors stay within 2^+-kDiagSpan
+        // when the decay over the block is at most that; otherwise the mask
+        // is built element by element.
+        const float sbe = send(pb, Jd);
+        const bool fast = __builtin_amdgcn_readfirstlane(s_s[pb][32 * Jd] - sbe <= kDiagSpan ? 1 : 0) != 0;
         const float4 d0 = *reinterpret_cast<const float4*>(&s_dt[pb][j0]);
         const float4 d1 = *reinterpret_cast<const float4*>(&s_dt[pb][j0 + 4]);
         const float4 q0 = *reinterpret_cast<const float4*>(&s_s[pb][j0]);
         const float4 q1 = *reinterpret_cast<const float4*>(&s_s[pb][j0 + 4]);
-        u32x4_t xd[2], hb[2][2];
+        u32x4_t xd[2], xe[2], hb[2][2];
         uint2 xr[2];                     // x of this lane's output rows (skip term)
 #pragma unroll
         for (int pt = 0; pt < 2; ++pt) {
             xd[pt] = lds128(&xT[pb][16 * pt + m][16 * Jd + 4 * kg]);
+            xe[pt] = lds128(&xsT[pb][16 * pt + m][16 * Jd + 4 * kg]);
             hb[0][pt] = lds128(&Hb[pb][16 * pt + m][4 * kg]);
             xr[pt] = *reinterpret_cast<const uint2*>(&xT[pb][16 * pt + m][(i0 + 4 * kg) >> 1]);
         }
         const float4 sr = *reinterpret_cast<const float4*>(&s_s[pb][i0 + 4 * kg]);
         __builtin_amdgcn_sched_barrier(0);
-        // diagonal token block: mask built element by element, dt folded in, plain x
+        // diagonal token block
         {
             // the two candidate tiles pass through an empty asm, so the
             // choice stays a select: an index into `ga` would put it in scratch
             u32x4_t g0 = gt[2 * rb], g1 = gt[2 * rb + 1];
             asm("" : "+v"(g0), "+v"(g1));
             const u32x4_t gv = jhi ? g1 : g0;
-            const float dj[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-            const float sj[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-            uint32_t av[4];
+            if (fast) {
+                // keep G_ij for j <= i: element e of the lane's 8 is j0 + e
+                const int k = i - j0;
+                u32x4_t a;
 #pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-                const uint32_t gw = gv[e / 2];
-                float v0 = __uint_as_float(gw << 16) * dj[e] * fast_exp2(si - sj[e]);
-                float v1 = __uint_as_float(gw & 0xffff0000u) * dj[e + 1] * fast_exp2(si - sj[e + 1]);
-                keep_select(v0);
-                keep_select(v1);
-                av[e / 2] = pack_bf16x2(j0 + e <= i ? v0 : 0.f, j0 + e + 1 <= i ? v1 : 0.f);
+                for (int w2 = 0; w2 < 4; ++w2)
+                    a[w2] = gv[w2] & (k >= 2 * w2 + 1 ? 0xffffffffu : (k == 2 * w2 ? 0x0000ffffu : 0u));
+#pragma unroll
+                for (int pt = 0; pt < 2; ++pt) dg[pt] = mfma16(a, xe[pt], dg[pt]);
+            } else {
+                // element by element: dt and the decay folded into G, plain x
+                const float dj[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+                const float sj[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+                uint32_t av[4];
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    const uint32_t gw = gv[e / 2];
+                    float v0 = __uint_as_float(gw << 16) * dj[e] * fast_exp2(si - sj[e]);
+                    float v1 = __uint_as_float(gw & 0xffff0000u) * dj[e + 1] * fast_exp2(si - sj[e + 1]);
+                    keep_select(v0);
+                    keep_select(v1);
+                    av[e / 2] = pack_bf16x2(j0 + e <= i ? v0 : 0.f, j0 + e + 1 <= i ? v1 : 0.f);
+                }
+                const u32x4_t a = {av[0], av[1], av[2], av[3]};
+#pragma unroll
+                for (int pt = 0; pt < 2; ++pt) dg[pt] = mfma16(a, xd[pt], dg[pt]);
             }
-            const u32x4_t a = {av[0], av[1], av[2], av[3]};
-#pragma unroll
-            for (int pt = 0; pt < 2; ++pt) dg[pt] = mfma16(a, xd[pt], dg[pt]);
         }
         // carried-in state: C rows times H_in^T
 #pragma unroll
@@ -446,11 +468,12 @@ __global__ __launch_bounds__(512) void ssd_main_kernel(
         for (int r = 0; r < 4; ++r) {
             const float al = fast_exp2(srv[r] - si0);
             const float ei = fast_exp2(srv[r]);
+            const float dr = fast ? fast_exp2(srv[r] - sbe) : 1.f;   // the fast diagonal block's row factor
 #pragma unroll
             for (int pt = 0; pt < 2; ++pt) {
                 const uint32_t xw = (r >> 1) ? xr[pt].y : xr[pt].x;
                 const float xv = __uint_as_float((r & 1) ? (xw & 0xffff0000u) : (xw << 16));
-                float yv = al * off_[pt][r] + dg[pt][r] + ei * yo[pt][r] + dskip * xv;
+                float yv = al * off_[pt][r] + dr * dg[pt][r] + ei * yo[pt][r] + dskip * xv;
                 if constexpr (HASZ) yv *= silu(__uint_as_float(zz[sl][2 * r + pt] << 16));
                 yt16[(4 * kg + r) * kPW + 16 * pt + m] = to_bf16(yv);
             }

@@ -82,6 +82,26 @@ def test_mamba2_workload_state_only():
     _check(inp, s["chunk"], w.name + "_noD")
 
 
+@pytest.mark.parametrize("chunk", [64, 256])
+def test_strong_decay_blocks(chunk):
+    """Token blocks whose decay over 32 tokens exceeds 2^64 (the product of
+    its two factors would leave float range) build the diagonal mask element
+    by element; the others take the factored form.  Here both kinds mix
+    within heads and chunks: dt is scaled by 40 in every other 32-token block
+    of head 0 and everywhere in head 2."""
+    inp = synth.ssd_inputs(2, 600, 4, 64, 128, 1, dtype="bf16", seed=77, gate=True, init_state=True)
+    dt = synth.widen(inp["dt"], "bf16")
+    f = np.ones_like(dt)
+    f[:, (np.arange(600) // 32) % 2 == 1, 0] = 40.0
+    f[:, :, 2] = 40.0
+    inp["dt"] = synth.round_to(dt * f, "bf16")
+    # decay over each whole 32-token block (log2 units): both kinds occur
+    a = synth.widen(inp["dt"], "bf16")[:, :576] * np.abs(inp["A"])[None, None, :] / np.log(2.0)
+    span = a.reshape(2, 18, 32, 4)[:, :, 1:, :].sum(axis=2)
+    assert (span > 64).any() and (span < 32).any()
+    _check(inp, chunk, f"strong_decay_q{chunk}")
+
+
 def test_chunk_size_invariance():
     """The chunk length only changes rounding (the chunked form is exact)."""
     inp = synth.ssd_inputs(2, 768, 4, 64, 128, 1, dtype="bf16", seed=41, init_state=True)
