@@ -228,6 +228,25 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(const uint16_t* __restric
 //     next chunk (running sum, x^T and its two scaled copies), so staging is
 //     off the output waves' path.  Every LDS buffer a chunk is read from is
 //     double-buffered by chunk parity: one barrier per chunk.
+// Inclusive prefix sum over the 64 lanes of a wave, on DPP moves: within
+// each row of 16 lanes by shifts of 1, 2, 4 and 8 lanes, then across rows by
+// adding lane 15 of row 0 / 2 to rows 1 / 3 and lane 31 to rows 2 and 3.
+// Lanes a move does not reach add 0 (the `old` operand).
+__device__ __forceinline__ float wave_incl_scan(float v) {
+    auto step = [](float x, auto ctrl, auto rows) {
+        return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), decltype(ctrl)::value,
+                                                              decltype(rows)::value, 0xf, false));
+    };
+    using std::integral_constant;
+    v = step(v, integral_constant<int, 0x111>{}, integral_constant<int, 0xf>{});   // row_shr:1
+    v = step(v, integral_constant<int, 0x112>{}, integral_constant<int, 0xf>{});   // row_shr:2
+    v = step(v, integral_constant<int, 0x114>{}, integral_constant<int, 0xf>{});   // row_shr:4
+    v = step(v, integral_constant<int, 0x118>{}, integral_constant<int, 0xf>{});   // row_shr:8
+    v = step(v, integral_constant<int, 0x142>{}, integral_constant<int, 0xa>{});   // row_bcast:15
+    v = step(v, integral_constant<int, 0x143>{}, integral_constant<int, 0xc>{});   // row_bcast:31
+    return v;
+}
+
 // ---------------------------------------------------------------------------
 // HASZ: a gate z is given.  Loads for the chunk after the last read zeros
 // through zero-size buffer resources (no branches around loads, which would
@@ -603,17 +622,12 @@ __global__ __launch_bounds__(512) void ssd_main_kernel(
                 run += dv[i] * a_h;
                 sv[i] = run;
             }
-            float tot = run;                     // inclusive scan of the lane totals
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                const float o = __shfl_up(tot, d, 64);
-                if (lane >= d) tot += o;
-            }
+            const float tot = wave_incl_scan(run);   // inclusive scan of the lane totals
             const float base = tot - run;
 #pragma unroll
             for (int i = 0; i < TPL; ++i) sv[i] += base;
             const float s_be = __shfl(tot, ((lane * TPL) | 31) / TPL, 64);   // end of my 32-token block
-            const float s_end = __shfl(tot, 63, 64);                        // end of the chunk
+            const float s_end = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tot), 63));  // end of the chunk
             if (wr == 0) {
 #pragma unroll
                 for (int i = 0; i < TPL; ++i) {
