@@ -219,15 +219,6 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(const uint16_t* __restric
     }
 }
 
-// ---------------------------------------------------------------------------
-// Main: one workgroup per (b, head, half of headdim); chunks in order.
-// 512 threads in two roles (one wave of each on every SIMD):
-//   output waves 0-3: the chunk's outputs from the staged chunk and the
-//     carried-in state (Y_diag, Y_off, skip, gate, store);
-//   state waves 4-7: the state update for the chunk, then the staging of the
-//     next chunk (running sum, x^T and its two scaled copies), so staging is
-//     off the output waves' path.  Every LDS buffer a chunk is read from is
-//     double-buffered by chunk parity: one barrier per chunk.
 // Inclusive prefix sum over the 64 lanes of a wave, on DPP moves: within
 // each row of 16 lanes by shifts of 1, 2, 4 and 8 lanes, then across rows by
 // adding lane 15 of row 0 / 2 to rows 1 / 3 and lane 31 to rows 2 and 3.
@@ -247,6 +238,15 @@ __device__ __forceinline__ float wave_incl_scan(float v) {
     return v;
 }
 
+// ---------------------------------------------------------------------------
+// Main: one workgroup per (b, head, half of headdim); chunks in order.
+// 512 threads in two roles (one wave of each on every SIMD):
+//   output waves 0-3: the chunk's outputs from the staged chunk and the
+//     carried-in state (Y_diag, Y_off, skip, gate, store);
+//   state waves 4-7: the state update for the chunk, then the staging of the
+//     next chunk (running sum, x^T and its two scaled copies), so staging is
+//     off the output waves' path.  Every LDS buffer a chunk is read from is
+//     double-buffered by chunk parity: one barrier per chunk.
 // ---------------------------------------------------------------------------
 // HASZ: a gate z is given.  Loads for the chunk after the last read zeros
 // through zero-size buffer resources (no branches around loads, which would
