@@ -114,8 +114,13 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(const uint16_t* __restric
     __shared__ __align__(16) uint32_t sT[4][16][20];   // per wave: one 16 x 32 tile (bf16 pairs, padded)
     auto piece = [](int r, int q) { return q ^ (r & SWZ); };
 
-    const int rp = blockIdx.x % KB;
-    const int bcg = blockIdx.x / KB;             // (b * nc + c) * G + g
+    // Blocks are dispatched round-robin over the 8 XCDs; number them so that
+    // the Q/32 blocks of one (b, chunk, group), which read overlapping B
+    // rows, share an XCD and its L2.
+    uint32_t lid = blockIdx.x;
+    if ((gridDim.x & 7u) == 0u) lid = (blockIdx.x & 7u) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+    const int rp = lid % KB;
+    const int bcg = lid / KB;                    // (b * nc + c) * G + g
     const int g = bcg % G;
     const int c = (bcg / G) % nc;
     const int64_t b = (bcg / G) / nc;
