@@ -114,8 +114,14 @@ __global__ __launch_bounds__((kScanWaves + kRowWaves) * 64) void s6_scan_kernel(
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t nblk_d = (dim + 63) / 64;
-    const int64_t b = blockIdx.x / nblk_d;
-    const int64_t d0 = (blockIdx.x % nblk_d) * 64;
+    // Blocks are dispatched round-robin over the 8 XCDs; number them so that
+    // consecutive ids (channel blocks of one batch row, which read the same
+    // B and C rows) share an XCD and its L2.
+    uint32_t lid = blockIdx.x;
+    if ((gridDim.x & 7u) == 0u) lid = (blockIdx.x & 7u) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+    const int64_t b = lid / nblk_d;
+    const int64_t dblk = lid % nblk_d;
+    const int64_t d0 = dblk * 64;
     const int nrows = (int)((dim - d0) < 64 ? (dim - d0) : 64);
     const int nchunks = (L + TC - 1) / TC;
     // Both roles run `nit` chunk iterations (a multiple of RING, so the row
