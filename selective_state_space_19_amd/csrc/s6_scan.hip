@@ -429,11 +429,11 @@ __global__ __launch_bounds__((kScanWaves + kRowWaves) * 64) void s6_scan_kernel(
                 }
                 const float a4[4] = {acc.x, acc.y, acc.z, acc.w};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float o = fmaf(dskip, uk[j + i], a4[i]);
-                    if (z_in) o *= silu(Elem<T>::get(cz, j + i));
-                    out[j + i] = o;
-                }
+                for (int i = 0; i < 4; ++i) out[j + i] = fmaf(dskip, uk[j + i], a4[i]);
+            }
+            if (z_in) {                           // one uniform branch per chunk, not per token
+#pragma unroll
+                for (int j = 0; j < TPT; ++j) out[j] *= silu(Elem<T>::get(cz, j));
             }
             if constexpr (ALIGNED) {
                 uint32_t wy[WPT];
