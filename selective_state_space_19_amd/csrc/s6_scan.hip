@@ -393,8 +393,14 @@ __global__ __launch_bounds__((kScanWaves + kRowWaves) * 64) void s6_scan_kernel(
                 }
 #pragma unroll
                 for (int j = 0; j < TPT; j += 2) {
-                    const float d0v = t0 + toff + j < L ? softplus_f(Elem<T>::get(cdl, j) + dbias) : 0.f;
-                    const float d1v = t0 + toff + j + 1 < L ? softplus_f(Elem<T>::get(cdl, j + 1) + dbias) : 0.f;
+                    // computed for every token, then selected: a conditional
+                    // call would become a branch per token
+                    float s0 = softplus_f(Elem<T>::get(cdl, j) + dbias);
+                    float s1 = softplus_f(Elem<T>::get(cdl, j + 1) + dbias);
+                    keep_select(s0);
+                    keep_select(s1);
+                    const float d0v = t0 + toff + j < L ? s0 : 0.f;
+                    const float d1v = t0 + toff + j + 1 < L ? s1 : 0.f;
                     s_dd[par][(toff + j) / 2][cr] = make_float4(d0v, d0v * uk[j], d1v, d1v * uk[j + 1]);
                 }
             } else {
