@@ -28,7 +28,10 @@ def _dtype_code(t):
     raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
 
 
-def _dev(t, name, shape=None, dtype=None, device=None):
+def _dev(t, name, shape=None, dtype=None, device=None, written=False):
+    """Check a tensor argument.  Inputs that are not contiguous are copied;
+    a tensor the kernel writes (an output, a workspace, a state updated in
+    place) must be contiguous itself, since a copy would take the writes."""
     if t is None:
         return None
     torch = _torch()
@@ -40,6 +43,10 @@ def _dev(t, name, shape=None, dtype=None, device=None):
         raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if written:
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous (the kernel writes it in place)")
+        return t
     return t if t.is_contiguous() else t.contiguous()
 
 
@@ -47,10 +54,25 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
-def _stream(stream, device):
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def _stream(stream, device, *tensors):
+    """The stream handle to launch on.  Copies and allocations above were
+    made on the current stream; when the caller names another stream, it
+    first waits for the current one, and every tensor handed to the kernel
+    is marked as in use on it, so the caching allocator does not reuse a
+    temporary while the kernel may still read or write it."""
     torch = _torch()
-    s = stream if stream is not None else torch.cuda.current_stream(device)
-    return s.cuda_stream
+    cur = torch.cuda.current_stream(device)
+    if stream is None or stream == cur:
+        return cur.cuda_stream
+    stream.wait_stream(cur)
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
+    return stream.cuda_stream
 
 
 def selective_scan(u, delta, A, B, C, D=None, z=None, h0=None, *, return_final_state=False,
@@ -76,27 +98,23 @@ def selective_scan(u, delta, A, B, C, D=None, z=None, h0=None, *, return_final_s
     A = _dev(A, "A", (dim, N), torch.float32, dev)
     D = _dev(D, "D", (dim,), torch.float32, dev)
     h0 = _dev(h0, "h0", (bsz, dim, N), torch.float32, dev)
-    y = out if out is not None else torch.empty_like(u)
-    _dev(y, "out", u.shape, dt, dev)
-    if not y.is_contiguous():
-        raise ValueError("out must be contiguous")
+    y = _dev(out if out is not None else torch.empty_like(u), "out", u.shape, dt, dev, written=True)
     hf = None
     if return_final_state or h_final is not None:
         hf = h_final if h_final is not None else torch.empty((bsz, dim, N), dtype=torch.float32, device=dev)
-        _dev(hf, "h_final", (bsz, dim, N), torch.float32, dev)
-        if not hf.is_contiguous():
-            raise ValueError("h_final must be contiguous")
+        hf = _dev(hf, "h_final", (bsz, dim, N), torch.float32, dev, written=True)
+    ins = (u, delta, A, B, C, D, z, h0, y, hf)
     if save_workspace is not None:
         if zoh:
             raise ValueError("save_workspace is for the Euler scan (the backward pass is of that scan)")
-        ws = _dev(save_workspace, "save_workspace", device=dev)
+        ws = _dev(save_workspace, "save_workspace", device=dev, written=True)
         check(lib().mssm_selective_scan_fwd_save(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                                                  _ptr(h0), _ptr(y), _ptr(hf), bsz, dim, L, N, _ptr(ws),
-                                                 ws.numel() * ws.element_size(), code, _stream(stream, dev)))
+                                                 _nbytes(ws), code, _stream(stream, dev, *ins, ws)))
     else:
         fn = lib().mssm_selective_scan_zoh_fwd if zoh else lib().mssm_selective_scan_fwd
         check(fn(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(hf),
-                 bsz, dim, L, N, code, _stream(stream, dev)))
+                 bsz, dim, L, N, code, _stream(stream, dev, *ins)))
     return (y, hf) if hf is not None else y
 
 
@@ -126,20 +144,15 @@ def selective_scan_fused(x, conv_w, delta_raw, A, B, C, D=None, z=None, h0=None,
     A = _dev(A, "A", (dim, N), torch.float32, dev)
     D = _dev(D, "D", (dim,), torch.float32, dev)
     h0 = _dev(h0, "h0", (bsz, dim, N), torch.float32, dev)
-    y = out if out is not None else torch.empty_like(x)
-    _dev(y, "out", x.shape, dt, dev)
-    if not y.is_contiguous():
-        raise ValueError("out must be contiguous")
+    y = _dev(out if out is not None else torch.empty_like(x), "out", x.shape, dt, dev, written=True)
     hf = None
     if return_final_state or h_final is not None:
         hf = h_final if h_final is not None else torch.empty((bsz, dim, N), dtype=torch.float32, device=dev)
-        _dev(hf, "h_final", (bsz, dim, N), torch.float32, dev)
-        if not hf.is_contiguous():
-            raise ValueError("h_final must be contiguous")
+        hf = _dev(hf, "h_final", (bsz, dim, N), torch.float32, dev, written=True)
+    s = _stream(stream, dev, x, conv_w, conv_b, conv_init, delta_raw, delta_bias, A, B, C, D, z, h0, y, hf)
     check(lib().mssm_selective_scan_fused_fwd(_ptr(x), _ptr(conv_w), _ptr(conv_b), _ptr(conv_init), _ptr(delta_raw),
                                               _ptr(delta_bias), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                                              _ptr(h0), _ptr(y), _ptr(hf), bsz, dim, L, N, K, code,
-                                              _stream(stream, dev)))
+                                              _ptr(h0), _ptr(y), _ptr(hf), bsz, dim, L, N, K, code, s))
     return (y, hf) if hf is not None else y
 
 
@@ -182,11 +195,13 @@ def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, h0=None, dh_fina
         if saved:
             raise ValueError("saved=True needs the workspace the forward call filled")
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    workspace = _dev(workspace, "workspace", device=dev, written=True)
+    s = _stream(stream, dev, u, delta, A, B, C, D, z, h0, dout, dh_final, workspace, *g.values())
     fn = lib().mssm_selective_scan_bwd_saved if saved else lib().mssm_selective_scan_bwd
     check(fn(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(dout),
              _ptr(dh_final), _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
              _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["dh0"]), bsz, dim, L, N, _ptr(workspace),
-             workspace.numel() * workspace.element_size(), code, _stream(stream, dev)))
+             _nbytes(workspace), code, s))
     return {k: v for k, v in g.items() if v is not None}
 
 
@@ -195,9 +210,7 @@ def state_update(state, u, delta, A, B, C, D=None, z=None, *, out=None, stream=N
     u, delta, z: [b, d]; B, C: [b, N]; A: [d, N]; D: [d].  Returns y [b, d]."""
     torch = _torch()
     dev = state.device
-    state = _dev(state, "state", dtype=torch.float32)
-    if not state.is_contiguous():
-        raise ValueError("state must be contiguous (it is updated in place)")
+    state = _dev(state, "state", dtype=torch.float32, written=True)
     bsz, dim, N = state.shape
     dt = u.dtype
     code = _dtype_code(u)
@@ -208,10 +221,11 @@ def state_update(state, u, delta, A, B, C, D=None, z=None, *, out=None, stream=N
     C = _dev(C, "C", (bsz, N), dt, dev)
     A = _dev(A, "A", (dim, N), torch.float32, dev)
     D = _dev(D, "D", (dim,), torch.float32, dev)
-    y = out if out is not None else torch.empty((bsz, dim), dtype=dt, device=dev)
-    _dev(y, "out", (bsz, dim), dt, dev)
+    y = _dev(out if out is not None else torch.empty((bsz, dim), dtype=dt, device=dev), "out", (bsz, dim), dt, dev,
+             written=True)
+    s = _stream(stream, dev, state, u, delta, A, B, C, D, z, y)
     check(lib().mssm_state_update(_ptr(state), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
-                                  _ptr(z), _ptr(y), bsz, dim, N, code, _stream(stream, dev)))
+                                  _ptr(z), _ptr(y), bsz, dim, N, code, s))
     return y
 
 
@@ -221,9 +235,7 @@ def ssd_state_update(state, x, dt, A, B, C, D=None, z=None, *, out=None, stream=
     Returns y [b, H, P]."""
     torch = _torch()
     dev = state.device
-    state = _dev(state, "state", dtype=torch.float32)
-    if not state.is_contiguous():
-        raise ValueError("state must be contiguous (it is updated in place)")
+    state = _dev(state, "state", dtype=torch.float32, written=True)
     bsz, H, P, N = state.shape
     G = B.shape[1]
     ty = x.dtype
@@ -235,10 +247,11 @@ def ssd_state_update(state, x, dt, A, B, C, D=None, z=None, *, out=None, stream=
     C = _dev(C, "C", (bsz, G, N), ty, dev)
     A = _dev(A, "A", (H,), torch.float32, dev)
     D = _dev(D, "D", (H,), torch.float32, dev)
-    y = out if out is not None else torch.empty((bsz, H, P), dtype=ty, device=dev)
-    _dev(y, "out", (bsz, H, P), ty, dev)
+    y = _dev(out if out is not None else torch.empty((bsz, H, P), dtype=ty, device=dev), "out", (bsz, H, P), ty,
+             dev, written=True)
+    s = _stream(stream, dev, state, x, dt, A, B, C, D, z, y)
     check(lib().mssm_ssd_state_update(_ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
-                                      _ptr(z), _ptr(y), bsz, H, P, N, G, code, _stream(stream, dev)))
+                                      _ptr(z), _ptr(y), bsz, H, P, N, G, code, s))
     return y
 
 
@@ -265,18 +278,17 @@ def ssd_chunk(x, dt, A, B, C, D=None, z=None, h0=None, *, chunk=256, return_fina
     A = _dev(A, "A", (H,), torch.float32, dev)
     D = _dev(D, "D", (H,), torch.float32, dev)
     h0 = _dev(h0, "h0", (bsz, H, P, N), torch.float32, dev)
-    y = out if out is not None else torch.empty_like(x)
-    _dev(y, "out", x.shape, ty, dev)
+    y = _dev(out if out is not None else torch.empty_like(x), "out", x.shape, ty, dev, written=True)
     hf = None
     if return_final_state or h_final is not None:
         hf = h_final if h_final is not None else torch.empty((bsz, H, P, N), dtype=torch.float32, device=dev)
-        _dev(hf, "h_final", (bsz, H, P, N), torch.float32, dev)
+        hf = _dev(hf, "h_final", (bsz, H, P, N), torch.float32, dev, written=True)
     need = ssd_workspace_size(bsz, L, H, P, N, G, chunk)
     ws = workspace
     if need > 0 and ws is None:
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
-    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    ws = _dev(ws, "workspace", device=dev, written=True)
+    s = _stream(stream, dev, x, dt, A, B, C, D, z, h0, y, hf, ws)
     check(lib().mssm_ssd_chunk_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
-                                   _ptr(y), _ptr(hf), bsz, L, H, P, N, G, chunk, _ptr(ws), wsb, code,
-                                   _stream(stream, dev)))
+                                   _ptr(y), _ptr(hf), bsz, L, H, P, N, G, chunk, _ptr(ws), _nbytes(ws), code, s))
     return (y, hf) if hf is not None else y

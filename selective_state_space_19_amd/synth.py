@@ -11,6 +11,14 @@ with eps ~ N(0, 1), so that delta > 0 and is centred on dt.  u, z, B, C ~ N(0, 1
 A[d, n] = -(n + 1) (negative, as the page requires); D = 1.  B and C are
 per token and shared by all channels of a batch row ([B, N, L]).
 
+``varied=True`` (any generator) instead draws the per-channel / per-head
+parameters the way the same page initialises a layer: A[d, n] = -exp(U[0, 1))
+for every (channel, state) and D ~ N(0, 1) per channel (Mamba-2: D_h ~ N(0, 1)
+per head; A_h is per head already).  These come from their own generator
+``PCG64([seed, 2_000_000])``, so every other array is the same as without it.
+Parity tests use it so that a kernel that reads A or D of the wrong channel or
+head cannot pass.
+
 Mamba-2 SSD workloads ("Mamba - Selective State Space Models" page, "Workflow 3 / Mamba-2"): headdim 64,
 d_state 128, ngroups 1; the scalar per-head A_h = -U[1, 16); dt per head.
 
@@ -83,6 +91,22 @@ def _delta(rng, dt_inv, shape):
     return _softplus(0.5 * rng.standard_normal(shape) + dt_inv)
 
 
+def _varied_params(seed, d_inner, d_state):
+    """A[d, n] = -exp(U[0, 1)) per (channel, state) and D[d] ~ N(0, 1) per
+    channel ("Mamba Architecture Details", Initialization Strategy), from a
+    generator of their own."""
+    g = np.random.Generator(np.random.PCG64([seed, 2_000_000]))
+    A = (-np.exp(g.random((d_inner, d_state)))).astype(np.float32)
+    D = g.standard_normal(d_inner).astype(np.float32)
+    return A, D
+
+
+def _varied_head_skip(seed, nheads):
+    """D_h ~ N(0, 1) per head, from a generator of its own."""
+    g = np.random.Generator(np.random.PCG64([seed, 2_000_000]))
+    return g.standard_normal(nheads).astype(np.float32)
+
+
 def periodic_window(a, axis: int, start: int, length: int) -> np.ndarray:
     """Tokens start .. start+length-1 of the sequence that repeats `a` along
     `axis` (a holds one period).  Used to build sequences far longer than
@@ -97,7 +121,7 @@ def periodic_window(a, axis: int, start: int, length: int) -> np.ndarray:
 # S6 selective scan inputs
 # --------------------------------------------------------------------------
 def s6_inputs(batch, d_inner, seqlen, d_state, dtype="f32", seed=0,
-              gate=True, skip=True, init_state=False):
+              gate=True, skip=True, init_state=False, varied=False):
     """u, delta, z: [batch, d_inner, seqlen]; B, C: [batch, d_state, seqlen]
     (stored dtype); A: [d_inner, d_state] f32; D: [d_inner] f32 or None;
     h0: [batch, d_inner, d_state] f32 ~ N(0, 0.1) or None."""
@@ -124,11 +148,14 @@ def s6_inputs(batch, d_inner, seqlen, d_state, dtype="f32", seed=0,
         Cm[b] = round_to(rng.standard_normal((d_state, seqlen)), dtype)
     A = np.broadcast_to(-(np.arange(d_state, dtype=np.float32) + 1.0), (d_inner, d_state)).copy()
     D = np.ones(d_inner, np.float32) if skip else None
+    if varied:
+        A, Dv = _varied_params(seed, d_inner, d_state)
+        D = Dv if skip else None
     return dict(u=u, delta=dl, A=A, B=Bm, C=Cm, D=D, z=z, h0=h0, dtype=dtype)
 
 
 def s6_fused_inputs(batch, d_inner, seqlen, d_state, d_conv=4, dtype="f32", seed=0, gate=True, skip=True,
-                    init_state=False, conv_history=False):
+                    init_state=False, conv_history=False, varied=False):
     """Inputs of the scan with its front end: x (before the causal conv) and
     the raw step delta_raw (before softplus) [B, D, L] in the stored dtype;
     conv_w [D, d_conv] and conv_b [D] ~ U(-1/sqrt(d_conv), 1/sqrt(d_conv))
@@ -162,6 +189,9 @@ def s6_fused_inputs(batch, d_inner, seqlen, d_state, d_conv=4, dtype="f32", seed
             ci[b] = round_to(rng.standard_normal((d_inner, d_conv - 1)), dtype)
     A = np.broadcast_to(-(np.arange(d_state, dtype=np.float32) + 1.0), (d_inner, d_state)).copy()
     D = np.ones(d_inner, np.float32) if skip else None
+    if varied:
+        A, Dv = _varied_params(seed, d_inner, d_state)
+        D = Dv if skip else None
     return dict(x=x, conv_w=conv_w, conv_b=conv_b, conv_init=ci, delta_raw=dr,
                 delta_bias=dt_inv.astype(np.float32), A=A, B=Bm, C=Cm, D=D, z=z, h0=h0, dtype=dtype)
 
@@ -169,7 +199,7 @@ def s6_fused_inputs(batch, d_inner, seqlen, d_state, d_conv=4, dtype="f32", seed
 # --------------------------------------------------------------------------
 # Decode (single-token state update) inputs
 # --------------------------------------------------------------------------
-def decode_initial(batch, d_inner, d_state, seed=0):
+def decode_initial(batch, d_inner, d_state, seed=0, varied=False):
     """Initial state [batch, d_inner, d_state] f32 ~ N(0, 0.1); A, D; and the
     per-channel softplus^-1(dt) used by every step."""
     base = np.random.Generator(np.random.PCG64(seed))
@@ -177,6 +207,8 @@ def decode_initial(batch, d_inner, d_state, seed=0):
     dt_inv = _softplus_inv(_dt_per_channel(base, d_inner))[None, :]
     A = np.broadcast_to(-(np.arange(d_state, dtype=np.float32) + 1.0), (d_inner, d_state)).copy()
     D = np.ones(d_inner, np.float32)
+    if varied:
+        A, D = _varied_params(seed, d_inner, d_state)
     return dict(state=state, A=A, D=D, dt_inv=dt_inv)
 
 
@@ -197,7 +229,7 @@ def decode_step(init, step, batch, d_inner, d_state, dtype="bf16", seed=0, gate=
 # Mamba-2 SSD inputs
 # --------------------------------------------------------------------------
 def ssd_inputs(batch, seqlen, nheads, headdim, d_state, ngroups=1, dtype="bf16",
-               seed=0, gate=False, skip=True, init_state=False):
+               seed=0, gate=False, skip=True, init_state=False, varied=False):
     """x, z: [batch, seqlen, nheads, headdim]; dt: [batch, seqlen, nheads];
     B, C: [batch, seqlen, ngroups, d_state] (stored dtype); A: [nheads] f32
     = -U[1, 16); D: [nheads] f32 or None; h0: [batch, nheads, headdim,
@@ -223,13 +255,15 @@ def ssd_inputs(batch, seqlen, nheads, headdim, d_state, ngroups=1, dtype="bf16",
         if gate:
             z[b] = round_to(rng.standard_normal((seqlen, nheads, headdim)), dtype)
     D = np.ones(nheads, np.float32) if skip else None
+    if varied and skip:
+        D = _varied_head_skip(seed, nheads)
     return dict(x=x, dt=dt, A=A, B=Bm, C=Cm, D=D, z=z, h0=h0, dtype=dtype)
 
 
 # --------------------------------------------------------------------------
 # Mamba-2 decode (single-token SSD state update) inputs
 # --------------------------------------------------------------------------
-def mamba2_decode_initial(batch, nheads, headdim, d_state, seed=0):
+def mamba2_decode_initial(batch, nheads, headdim, d_state, seed=0, varied=False):
     """Initial state [batch, nheads, headdim, d_state] f32 ~ N(0, 0.1); A [nheads]
     = -U[1, 16); D [nheads] = 1; and the per-head softplus^-1(dt) used by every step."""
     base = np.random.Generator(np.random.PCG64(seed))
@@ -237,6 +271,8 @@ def mamba2_decode_initial(batch, nheads, headdim, d_state, seed=0):
     dt_inv = _softplus_inv(_dt_per_channel(base, nheads))[None, :]
     state = base.normal(0.0, 0.1, (batch, nheads, headdim, d_state)).astype(np.float32)
     D = np.ones(nheads, np.float32)
+    if varied:
+        D = _varied_head_skip(seed, nheads)
     return dict(state=state, A=A, D=D, dt_inv=dt_inv)
 
 

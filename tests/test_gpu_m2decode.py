@@ -11,11 +11,11 @@ from selective_state_space_19_amd import synth
 pytestmark = pytest.mark.gpu
 
 
-def _steps(batch, H, P, N, G, steps, dtype, seed, gate=True, skip=True):
+def _steps(batch, H, P, N, G, steps, dtype, seed, gate=True, skip=True, varied=False):
     """Run `steps` tokens on the GPU (one state buffer, updated in place) and
     in the oracle; return the worst per-step y error and the final state error."""
     import torch
-    init = synth.mamba2_decode_initial(batch, H, P, N, seed=seed)
+    init = synth.mamba2_decode_initial(batch, H, P, N, seed=seed, varied=varied)
     st_gpu = dev(init["state"])
     st_ref = init["state"].astype(np.float64)
     A = dev(init["A"])
@@ -36,15 +36,20 @@ def _steps(batch, H, P, N, G, steps, dtype, seed, gate=True, skip=True):
     return worst, es
 
 
-@pytest.mark.parametrize("case", [
+SMALL = [
     # (batch, H, P, N, G, steps, dtype)
     (1, 1, 1, 16, 1, 3, "f32"), (2, 3, 5, 32, 1, 4, "f32"), (3, 4, 7, 64, 2, 3, "f32"),
     (1, 2, 9, 256, 1, 3, "f32"), (2, 2, 64, 128, 1, 4, "bf16"), (1, 4, 16, 256, 2, 3, "bf16"),
     (2, 8, 64, 128, 4, 3, "bf16"), (1, 1, 3, 16, 1, 2, "bf16"),
-], ids=lambda c: "b{}_H{}_P{}_N{}_G{}_x{}_{}".format(*c))
-def test_small_shapes(case):
+]
+
+
+# Every other case draws D_h per head (synth's varied=True; A_h is per head always).
+@pytest.mark.parametrize("i,case", list(enumerate(SMALL)),
+                         ids=lambda c: "b{}_H{}_P{}_N{}_G{}_x{}_{}".format(*c) if isinstance(c, tuple) else None)
+def test_small_shapes(i, case):
     b, H, P, N, G, steps, dt = case
-    ey, es = _steps(b, H, P, N, G, steps, dt, seed=700 + H + P + N)
+    ey, es = _steps(b, H, P, N, G, steps, dt, seed=700 + H + P + N, varied=i % 2 == 1)
     say(f"  {case}: y {ey:.3e} state {es:.3e}")
     assert ey <= TOL[dt] and es <= TOL[dt]
 
@@ -63,6 +68,16 @@ def test_mamba2_decode_workload():
     ey, es = _steps(s["batch"], s["nheads"], s["headdim"], s["d_state"], s["ngroups"], s["steps"], w.dtype,
                     seed=w.seed)
     say(f"  {w.name}: worst step y err {ey:.3e}, final state err {es:.3e}")
+    assert ey <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+def test_mamba2_decode_shape_varied_skip():
+    """The Mamba-2 decode shape with D_h drawn per head, 16 tokens."""
+    w = synth.WORKLOADS["decode_mamba2_bf16"]
+    s = w.shape
+    ey, es = _steps(s["batch"], s["nheads"], s["headdim"], s["d_state"], s["ngroups"], 16, w.dtype,
+                    seed=w.seed, varied=True)
+    say(f"  {w.name} varied: worst step y err {ey:.3e}, final state err {es:.3e}")
     assert ey <= TOL["bf16"] and es <= TOL["bf16"]
 
 

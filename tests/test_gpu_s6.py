@@ -67,12 +67,16 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=lambda c: "b{}_d{}_L{}_N{}_{}_z{}_D{}_h{}".format(*c))
-def test_ragged_shapes(case):
+# Every other case draws A[d, n] and D[d] per channel (synth's varied=True),
+# so a kernel that reads A or D of the wrong channel fails.
+@pytest.mark.parametrize("i,case", list(enumerate(CASES)),
+                         ids=lambda c: "b{}_d{}_L{}_N{}_{}_z{}_D{}_h{}".format(*c) if isinstance(c, tuple) else None)
+def test_ragged_shapes(i, case):
     b, d, L, N, dt, gate, skip, h0 = case
+    varied = i % 2 == 1
     inp = synth.s6_inputs(b, d, L, N, dtype=dt, seed=1000 + b * 7 + d + L + N, gate=gate, skip=skip,
-                          init_state=h0)
-    _check(inp, "x".join(map(str, case)))
+                          init_state=h0, varied=varied)
+    _check(inp, "x".join(map(str, case)) + ("_varied" if varied else ""))
 
 
 def test_mamba130m_workload_full():
@@ -87,41 +91,19 @@ def test_mamba130m_state_only():
     _check(synth.s6_inputs(**w.shape, dtype=w.dtype, seed=w.seed, gate=False, skip=False), w.name + "_noDz")
 
 
-def _sampled(inp, y, hf, rows, tol, name):
-    """Oracle on a sample of channels (b, d) of a full-size run."""
-    y, hf = host(y), host(hf)
-    worst = 0.0
-    for b in sorted(set(r[0] for r in rows)):
-        ds = np.array(sorted(r[1] for r in rows if r[0] == b))
-        sub = dict(dtype=inp["dtype"])
-        for k in ("u", "delta", "z"):
-            sub[k] = None if inp[k] is None else inp[k][b:b + 1, ds]
-        sub["B"], sub["C"] = inp["B"][b:b + 1], inp["C"][b:b + 1]
-        sub["A"] = inp["A"][ds]
-        sub["D"] = None if inp["D"] is None else inp["D"][ds]
-        sub["h0"] = None if inp["h0"] is None else inp["h0"][b:b + 1, ds]
-        yo, ho = _oracle(sub)
-        ey = normwise(y[b:b + 1, ds], yo)
-        eh = normwise(hf[b:b + 1, ds], ho)
-        worst = max(worst, ey, eh)
-        assert ey <= tol and eh <= tol, f"{name} b={b}: y {ey} h {eh}"
-    say(f"  {name}: sampled worst err {worst:.3e} (tol {tol})")
+def test_mamba130m_varied_params_full():
+    """Mamba-130M layer shape with A[d, n] and D[d] drawn per channel
+    (synth's varied=True): every output."""
+    w = synth.WORKLOADS["s6_mamba130m_f32"]
+    _check(synth.s6_inputs(**w.shape, dtype=w.dtype, seed=w.seed, varied=True), w.name + "_varied")
 
 
-def test_mamba1p4b_workload_sampled():
-    """Mamba-1.4B layer shape (4 x 4096 x 8192, N 16, bf16 in / fp32 state),
-    in the benchmark's launch configuration; 96 channels checked against the
-    oracle, every output checked finite."""
+def test_mamba1p4b_workload_full():
+    """Mamba-1.4B layer shape (4 x 4096 x 8192, N 16, bf16 in / fp32 state,
+    h_final out), in the benchmark's launch configuration: every output and
+    every final state against the oracle."""
     w = synth.WORKLOADS["s6_mamba1p4b_bf16"]
-    inp = synth.s6_inputs(**w.shape, dtype=w.dtype, seed=w.seed)
-    y, hf = _run_gpu(inp)
-    assert bool(np.isfinite(host(hf)).all())
-    import torch
-    assert bool(torch.isfinite(y).all())
-    rng = np.random.default_rng(5)
-    rows = [(int(b), int(d)) for b, d in zip(rng.integers(0, 4, 96), rng.integers(0, 4096, 96))]
-    rows += [(0, 0), (3, 4095), (1, 63), (2, 64)]
-    _sampled(inp, y, hf, sorted(set(rows)), TOL["bf16"], w.name)
+    _check(synth.s6_inputs(**w.shape, dtype=w.dtype, seed=w.seed), w.name)
 
 
 def test_bitwise_deterministic():

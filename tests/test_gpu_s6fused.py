@@ -63,11 +63,14 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=lambda c: "b{}_d{}_L{}_N{}_K{}_{}_z{}_D{}_h{}_hist{}".format(*c))
-def test_ragged_shapes(case):
+# Every other case draws A[d, n] and D[d] per channel (synth's varied=True).
+@pytest.mark.parametrize("i,case", list(enumerate(CASES)),
+                         ids=lambda c: "b{}_d{}_L{}_N{}_K{}_{}_z{}_D{}_h{}_hist{}".format(*c) if isinstance(c, tuple)
+                         else None)
+def test_ragged_shapes(i, case):
     b, d, L, N, K, dt, gate, skip, h0, hist = case
     inp = synth.s6_fused_inputs(b, d, L, N, d_conv=K, dtype=dt, seed=2000 + d + L + N + K, gate=gate, skip=skip,
-                                init_state=h0, conv_history=hist)
+                                init_state=h0, conv_history=hist, varied=i % 2 == 1)
     y, hf = _run_gpu(inp)
     yo, ho = _oracle(inp)
     tol = TOL[dt]
@@ -77,23 +80,16 @@ def test_ragged_shapes(case):
     assert ey <= tol and eh <= tol
 
 
-def test_mamba1p4b_fused_workload_sampled():
+def test_mamba1p4b_fused_workload_full():
     """Mamba-1.4B layer shape (4 x 4096 x 8192, N 16, d_conv 4, bf16) in the
-    benchmark's launch configuration; 64 channels of one batch row checked
-    against the oracle, every output checked finite."""
-    import torch
+    benchmark's launch configuration: every output and final state against
+    the oracle."""
     w = synth.WORKLOADS["s6fused_mamba1p4b_bf16"]
     inp = synth.s6_fused_inputs(**w.shape, dtype=w.dtype, seed=w.seed)
     y, hf = _run_gpu(inp)
-    assert bool(torch.isfinite(y).all()) and bool(np.isfinite(host(hf)).all())
-    rng = np.random.default_rng(8)
-    b = 2
-    ds = np.sort(np.concatenate([rng.choice(4096, 60, replace=False), [0, 63, 64, 4095]]))
-    ds = np.unique(ds)
-    yo, ho = _oracle(inp, (b, ds))
-    ey = normwise(host(y[b:b + 1, ds]), yo)
-    eh = normwise(host(hf[b:b + 1, ds]), ho)
-    say(f"  {w.name}: sampled y err {ey:.3e}  h_final err {eh:.3e}")
+    yo, ho = _oracle(inp)
+    ey, eh = normwise(host(y), yo), normwise(host(hf), ho)
+    say(f"  {w.name}: y err {ey:.3e}  h_final err {eh:.3e}")
     assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
 
 

@@ -2,7 +2,7 @@
 (mssm_selective_scan_zoh_fwd) against the fp64 oracle's hold form, on the
 same seeded inputs, through the C ABI.  The step and A values span both
 sides of the kernel's series / direct switch for the hold gain (|delta A|
-below and above 1/4), and include A = 0 and tiny A."""
+below and above 1/16), and include A = 0 and tiny A."""
 import numpy as np
 import pytest
 
@@ -74,25 +74,40 @@ def test_mamba130m_workload_full():
     _check(synth.s6_inputs(**w.shape, dtype=w.dtype, seed=w.seed), w.name + "_zoh")
 
 
-def test_mamba1p4b_workload_sampled():
-    """Mamba-1.4B layer shape (4 x 4096 x 8192, N 16, bf16): 64 channels of
-    two batch rows against the oracle, every output finite."""
+def test_mamba1p4b_workload_full():
+    """Mamba-1.4B layer shape (4 x 4096 x 8192, N 16, bf16): every output and
+    final state against the oracle's hold form."""
     w = synth.WORKLOADS["s6_mamba1p4b_bf16"]
-    inp = synth.s6_inputs(**w.shape, dtype=w.dtype, seed=w.seed)
-    say("  zoh gpu call: Mamba-1.4B shape")
+    _check(synth.s6_inputs(**w.shape, dtype=w.dtype, seed=w.seed), w.name + "_zoh")
+
+
+def test_mamba130m_varied_params_full():
+    """Mamba-130M layer shape, fp32, with A[d, n] = -exp(U[0, 1)) and D[d]
+    drawn per channel: every output."""
+    w = synth.WORKLOADS["s6_mamba130m_f32"]
+    _check(synth.s6_inputs(**w.shape, dtype=w.dtype, seed=w.seed, varied=True), w.name + "_zoh_varied")
+
+
+def test_gain_switch_straddled_fp32():
+    """fp32 with delta*A clustered around the gain's series / direct switch
+    (|delta A| = 1/16): A[d, n] is set from the channel's median step so that
+    most elements fall within a factor 2 of it, on both sides.  The error
+    budget of the gain there is ~1e-6 relative, so the outputs are held to
+    3e-6, tighter than the fp32 tolerance."""
+    inp = synth.s6_inputs(2, 96, 400, 16, dtype="f32", seed=3777, init_state=True)
+    dl = inp["delta"].astype(np.float64)
+    med = np.median(dl, axis=(0, 2))                        # per channel
+    f = np.exp(np.linspace(np.log(0.5), np.log(2.0), 16))  # per state, both sides of the switch
+    inp["A"] = (-(1.0 / 16.0) / med[:, None] * f[None, :]).astype(np.float32)
+    x = np.abs(dl[:, :, None, :] * inp["A"][None, :, :, None].astype(np.float64))
+    near = np.mean((x > 1.0 / 32.0) & (x < 1.0 / 8.0))
+    assert near > 0.5 and np.mean(x < 1.0 / 16.0) > 0.2 and np.mean(x > 1.0 / 16.0) > 0.2
+    say("  zoh gpu call: gain switch straddled, fp32")
     args = [dev(inp[k]) for k in ("u", "delta", "A", "B", "C", "D", "z", "h0")]
     y, hf = mssm.selective_scan(*args, return_final_state=True, zoh=True)
     import torch
     torch.cuda.synchronize()
-    assert bool(torch.isfinite(y).all()) and bool(torch.isfinite(hf).all())
-    y, hf = host(y), host(hf)
-    tol = TOL[inp["dtype"]]
-    for b, ds in ((0, np.arange(0, 4096, 128)), (3, np.arange(77, 4096, 128))):
-        sub = {k: None if inp[k] is None else inp[k][b:b + 1, ds] for k in ("u", "delta", "z")}
-        sub.update(dtype=inp["dtype"], B=inp["B"][b:b + 1], C=inp["C"][b:b + 1], A=inp["A"][ds],
-                   D=None if inp["D"] is None else inp["D"][ds],
-                   h0=None if inp["h0"] is None else inp["h0"][b:b + 1, ds])
-        yo, ho = oracle.s6_scan(*(wide(sub, k) for k in ("u", "delta", "A", "B", "C", "D", "z", "h0")), zoh=True)
-        ey, eh = normwise(y[b:b + 1, ds], yo), normwise(hf[b:b + 1, ds], ho)
-        say(f"  1.4B zoh b={b}: y {ey:.3e} h {eh:.3e}")
-        assert ey <= tol and eh <= tol
+    yo, ho = oracle.s6_scan(*(wide(inp, k) for k in ("u", "delta", "A", "B", "C", "D", "z", "h0")), zoh=True)
+    ey, eh = normwise(host(y), yo), normwise(host(hf), ho)
+    say(f"  straddle: y err {ey:.3e}  h_final err {eh:.3e}  (tol 3e-6)")
+    assert ey <= 3e-6 and eh <= 3e-6

@@ -56,12 +56,16 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=lambda c: "b{}_L{}_H{}_N{}_G{}_Q{}_z{}_D{}_h{}".format(*c))
-def test_ragged_shapes(case):
+# Every other case draws D_h per head (synth's varied=True; A_h is per head always).
+@pytest.mark.parametrize("i,case", list(enumerate(CASES)),
+                         ids=lambda c: "b{}_L{}_H{}_N{}_G{}_Q{}_z{}_D{}_h{}".format(*c) if isinstance(c, tuple)
+                         else None)
+def test_ragged_shapes(i, case):
     b, L, H, N, G, Q, gate, skip, h0 = case
+    varied = i % 2 == 1
     inp = synth.ssd_inputs(b, L, H, 64, N, G, dtype="bf16", seed=300 + L + H + N, gate=gate, skip=skip,
-                           init_state=h0)
-    _check(inp, Q, "x".join(map(str, case)))
+                           init_state=h0, varied=varied)
+    _check(inp, Q, "x".join(map(str, case)) + ("_varied" if varied else ""))
 
 
 def test_mamba2_workload_full():
@@ -144,3 +148,16 @@ def test_zero_length_and_errors():
     with pytest.raises(mssm.MssmError) as e:
         mssm.ssd_chunk(*(dev(inp[k]) for k in ("x", "dt", "A", "B", "C", "D", "z", "h0")), chunk=96)
     assert e.value.code == -4
+
+
+@pytest.mark.parametrize("chunk", [64, 256])
+def test_carried_state_term_isolated(chunk):
+    """x = 0 and a large h0: every output is the carried-in state's term
+    exp(s_i) C_i H_in (no intra-chunk product, no skip term), which the
+    kernel forms from the state rounded to bf16 (an MFMA operand).  Its error
+    is measured alone here, against the oracle's fp64 state."""
+    inp = synth.ssd_inputs(2, 700, 4, 64, 128, 1, dtype="bf16", seed=91, gate=True, init_state=True, varied=True)
+    inp["x"] = np.zeros_like(inp["x"])
+    inp["h0"] = (inp["h0"] * 30.0).astype(np.float32)
+    ey, eh = _check(inp, chunk, f"carried_state_only_q{chunk}")
+    say(f"  carried state alone: y err {ey:.3e} (bf16 state operand), h_final err {eh:.3e}")

@@ -425,6 +425,56 @@ def test_fused_chaining(oracle_lib):
     np.testing.assert_allclose(h2, hT, rtol=0, atol=1e-12)
 
 
+def test_fused_bias_enters_before_softplus(oracle_lib):
+    """The step bias is added to the raw step before softplus: for any
+    positive target step s and any bias, raw = log(expm1(s)) - bias (the
+    textbook inverse of softplus) must give exactly the scan with step s.
+    Adding the bias after softplus would give softplus(raw) + bias, which is
+    not s (it is not even positive for a negative bias)."""
+    rng = np.random.default_rng(35)
+    b, d, L, N, K = 2, 4, 30, 3, 4
+    x = rng.standard_normal((b, d, L))
+    s = np.exp(rng.uniform(np.log(1e-3), np.log(0.5), (b, d, L)))      # target steps
+    bias = rng.uniform(-3.0, 3.0, d)
+    raw = np.log(np.expm1(s)) - bias[None, :, None]
+    w = np.zeros((d, K))
+    w[:, K - 1] = 1.0                                                    # identity conv: u = silu(x)
+    A = -rng.uniform(0.5, 3.0, (d, N))
+    Bm, Cm, z = rng.standard_normal((b, N, L)), rng.standard_normal((b, N, L)), rng.standard_normal((b, d, L))
+    D = rng.standard_normal(d)
+    y, hT = oracle.s6_scan_fused(x, w, None, None, raw, bias, A, Bm, Cm, D, z, lib=oracle_lib)
+    yr, hr = oracle.s6_scan(silu(x), s, A, Bm, Cm, D, z, lib=oracle_lib)
+    assert normwise_err(y, yr) < 1e-12 and normwise_err(hT, hr) < 1e-12
+    # the other placement is far off
+    wrong = oracle.softplus(raw) + bias[None, :, None]
+    assert np.max(np.abs(wrong - s)) > 0.5
+
+
+def test_varied_parameters_expose_a_wrong_channel(oracle_lib):
+    """With synth's varied=True (A[d, n] and D[d] drawn per channel, D_h per
+    head), reading A or D of a neighbouring channel or head moves the outputs
+    far outside the bf16 tolerance (2e-2), so the GPU parity cases that use
+    it would catch such an indexing slip.  With the configurations' A = -(n+1)
+    and D = 1 the same slip changes nothing."""
+    inp = synth.s6_inputs(2, 33, 64, 16, dtype="f32", seed=11, init_state=True, varied=True)
+    args = [synth.widen(inp[k], "f32") for k in ("u", "delta", "A", "B", "C", "D", "z", "h0")]
+    y, hT = oracle.s6_scan(*args, lib=oracle_lib)
+    for k in (2, 5):                                   # A, then D, of channel d + 1
+        bad = list(args)
+        bad[k] = np.roll(args[k], 1, axis=0)
+        yb, hb = oracle.s6_scan(*bad, lib=oracle_lib)
+        assert max(normwise_err(yb, y), normwise_err(hb, hT)) > 0.1
+    plain = synth.s6_inputs(2, 33, 64, 16, dtype="f32", seed=11, init_state=True)
+    assert np.all(plain["A"] == plain["A"][:1]) and np.all(plain["D"] == 1.0)
+    # Mamba-2: D_h of the neighbouring head
+    si = synth.ssd_inputs(1, 40, 4, 8, 16, 1, dtype="f32", seed=12, varied=True)
+    sa = [si[k] for k in ("x", "dt", "A", "B", "C", "D", "z", "h0")]
+    ys, _ = oracle.ssd(*sa, lib=oracle_lib)
+    sa[5] = np.roll(si["D"], 1)
+    yb, _ = oracle.ssd(*sa, lib=oracle_lib)
+    assert normwise_err(yb, ys) > 0.1
+
+
 def test_fused_generator_matches_step_distribution():
     """softplus(delta_raw + delta_bias) of the fused inputs is positive and
     centred like s6_inputs' delta; conv weights are bounded by 1/sqrt(d_conv)."""
