@@ -326,6 +326,31 @@ int mssm_ssd_chunk_fwd(const void* x, const void* dt, const float* A, const void
                        mssm_dtype dtype, void* stream);
 
 /*
+ * mssm_ssd_chunk_fwd for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  It takes no workspace: its scratch is a fixed array of
+ * MSSM_NOALLOC_SCRATCH_BYTES in device memory, one copy per GPU, which stays
+ * reserved until the process ends.  Arguments, layouts, limits and results
+ * are those of mssm_ssd_chunk_fwd; the caller still passes every input and
+ * output.  Sizes whose workspace (mssm_ssd_workspace_size) exceeds the array
+ * return MSSM_ERR_WORKSPACE, before anything is enqueued.  The call itself
+ * allocates nothing; the first call on a device looks the array's address up
+ * once (hipGetSymbolAddress).
+ *
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (the kernels write every scratch byte they read, so no clearing is
+ * needed): calls that may overlap on one GPU -- on different streams, or from
+ * different threads without ordering -- race on it and must not be issued.
+ */
+#define MSSM_NOALLOC_SCRATCH_BYTES (64LL << 20)
+int mssm_ssd_chunk_fwd_noalloc(const void* x, const void* dt, const float* A, const void* Bm,
+                               const void* Cm, const float* Dskip, const void* z,
+                               const float* h0, void* y, float* h_final, int64_t batch,
+                               int64_t seqlen, int64_t nheads, int64_t headdim,
+                               int64_t d_state, int64_t ngroups, int64_t chunk,
+                               mssm_dtype dtype, void* stream);
+
+/*
  * Mamba-2 decode: one token of the SSD recurrence, state updated in place.
  *
  * Defined by: "Mamba - Selective State Space Models" page, "Workflow 3" --

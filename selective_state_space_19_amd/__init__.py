@@ -11,7 +11,8 @@ from __future__ import annotations
 from ._lib import MSSM_BF16, MSSM_F32, MssmError, check, lib
 
 __all__ = ["selective_scan", "selective_scan_fused", "selective_scan_bwd", "selective_scan_bwd_workspace_size",
-           "state_update", "ssd_chunk", "ssd_state_update", "ssd_workspace_size", "MssmError", "lib"]
+           "state_update", "ssd_chunk", "ssd_chunk_noalloc", "ssd_state_update", "ssd_workspace_size", "MssmError",
+           "lib"]
 
 
 def _torch():
@@ -291,4 +292,33 @@ def ssd_chunk(x, dt, A, B, C, D=None, z=None, h0=None, *, chunk=256, return_fina
     s = _stream(stream, dev, x, dt, A, B, C, D, z, h0, y, hf, ws)
     check(lib().mssm_ssd_chunk_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
                                    _ptr(y), _ptr(hf), bsz, L, H, P, N, G, chunk, _ptr(ws), _nbytes(ws), code, s))
+    return (y, hf) if hf is not None else y
+
+
+def ssd_chunk_noalloc(x, dt, A, B, C, D=None, z=None, h0=None, *, out, h_final=None, chunk=256, stream=None):
+    """ssd_chunk for callers that cannot allocate (mssm_ssd_chunk_fwd_noalloc):
+    the library's static per-GPU scratch replaces the workspace, and this
+    wrapper allocates nothing either -- every tensor, `out` (and `h_final` if
+    wanted) included, is the caller's and must already be contiguous.  Calls
+    that may overlap on one GPU share the scratch and must not be issued."""
+    torch = _torch()
+    dev = x.device
+    x = _dev(x, "x", written=True)
+    bsz, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    ty = x.dtype
+    code = _dtype_code(x)
+    dt = _dev(dt, "dt", (bsz, L, H), ty, dev, written=True)
+    B = _dev(B, "B", (bsz, L, G, N), ty, dev, written=True)
+    C = _dev(C, "C", (bsz, L, G, N), ty, dev, written=True)
+    z = _dev(z, "z", x.shape, ty, dev, written=True)
+    A = _dev(A, "A", (H,), torch.float32, dev, written=True)
+    D = _dev(D, "D", (H,), torch.float32, dev, written=True)
+    h0 = _dev(h0, "h0", (bsz, H, P, N), torch.float32, dev, written=True)
+    y = _dev(out, "out", x.shape, ty, dev, written=True)
+    hf = _dev(h_final, "h_final", (bsz, H, P, N), torch.float32, dev, written=True)
+    cur = torch.cuda.current_stream(dev)
+    s = (stream if stream is not None else cur).cuda_stream
+    check(lib().mssm_ssd_chunk_fwd_noalloc(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
+                                           _ptr(y), _ptr(hf), bsz, L, H, P, N, G, chunk, code, s))
     return (y, hf) if hf is not None else y

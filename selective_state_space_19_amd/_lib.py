@@ -24,6 +24,13 @@ ERRORS = {
 }
 
 
+def noalloc_scratch_bytes() -> int:
+    """MSSM_NOALLOC_SCRATCH_BYTES from include/mssm.h: the static scratch of
+    mssm_ssd_chunk_fwd_noalloc."""
+    m = re.search(r"#define MSSM_NOALLOC_SCRATCH_BYTES \((\d+)LL << (\d+)\)", open(HEADER).read())
+    return int(m.group(1)) << int(m.group(2))
+
+
 class MssmError(RuntimeError):
     def __init__(self, code: int, msg: str):
         super().__init__(f"{ERRORS.get(code, code)}: {msg}")
@@ -59,6 +66,8 @@ def _bind(lib):
     lib.mssm_ssd_workspace_size.restype = _sz
     lib.mssm_ssd_chunk_fwd.argtypes = [_vp] * 10 + [_i64] * 7 + [_vp, _sz, _i32, _vp]
     lib.mssm_ssd_chunk_fwd.restype = _i32
+    lib.mssm_ssd_chunk_fwd_noalloc.argtypes = [_vp] * 10 + [_i64] * 7 + [_i32, _vp]
+    lib.mssm_ssd_chunk_fwd_noalloc.restype = _i32
     lib.mssm_last_error.argtypes = []
     lib.mssm_last_error.restype = ctypes.c_char_p
     lib.mssm_version.argtypes = []

@@ -11,6 +11,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "kernels.h"
@@ -53,6 +54,36 @@ bool prod_ok(int64_t a, int64_t b, int64_t c, int64_t* out) {
 
 int launched(const char* fn, hipError_t e) {
     if (e != hipSuccess) return fail(MSSM_ERR_LAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return MSSM_OK;
+}
+
+// Scratch for the entry point that allocates nothing
+// (mssm_ssd_chunk_fwd_noalloc): a fixed array in device memory, one copy per
+// GPU, held until the process ends.  In host code `scratch` names a host-side
+// stand-in, not device memory: kernels get the device address that
+// hipGetSymbolAddress returns, looked up once per device (with that device
+// current) on the entry point's first call there and kept in g_scratch.
+constexpr size_t kScratchBytes = size_t(MSSM_NOALLOC_SCRATCH_BYTES);
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+int scratch_address(const char* fn, void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(MSSM_ERR_LAUNCH, "%s: hipGetDevice failed: %s", fn, hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(MSSM_ERR_UNSUPPORTED, "%s: device %d beyond %d", fn, dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(MSSM_ERR_LAUNCH, "%s: hipGetSymbolAddress(scratch) failed: %s", fn, hipGetErrorString(e));
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
     return MSSM_OK;
 }
 
@@ -337,12 +368,13 @@ size_t mssm_ssd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads, in
     return mssm::ssd_workspace_bytes(batch, seqlen, nheads, headdim, d_state, ngroups, chunk);
 }
 
-int mssm_ssd_chunk_fwd(const void* x, const void* dt, const float* A, const void* Bm, const void* Cm,
-                       const float* Dskip, const void* z, const float* h0, void* y, float* h_final,
-                       int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t d_state,
-                       int64_t ngroups, int64_t chunk, void* workspace, size_t workspace_bytes,
-                       mssm_dtype dtype, void* stream) {
-    static const char* fn = "mssm_ssd_chunk_fwd";
+// scratch: the caller passed no workspace; once the arguments pass, this
+// device's static scratch array (workspace_bytes long) is used instead, and a
+// size above it is reported as the array's limit.
+static int ssd_fwd(const char* fn, const void* x, const void* dt, const float* A, const void* Bm, const void* Cm,
+                   const float* Dskip, const void* z, const float* h0, void* y, float* h_final, int64_t batch,
+                   int64_t seqlen, int64_t nheads, int64_t headdim, int64_t d_state, int64_t ngroups, int64_t chunk,
+                   void* workspace, size_t workspace_bytes, bool scratch, mssm_dtype dtype, void* stream) {
     g_err.clear();
     if (dtype != MSSM_F32 && dtype != MSSM_BF16) return fail(MSSM_ERR_DTYPE, "%s: unknown dtype %d", fn, (int)dtype);
     if (batch < 0 || seqlen < 0 || nheads < 0 || headdim < 0 || d_state < 0 || ngroups < 0 || chunk < 0)
@@ -379,6 +411,15 @@ int mssm_ssd_chunk_fwd(const void* x, const void* dt, const float* A, const void
     CHECK_OPT(Dskip);
     CHECK_OPT(z);
     const size_t need = mssm::ssd_workspace_bytes(batch, seqlen, nheads, headdim, d_state, ngroups, chunk);
+    if (scratch) {
+        if (need > workspace_bytes)
+            return fail(MSSM_ERR_WORKSPACE,
+                        "%s: these sizes need %zu bytes of scratch, above the %zu bytes of the static scratch "
+                        "array (call mssm_ssd_chunk_fwd with a workspace instead)",
+                        fn, need, workspace_bytes);
+        const int rc = scratch_address(fn, &workspace);
+        if (rc != MSSM_OK) return rc;
+    }
     if (need > 0) {
         if (!workspace) return fail(MSSM_ERR_WORKSPACE, "%s: workspace is NULL (%zu bytes needed)", fn, need);
         if (!aligned16(workspace)) return fail(MSSM_ERR_ALIGN, "%s: workspace is not 16-byte aligned", fn);
@@ -388,6 +429,24 @@ int mssm_ssd_chunk_fwd(const void* x, const void* dt, const float* A, const void
     mssm::SSDParams p{x, dt, A, Bm, Cm, Dskip, z, h0, y, h_final, workspace, batch, (int32_t)seqlen,
                       (int32_t)nheads, (int32_t)headdim, (int32_t)d_state, (int32_t)ngroups, (int32_t)chunk};
     return launched(fn, mssm::launch_ssd(p, s));
+}
+
+int mssm_ssd_chunk_fwd(const void* x, const void* dt, const float* A, const void* Bm, const void* Cm,
+                       const float* Dskip, const void* z, const float* h0, void* y, float* h_final,
+                       int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t d_state,
+                       int64_t ngroups, int64_t chunk, void* workspace, size_t workspace_bytes,
+                       mssm_dtype dtype, void* stream) {
+    return ssd_fwd("mssm_ssd_chunk_fwd", x, dt, A, Bm, Cm, Dskip, z, h0, y, h_final, batch, seqlen, nheads, headdim,
+                   d_state, ngroups, chunk, workspace, workspace_bytes, false, dtype, stream);
+}
+
+int mssm_ssd_chunk_fwd_noalloc(const void* x, const void* dt, const float* A, const void* Bm, const void* Cm,
+                               const float* Dskip, const void* z, const float* h0, void* y, float* h_final,
+                               int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t d_state,
+                               int64_t ngroups, int64_t chunk, mssm_dtype dtype, void* stream) {
+    // the scratch address is looked up after the arguments are checked
+    return ssd_fwd("mssm_ssd_chunk_fwd_noalloc", x, dt, A, Bm, Cm, Dskip, z, h0, y, h_final, batch, seqlen, nheads,
+                   headdim, d_state, ngroups, chunk, nullptr, kScratchBytes, true, dtype, stream);
 }
 
 }  // extern "C"

@@ -25,7 +25,8 @@ def test_exports_every_declared_function(lib):
                           "mssm_selective_scan_fwd_save", "mssm_selective_scan_bwd_saved",
                           "mssm_selective_scan_bwd_workspace_size", "mssm_state_update",
                           "mssm_ssd_workspace_size",
-                          "mssm_ssd_chunk_fwd", "mssm_ssd_state_update", "mssm_last_error", "mssm_version"}
+                          "mssm_ssd_chunk_fwd", "mssm_ssd_chunk_fwd_noalloc", "mssm_ssd_state_update",
+                          "mssm_last_error", "mssm_version"}
     for n in names:
         assert hasattr(lib, n), n
         assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
@@ -129,6 +130,34 @@ def test_ssd_argument_errors(lib):
         assert _ssd(lib, ws=None) == ERR_WS
         assert _ssd(lib, wsb=need - 1) == ERR_WS
     assert _ssd(lib, b=0) == 0
+
+
+def _ssd_na(lib, **kw):
+    a = dict(x=FAKE, dt=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, h0=None, y=FAKE, hf=None,
+             b=1, L=512, H=4, P=64, N=64, G=1, Q=256, dtype=1)
+    a.update(kw)
+    return lib.mssm_ssd_chunk_fwd_noalloc(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["z"], a["h0"],
+                                          a["y"], a["hf"], a["b"], a["L"], a["H"], a["P"], a["N"], a["G"], a["Q"],
+                                          a["dtype"], None)
+
+
+def test_ssd_noalloc_argument_errors(lib):
+    """The entry point without a workspace checks its arguments like
+    mssm_ssd_chunk_fwd, and rejects sizes whose workspace exceeds its static
+    scratch before looking the scratch up (no GPU is touched here)."""
+    limit = _lib.noalloc_scratch_bytes()
+    assert limit == 64 << 20
+    assert _ssd_na(lib, x=None) == ERR_NULL
+    assert _ssd_na(lib, H=3, G=2) == ERR_SHAPE
+    assert _ssd_na(lib, Q=100) == ERR_UNSUP
+    assert _ssd_na(lib, dtype=9) == ERR_DTYPE
+    assert _ssd_na(lib, b=0) == 0
+    # the Mamba-2 layer at batch 4 fits; at batch 32 its workspace does not
+    assert lib.mssm_ssd_workspace_size(4, 4096, 32, 64, 128, 1, 256) <= limit
+    big = lib.mssm_ssd_workspace_size(32, 4096, 32, 64, 128, 1, 256)
+    assert big > limit
+    assert _ssd_na(lib, b=32, L=4096, H=32, N=128) == ERR_WS
+    assert b"static scratch" in lib.mssm_last_error()
 
 
 def test_workspace_size_is_pure(lib):
