@@ -11,10 +11,13 @@ written once) divided by the time per step; also reported: tokens-ch/s
 fp64 CPU oracle timed on the same workload, and the other entry points
 (decode step at the Mamba-2.8B shape, Mamba-2 SSD) inside the same object.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--only s6,s6fused,s6bwd,decode,decode2,ssd,copy]
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+                    [--only s6,calib,s6c1,s6fused,s6zoh,s6bwd,decode,decode2,ssd,copy]
 
 Prints exactly one JSON line on stdout; progress goes to stderr.  `--only`
-restricts the run (for profiling); `copy` times a plain 1 GiB device copy,
+restricts the run (for profiling); `calib` measures the copy / read
+ceilings and VALU issue rates on the GPU at hand; `s6c1` times the scan at
+the Mamba-130M layer shape (fp32); `copy` times a plain 1 GiB device copy,
 the reference used to scale the HBM byte counters.
 """
 from __future__ import annotations
@@ -34,12 +37,18 @@ sys.path.insert(0, ROOT)
 METRIC = "selective-scan effective HBM GB/s (% of peak) + B·L·D_inner tokens-ch/s"
 HBM_PEAK_GBS = 8000.0                  # MI355X HBM3E, 8 TB/s
 WARM_MS = 100.0                        # wall-clock warm-up before each secondary timing
-# fp32 VALU issue rate without packed math: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz.
-VALU_LANE_INSTR = 256 * 4 * 16 * 2.4e9
-# One S6 state element: v_mul (delta*A), v_exp, v_mul (delta*u*B), v_fma (h), v_fma (y):
-# 5 VALU instructions, counted as 7 flop (mul 1, exp 1, fma 2).
-S6_INSTR_PER_ELEM, S6_FLOP_PER_ELEM = 5, 7
-S6_ALU_PEAK_TFLOPS = VALU_LANE_INSTR / S6_INSTR_PER_ELEM * S6_FLOP_PER_ELEM / 1e12   # 55.05
+WARM_MS_HEADLINE = 300.0               # and before the headline timing
+# fp32 vector peak: 157.3 TFLOP/s published = 78.6e12 lane-FMA/s (256 CUs x 4 SIMDs
+# x 2.4 GHz x 32 fp32 lanes per SIMD per clock; the calibration probes reach
+# 0.7-0.8 of it with plain v_fma_f32, no packed math).
+FP32_FMA_LANE_PEAK = 157.3e12 / 2
+VALU_LANE_SLOTS = 256 * 4 * 16 * 2.4e9           # the 16-lane figure, reported for comparison
+# One S6 state element: v_mul (delta*A), v_exp_f32, v_mul (delta*u*B), v_fma (h),
+# v_fma (y), counted as 7 flop (mul 1, exp 1, mul 1, fma 2, fma 2).  v_exp_f32
+# issues at a quarter of the FMA rate (measured 0.29-0.33 of it) and does not
+# overlap the FMAs (measured), so an element takes 4 + 4 = 8 FMA issue slots.
+S6_SLOTS_PER_ELEM, S6_FLOP_PER_ELEM = 8, 7
+S6_ALU_PEAK_TFLOPS = FP32_FMA_LANE_PEAK / S6_SLOTS_PER_ELEM * S6_FLOP_PER_ELEM / 1e12   # 68.8
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -176,7 +185,7 @@ def bench_s6(args):
     log(f"[bench] s6: timing {args.steps} steps after {args.warmup} warm-up")
     torch.cuda.synchronize()
     wall = []
-    total_ms, per = time_launches(step, args.steps, args.warmup, stream, wall)
+    total_ms, per = time_launches(step, args.steps, args.warmup, stream, wall, warm_ms=WARM_MS_HEADLINE)
     nbytes = s6_bytes(s["batch"], s["d_inner"], s["seqlen"], s["d_state"], 2 if wl.dtype == "bf16" else 4)
     return dict(wl=wl, inp=inp, y=y, hf=hf, ms=wall[0] / args.steps, event_ms=total_ms / args.steps, per=per,
                 kern_ms=float(np.mean(per)), bytes=nbytes)
@@ -297,6 +306,132 @@ def bench_s6bwd(args):
                 "s6_scan_bwd_kernel from saved states": profiled_traffic("s6_scan_bwd_saved_mamba1p4b_bf16.md")}}
 
 
+def bench_s6_130m(args):
+    """The scan at the Mamba-130M layer shape in fp32 (batch 8, d_inner 1536,
+    seqlen 2048, d_state 16).  Two input sets (2 x 405 MB, above the 256 MB
+    Infinity Cache) alternate, so every call streams from HBM."""
+    import torch
+    import selective_state_space_19_amd as mssm
+    from selective_state_space_19_amd import synth
+    wl = synth.WORKLOADS["s6_mamba130m_f32"]
+    s = wl.shape
+    log(f"[bench] s6 130m: generating {wl.name} inputs")
+    inp = synth.s6_inputs(**s, dtype=wl.dtype, seed=wl.seed)
+    sets = []
+    for _ in range(2):
+        d = {k: to_dev(inp[k]) for k in ("u", "delta", "A", "B", "C", "D", "z")}
+        d["y"] = torch.empty_like(d["u"])
+        d["hf"] = torch.empty((s["batch"], s["d_inner"], s["d_state"]), dtype=torch.float32, device="cuda")
+        sets.append(d)
+    stream = torch.cuda.current_stream()
+    it = [0]
+
+    def step():
+        d = sets[it[0] & 1]
+        it[0] += 1
+        mssm.selective_scan(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], out=d["y"], h_final=d["hf"],
+                            stream=stream)
+
+    steps = max(10, args.steps)
+    total, _ = time_launches(step, steps, 4, stream, warm_ms=WARM_MS)
+    ms = total / steps
+    nb = s6_bytes(s["batch"], s["d_inner"], s["seqlen"], s["d_state"], 4)
+    tok = s["batch"] * s["d_inner"] * s["seqlen"]
+    elems = tok * s["d_state"]
+    alu = elems * S6_FLOP_PER_ELEM / (ms * 1e-3) / 1e12
+    return {"workload": f"{wl.name}: batch {s['batch']}, d_inner {s['d_inner']}, seqlen {s['seqlen']}, "
+                        f"d_state {s['d_state']}, fp32, z gate, D skip, h_final out; 2 input sets alternating",
+            "us": ms * 1e3, "GBs": nb / (ms * 1e-3) / 1e9, "hbm_frac": nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "alu_TFLOPs": alu, "alu_frac": alu / S6_ALU_PEAK_TFLOPS,
+            "tokens_ch_per_s": tok / (ms * 1e-3), "algorithmic_bytes": nb,
+            "workgroups": s["batch"] * ((s["d_inner"] + 63) // 64),
+            "traffic_bytes_per_launch": profiled_traffic("s6_scan_mamba130m_f32.md")}
+
+
+def _calib_lib():
+    import ctypes
+    path = os.path.join(ROOT, "selective_state_space_19_amd", "libmssm_calib.so")
+    lib = ctypes.CDLL(path)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.mssm_calib_copy.argtypes = [vp, vp, i64, i32, vp]
+    lib.mssm_calib_read.argtypes = [vp, vp, i64, i32, vp]
+    lib.mssm_calib_valu.argtypes = [vp, vp, i32, i32, i32, ctypes.c_float, vp]
+    for f in (lib.mssm_calib_copy, lib.mssm_calib_read, lib.mssm_calib_valu):
+        f.restype = i32
+    return lib
+
+
+def bench_calib(args):
+    """Ceilings measured on this GPU in the same run (libmssm_calib.so):
+    a streaming copy and a streaming read of 1 GiB (HBM), a copy of 21 MB
+    over 16 rotating buffer pairs (the decode step's state size, cold), and
+    the VALU issue rates of v_fma_f32, v_exp_f32 and of the scan's own
+    per-element instruction mix."""
+    import torch
+    lib = _calib_lib()
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    res = {}
+
+    def chk(rc):
+        if rc != 0:
+            raise RuntimeError(f"calibration launch failed: {rc}")
+
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    blocks = 256 * 16
+    total, _ = time_launches(lambda: chk(lib.mssm_calib_copy(a.data_ptr(), b.data_ptr(), n, blocks, sh)), 10, 3,
+                             stream, warm_ms=WARM_MS)
+    res["copy_1GiB_GBs"] = 2 * n / (total / 10 * 1e-3) / 1e9
+    sink = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+    total, _ = time_launches(lambda: chk(lib.mssm_calib_read(a.data_ptr(), sink.data_ptr(), n, blocks, sh)), 10, 3,
+                             stream, warm_ms=WARM_MS)
+    res["read_1GiB_GBs"] = n / (total / 10 * 1e-3) / 1e9
+    del a, b
+    m = 64 * 5120 * 16 * 4
+    pairs = [(torch.ones(m // 4, dtype=torch.float32, device="cuda"), torch.empty(m // 4, dtype=torch.float32,
+                                                                                  device="cuda")) for _ in range(16)]
+    it = [0]
+
+    def small():
+        src, dst = pairs[it[0] % 16]
+        it[0] += 1
+        chk(lib.mssm_calib_copy(src.data_ptr(), dst.data_ptr(), m, 256 * 8, sh))
+
+    total, _ = time_launches(small, 64, 16, stream, warm_ms=WARM_MS)
+    res["copy_21MB_16_rotating_GBs"] = 2 * m / (total / 64 * 1e-3) / 1e9
+    del pairs
+    out = torch.empty(256 * 8 * 256, dtype=torch.float32, device="cuda")
+    lanes = 256 * 8 * 256
+    uni = torch.tensor([0.5, 0.7, -0.3, 0.2, 0.9, 0, 0, 0], dtype=torch.float32, device="cuda")
+    secs = {}
+    # (mode, iterations, workgroups): 2048 workgroups are 8 waves per SIMD, 512 are 2
+    for key, mode, iters, blocks in ((0, 0, 2048, 2048), (1, 1, 1024, 2048), (2, 2, 256, 2048), (3, 3, 512, 2048),
+                                     (7, 7, 256, 2048), ("2w2", 2, 256, 512)):
+        total, _ = time_launches(lambda: chk(lib.mssm_calib_valu(out.data_ptr(), uni.data_ptr(), blocks, iters, mode,
+                                                                 0.5, sh)), 5, 2, stream, warm_ms=WARM_MS)
+        secs[key] = (total / 5 * 1e-3, iters, blocks)
+    rate = lambda key, per: secs[key][2] * 256 * secs[key][1] * per / secs[key][0]  # noqa: E731
+    fma, exp = rate(0, 16), rate(1, 16)
+    res["fma_lane_instr_per_s"] = fma
+    res["fma_vs_published_fp32_peak"] = fma / FP32_FMA_LANE_PEAK
+    res["exp_lane_instr_per_s"] = exp
+    res["exp_rate_vs_fma"] = exp / fma
+    res["s6_mix_elements_per_s"] = rate(2, 32)
+    res["s6_mix_fma_slots_per_element"] = fma / res["s6_mix_elements_per_s"]
+    res["s6_mix_scalar_bc_elements_per_s"] = rate(7, 32)
+    res["s6_mix_2_waves_per_simd_elements_per_s"] = rate("2w2", 32)
+    t3, it3, _ = secs[3]
+    res["exp16_fma64_us"] = t3 * 1e6
+    res["exp16_fma64_us_if_added"] = lanes * it3 * (16 / exp + 64 / fma) * 1e6
+    res["exp16_fma64_us_if_overlapped"] = lanes * it3 * max(16 / exp, 64 / fma) * 1e6
+    res["note"] = ("2048 workgroups x 256 threads (8 waves per SIMD) unless marked; the S6 mix is the scan kernel's "
+                   "own group layout (16 tokens x 2 states per lane)")
+    return res
+
+
 def parity_sample(inp, y, hf, rows=32, seed=0):
     """fp64 oracle on a few channels of the benchmarked output."""
     import oracle
@@ -339,7 +474,35 @@ def cpu_baseline(inp, budget_s=30.0):
     return {"value": nbytes / used / 1e9, "unit": "GB/s", "cores": nth, "kind": "oracle",
             "sample": f"{rows} of {bsz} batch rows of the benchmarked workload ({rows * dim} channels x "
                       f"{L} tokens, d_state {N}), fp64 sequential recurrence, {used:.2f} s wall",
-            "tokens_ch_per_s": rows * dim * L / used, "seconds": used}
+            "tokens_ch_per_s": rows * dim * L / used, "seconds": used,
+            "single_thread": cpu_single_thread()}
+
+
+def cpu_single_thread():
+    """The oracle on one thread: the whole tiny workload (1 x 32 x 64,
+    N 16, fp32) and one batch row of the Mamba-130M layer shape (1536
+    channels x 2048 tokens, N 16, fp32)."""
+    import oracle
+    from selective_state_space_19_amd import synth
+    res = {}
+    for name, rows in (("s6_tiny_f32", None), ("s6_mamba130m_f32", 1)):
+        wl = synth.WORKLOADS[name]
+        shape = dict(wl.shape)
+        if rows is not None:
+            shape["batch"] = rows
+        inp = synth.s6_inputs(**shape, dtype=wl.dtype, seed=wl.seed)
+        w = {k: synth.widen(inp[k], "f32") for k in ("u", "delta", "A", "B", "C", "D", "z")}
+        reps = 20 if rows is None else 1
+        t = time.perf_counter()
+        for _ in range(reps):
+            oracle.s6_scan(w["u"], w["delta"], w["A"], w["B"], w["C"], w["D"], w["z"], nthreads=1)
+        sec = (time.perf_counter() - t) / reps
+        tok = shape["batch"] * shape["d_inner"] * shape["seqlen"]
+        res[name] = {"sample": "whole workload" if rows is None else f"{rows} of {wl.shape['batch']} batch rows",
+                     "seconds": sec, "tokens_ch_per_s": tok / sec,
+                     "GBs": s6_bytes(shape["batch"], shape["d_inner"], shape["seqlen"], shape["d_state"], 4,
+                                     final=False) / sec / 1e9}
+    return res
 
 
 # --------------------------------------------------------------------------
@@ -470,28 +633,38 @@ def bench_ssd(args):
     log("[bench] ssd: generating inputs")
     inp = synth.ssd_inputs(s["batch"], s["seqlen"], s["nheads"], s["headdim"], s["d_state"], s["ngroups"],
                            dtype=wl.dtype, seed=wl.seed)
-    d = {k: to_dev(inp[k]) for k in ("x", "dt", "A", "B", "C", "D")}
-    y = torch.empty_like(d["x"])
     need = mssm.ssd_workspace_size(s["batch"], s["seqlen"], s["nheads"], s["headdim"], s["d_state"],
                                    s["ngroups"], s["chunk"])
-    ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+    # Cold: K input sets (x, dt, B, C, y and the workspace each, about 160 MB)
+    # used in turn, so a call's data were last touched K - 1 calls (about
+    # 480 MB of traffic) earlier, beyond the 256 MB Infinity Cache.
+    K = 4
+    sets = []
+    for _ in range(K):
+        d = {k: to_dev(inp[k]) for k in ("x", "dt", "A", "B", "C", "D")}
+        d["y"] = torch.empty_like(d["x"])
+        d["ws"] = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+        sets.append(d)
     stream = torch.cuda.current_stream()
+    it = [0]
 
-    def step():
-        mssm.ssd_chunk(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], chunk=s["chunk"], out=y,
-                       workspace=ws, stream=stream)
+    def step(chunk=s["chunk"], rotate=True):
+        d = sets[it[0] % K] if rotate else sets[0]
+        it[0] += 1
+        mssm.ssd_chunk(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], chunk=chunk, out=d["y"],
+                       workspace=d["ws"], stream=stream)
 
-    total, per = time_launches(step, 20, 3, stream, warm_ms=WARM_MS)
+    total, per = time_launches(step, 20, 4, stream, warm_ms=WARM_MS)
     ms = total / 20
+    total_hot, _ = time_launches(lambda: step(rotate=False), 20, 4, stream, warm_ms=WARM_MS)
     # The chunk length is a tile size: the result is the same up to rounding.
     # The same call with 64-token chunks, for comparison (not the workload).
-    y64 = torch.empty_like(y)
-    total64, _ = time_launches(lambda: mssm.ssd_chunk(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], chunk=64,
-                                                      out=y64, workspace=ws, stream=stream), 20, 3, stream)
+    total64, _ = time_launches(lambda: step(chunk=64), 20, 4, stream, warm_ms=WARM_MS)
     nb = ssd_bytes(s["batch"], s["seqlen"], s["nheads"], s["headdim"], s["d_state"], s["ngroups"], 2)
     fl = ssd_flops(s["batch"], s["seqlen"], s["nheads"], s["headdim"], s["d_state"], s["ngroups"], s["chunk"])
-    return dict(workload=f"{wl.name}: batch 4, seqlen 4096, 32 heads x 64, d_state 128, ngroups 1, chunk 256, bf16",
-                us_same_call_chunk64=total64 / 20 * 1e3,
+    return dict(workload=f"{wl.name}: batch 4, seqlen 4096, 32 heads x 64, d_state 128, ngroups 1, chunk 256, bf16; "
+                         f"{K} input sets in turn (cold)",
+                us_same_call_chunk64=total64 / 20 * 1e3, us_hot_one_input_set=total_hot / 20 * 1e3,
                 us=ms * 1e3, GBs=nb / (ms * 1e-3) / 1e9, hbm_frac=nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                 mfma_TFLOPs=fl / (ms * 1e-3) / 1e12, mfma_frac=fl / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                 tokens_ch_per_s=s["batch"] * s["seqlen"] * s["nheads"] * s["headdim"] / (ms * 1e-3),
@@ -519,7 +692,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--only", default="s6,s6fused,s6zoh,s6bwd,decode,decode2,ssd")
+    ap.add_argument("--only", default="s6,calib,s6c1,s6fused,s6zoh,s6bwd,decode,decode2,ssd")
+    ap.add_argument("--warm-ms", type=float, default=None,
+                    help="wall-clock warm-up before each timing (default: 300 ms headline, 100 ms the others); "
+                         "0 for profiling runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
     args = ap.parse_args()
@@ -528,6 +704,9 @@ def main():
               "(the scan shards by batch / channel with no exchange).", file=sys.stderr)
         sys.exit(2)
     parts = set(args.only.split(","))
+    if args.warm_ms is not None:
+        global WARM_MS, WARM_MS_HEADLINE
+        WARM_MS = WARM_MS_HEADLINE = args.warm_ms
 
     import torch
     if not torch.cuda.is_available():
@@ -555,14 +734,16 @@ def main():
             "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
             "tokens_ch_per_s": tok / (r["ms"] * 1e-3),
             "event_ms_per_step": round(r["event_ms"], 5),
-            # The scan is bound by VALU work, not HBM: 5 VALU instructions per
-            # state element take longer at peak (273 us here) than its bytes
-            # (135 us at 8 TB/s).  Peak = non-packed fp32 VALU issue rate.
+            # The scan is bound by VALU issue, not HBM (counters: VALU busy
+            # ~92%, HBM ~29%): 8 FMA issue slots per state element at the
+            # published fp32 rate (218 us here) outweigh its bytes (135 us at
+            # 8 TB/s).  Peak = 78.6e12 FMA slots/s / 8 slots per element x 7 flop.
             "roofline": {"bound": "alu", "achieved": round(alu_tflops, 3), "peak": round(S6_ALU_PEAK_TFLOPS, 3),
                          "unit": "TFLOP/s", "frac": round(alu_tflops / S6_ALU_PEAK_TFLOPS, 4),
                          "traffic": profiled_traffic("s6_scan_mamba1p4b_bf16.md"),
                          "kernel": "s6_scan_kernel", "avg_launch_ms": round(r["kern_ms"], 5),
-                         "state_elements_per_launch": elems, "flop_per_element": S6_FLOP_PER_ELEM},
+                         "state_elements_per_launch": elems, "flop_per_element": S6_FLOP_PER_ELEM,
+                         "issue_slots_per_element": S6_SLOTS_PER_ELEM},
             "roofline_hbm": {"achieved": round(r["bytes"] / kern_s / 1e9, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": round(r["bytes"] / kern_s / 1e9 / HBM_PEAK_GBS, 4),
                              "algorithmic_bytes_per_launch": r["bytes"]},
@@ -574,6 +755,16 @@ def main():
             log("[bench] s6: cpu baseline (the oracle on the same workload)")
             out["cpu_baseline"] = cpu_baseline(r["inp"])
         del r
+    if "calib" in parts:
+        try:
+            out["calibration"] = bench_calib(args)
+        except Exception as e:  # reported, not hidden
+            out["calibration"] = {"error": repr(e)}
+    if "s6c1" in parts:
+        try:
+            out["secondary_s6_mamba130m_f32"] = bench_s6_130m(args)
+        except Exception as e:  # reported, not hidden
+            out["secondary_s6_mamba130m_f32"] = {"error": repr(e)}
     if "s6bwd" in parts:
         try:
             out["secondary_s6_backward"] = bench_s6bwd(args)

@@ -365,7 +365,9 @@ size_t mssm_ssd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads, in
                                int64_t d_state, int64_t ngroups, int64_t chunk) {
     if (batch < 0 || seqlen < 0 || nheads < 1 || headdim < 1 || d_state < 1 || ngroups < 1 || chunk < 1)
         return 0;
-    return mssm::ssd_workspace_bytes(batch, seqlen, nheads, headdim, d_state, ngroups, chunk);
+    // the MFMA path's workspace where it applies (bf16); the other path needs none
+    if (!mssm::ssd_fast_supported(seqlen, nheads, headdim, d_state, ngroups, chunk)) return 0;
+    return mssm::ssd_fast_workspace_bytes(batch, seqlen, nheads, headdim, d_state, ngroups, chunk);
 }
 
 // scratch: the caller passed no workspace; once the arguments pass, this
@@ -382,15 +384,16 @@ static int ssd_fwd(const char* fn, const void* x, const void* dt, const float* A
     if (nheads < 1 || ngroups < 1 || nheads % ngroups != 0)
         return fail(MSSM_ERR_SHAPE, "%s: nheads %lld must be a positive multiple of ngroups %lld", fn,
                     (long long)nheads, (long long)ngroups);
-    if (dtype != MSSM_BF16) return fail(MSSM_ERR_UNSUPPORTED, "%s: only MSSM_BF16 is implemented", fn);
-    if (headdim != 64) return fail(MSSM_ERR_UNSUPPORTED, "%s: headdim %lld (only 64)", fn, (long long)headdim);
-    if (!(d_state == 32 || d_state == 64 || d_state == 128 || d_state == 256))
-        return fail(MSSM_ERR_UNSUPPORTED, "%s: d_state %lld (32, 64, 128 or 256)", fn, (long long)d_state);
+    if (headdim < 1 || !mssm::ssd_general_supported(headdim, d_state))
+        return fail(MSSM_ERR_UNSUPPORTED, "%s: headdim %lld / d_state %lld (headdim >= 1, 1 <= d_state <= 256)", fn,
+                    (long long)headdim, (long long)d_state);
     if (chunk != 64 && chunk != 128 && chunk != 256)
         return fail(MSSM_ERR_UNSUPPORTED, "%s: chunk %lld (64, 128 or 256)", fn, (long long)chunk);
-    if (seqlen > INT32_MAX || nheads > INT32_MAX) return fail(MSSM_ERR_UNSUPPORTED, "%s: size too large", fn);
-    if (!mssm::ssd_supported(seqlen, nheads, headdim, d_state, ngroups, chunk))
-        return fail(MSSM_ERR_UNSUPPORTED, "%s: one batch row exceeds 2 GiB of x, B or C", fn);
+    if (seqlen > INT32_MAX || nheads > INT32_MAX || headdim > INT32_MAX)
+        return fail(MSSM_ERR_UNSUPPORTED, "%s: size too large", fn);
+    // bf16 at the sizes the MFMA kernels take runs there; everything else in
+    // the plain fp32 kernel (which needs no workspace)
+    const bool fast = dtype == MSSM_BF16 && mssm::ssd_fast_supported(seqlen, nheads, headdim, d_state, ngroups, chunk);
     if (!prod_ok(batch, seqlen, nheads * headdim, nullptr) || !prod_ok(batch, nheads * headdim, d_state, nullptr) ||
         !prod_ok(batch, seqlen, ngroups * d_state, nullptr))
         return fail(MSSM_ERR_SHAPE, "%s: tensor too large", fn);
@@ -410,7 +413,8 @@ static int ssd_fwd(const char* fn, const void* x, const void* dt, const float* A
     CHECK_PTR(y);
     CHECK_OPT(Dskip);
     CHECK_OPT(z);
-    const size_t need = mssm::ssd_workspace_bytes(batch, seqlen, nheads, headdim, d_state, ngroups, chunk);
+    const size_t need =
+        fast ? mssm::ssd_fast_workspace_bytes(batch, seqlen, nheads, headdim, d_state, ngroups, chunk) : 0;
     if (scratch) {
         if (need > workspace_bytes)
             return fail(MSSM_ERR_WORKSPACE,
@@ -428,7 +432,7 @@ static int ssd_fwd(const char* fn, const void* x, const void* dt, const float* A
     }
     mssm::SSDParams p{x, dt, A, Bm, Cm, Dskip, z, h0, y, h_final, workspace, batch, (int32_t)seqlen,
                       (int32_t)nheads, (int32_t)headdim, (int32_t)d_state, (int32_t)ngroups, (int32_t)chunk};
-    return launched(fn, mssm::launch_ssd(p, s));
+    return launched(fn, fast ? mssm::launch_ssd_fast(p, s) : mssm::launch_ssd_general(p, dtype == MSSM_BF16, s));
 }
 
 int mssm_ssd_chunk_fwd(const void* x, const void* dt, const float* A, const void* Bm, const void* Cm,

@@ -800,7 +800,8 @@ hipError_t launch_q(const SSDParams& p, hipStream_t stream) {
 
 }  // namespace
 
-size_t ssd_workspace_bytes(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int64_t Q) {
+size_t ssd_fast_workspace_bytes(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G,
+                                int64_t Q) {
     (void)H;
     (void)P;
     if (Q <= 0) return 0;
@@ -808,7 +809,7 @@ size_t ssd_workspace_bytes(int64_t batch, int64_t L, int64_t H, int64_t P, int64
     return (size_t)(batch * nc * G * Q * (Q + 2 * N) * 2);     // G, B^T and C tiles
 }
 
-bool ssd_supported(int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int64_t Q) {
+bool ssd_fast_supported(int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int64_t Q) {
     if (P != kP) return false;
     if (!(N == 32 || N == 64 || N == 128 || N == 256)) return false;
     if (!(Q == 64 || Q == 128 || Q == 256)) return false;
@@ -817,7 +818,7 @@ bool ssd_supported(int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int64_
     return L * H * P * 2 < lim && L * G * N * 2 < lim && L * H * 2 < lim;
 }
 
-hipError_t launch_ssd(const SSDParams& p, hipStream_t stream) {
+hipError_t launch_ssd_fast(const SSDParams& p, hipStream_t stream) {
     switch (p.Q) {
         case 64: return launch_q<64>(p, stream);
         case 128: return launch_q<128>(p, stream);

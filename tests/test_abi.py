@@ -118,10 +118,13 @@ def _ssd(lib, **kw):
 def test_ssd_argument_errors(lib):
     assert _ssd(lib, x=None) == ERR_NULL
     assert _ssd(lib, H=3, G=2) == ERR_SHAPE
-    assert _ssd(lib, dtype=0) == ERR_UNSUP
-    assert _ssd(lib, P=32) == ERR_UNSUP
-    assert _ssd(lib, N=24) == ERR_UNSUP
-    assert _ssd(lib, N=16) == ERR_UNSUP
+    # float32 storage, other headdims and d_state up to 256 are taken (the
+    # error here is the NULL x, found after the size checks)
+    assert _ssd(lib, dtype=0, x=None) == ERR_NULL
+    assert _ssd(lib, P=32, N=48, x=None) == ERR_NULL
+    assert _ssd(lib, P=128, N=16, x=None) == ERR_NULL
+    assert _ssd(lib, N=257) == ERR_UNSUP
+    assert _ssd(lib, P=0) == ERR_UNSUP
     assert _ssd(lib, Q=100) == ERR_UNSUP
     assert _ssd(lib, dtype=9) == ERR_DTYPE
     assert _ssd(lib, h0=MISALIGNED) == ERR_ALIGN
@@ -162,8 +165,11 @@ def test_ssd_noalloc_argument_errors(lib):
 
 def test_workspace_size_is_pure(lib):
     a = lib.mssm_ssd_workspace_size(4, 4096, 32, 64, 128, 1, 256)
-    assert a == lib.mssm_ssd_workspace_size(4, 4096, 32, 64, 128, 1, 256)
+    assert a == lib.mssm_ssd_workspace_size(4, 4096, 32, 64, 128, 1, 256) > 0
     assert lib.mssm_ssd_workspace_size(-1, 4096, 32, 64, 128, 1, 256) == 0
+    # sizes only the plain-fp32 kernel takes need no workspace
+    assert lib.mssm_ssd_workspace_size(4, 4096, 32, 32, 128, 1, 256) == 0
+    assert lib.mssm_ssd_workspace_size(4, 4096, 32, 64, 48, 1, 256) == 0
 
 
 def _m2(lib, **kw):

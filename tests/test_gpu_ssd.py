@@ -68,6 +68,43 @@ def test_ragged_shapes(i, case):
     _check(inp, Q, "x".join(map(str, case)) + ("_varied" if varied else ""))
 
 
+# Sizes the MFMA kernels do not take run in the plain-fp32 chunked kernel:
+# float32 storage, headdim other than 64, d_state not in {32, 64, 128, 256}.
+GENERAL = [
+    # (batch, L, H, P, N, G, chunk, dtype, gate, skip, h0)
+    (1, 1, 1, 64, 128, 1, 64, "f32", True, True, True),
+    (1, 100, 2, 64, 128, 1, 64, "f32", False, True, True),
+    (2, 257, 4, 32, 16, 2, 128, "f32", True, True, False),
+    (1, 300, 2, 128, 48, 1, 256, "f32", True, False, True),
+    (1, 64, 3, 16, 64, 3, 64, "f32", False, True, True),
+    (1, 90, 2, 80, 256, 1, 256, "f32", True, True, True),
+    (2, 300, 4, 32, 16, 1, 128, "bf16", True, True, True),
+    (1, 500, 2, 128, 48, 2, 256, "bf16", False, True, True),
+    (1, 200, 2, 16, 80, 1, 64, "bf16", True, True, False),
+    (1, 130, 2, 96, 32, 1, 128, "bf16", True, False, True),
+]
+
+
+@pytest.mark.parametrize("i,case", list(enumerate(GENERAL)),
+                         ids=lambda c: "b{}_L{}_H{}_P{}_N{}_G{}_Q{}_{}_z{}_D{}_h{}".format(*c) if isinstance(c, tuple)
+                         else None)
+def test_general_sizes(i, case):
+    b, L, H, P, N, G, Q, dt, gate, skip, h0 = case
+    inp = synth.ssd_inputs(b, L, H, P, N, G, dtype=dt, seed=900 + L + P + N, gate=gate, skip=skip, init_state=h0,
+                           varied=i % 2 == 1)
+    _check(inp, Q, "general_" + "x".join(map(str, case)), tol=TOL[dt])
+
+
+def test_mamba2_shape_fp32():
+    """The Mamba-2 layer shape (batch 4, seqlen 4096, 32 heads x 64, d_state
+    128) with float32 storage: every output within the fp32 tolerance."""
+    w = synth.WORKLOADS["ssd_mamba2_bf16"]
+    s = w.shape
+    inp = synth.ssd_inputs(s["batch"], s["seqlen"], s["nheads"], s["headdim"], s["d_state"], s["ngroups"],
+                           dtype="f32", seed=w.seed, varied=True)
+    _check(inp, s["chunk"], w.name + "_f32", tol=TOL["f32"])
+
+
 def test_mamba2_workload_full():
     """Mamba-2 layer (batch 4, seqlen 4096, 32 heads x 64, d_state 128,
     ngroups 1, chunk 256), every output against the oracle."""
@@ -147,6 +184,10 @@ def test_zero_length_and_errors():
     inp = synth.ssd_inputs(1, 64, 2, 64, 64, 1, dtype="bf16", seed=1)
     with pytest.raises(mssm.MssmError) as e:
         mssm.ssd_chunk(*(dev(inp[k]) for k in ("x", "dt", "A", "B", "C", "D", "z", "h0")), chunk=96)
+    assert e.value.code == -4
+    inp = synth.ssd_inputs(1, 64, 2, 64, 272, 1, dtype="f32", seed=1)
+    with pytest.raises(mssm.MssmError) as e:      # d_state above 256
+        mssm.ssd_chunk(*(dev(inp[k]) for k in ("x", "dt", "A", "B", "C", "D", "z", "h0")), chunk=64)
     assert e.value.code == -4
 
 
