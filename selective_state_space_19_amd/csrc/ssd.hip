@@ -62,14 +62,6 @@ __device__ __forceinline__ void static_for(F&& f) {
         static_for<B + 1, E>(f);
     }
 }
-// Eight packed bf16 values times f, rounded back to bf16.
-__device__ __forceinline__ u32x4_t scale_bf16x8(const u32x4_t v, float f) {
-    u32x4_t o;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-        o[q] = pack_bf16x2(__uint_as_float(v[q] << 16) * f, __uint_as_float(v[q] & 0xffff0000u) * f);
-    return o;
-}
 __device__ __forceinline__ u32x4_t gload128(rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
@@ -604,18 +596,35 @@ __global__ __launch_bounds__(512) void ssd_main_kernel(
             for (int k = 0; k < BSL; ++k) load_bt(cc, k);
         };
 
-        // Staging of one chunk: lane l takes tokens l*TPL .. l*TPL+TPL-1 and
-        // this wave's 8 head channels 8 wr .. 8 wr + 7.  Every state wave
-        // computes the chunk's running sum itself (no cross-wave step); wave
-        // 4 also publishes s and dt for the output waves.
-        uint32_t xv[TPL][4];
+        // Staging of one chunk.  The running sum: lane l takes the dt of tokens
+        // l*TPL .. l*TPL+TPL-1, and every state wave scans the whole chunk
+        // itself (no cross-wave step); wave 4 also publishes s and dt for the
+        // output waves.  x: 16-token blocks tb = wr + 4 k, read as MFMA A
+        // operands (lane (kg, m): token 16 tb + m, head channels 8 kg .. 8 kg + 7
+        // of this half, so one load moves 16 tokens x 64 contiguous bytes) and
+        // transposed by an MFMA against an identity operand (exact), which
+        // leaves 4 consecutive tokens of one head channel in each lane: those
+        // go to x^T and its two scaled copies as 8-byte LDS stores.
+        constexpr int XU = Q / 64;               // 16-token blocks per state wave
+        u32x4_t xv[XU];
         uint32_t dtw[TPL];
+        u32x4_t ident[2];                        // B[K][n] = 1 where K = 16 cb + n
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                ident[cb][q] = (8 * kg + 2 * q == 16 * cb + m ? 0x3F80u : 0u) |
+                               (8 * kg + 2 * q + 1 == 16 * cb + m ? 0x3F800000u : 0u);
         auto stage_load = [&](int cc) {
 #pragma unroll
             for (int i = 0; i < TPL; ++i) {
                 const int t = cc * Q + lane * TPL + i;
                 dtw[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rDT, off_if(t < L, ((uint32_t)t * H + h) * 2u), 0, 0);
-                buf_load<4>(rX, off_if(t < L, (uint32_t)t * xrow + chan0 + 16u * wr), xv[i]);
+            }
+#pragma unroll
+            for (int k = 0; k < XU; ++k) {
+                const int t = cc * Q + 16 * (wr + 4 * k) + m;
+                xv[k] = gload128(rX, off_if(t < L, (uint32_t)t * xrow + chan0 + 16u * kg));
             }
         };
         auto stage_store = [&](int pb) -> float {
@@ -646,42 +655,29 @@ __global__ __launch_bounds__(512) void ssd_main_kernel(
                 fs[i] = dv[i] * fast_exp2(s_be - sv[i]);
                 fw[i] = dv[i] * fast_exp2(s_end - sv[i]);
             }
+            const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {        // head channel 8 wr + e
-                float xf[TPL];
-                uint32_t xb[TPL];
+            for (int k = 0; k < XU; ++k) {
+                const int tb = wr + 4 * k;
+                // the factors of this lane's tokens 16 tb + 4 kg + r, from the lanes that scanned them
+                float f1[4], f2[4];
 #pragma unroll
-                for (int i = 0; i < TPL; ++i) {
-                    const uint32_t wv = xv[i][e >> 1];
-                    xb[i] = (e & 1) ? (wv >> 16) : (wv & 0xffffu);
-                    xf[i] = __uint_as_float(xb[i] << 16);
+                for (int r = 0; r < 4; ++r) {
+                    const int tok = 16 * tb + 4 * kg + r;
+                    f1[r] = __shfl(fs[r % TPL], tok / TPL, 64);
+                    f2[r] = __shfl(fw[r % TPL], tok / TPL, 64);
                 }
-                const int row = 8 * wr + e;
-                if constexpr (TPL == 1) {
-                    uint16_t* p0 = reinterpret_cast<uint16_t*>(&xT[pb][row][0]) + lane;
-                    uint16_t* p1 = reinterpret_cast<uint16_t*>(&xsT[pb][row][0]) + lane;
-                    uint16_t* p2 = reinterpret_cast<uint16_t*>(&xwT[pb][row][0]) + lane;
-                    *p0 = (uint16_t)xb[0];
-                    *p1 = to_bf16(xf[0] * fs[0]);
-                    *p2 = to_bf16(xf[0] * fw[0]);
-                } else {
-                    constexpr int WPL = TPL / 2;     // words per lane
-                    uint32_t a0[WPL], a1[WPL], a2[WPL];
+                const int wd = 8 * tb + 2 * kg;
 #pragma unroll
-                    for (int q = 0; q < WPL; ++q) {
-                        a0[q] = xb[2 * q] | (xb[2 * q + 1] << 16);
-                        a1[q] = pack_bf16x2(xf[2 * q] * fs[2 * q], xf[2 * q + 1] * fs[2 * q + 1]);
-                        a2[q] = pack_bf16x2(xf[2 * q] * fw[2 * q], xf[2 * q + 1] * fw[2 * q + 1]);
-                    }
-                    if constexpr (WPL == 1) {
-                        xT[pb][row][lane] = a0[0];
-                        xsT[pb][row][lane] = a1[0];
-                        xwT[pb][row][lane] = a2[0];
-                    } else {
-                        *reinterpret_cast<uint2*>(&xT[pb][row][2 * lane]) = make_uint2(a0[0], a0[1]);
-                        *reinterpret_cast<uint2*>(&xsT[pb][row][2 * lane]) = make_uint2(a1[0], a1[1]);
-                        *reinterpret_cast<uint2*>(&xwT[pb][row][2 * lane]) = make_uint2(a2[0], a2[1]);
-                    }
+                for (int cb = 0; cb < 2; ++cb) {
+                    const f32x4_t v = mfma16(xv[k], ident[cb], zero4);   // v[r] = x[16 tb + 4 kg + r][16 cb + m]
+                    const int row = 16 * cb + m;
+                    *reinterpret_cast<uint2*>(&xT[pb][row][wd]) =
+                        make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                    *reinterpret_cast<uint2*>(&xsT[pb][row][wd]) =
+                        make_uint2(pack_bf16x2(v[0] * f1[0], v[1] * f1[1]), pack_bf16x2(v[2] * f1[2], v[3] * f1[3]));
+                    *reinterpret_cast<uint2*>(&xwT[pb][row][wd]) =
+                        make_uint2(pack_bf16x2(v[0] * f2[0], v[1] * f2[1]), pack_bf16x2(v[2] * f2[2], v[3] * f2[3]));
                 }
             }
             return s_end;
