@@ -53,22 +53,34 @@ namespace {
 
 struct alignas(16) Words8 { uint32_t w[8]; };   // bases are 16-byte aligned
 
-// The zero-order-hold gain expm1(x) / x of x = delta*A, given e = exp(x)
-// (so the hold input term is delta*u*B times this): for |x| < 1/16 the
-// Taylor series through x^3/24 (truncation x^4/120 under 1.3e-7 relative),
-// otherwise (e - 1) / x.  There |e - 1| >= 1 - exp(-1/16) ~ 0.0606, so an
-// error of one ulp in e (6e-8 near 1) moves the gain by at most ~1e-6
-// relative, at the switch, and less beyond it.  At x = 0 the series gives
-// exactly 1, the Euler term.
-__device__ __forceinline__ float zoh_gain(float x, float e) {
-    const float p = fmaf(x, fmaf(x, fmaf(x, 1.f / 24.f, 1.f / 6.f), 0.5f), 1.f);
-    const float r = (e - 1.f) * __builtin_amdgcn_rcpf(x);
-    return fabsf(x) < 0.0625f ? p : r;
+// The zero-order-hold input factor (exp(delta*A) - 1) / A, given delta,
+// x2 = delta * A * log2(e), e = exp2(x2) and ia = 1/A (0 where A = 0); the
+// hold input term is u * B times this.
+// - |x2| >= kHoldSwitch2 (|delta*A| >= 1/32): (e - 1) * ia as one fma, so
+//   e - 1 is never rounded on its own.  The rounding of e (about 6e-8 near
+//   1) moves the factor by at most ~2e-6 relative at the switch, less beyond.
+// - below it: delta * (1 + x/2 + x^2/6) for x = delta*A, written in x2; the
+//   first dropped term, x^3/24, is under 1.3e-6 relative there.  At A = 0
+//   (or delta = 0) this gives exactly delta, the Euler factor.
+// Per state element that is one fma, a degree-2 series (two fma and a mul),
+// a compare and a select: no division and no second transcendental.
+constexpr float kHoldSwitch2 = kLog2e / 32.f;
+constexpr float kHold1 = kLn2 / 2.f;              // x/2 in powers of x2
+constexpr float kHold2 = kLn2 * kLn2 / 6.f;       // x^2/6 in powers of x2
+__device__ __forceinline__ float zoh_factor(float dl, float x2, float e, float ia) {
+    const float direct = fmaf(e, ia, -ia);
+    const float series = dl * fmaf(x2, fmaf(x2, kHold2, kHold1), 1.f);
+    return fabsf(x2) < kHoldSwitch2 ? series : direct;
 }
 
 constexpr int kScanWaves = 8;     // waves running the recurrence
 constexpr int kRowWaves = 4;      // waves streaming rows: loads, staging, epilogue
-constexpr int kRing = 4;          // row-wave register ring: chunks of loads in flight + 1
+// Row-wave register ring (slots of chunk loads).  A chunk's row run is
+// TC * sizeof(T) bytes; when that is half a 128-byte line (bf16) the loads
+// of two chunks -- the two halves of each line -- are issued back to back,
+// so a line is fetched from HBM once rather than once per half when it is
+// evicted from L2 between the two uses.  That needs two more slots.
+template <typename T, int TC> constexpr int kRing = TC * int(sizeof(T)) < 128 ? 6 : 4;
 
 // Tokens between the saved states the backward pass starts its chunks from
 // (its chunk length: 16 with up to 2 states per lane, else 8).
@@ -102,14 +114,16 @@ __global__ __launch_bounds__((kScanWaves + kRowWaves) * 64) void s6_scan_kernel(
     constexpr int QR = TC / 4;                     // token quads per chunk
     static_assert(TPT % 4 == 0 && (WPT == 2 || WPT == 4 || WPT == 8), "row runs are 8-, 16- or 32-byte vectors");
     static_assert(TC % G == 0 && NGRP % 2 == 0, "whole scan groups per chunk, even count");
-    static_assert(RING >= 3 && RING % 2 == 0, "ring: stage, epilogue and reload use distinct slots");
+    constexpr bool PAIR = TC * int(sizeof(T)) < 128;  // loads of chunk pairs: whole 128-byte lines
+    static_assert(RING >= 4 && RING % 2 == 0 && (!PAIR || RING >= 6),
+                  "ring: stage, epilogue and reload use distinct slots; pairs need two more");
 
     // Double-buffered by chunk parity, 16 bytes per (channel, token pair or
     // quad).  The scan waves access one pair / quad per instruction with the
     // 64 channels on consecutive lanes; each quarter-wave of a row wave covers
     // 16 channels of one pair / quad.  Both are free of bank conflicts with
     // the plain layout, and the scan side needs no address arithmetic.
-    __shared__ float4 s_dd[2][PR][64];             // (delta_t, (delta*u)_t, delta_t+1, (delta*u)_t+1)
+    __shared__ float4 s_dd[2][PR][64];             // (delta_t, (delta*u)_t, delta_t+1, (delta*u)_t+1); ZOH: u for delta*u
     __shared__ float4 s_y[2][NW][QR][64];          // per-scan-wave partial outputs, token quads
 
     const int tid = threadIdx.x;
@@ -124,11 +138,9 @@ __global__ __launch_bounds__((kScanWaves + kRowWaves) * 64) void s6_scan_kernel(
     const int64_t dblk = lid % nblk_d;
     const int64_t d0 = dblk * 64;
     const int nrows = (int)((dim - d0) < 64 ? (dim - d0) : 64);
-    const int nchunks = (L + TC - 1) / TC;
-    // Both roles run `nit` chunk iterations (a multiple of RING, so the row
-    // waves' ring slots are compile-time indices); chunks past the end read
-    // zeros (a zero step leaves h unchanged) and store nothing.
-    const int nit = (nchunks + RING - 1) / RING * RING;
+    // The scan waves run one iteration per chunk and the row waves one more
+    // (the last epilogue); each iteration starts at a barrier.
+    const int nit = (L + TC - 1) / TC;
 
     if (wave < NW) {
         // ================= scan role: lane = channel cs, wave = state group w =================
@@ -138,7 +150,7 @@ __global__ __launch_bounds__((kScanWaves + kRowWaves) * 64) void s6_scan_kernel(
         const T* brow[NS];
         const T* crow[NS];
         bool sval[NS];
-        float h[NS], a2[NS], af[NS];
+        float h[NS], a2[NS], ia[NS];
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             const int n = w * NS + s;
@@ -147,8 +159,9 @@ __global__ __launch_bounds__((kScanWaves + kRowWaves) * 64) void s6_scan_kernel(
             brow[s] = B_in + off;
             crow[s] = C_in + off;
             const bool ok = sval_d && sval[s];
-            af[s] = ok ? A_in[(d0 + cs) * N + n] : 0.f;
-            a2[s] = af[s] * kLog2e;
+            const float af = ok ? A_in[(d0 + cs) * N + n] : 0.f;
+            a2[s] = af * kLog2e;
+            ia[s] = af != 0.f ? 1.f / af : 0.f;       // hold form only
             h[s] = (ok && h0_in) ? h0_in[(b * dim + d0 + cs) * N + n] : 0.f;
         }
 
@@ -205,11 +218,14 @@ __global__ __launch_bounds__((kScanWaves + kRowWaves) * 64) void s6_scan_kernel(
                 const float4 q = ddr[buf][k / 2];
 #pragma unroll
                 for (int s = 0; s < NS; ++s) {
-                    dA[k][s] = fast_exp2(q.x * a2[s]);
-                    dA[k + 1][s] = fast_exp2(q.z * a2[s]);
+                    const float x0 = q.x * a2[s], x1 = q.z * a2[s];
+                    dA[k][s] = fast_exp2(x0);
+                    dA[k + 1][s] = fast_exp2(x1);
                     if constexpr (ZOH) {
-                        bu[k][s] = (q.y * zoh_gain(q.x * af[s], dA[k][s])) * Elem<T>::get(bw[buf][s], k);
-                        bu[k + 1][s] = (q.w * zoh_gain(q.z * af[s], dA[k + 1][s])) * Elem<T>::get(bw[buf][s], k + 1);
+                        // staged (delta, u) pairs: the hold factor times u * B
+                        bu[k][s] = zoh_factor(q.x, x0, dA[k][s], ia[s]) * (q.y * Elem<T>::get(bw[buf][s], k));
+                        bu[k + 1][s] =
+                            zoh_factor(q.z, x1, dA[k + 1][s], ia[s]) * (q.w * Elem<T>::get(bw[buf][s], k + 1));
                     } else {
                         bu[k][s] = q.y * Elem<T>::get(bw[buf][s], k);
                         bu[k + 1][s] = q.w * Elem<T>::get(bw[buf][s], k + 1);
@@ -410,7 +426,9 @@ __global__ __launch_bounds__((kScanWaves + kRowWaves) * 64) void s6_scan_kernel(
 #pragma unroll
                 for (int j = 0; j < TPT; j += 2) {
                     const float e0 = Elem<T>::get(cdl, j), e1 = Elem<T>::get(cdl, j + 1);
-                    s_dd[par][(toff + j) / 2][cr] = make_float4(e0, e0 * uk[j], e1, e1 * uk[j + 1]);
+                    // ZOH: (delta, u) -- the hold factor replaces delta in the input term
+                    s_dd[par][(toff + j) / 2][cr] = ZOH ? make_float4(e0, uk[j], e1, uk[j + 1])
+                                                        : make_float4(e0, e0 * uk[j], e1, e1 * uk[j + 1]);
                 }
             }
         };
@@ -455,25 +473,39 @@ __global__ __launch_bounds__((kScanWaves + kRowWaves) * 64) void s6_scan_kernel(
         float uk[2][TPT];                          // kept u of the chunks of each parity
 #pragma unroll
         for (int j = 0; j < TPT; ++j) uk[0][j] = uk[1][j] = 0.f;
+        // Chunk c lives in slot c % RING from its load until its epilogue.
+        // Unpaired: iteration ck loads chunk ck+RING-1 into the slot the
+        // epilogue of chunk ck-1 has just released.  Paired: even iterations
+        // load chunks ck+RING-2 (slot released one iteration earlier) and
+        // ck+RING-1 together, each at least RING-3 iterations before staging.
+        constexpr int AHEAD = PAIR ? RING - 2 : RING - 1;
 #pragma unroll
-        for (int r = 0; r < RING - 1; ++r) load_chunk(r, ru[r], rdl[r], rz[r]);
+        for (int r = 0; r < AHEAD; ++r) load_chunk(r, ru[r], rdl[r], rz[r]);
         stage(0, ru[0], rdl[0], uk[0]);
         // Iteration ck: the scan waves scan chunk ck; here the epilogue of
-        // chunk ck-1, the staging of chunk ck+1 and the loads of chunk
-        // ck+RING-1 (into the slot the epilogue just released).
-        for (int ck0 = 0; ck0 < nit; ck0 += RING) {
+        // chunk ck-1, the staging of chunk ck+1 and the loads ahead.  The
+        // last iteration (ck = nit) has only the epilogue to do; its staging
+        // and loads are of chunks past the end (zeros, nothing stored).
+        for (int ck0 = 0; ck0 <= nit; ck0 += RING) {
 #pragma unroll
             for (int r = 0; r < RING; ++r) {
                 const int ck = ck0 + r;
+                if (ck > nit) break;
                 const int sp = (r + RING - 1) % RING, sn = (r + 1) % RING;
                 __syncthreads();
                 epilogue(ck - 1, rz[sp], uk[(r + 1) & 1]);
                 stage(ck + 1, ru[sn], rdl[sn], uk[(r + 1) & 1]);
-                load_chunk(ck + RING - 1, ru[sp], rdl[sp], rz[sp]);
+                if constexpr (PAIR) {
+                    if ((r & 1) == 0) {
+                        const int s2 = (r + RING - 2) % RING;
+                        load_chunk(ck + RING - 2, ru[s2], rdl[s2], rz[s2]);
+                        load_chunk(ck + RING - 1, ru[sp], rdl[sp], rz[sp]);
+                    }
+                } else {
+                    load_chunk(ck + RING - 1, ru[sp], rdl[sp], rz[sp]);
+                }
             }
         }
-        __syncthreads();
-        epilogue(nit - 1, rz[RING - 1], uk[1]);
     }
 }
 
@@ -486,18 +518,18 @@ hipError_t launch_cfg(const S6Params& p, const S6FrontEnd* fe, bool zoh, hipStre
     const bool fulln = p.N == kScanWaves * NS;
     // The hold form and the saved states are built for the plain scan only
     // (the fused front end is Euler; the backward pass is of the plain scan).
-    auto kern = fe ? (aligned ? (fulln ? s6_scan_kernel<T, NS, TC, true, true, true, false, false, kRing>
-                                       : s6_scan_kernel<T, NS, TC, true, false, true, false, false, kRing>)
-                              : s6_scan_kernel<T, NS, TC, false, false, true, false, false, kRing>)
-            : zoh ? (aligned ? (fulln ? s6_scan_kernel<T, NS, TC, true, true, false, true, false, kRing>
-                                      : s6_scan_kernel<T, NS, TC, true, false, false, true, false, kRing>)
-                             : s6_scan_kernel<T, NS, TC, false, false, false, true, false, kRing>)
-            : p.ckpt ? (aligned ? (fulln ? s6_scan_kernel<T, NS, TC, true, true, false, false, true, kRing>
-                                         : s6_scan_kernel<T, NS, TC, true, false, false, false, true, kRing>)
-                                : s6_scan_kernel<T, NS, TC, false, false, false, false, true, kRing>)
-                  : (aligned ? (fulln ? s6_scan_kernel<T, NS, TC, true, true, false, false, false, kRing>
-                                      : s6_scan_kernel<T, NS, TC, true, false, false, false, false, kRing>)
-                             : s6_scan_kernel<T, NS, TC, false, false, false, false, false, kRing>);
+    auto kern = fe ? (aligned ? (fulln ? s6_scan_kernel<T, NS, TC, true, true, true, false, false, kRing<T, TC>>
+                                       : s6_scan_kernel<T, NS, TC, true, false, true, false, false, kRing<T, TC>>)
+                              : s6_scan_kernel<T, NS, TC, false, false, true, false, false, kRing<T, TC>>)
+            : zoh ? (aligned ? (fulln ? s6_scan_kernel<T, NS, TC, true, true, false, true, false, kRing<T, TC>>
+                                      : s6_scan_kernel<T, NS, TC, true, false, false, true, false, kRing<T, TC>>)
+                             : s6_scan_kernel<T, NS, TC, false, false, false, true, false, kRing<T, TC>>)
+            : p.ckpt ? (aligned ? (fulln ? s6_scan_kernel<T, NS, TC, true, true, false, false, true, kRing<T, TC>>
+                                         : s6_scan_kernel<T, NS, TC, true, false, false, false, true, kRing<T, TC>>)
+                                : s6_scan_kernel<T, NS, TC, false, false, false, false, true, kRing<T, TC>>)
+                  : (aligned ? (fulln ? s6_scan_kernel<T, NS, TC, true, true, false, false, false, kRing<T, TC>>
+                                      : s6_scan_kernel<T, NS, TC, true, false, false, false, false, kRing<T, TC>>)
+                             : s6_scan_kernel<T, NS, TC, false, false, false, false, false, kRing<T, TC>>);
     const S6FrontEnd none{};
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3((kScanWaves + kRowWaves) * 64), 0, stream,
                        static_cast<const T*>(p.u), static_cast<const T*>(p.delta), static_cast<const T*>(p.Bm),

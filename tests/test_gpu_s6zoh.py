@@ -1,8 +1,8 @@
 """GPU parity of the S6 scan with the zero-order-hold input term
 (mssm_selective_scan_zoh_fwd) against the fp64 oracle's hold form, on the
 same seeded inputs, through the C ABI.  The step and A values span both
-sides of the kernel's series / direct switch for the hold gain (|delta A|
-below and above 1/16), and include A = 0 and tiny A."""
+sides of the kernel's series / direct switch for the hold factor (|delta A|
+below and above 1/32), and include A = 0 and tiny A."""
 import numpy as np
 import pytest
 
