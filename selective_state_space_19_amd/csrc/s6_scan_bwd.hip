@@ -87,6 +87,40 @@ __device__ __forceinline__ void tree(float (&v)[CAP]) {
 
 constexpr int log2i(int n) { return n <= 1 ? 0 : 1 + log2i(n / 2); }
 
+// Chunks whose row runs (TC tokens of T) share one 128-byte line, at most 4.
+// The row threads load the runs of such a group of chunks together, so every
+// line is fetched from HBM once, not once per chunk when L2 has evicted it in
+// between.
+template <typename T, int TC> constexpr int kLineGroup =
+    128 / (TC * int(sizeof(T))) < 1 ? 1 : (128 / (TC * int(sizeof(T))) > 4 ? 4 : 128 / (TC * int(sizeof(T))));
+
+// Values made opaque to the optimiser (an empty asm on each 32-bit word).
+__device__ __forceinline__ void opaque(uint32_t& x) { asm("" : "+v"(x)); }
+__device__ __forceinline__ void opaque(uint2& x) { asm("" : "+v"(x.x)); asm("" : "+v"(x.y)); }
+__device__ __forceinline__ void opaque(float& x) { asm("" : "+v"(x)); }
+__device__ __forceinline__ void opaque(uint16_t& x) {
+    uint32_t y = x;
+    asm("" : "+v"(y));
+    x = (uint16_t)y;
+}
+
+// a[i] for a wave-uniform i < G, as a chain of selects.  The elements go
+// through `opaque` first: a select between two array elements could
+// otherwise become one load at a computed index, which would move the whole
+// array to scratch memory.
+template <int G, typename V>
+__device__ __forceinline__ V pick(const V (&a)[G], int i) {
+    V v = a[0];
+    opaque(v);
+#pragma unroll
+    for (int k = 1; k < G; ++k) {
+        V x = a[k];
+        opaque(x);
+        v = i == k ? x : v;
+    }
+    return v;
+}
+
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 // An element of type T widened to float (bf16: the upper half of a float).
@@ -102,6 +136,7 @@ template <typename T, int NS, bool BUF, bool SAVED>
 __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
     constexpr int kTC = ChunkLen<NS>::value;
     constexpr int kTPT = kTC / kSegs;      // tokens per row thread
+    constexpr int kLG = kLineGroup<T, kTC>;
     __shared__ float4 s_tk[kTC][64 + 1];          // (delta, delta*u, u, g) per token and channel
     __shared__ float s_y[kNW][kTC][64 + 1];       // per-wave partial sum_n C h
     __shared__ float2 s_p[kNW][kTC][64 + 1];      // per-wave partial (du, ddelta)
@@ -123,8 +158,14 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
     constexpr int kNSP = NS < 2 ? 2 : NS;                 // states per wave in the dB / dC layout
     constexpr int kVPW = 2 * kNSP * kTC;                  // dB / dC partials per wave and chunk
     static_assert(kVPW == 64 || kVPW == 128, "reduction layout");
-    const int64_t b = blockIdx.x / nblk_d;
-    const int64_t d0 = (blockIdx.x % nblk_d) * 64;
+    // Blocks are dispatched round-robin over the 8 XCDs; number them so that
+    // consecutive ids (channel blocks of one batch row, which read the same
+    // B and C rows) share an XCD and its L2.
+    uint32_t lid = blockIdx.x;
+    if ((gridDim.x & 7u) == 0u) lid = (blockIdx.x & 7u) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+    const int64_t b = lid / nblk_d;
+    const int64_t dblk = lid % nblk_d;
+    const int64_t d0 = dblk * 64;
     const int nrows = (int)((dim - d0) < 64 ? (dim - d0) : 64);
 
     // ---- scan mapping: lane = channel cs, wave = state group w ----------------
@@ -267,29 +308,41 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
     };
 
     // ================= 1. forward sweep: chunk-start checkpoints =================
-    // (delta, u) of the next chunk are loaded while this one is scanned.
-    Pair f_dl, f_u;
-    T f_bc[kBPT];
-    auto fetch_fwd = [&](int ck) {
-        const int t = ck * kTC + toff;
-        f_dl = ld(dl_in, rs_dl, t);
-        f_u = ld(u_in, rs_u, t);
-        fetch_bc(ck, f_bc);
+    // (delta, u) and B / C of the next line group of chunks are loaded while
+    // the last chunk of this group is scanned.
+    Pair f_dl[kLG], f_u[kLG];
+    T f_bc[kLG][kBPT];
+    auto fetch_fwd = [&](int g0) {                // chunks g0 .. g0 + kLG - 1
+#pragma unroll
+        for (int c = 0; c < kLG; ++c) {
+            const int t = (g0 + c) * kTC + toff;
+            f_dl[c] = ld(dl_in, rs_dl, t);
+            f_u[c] = ld(u_in, rs_u, t);
+        }
+#pragma unroll
+        for (int c = 0; c < kLG; ++c) fetch_bc(g0 + c, f_bc[c]);
     };
-    // Staging of chunk ck into buffer ck & 1 (and the fetch of chunk ck + 1);
-    // chunk ck + 1 is staged right after chunk ck is scanned, so one barrier
-    // per chunk suffices.
+    // Staging of chunk ck into buffer ck & 1 (and, at the last chunk of its
+    // group, the fetch of the next group); chunk ck + 1 is staged right after
+    // chunk ck is scanned, so one barrier per chunk suffices.
     auto stage_fwd = [&](int ck) {
         float dlv[kTPT], uv[kTPT];
         T bcv[kBPT];
+        const int c = ck % kLG;
+        const Pair pdl = pick(f_dl, c), pu = pick(f_u, c);
 #pragma unroll
         for (int j = 0; j < kTPT; ++j) {
-            dlv[j] = rv(f_dl, j, ck * kTC + toff + j);
-            uv[j] = rv(f_u, j, ck * kTC + toff + j);
+            dlv[j] = rv(pdl, j, ck * kTC + toff + j);
+            uv[j] = rv(pu, j, ck * kTC + toff + j);
         }
 #pragma unroll
-        for (int q = 0; q < kBPT; ++q) bcv[q] = f_bc[q];
-        if (ck + 1 < nck) fetch_fwd(ck + 1);
+        for (int q = 0; q < kBPT; ++q) {
+            T col[kLG];
+#pragma unroll
+            for (int g = 0; g < kLG; ++g) col[g] = f_bc[g][q];
+            bcv[q] = pick(col, c);
+        }
+        if (c == kLG - 1 && ck + 1 < nck) fetch_fwd(ck + 1);
         stage_bc(ck, bcv, ck & 1);
 #pragma unroll
         for (int j = 0; j < kTPT; ++j) s_fw[ck & 1][toff + j][cr] = make_float2(dlv[j], dlv[j] * uv[j]);
@@ -321,39 +374,63 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
     // ================= 2. backward sweep, last chunk first =======================
     // The row data and the chunk-start states of the next chunk (ck - 1) are
     // loaded while this one is processed.
+    // The row data and B / C of a line group of chunks are loaded while the
+    // first chunk of the following group (walked last) is processed; the
+    // chunk-start states one chunk ahead.  (Stores need no grouping: L2
+    // merges the partial writes of a line, and the bytes written stay the
+    // algorithmic ones.)
     float dDacc = 0.f;
-    Pair b_dl, b_u, b_go, b_z;
-    T b_bc[kBPT];
+    Pair b_dl[kLG], b_u[kLG], b_go[kLG], b_z[kLG];
+    T b_bc[kLG][kBPT];
     float b_hc[NS];
-    auto fetch_bwd = [&](int ck) {
-        const int t = ck * kTC + toff;
-        b_dl = ld(dl_in, rs_dl, t);
-        b_u = ld(u_in, rs_u, t);
-        b_go = ld(go_in, rs_go, t);
-        b_z = ld(zl_in, rs_z, t);
+    auto fetch_bwd = [&](int g0) {                // chunks g0 .. g0 + kLG - 1
+#pragma unroll
+        for (int c = 0; c < kLG; ++c) {
+            const int t = (g0 + c) * kTC + toff;
+            b_dl[c] = ld(dl_in, rs_dl, t);
+            b_u[c] = ld(u_in, rs_u, t);
+            b_go[c] = ld(go_in, rs_go, t);
+            b_z[c] = ld(zl_in, rs_z, t);
+        }
+#pragma unroll
+        for (int c = 0; c < kLG; ++c) fetch_bc(g0 + c, b_bc[c]);
+    };
+    auto fetch_hc = [&](int ck) {
 #pragma unroll
         for (int s = 0; s < NS; ++s) b_hc[s] = *ckpt_in(ck, s);
-        fetch_bc(ck, b_bc);
     };
-    if (nck > 0) fetch_bwd(nck - 1);
+    if (nck > 0) {
+        fetch_bwd((nck - 1) / kLG * kLG);
+        fetch_hc(nck - 1);
+    }
     for (int ck = nck - 1; ck >= 0; --ck) {
         const int t0 = ck * kTC;
+        const int g0 = ck / kLG * kLG, c = ck - g0;
         // stage (delta, delta*u, u, g) -- the row thread keeps its own tokens
         float uu[kTPT], zz[kTPT], go[kTPT], gg[kTPT], dlv[kTPT], hc[NS];
+        {
+            const Pair pdl = pick(b_dl, c), pu = pick(b_u, c), pgo = pick(b_go, c), pz = pick(b_z, c);
 #pragma unroll
-        for (int j = 0; j < kTPT; ++j) {
-            const int t = t0 + toff + j;
-            dlv[j] = rv(b_dl, j, t);
-            uu[j] = rv(b_u, j, t);
-            go[j] = rv(b_go, j, t);
-            zz[j] = z_in ? rv(b_z, j, t) : 0.f;
+            for (int j = 0; j < kTPT; ++j) {
+                const int t = t0 + toff + j;
+                dlv[j] = rv(pdl, j, t);
+                uu[j] = rv(pu, j, t);
+                go[j] = rv(pgo, j, t);
+                zz[j] = z_in ? rv(pz, j, t) : 0.f;
+            }
         }
 #pragma unroll
         for (int s = 0; s < NS; ++s) hc[s] = (cval && w * NS + s < N) ? b_hc[s] : 0.f;
         T bcv[kBPT];
 #pragma unroll
-        for (int q = 0; q < kBPT; ++q) bcv[q] = b_bc[q];
-        if (ck > 0) fetch_bwd(ck - 1);
+        for (int q = 0; q < kBPT; ++q) {
+            T col[kLG];
+#pragma unroll
+            for (int g = 0; g < kLG; ++g) col[g] = b_bc[g][q];
+            bcv[q] = pick(col, c);
+        }
+        if (ck > 0) fetch_hc(ck - 1);
+        if (c == 0 && ck > 0) fetch_bwd(g0 - kLG);
         stage_bc(ck, bcv, 0);
 #pragma unroll
         for (int j = 0; j < kTPT; ++j) {
@@ -442,7 +519,7 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
             // this workgroup's partial sums for the chunk: lane L holds the
             // values L R .. L R + R - 1 of the wave's kVPW
             constexpr int R = kVPW / 64;
-            float* part = p.part + ((b * nblk_d + blockIdx.x % nblk_d) * nck + ck) * (int64_t)(kNW * kVPW) + w * kVPW +
+            float* part = p.part + ((b * nblk_d + dblk) * nck + ck) * (int64_t)(kNW * kVPW) + w * kVPW +
                           cs * R;
             if constexpr (R == 1) part[0] = rk[0];
             else *reinterpret_cast<float2*>(part) = make_float2(rk[0], rk[1]);
