@@ -158,13 +158,8 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
     constexpr int kNSP = NS < 2 ? 2 : NS;                 // states per wave in the dB / dC layout
     constexpr int kVPW = 2 * kNSP * kTC;                  // dB / dC partials per wave and chunk
     static_assert(kVPW == 64 || kVPW == 128, "reduction layout");
-    // Blocks are dispatched round-robin over the 8 XCDs; number them so that
-    // consecutive ids (channel blocks of one batch row, which read the same
-    // B and C rows) share an XCD and its L2.
-    uint32_t lid = blockIdx.x;
-    if ((gridDim.x & 7u) == 0u) lid = (blockIdx.x & 7u) * (gridDim.x >> 3) + (blockIdx.x >> 3);
-    const int64_t b = lid / nblk_d;
-    const int64_t dblk = lid % nblk_d;
+    const int64_t b = blockIdx.x / nblk_d;
+    const int64_t dblk = blockIdx.x % nblk_d;
     const int64_t d0 = dblk * 64;
     const int nrows = (int)((dim - d0) < 64 ? (dim - d0) : 64);
 

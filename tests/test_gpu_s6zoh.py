@@ -89,19 +89,22 @@ def test_mamba130m_varied_params_full():
 
 
 def test_gain_switch_straddled_fp32():
-    """fp32 with delta*A clustered around the gain's series / direct switch
-    (|delta A| = 1/16): A[d, n] is set from the channel's median step so that
-    most elements fall within a factor 2 of it, on both sides.  The error
-    budget of the gain there is ~1e-6 relative, so the outputs are held to
-    3e-6, tighter than the fp32 tolerance."""
+    """fp32 with delta*A clustered around the hold factor's series / direct
+    switch (|delta A| = 1/32): A[d, n] is set from the channel's median step
+    so that most elements fall within a factor 2 of it, on both sides.  The
+    error budget of the factor there is ~2e-6 relative (the rounding of
+    exp(delta A) near 1 in the direct form, the x^3/24 truncation in the
+    series), so the outputs are held to 3e-6, tighter than the fp32
+    tolerance."""
     inp = synth.s6_inputs(2, 96, 400, 16, dtype="f32", seed=3777, init_state=True)
     dl = inp["delta"].astype(np.float64)
     med = np.median(dl, axis=(0, 2))                        # per channel
     f = np.exp(np.linspace(np.log(0.5), np.log(2.0), 16))  # per state, both sides of the switch
-    inp["A"] = (-(1.0 / 16.0) / med[:, None] * f[None, :]).astype(np.float32)
+    sw = 1.0 / 32.0
+    inp["A"] = (-sw / med[:, None] * f[None, :]).astype(np.float32)
     x = np.abs(dl[:, :, None, :] * inp["A"][None, :, :, None].astype(np.float64))
-    near = np.mean((x > 1.0 / 32.0) & (x < 1.0 / 8.0))
-    assert near > 0.5 and np.mean(x < 1.0 / 16.0) > 0.2 and np.mean(x > 1.0 / 16.0) > 0.2
+    near = np.mean((x > sw / 2) & (x < sw * 2))
+    assert near > 0.5 and np.mean(x < sw) > 0.2 and np.mean(x > sw) > 0.2
     say("  zoh gpu call: gain switch straddled, fp32")
     args = [dev(inp[k]) for k in ("u", "delta", "A", "B", "C", "D", "z", "h0")]
     y, hf = mssm.selective_scan(*args, return_final_state=True, zoh=True)
