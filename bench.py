@@ -12,13 +12,14 @@ fp64 CPU oracle timed on the same workload, and the other entry points
 (decode step at the Mamba-2.8B shape, Mamba-2 SSD) inside the same object.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
-                    [--only s6,calib,s6c1,s6fused,s6zoh,s6bwd,decode,decode2,ssd,copy]
+                    [--only s6,calib,s6c1,s6fused,s6zoh,s6bwd,decode,decode2,ssd,ssdf32,copy]
 
 Prints exactly one JSON line on stdout; progress goes to stderr.  `--only`
 restricts the run (for profiling); `calib` measures the copy / read
 ceilings and VALU issue rates on the GPU at hand; `s6c1` times the scan at
-the Mamba-130M layer shape (fp32); `copy` times a plain 1 GiB device copy,
-the reference used to scale the HBM byte counters.
+the Mamba-130M layer shape (fp32); `ssdf32` the SSD at the Mamba-2 layer
+shape with float32 storage (the plain-fp32 chunked kernel); `copy` times a
+plain 1 GiB device copy, the reference used to scale the HBM byte counters.
 """
 from __future__ import annotations
 
@@ -673,6 +674,36 @@ def bench_ssd(args):
                                         "ssd_main_kernel": profiled_traffic("ssd_main_mamba2_chunk256.md")})
 
 
+def bench_ssd_f32(args):
+    """The SSD at the Mamba-2 layer shape with float32 storage, which runs on
+    the plain-fp32 chunked kernel (the MFMA kernels take bf16).  One input
+    set (x and y 134 MB each, with dt, B, C about 290 MB: beyond the 256 MB
+    Infinity Cache)."""
+    import torch
+    import selective_state_space_19_amd as mssm
+    from selective_state_space_19_amd import synth
+    wl = synth.WORKLOADS["ssd_mamba2_bf16"]
+    s = wl.shape
+    log("[bench] ssd fp32: generating inputs")
+    inp = synth.ssd_inputs(s["batch"], s["seqlen"], s["nheads"], s["headdim"], s["d_state"], s["ngroups"],
+                           dtype="f32", seed=wl.seed)
+    d = {k: to_dev(inp[k]) for k in ("x", "dt", "A", "B", "C", "D")}
+    y = torch.empty_like(d["x"])
+    stream = torch.cuda.current_stream()
+
+    def step():
+        mssm.ssd_chunk(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], chunk=s["chunk"], out=y, stream=stream)
+
+    total, _ = time_launches(step, 10, 2, stream, warm_ms=WARM_MS)
+    ms = total / 10
+    nb = ssd_bytes(s["batch"], s["seqlen"], s["nheads"], s["headdim"], s["d_state"], s["ngroups"], 4)
+    return dict(workload=f"{wl.name} shape with float32 storage: batch 4, seqlen 4096, 32 heads x 64, d_state 128, "
+                         f"ngroups 1 (plain-fp32 chunked kernel)",
+                us=ms * 1e3, GBs=nb / (ms * 1e-3) / 1e9, hbm_frac=nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                tokens_ch_per_s=s["batch"] * s["seqlen"] * s["nheads"] * s["headdim"] / (ms * 1e-3),
+                algorithmic_bytes=nb)
+
+
 def bench_copy(args):
     """A plain 1 GiB device-to-device copy: the reference for scaling the
     FETCH_SIZE / WRITE_SIZE counters to bytes."""
@@ -692,7 +723,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--only", default="s6,calib,s6c1,s6fused,s6zoh,s6bwd,decode,decode2,ssd")
+    ap.add_argument("--only", default="s6,calib,s6c1,s6fused,s6zoh,s6bwd,decode,decode2,ssd,ssdf32")
     ap.add_argument("--warm-ms", type=float, default=None,
                     help="wall-clock warm-up before each timing (default: 300 ms headline, 100 ms the others); "
                          "0 for profiling runs")
@@ -795,6 +826,11 @@ def main():
             out["secondary_ssd"] = bench_ssd(args)
         except Exception as e:
             out["secondary_ssd"] = {"error": repr(e)}
+    if "ssdf32" in parts:
+        try:
+            out["secondary_ssd_fp32"] = bench_ssd_f32(args)
+        except Exception as e:
+            out["secondary_ssd_fp32"] = {"error": repr(e)}
     if "copy" in parts:
         out["copy_reference"] = bench_copy(args)
     print(json.dumps(out), flush=True)
