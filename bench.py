@@ -98,21 +98,22 @@ def ssd_flops(batch, L, H, P, N, G, Q):
     return cb + ydiag + states + yoff + spass
 
 
-def profiled_traffic(profile):
-    """HBM bytes per launch of a kernel, from its committed rocprofv3 counter
-    summary under profiles/ (FETCH_SIZE and WRITE_SIZE, each scaled by what
-    the counter reads for a plain 1 GiB copy).  None when the summary is
-    missing or the kernel's sources changed after the counters were taken."""
+def profile_fields(profile):
+    """The machine-readable block of a kernel's committed rocprofv3 summary
+    under profiles/ (traffic per launch, and for some kernels busy shares of
+    the VALU or MFMA units), or None when the summary is missing or the
+    kernel's sources changed after the counters were taken."""
     try:
         text = open(os.path.join(ROOT, "profiles", profile)).read()
     except OSError:
         return None
     kv = {}
-    for line in text.splitlines():
+    block = text.partition("## Machine-readable")[2]
+    for line in block.splitlines():
         k, sep, v = line.partition(": ")
-        if sep and k in ("traffic_bytes_per_launch", "kernel_sources", "kernel_source_sha256"):
-            kv[k] = v.strip()
-    if len(kv) != 3:
+        if sep:
+            kv[k.strip()] = v.strip()
+    if "kernel_sources" not in kv or "kernel_source_sha256" not in kv:
         return None
     h = hashlib.sha256()
     for f in kv["kernel_sources"].split():
@@ -120,7 +121,25 @@ def profiled_traffic(profile):
             h.update(open(os.path.join(ROOT, "selective_state_space_19_amd", "csrc", f), "rb").read())
         except OSError:
             return None
-    return int(kv["traffic_bytes_per_launch"]) if h.hexdigest() == kv["kernel_source_sha256"] else None
+    return kv if h.hexdigest() == kv["kernel_source_sha256"] else None
+
+
+def profiled_traffic(profile):
+    """HBM bytes per launch of a kernel from its summary under profiles/
+    (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads for a
+    plain 1 GiB copy); None when missing or stale (see profile_fields)."""
+    kv = profile_fields(profile)
+    return int(kv["traffic_bytes_per_launch"]) if kv and "traffic_bytes_per_launch" in kv else None
+
+
+def profiled_counters(profile, keys):
+    """Counter-derived figures recorded in a kernel's summary (floats), or
+    None when missing or stale."""
+    kv = profile_fields(profile)
+    if not kv:
+        return None
+    out = {k: float(kv[k]) for k in keys if k in kv}
+    return dict(out, source="profiles/" + profile) if out else None
 
 
 def to_dev(a):
@@ -346,7 +365,8 @@ def bench_s6_130m(args):
             "alu_TFLOPs": alu, "alu_frac": alu / S6_ALU_PEAK_TFLOPS,
             "tokens_ch_per_s": tok / (ms * 1e-3), "algorithmic_bytes": nb,
             "workgroups": s["batch"] * ((s["d_inner"] + 63) // 64),
-            "traffic_bytes_per_launch": profiled_traffic("s6_scan_mamba130m_f32.md")}
+            "traffic_bytes_per_launch": profiled_traffic("s6_scan_mamba130m_f32.md"),
+            "counters": profiled_counters("s6_scan_mamba130m_f32.md", ("valu_busy_pct", "valu_instr_per_element"))}
 
 
 def _calib_lib():
@@ -472,7 +492,15 @@ def cpu_baseline(inp, budget_s=30.0):
         if used * (rows + 1) / rows > budget_s:
             break
     nbytes = s6_bytes(rows, dim, L, N, 2 if dt == "bf16" else 4)
-    return {"value": nbytes / used / 1e9, "unit": "GB/s", "cores": nth, "kind": "oracle",
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.partition(":")[2].strip()
+                break
+    except OSError:
+        pass
+    return {"value": nbytes / used / 1e9, "unit": "GB/s", "cores": nth, "kind": "oracle", "cpu_model": model,
             "sample": f"{rows} of {bsz} batch rows of the benchmarked workload ({rows * dim} channels x "
                       f"{L} tokens, d_state {N}), fp64 sequential recurrence, {used:.2f} s wall",
             "tokens_ch_per_s": rows * dim * L / used, "seconds": used,
@@ -657,6 +685,12 @@ def bench_ssd(args):
 
     total, per = time_launches(step, 20, 4, stream, warm_ms=WARM_MS)
     ms = total / 20
+    # the dense-block count: every 16 x 16 MFMA block a chunked form would
+    # issue, causal blocks in full (the pages' chunked form, not this
+    # kernel's triangle skipping); reported beside, labelled
+    nc = (s["seqlen"] + s["chunk"] - 1) // s["chunk"]
+    Q, Hh, P, N, G = s["chunk"], s["nheads"], s["headdim"], s["d_state"], s["ngroups"]
+    dense = 2 * s["batch"] * nc * (G * Q * Q * N + Hh * Q * Q * P + 2 * Hh * Q * N * P + Hh * P * N)
     total_hot, _ = time_launches(lambda: step(rotate=False), 20, 4, stream, warm_ms=WARM_MS)
     # The chunk length is a tile size: the result is the same up to rounding.
     # The same call with 64-token chunks, for comparison (not the workload).
@@ -669,6 +703,9 @@ def bench_ssd(args):
                 us=ms * 1e3, GBs=nb / (ms * 1e-3) / 1e9, hbm_frac=nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                 mfma_TFLOPs=fl / (ms * 1e-3) / 1e12, mfma_frac=fl / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                 tokens_ch_per_s=s["batch"] * s["seqlen"] * s["nheads"] * s["headdim"] / (ms * 1e-3),
+                us_median=float(np.median(per)) * 1e3, us_min=float(np.min(per)) * 1e3,
+                dense_block_flops=dense, mfma_TFLOPs_dense_blocks=dense / (ms * 1e-3) / 1e12,
+                mfma_busy=profiled_counters("ssd_main_mamba2_chunk256.md", ("mfma_busy_pct",)),
                 algorithmic_bytes=nb, algorithmic_flops=fl, workspace_bytes=need,
                 traffic_bytes_per_call={"ssd_prep_kernel": profiled_traffic("ssd_prep_mamba2_chunk256.md"),
                                         "ssd_main_kernel": profiled_traffic("ssd_main_mamba2_chunk256.md")})
@@ -765,6 +802,8 @@ def main():
             "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
             "tokens_ch_per_s": tok / (r["ms"] * 1e-3),
             "event_ms_per_step": round(r["event_ms"], 5),
+            "event_us_median": round(float(np.median(r["per"])) * 1e3, 2),
+            "event_us_min": round(float(np.min(r["per"])) * 1e3, 2),
             # The scan is bound by VALU issue, not HBM (counters: VALU busy
             # ~92%, HBM ~29%): 8 FMA issue slots per state element at the
             # published fp32 rate (218 us here) outweigh its bytes (135 us at
@@ -774,7 +813,10 @@ def main():
                          "traffic": profiled_traffic("s6_scan_mamba1p4b_bf16.md"),
                          "kernel": "s6_scan_kernel", "avg_launch_ms": round(r["kern_ms"], 5),
                          "state_elements_per_launch": elems, "flop_per_element": S6_FLOP_PER_ELEM,
-                         "issue_slots_per_element": S6_SLOTS_PER_ELEM},
+                         "issue_slots_per_element": S6_SLOTS_PER_ELEM,
+                         "counters": profiled_counters("s6_scan_mamba1p4b_bf16.md",
+                                                       ("valu_busy_pct", "valu_instr_per_element",
+                                                        "transcendental_per_element", "issue_slots_per_element"))},
             "roofline_hbm": {"achieved": round(r["bytes"] / kern_s / 1e9, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": round(r["bytes"] / kern_s / 1e9 / HBM_PEAK_GBS, 4),
                              "algorithmic_bytes_per_launch": r["bytes"]},
@@ -785,6 +827,7 @@ def main():
         if not args.no_cpu_baseline:
             log("[bench] s6: cpu baseline (the oracle on the same workload)")
             out["cpu_baseline"] = cpu_baseline(r["inp"])
+            out["cpu_baseline"]["gpu_over_oracle"] = gbs / out["cpu_baseline"]["value"]
         del r
     if "calib" in parts:
         try:
