@@ -1,0 +1,77 @@
+"""Workspace contents must never reach a result: the SSD's operand tiles and
+the backward pass's checkpoints and partial sums are written before they
+are read.  Each call here runs twice on the same inputs, once with its
+workspace filled with 0xFF bytes (NaN in both fp32 and bf16) and once with
+zeros; the results must be bitwise equal (dA and dD, summed with atomics in
+no fixed order, to rounding) and match the oracle."""
+import numpy as np
+import pytest
+
+import oracle
+import selective_state_space_19_amd as mssm
+from gpu_util import TOL, dev, host, normwise, say
+from selective_state_space_19_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _ws(nbytes, fill):
+    import torch
+    return torch.full((max(nbytes, 1),), fill, dtype=torch.uint8, device="cuda")
+
+
+@pytest.mark.parametrize("case", [(2, 300, 4, 64, 128, 1, 256), (1, 200, 2, 64, 64, 2, 64),
+                                  (1, 513, 2, 64, 256, 1, 128)],
+                         ids=lambda c: "b{}_L{}_H{}_P{}_N{}_G{}_Q{}".format(*c))
+def test_ssd_ignores_workspace_contents(case):
+    import torch
+    b, L, H, P, N, G, Q = case
+    inp = synth.ssd_inputs(b, L, H, P, N, G, dtype="bf16", seed=4100 + L, gate=True, init_state=True, varied=True)
+    need = mssm.ssd_workspace_size(b, L, H, P, N, G, Q)
+    assert need > 0                               # the MFMA path, which uses it
+    args = [dev(inp[k]) for k in ("x", "dt", "A", "B", "C", "D", "z", "h0")]
+    outs = []
+    for fill in (0xFF, 0x00):
+        say(f"  ssd gpu call, workspace filled with {fill:#04x}: x{inp['x'].shape} N{N} G{G} Q{Q}")
+        outs.append(mssm.ssd_chunk(*args, chunk=Q, return_final_state=True, workspace=_ws(need, fill)))
+        torch.cuda.synchronize()
+    (y1, h1), (y2, h2) = outs
+    assert torch.equal(y1, y2) and torch.equal(h1, h2)
+    yo, ho = oracle.ssd(*(synth.widen(inp[k], "bf16") if inp[k] is not None and inp[k].dtype == np.uint16
+                          else inp[k] for k in ("x", "dt", "A", "B", "C", "D", "z", "h0")))
+    assert normwise(host(y1), yo) <= TOL["bf16"] and normwise(host(h1), ho) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("case", [(2, 100, 200, 16, "bf16"), (1, 70, 77, 32, "f32"), (1, 64, 33, 64, "bf16")],
+                         ids=lambda c: "b{}_d{}_L{}_N{}_{}".format(*c))
+def test_backward_ignores_workspace_contents(case):
+    import torch
+    b, d, L, N, dt = case
+    inp = synth.s6_inputs(b, d, L, N, dtype=dt, seed=4200 + L, init_state=True, varied=True)
+    rng = np.random.default_rng(L)
+    dout = synth.round_to(rng.standard_normal((b, d, L)), dt)
+    dhT = rng.standard_normal((b, d, N)).astype(np.float32)
+    need = mssm.selective_scan_bwd_workspace_size(b, d, L, N)
+    args = [dev(inp[k]) for k in ("u", "delta", "A", "B", "C")] + [dev(dout)]
+    kw = dict(D=dev(inp["D"]), z=dev(inp["z"]), h0=dev(inp["h0"]), dh_final=dev(dhT))
+    res = []
+    for fill in (0xFF, 0x00):
+        say(f"  bwd gpu call, workspace filled with {fill:#04x}: u{inp['u'].shape} N{N} {dt}")
+        res.append(mssm.selective_scan_bwd(*args, **kw, workspace=_ws(need, fill)))
+        torch.cuda.synchronize()
+    # the training pair: the forward fills a poisoned workspace, the backward reads it
+    ws = _ws(need, 0xFF)
+    say(f"  fwd_save + bwd_saved, poisoned workspace: u{inp['u'].shape} N{N} {dt}")
+    mssm.selective_scan(*(dev(inp[k]) for k in ("u", "delta", "A", "B", "C", "D", "z", "h0")), save_workspace=ws)
+    res.append(mssm.selective_scan_bwd(*args, **kw, workspace=ws, saved=True))
+    torch.cuda.synchronize()
+    w = lambda a: None if a is None else synth.widen(a, dt)  # noqa: E731
+    o = oracle.s6_scan_bwd(w(inp["u"]), w(inp["delta"]), inp["A"], w(inp["B"]), w(inp["C"]), inp["D"], w(inp["z"]),
+                           inp["h0"], w(dout), dhT)
+    for k in res[0]:
+        for r in res[1:]:
+            if k in ("dA", "dD"):
+                assert normwise(host(r[k]), host(res[0][k])) <= 1e-6, k
+            else:
+                assert torch.equal(r[k], res[0][k]), k
+        assert normwise(host(res[0][k]), o[k]) <= TOL[dt], k
