@@ -18,7 +18,7 @@ Prints exactly one JSON line on stdout; progress goes to stderr.  `--only`
 restricts the run (for profiling); `calib` measures the copy / read
 ceilings and VALU issue rates on the GPU at hand; `s6c1` times the scan at
 the Mamba-130M layer shape (fp32); `ssdf32` the SSD at the Mamba-2 layer
-shape with float32 storage (the plain-fp32 chunked kernel); `copy` times a
+shape with float32 storage (the general chunked kernel); `copy` times a
 plain 1 GiB device copy, the reference used to scale the HBM byte counters.
 """
 from __future__ import annotations
@@ -713,7 +713,8 @@ def bench_ssd(args):
 
 def bench_ssd_f32(args):
     """The SSD at the Mamba-2 layer shape with float32 storage, which runs on
-    the plain-fp32 chunked kernel (the MFMA kernels take bf16).  One input
+    the general chunked kernel (fp32 matrix cores; the bf16 MFMA kernels
+    take bf16).  One input
     set (x and y 134 MB each, with dt, B, C about 290 MB: beyond the 256 MB
     Infinity Cache)."""
     import torch
@@ -735,7 +736,7 @@ def bench_ssd_f32(args):
     ms = total / 10
     nb = ssd_bytes(s["batch"], s["seqlen"], s["nheads"], s["headdim"], s["d_state"], s["ngroups"], 4)
     return dict(workload=f"{wl.name} shape with float32 storage: batch 4, seqlen 4096, 32 heads x 64, d_state 128, "
-                         f"ngroups 1 (plain-fp32 chunked kernel)",
+                         f"ngroups 1 (general chunked kernel, fp32 MFMA)",
                 us=ms * 1e3, GBs=nb / (ms * 1e-3) / 1e9, hbm_frac=nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                 tokens_ch_per_s=s["batch"] * s["seqlen"] * s["nheads"] * s["headdim"] / (ms * 1e-3),
                 algorithmic_bytes=nb)

@@ -1,6 +1,6 @@
 // ssd_general.hip -- Mamba-2 SSD, chunked, for any headdim and d_state up to
-// 256, float32 or bfloat16 storage (the sizes the MFMA kernels of ssd.hip do
-// not take).
+// 256, float32 or bfloat16 storage (the sizes the bf16 MFMA kernels of
+// ssd.hip do not take).
 //
 // What it computes ("State-Space Model Optimization Patterns" page, section 2
 // "State Space Duality" and section 9 "Chunked Computation"): per batch row
@@ -14,21 +14,23 @@
 // s the running sum of dt*A over the chunk, and the state passed to the next
 // chunk is exp(s_end) H_in + sum_j exp(s_end - s_j) dt_j x_j B_j^T.
 //
-// Design: one workgroup (256 threads) per (b, head, 32 head channels) walks
-// the sequence in chunks of K = 32 tokens with the fp32 state in LDS.  Per
-// chunk it stages dt, x, B and C (as fp32; rows of B, C and the state padded
-// to whole float4s with zeros), forms the running sum, then three products,
-// each thread holding a register tile so that one LDS read feeds several
-// FMAs and its accumulators are independent chains:
-//   scores  M = C B^T (lower 32 x 32 triangle, 2 x 2 per thread, float4 reads
-//           along n), then masked and scaled by the decay and dt;
-//   outputs Y = M X + diag(exp(s)) C H^T (2 tokens x 2 channels per thread);
-//   state   H = exp(s_end) H + Xw^T B (4 channels x 4 states per thread).
-// All arithmetic is plain fp32 on the VALU, so float32 inputs keep float32
-// accuracy.  The chunk length of the call is a tile size that does not change
-// the result beyond rounding; this path always uses 32.  Every exponent
-// s_i - s_j (j <= i), s_i and s_end - s_j is <= 0 for A_h <= 0, so no factor
-// exceeds 1.
+// Design: one workgroup (4 waves) per (b, head, 32 head channels) walks the
+// sequence in chunks of K = 32 tokens.  Per chunk it stages dt, x, B and C
+// in LDS as fp32 (rows of B, C padded with zeros to whole 16-state tiles),
+// forms the running sum, then computes the three products on the fp32
+// matrix cores (v_mfma_f32_16x16x4_f32: fp32 operands and accumulation, so
+// float32 inputs keep float32 accuracy), 16 x 16 tiles:
+//   scores   M = C B^T     the three tiles on or below the diagonal (waves
+//                          0-2), then masked and scaled by the decay and dt;
+//   outputs  Y = diag(e^s) C H^T + M X    one tile per wave;
+//   state    H = e^{s_end} H + Xw^T B     the state's tiles spread over the
+//                          waves and held in their accumulators across
+//                          chunks (copied to LDS for the next chunk's C H^T).
+// The next chunk's dt, x, z, B and C are loaded into registers while the
+// current one is computed.  The chunk length of the call is a tile size that
+// does not change the result beyond rounding; this path always uses 32.
+// Every exponent s_i - s_j (j <= i), s_i and s_end - s_j is <= 0 for A_h <= 0,
+// so no factor exceeds 1.
 #include "common.h"
 #include "kernels.h"
 
@@ -39,24 +41,27 @@ namespace {
 constexpr int kGK = 32;          // chunk length (tokens)
 constexpr int kGP = 32;          // head channels per workgroup
 constexpr int kGNMax = 256;      // largest d_state
-constexpr int kRS = kGNMax + 4;  // LDS row stride (floats) of B, C and the state
-constexpr int kXS = kGP + 4;     // LDS row stride (floats) of x and the scaled x
+// LDS row strides (floats), 4 mod 32: the 64 lanes of an operand read (16
+// rows x 4 columns) then hit every bank exactly twice, the least possible.
+constexpr int kRS = kGNMax + 4;  // B, C and the state
+constexpr int kXS = kGP + 4;     // x, the scaled x and the scores
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// D = A B + C for one 16 x 16 tile, K = 4: lane l holds A[l % 16][l / 16],
+// B[l / 16][l % 16], and D[4 (l / 16) + r][l % 16] in register r.
+__device__ __forceinline__ f32x4_t mfma4(float a, float b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
 
 template <typename T>
 __device__ __forceinline__ float ldx(const T* p) { return Elem<T>::load1(p); }
 
-// Four consecutive elements as floats; `vec` says p is aligned to them.
-__device__ __forceinline__ float4 ld4(const float* p, bool vec) {
-    if (vec) return *reinterpret_cast<const float4*>(p);
-    return make_float4(p[0], p[1], p[2], p[3]);
-}
-__device__ __forceinline__ float4 ld4(const uint16_t* p, bool vec) {
-    if (vec) {
-        const uint2 w = *reinterpret_cast<const uint2*>(p);
-        return make_float4(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y));
-    }
-    return make_float4(Elem<uint16_t>::load1(p), Elem<uint16_t>::load1(p + 1), Elem<uint16_t>::load1(p + 2),
-                       Elem<uint16_t>::load1(p + 3));
+// Four consecutive elements as floats from an address aligned to them.
+__device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 ld4(const uint16_t* p) {
+    const uint2 w = *reinterpret_cast<const uint2*>(p);
+    return make_float4(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y));
 }
 
 // Inclusive prefix sum of v over the 32 lanes of each half-wave (shuffles).
@@ -67,10 +72,6 @@ __device__ __forceinline__ float scan32(float v, int lane) {
         if ((lane & 31) >= o) v += u;
     }
     return v;
-}
-
-__device__ __forceinline__ float dot4(float4 a, float4 b, float acc) {
-    return fmaf(a.w, b.w, fmaf(a.z, b.z, fmaf(a.y, b.y, fmaf(a.x, b.x, acc))));
 }
 
 // VEC: B / C rows are whole aligned float4s (N a multiple of 4, aligned
@@ -85,8 +86,8 @@ __global__ __launch_bounds__(256) void ssd_general_kernel(
     __shared__ __align__(16) float sH[kGP][kRS];      // state H[p][n] of this workgroup's head channels
     __shared__ __align__(16) float sX[kGK][kXS];      // x[j][p]
     __shared__ __align__(16) float sXw[kGK][kXS];     // dt_j exp(s_end - s_j) x[j][p]
-    __shared__ float sM[kGK][kGK + 1];                // masked scores
-    __shared__ float sS[kGK], sDt[kGK];
+    __shared__ __align__(16) float sM[kGK][kXS];      // masked scores
+    __shared__ float sS[kGK], sDt[kGK], sE[kGK];     // running sum (log2 units), dt, 2^s
 
     const int npt = (P + kGP - 1) / kGP;
     const int pt = blockIdx.x % npt;
@@ -96,8 +97,12 @@ __global__ __launch_bounds__(256) void ssd_general_kernel(
     const int g = h / (H / G);
     const int p0 = pt * kGP;
     const int np = min(kGP, P - p0);
-    const int NP = (N + 3) & ~3;                      // state length in whole float4s
+    const int NQ = (N + 15) & ~15;                    // states in whole 16-wide tiles
+    const int NT = NQ / 16;
     const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l = tid & 63;
+    const int lr = l & 15, lk = l >> 4;               // operand row / column within a tile, k within a step
     const float a2 = Ah[h] * kLog2e;
     const float dskip = Dh ? Dh[h] : 0.f;
 
@@ -110,17 +115,34 @@ __global__ __launch_bounds__(256) void ssd_general_kernel(
     const T* Cb = Cm + b * L * brow + (int64_t)g * N;
     const T* dtb = DT + b * (int64_t)L * H + h;
 
-    // state from h0 (or zero); columns past N stay zero
-    for (int e = tid; e < kGP * NP; e += 256) {
-        const int p = e / NP, n = e % NP;
-        sH[p][n] = (h0 && p < np && n < N) ? h0[((b * H + h) * (int64_t)P + p0 + p) * N + n] : 0.f;
+    // The state's tiles: tile t = (channel block t & 1, state block t >> 1),
+    // wave w holds tiles w, w + 4, ...  (at most 8), lane l register r at
+    // channel 16 (t & 1) + 4 lk + r, state 16 (t >> 1) + lr.
+    constexpr int kMaxT = 2 * (kGNMax / 16) / 4;
+    f32x4_t acc_h[kMaxT];
+#pragma unroll
+    for (int m = 0; m < kMaxT; ++m) {
+        const int t = w + 4 * m;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int c = 16 * (t & 1) + 4 * lk + r, n = 16 * (t >> 1) + lr;
+            acc_h[m][r] = (h0 && t < 2 * NT && c < np && n < N) ? h0[((b * H + h) * (int64_t)P + p0 + c) * N + n]
+                                                                : 0.f;
+        }
     }
-
-    // thread tiles: outputs 2 x 2 (tokens i0, i0 + 1; channels c0, c0 + 1), state 4 x 4
-    const int i0 = 2 * (tid >> 4);
-    const int c0 = 2 * (tid & 15);
-    const int sp0 = 4 * (tid & 7);                // state channels sp0 .. sp0 + 3
-    const int sn0 = 4 * (tid >> 3);               // state columns sn0 + 128 r .. + 3
+    auto write_state = [&]() {
+#pragma unroll
+        for (int m = 0; m < kMaxT; ++m) {
+            const int t = w + 4 * m;
+            if (t < 2 * NT) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sH[16 * (t & 1) + 4 * lk + r][16 * (t >> 1) + lr] = acc_h[m][r];
+            }
+        }
+    };
+    write_state();
+    // the scores tile above the diagonal is never written: zero once
+    for (int e = tid; e < 16 * 16; e += 256) sM[e >> 4][16 + (e & 15)] = 0.f;
 
     // The next chunk's dt, x, z, B and C are loaded into registers while this
     // one is computed.  Every load is issued unconditionally from a clamped
@@ -131,7 +153,9 @@ __global__ __launch_bounds__(256) void ssd_general_kernel(
     // would put the zero in scratch memory).
     const int xj = tid >> 3, xp = 4 * (tid & 7);  // x: token xj, channels xp .. xp + 3
     const int bq = tid & 63;                      // B / C: float4 bq of rows (tid >> 6) + 4 m
-    float r_dt = 0.f, r_x[4], r_z[2][2];
+    // this wave's output tile: tokens 16 ob + 4 lk + r, channel 16 oc + lr
+    const int ob = w >> 1, oc = w & 1;
+    float r_dt = 0.f, r_x[4], r_z[4];
     float4 r_b[8], r_c[8];
     auto fetch = [&](int t0) {
         r_dt = ldx(dtb + (int64_t)min(t0 + tid, L - 1) * H);
@@ -140,20 +164,18 @@ __global__ __launch_bounds__(256) void ssd_general_kernel(
 #pragma unroll
             for (int k = 0; k < 4; ++k) r_x[k] = ldx(src + min(xp + k, np - 1));
         }
-        if (zb) {                                 // the gate of this thread's outputs (a uniform branch)
+        if (zb) {                                 // the gate of this lane's outputs (a uniform branch)
 #pragma unroll
-            for (int a = 0; a < 2; ++a)
-#pragma unroll
-                for (int c = 0; c < 2; ++c)
-                    r_z[a][c] = ldx(zb + (int64_t)min(t0 + i0 + a, L - 1) * xrow + min(c0 + c, np - 1));
+            for (int r = 0; r < 4; ++r)
+                r_z[r] = ldx(zb + (int64_t)min(t0 + 16 * ob + 4 * lk + r, L - 1) * xrow + min(16 * oc + lr, np - 1));
         }
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
             const int64_t ro = (int64_t)min(t0 + (tid >> 6) + 4 * m, L - 1) * brow;
             if constexpr (VEC) {
-                const int64_t o = ro + min(4 * bq, NP - 4);
-                r_b[m] = ld4(Bb + o, true);
-                r_c[m] = ld4(Cb + o, true);
+                const int64_t o = ro + min(4 * bq, N - 4);
+                r_b[m] = ld4(Bb + o);
+                r_c[m] = ld4(Cb + o);
             } else {
                 float eb[4], ec[4];
 #pragma unroll
@@ -178,148 +200,111 @@ __global__ __launch_bounds__(256) void ssd_general_kernel(
             const float s = scan32(dt * a2, tid);
             sDt[tid] = dt;
             sS[tid] = s;
+            sE[tid] = fast_exp2(s);
         }
 #pragma unroll
         for (int k = 0; k < 4; ++k) sX[xj][xp + k] = (xj < nt && xp + k < np) ? r_x[k] : 0.f;
-        if (4 * bq < NP) {
+        if (4 * bq < NQ) {
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
                 const int j = (tid >> 6) + 4 * m;
                 float4 vb = r_b[m], vc = r_c[m];
                 if (j >= nt) vb = vc = make_float4(0.f, 0.f, 0.f, 0.f);
-                if constexpr (!VEC) {             // columns past N (VEC: N is a multiple of 4)
-                    if (4 * bq + 1 > N) vb.x = vc.x = 0.f;
-                    if (4 * bq + 2 > N) vb.y = vc.y = 0.f;
-                    if (4 * bq + 3 > N) vb.z = vc.z = 0.f;
-                    if (4 * bq + 4 > N) vb.w = vc.w = 0.f;
-                }
+                if (4 * bq + 1 > N) vb.x = vc.x = 0.f;   // columns past N (padding of the last tile)
+                if (4 * bq + 2 > N) vb.y = vc.y = 0.f;
+                if (4 * bq + 3 > N) vb.z = vc.z = 0.f;
+                if (4 * bq + 4 > N) vb.w = vc.w = 0.f;
                 *reinterpret_cast<float4*>(&sB[j][4 * bq]) = vb;
                 *reinterpret_cast<float4*>(&sC[j][4 * bq]) = vc;
             }
         }
-        float z_cur[2][2];
+        float z_cur[4];
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int c = 0; c < 2; ++c) z_cur[a][c] = zb ? r_z[a][c] : 0.f;
+        for (int r = 0; r < 4; ++r) z_cur[r] = zb ? r_z[r] : 0.f;
         if (t0 + kGK < L) fetch(t0 + kGK);
         __syncthreads();
         const float send = sS[kGK - 1];           // tokens past the end have dt = 0
-        // ---- scores M[i][j] = (C_i . B_j) 2^(s_i - s_j) dt_j for j <= i, else 0 ----
-        if (tid < 136) {                          // the 2 x 2 blocks on or below the diagonal
-            int bi = (int)((sqrtf(8.f * tid + 1.f) - 1.f) * 0.5f);
-            if ((bi + 1) * (bi + 2) / 2 <= tid) ++bi;   // guard the float root
-            if (bi * (bi + 1) / 2 > tid) --bi;
-            const int r0 = 2 * bi, q0 = 2 * (tid - bi * (bi + 1) / 2);
-            float s00 = 0.f, s01 = 0.f, s10 = 0.f, s11 = 0.f;
-            {
+        if (w < 3) {
+            // ---- scores: tile (ti, tj) = (0, 0), (1, 0), (1, 1) ----
+            const int ti = w == 0 ? 0 : 1, tj = w == 2 ? 1 : 0;
+            f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;    // two chains over the states
 #pragma unroll 4
-                for (int n = 0; n < NP; n += 4) {
-                    const float4 ca = *reinterpret_cast<const float4*>(&sC[r0][n]);
-                    const float4 cb = *reinterpret_cast<const float4*>(&sC[r0 + 1][n]);
-                    const float4 ba = *reinterpret_cast<const float4*>(&sB[q0][n]);
-                    const float4 bb = *reinterpret_cast<const float4*>(&sB[q0 + 1][n]);
-                    s00 = dot4(ca, ba, s00);
-                    s01 = dot4(ca, bb, s01);
-                    s10 = dot4(cb, ba, s10);
-                    s11 = dot4(cb, bb, s11);
-                }
+            for (int k0 = 0; k0 < NQ; k0 += 8) {
+                s0 = mfma4(sC[16 * ti + lr][k0 + lk], sB[16 * tj + lr][k0 + lk], s0);
+                s1 = mfma4(sC[16 * ti + lr][k0 + 4 + lk], sB[16 * tj + lr][k0 + 4 + lk], s1);
             }
-            const float sv[2][2] = {{s00, s01}, {s10, s11}};
+            const int j = 16 * tj + lr;
 #pragma unroll
-            for (int a = 0; a < 2; ++a)
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * ti + 4 * lk + r;
+                sM[i][j] = j <= i ? (s0[r] + s1[r]) * fast_exp2(sS[i] - sS[j]) * sDt[j] : 0.f;
+            }
+        } else {
+            // ---- scaled inputs of the state update ----
 #pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    const int i = r0 + a, j = q0 + c;
-                    sM[i][j] = j <= i ? sv[a][c] * fast_exp2(sS[i] - sS[j]) * sDt[j] : 0.f;
-                }
-        }
-        {
-            // scaled inputs of the state update (M above the diagonal is never
-            // read, except inside the diagonal blocks, which are written)
-            const int j = tid >> 3, p = 4 * (tid & 7);
-            const float w = sDt[j] * fast_exp2(send - sS[j]);
-            float4 v = *reinterpret_cast<const float4*>(&sX[j][p]);
-            v.x *= w; v.y *= w; v.z *= w; v.w *= w;
-            *reinterpret_cast<float4*>(&sXw[j][p]) = v;
+            for (int e = 0; e < 16; ++e) {
+                const int j = 2 * e + (l >> 5), p = l & 31;
+                sXw[j][p] = sDt[j] * fast_exp2(send - sS[j]) * sX[j][p];
+            }
         }
         __syncthreads();
-        // ---- outputs: tokens i0, i0 + 1; channels c0, c0 + 1 ----
+        // ---- outputs: this wave's tile ----
         {
-            float yd[2][2] = {{0.f, 0.f}, {0.f, 0.f}}, yo[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
-            for (int j = 0; j <= i0 + 1; ++j) {   // M is zero above the diagonal
-                const float m0 = sM[i0][j], m1 = sM[i0 + 1][j];
-                const float2 xx = *reinterpret_cast<const float2*>(&sX[j][c0]);
-                yd[0][0] = fmaf(m0, xx.x, yd[0][0]);
-                yd[0][1] = fmaf(m0, xx.y, yd[0][1]);
-                yd[1][0] = fmaf(m1, xx.x, yd[1][0]);
-                yd[1][1] = fmaf(m1, xx.y, yd[1][1]);
-            }
+            f32x4_t y0 = {0.f, 0.f, 0.f, 0.f}, y1 = y0;
 #pragma unroll 4
-            for (int n = 0; n < NP; n += 4) {
-                const float4 ca = *reinterpret_cast<const float4*>(&sC[i0][n]);
-                const float4 cb = *reinterpret_cast<const float4*>(&sC[i0 + 1][n]);
-                const float4 ha = *reinterpret_cast<const float4*>(&sH[c0][n]);
-                const float4 hb = *reinterpret_cast<const float4*>(&sH[c0 + 1][n]);
-                yo[0][0] = dot4(ca, ha, yo[0][0]);
-                yo[0][1] = dot4(ca, hb, yo[0][1]);
-                yo[1][0] = dot4(cb, ha, yo[1][0]);
-                yo[1][1] = dot4(cb, hb, yo[1][1]);
+            for (int k0 = 0; k0 < NQ; k0 += 8) {          // C H^T
+                y0 = mfma4(sC[16 * ob + lr][k0 + lk], sH[16 * oc + lr][k0 + lk], y0);
+                y1 = mfma4(sC[16 * ob + lr][k0 + 4 + lk], sH[16 * oc + lr][k0 + 4 + lk], y1);
             }
 #pragma unroll
-            for (int a = 0; a < 2; ++a) {
-                const int i = i0 + a;
-                const float ei = fast_exp2(sS[i]);
+            for (int r = 0; r < 4; ++r) y0[r] = (y0[r] + y1[r]) * sE[16 * ob + 4 * lk + r];
+            // + M X (M is zero past the diagonal tile: 16 or 32 tokens)
 #pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    const int p = c0 + c;
-                    float out = fmaf(ei, yo[a][c], yd[a][c]) + dskip * sX[i][p];
-                    if (zb) out *= silu(z_cur[a][c]);
-                    if (i < nt && p < np) Elem<T>::store1(yb + (int64_t)(t0 + i) * xrow + p, out);
-                }
+            for (int k0 = 0; k0 < 16; k0 += 4) y0 = mfma4(sM[16 * ob + lr][k0 + lk], sX[k0 + lk][16 * oc + lr], y0);
+            if (ob) {
+#pragma unroll
+                for (int k0 = 16; k0 < 32; k0 += 4)
+                    y0 = mfma4(sM[16 * ob + lr][k0 + lk], sX[k0 + lk][16 * oc + lr], y0);
+            }
+            const int p = 16 * oc + lr;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * ob + 4 * lk + r;
+                float out = y0[r] + dskip * sX[i][p];
+                if (zb) out *= silu(z_cur[r]);
+                if (i < nt && p < np) Elem<T>::store1(yb + (int64_t)(t0 + i) * xrow + p, out);
             }
         }
-        __syncthreads();                          // outputs have read the old state
-        // ---- state update: H[p][n] = 2^send H[p][n] + sum_j xw[j][p] B[j][n] ----
+        __syncthreads();                          // every C H^T has read the old state
+        // ---- state: H = 2^send H + Xw^T B, this wave's tiles ----
         {
             const float ed = fast_exp2(send);
 #pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                const int n = sn0 + 128 * r;
-                if (n < NP) {
-                    float acc[4][4] = {};
-#pragma unroll 4
-                    for (int j = 0; j < kGK; ++j) {
-                        const float4 xw = *reinterpret_cast<const float4*>(&sXw[j][sp0]);
-                        const float4 bv = *reinterpret_cast<const float4*>(&sB[j][n]);
-                        const float xa[4] = {xw.x, xw.y, xw.z, xw.w};
+            for (int m = 0; m < kMaxT; ++m) {
+                const int t = w + 4 * m;
+                if (t < 2 * NT) {
+                    const int cb = t & 1, sb = t >> 1;
+                    f32x4_t acc = acc_h[m] * ed;
 #pragma unroll
-                        for (int c = 0; c < 4; ++c) {
-                            acc[c][0] = fmaf(xa[c], bv.x, acc[c][0]);
-                            acc[c][1] = fmaf(xa[c], bv.y, acc[c][1]);
-                            acc[c][2] = fmaf(xa[c], bv.z, acc[c][2]);
-                            acc[c][3] = fmaf(xa[c], bv.w, acc[c][3]);
-                        }
-                    }
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        float4* hp = reinterpret_cast<float4*>(&sH[sp0 + c][n]);
-                        float4 hv = *hp;
-                        hv.x = fmaf(ed, hv.x, acc[c][0]);
-                        hv.y = fmaf(ed, hv.y, acc[c][1]);
-                        hv.z = fmaf(ed, hv.z, acc[c][2]);
-                        hv.w = fmaf(ed, hv.w, acc[c][3]);
-                        *hp = hv;
-                    }
+                    for (int k0 = 0; k0 < kGK; k0 += 4)
+                        acc = mfma4(sXw[k0 + lk][16 * cb + lr], sB[k0 + lk][16 * sb + lr], acc);
+                    acc_h[m] = acc;
                 }
             }
+            write_state();
         }
     }
-    __syncthreads();
     if (hT) {
-        for (int e = tid; e < kGP * NP; e += 256) {
-            const int p = e / NP, n = e % NP;
-            if (p < np && n < N) hT[((b * H + h) * (int64_t)P + p0 + p) * N + n] = sH[p][n];
+#pragma unroll
+        for (int m = 0; m < kMaxT; ++m) {
+            const int t = w + 4 * m;
+            if (t < 2 * NT) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int c = 16 * (t & 1) + 4 * lk + r, n = 16 * (t >> 1) + lr;
+                    if (c < np && n < N) hT[((b * H + h) * (int64_t)P + p0 + c) * N + n] = acc_h[m][r];
+                }
+            }
         }
     }
 }
