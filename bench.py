@@ -739,7 +739,8 @@ def bench_ssd_f32(args):
                          f"ngroups 1 (general chunked kernel, fp32 MFMA)",
                 us=ms * 1e3, GBs=nb / (ms * 1e-3) / 1e9, hbm_frac=nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                 tokens_ch_per_s=s["batch"] * s["seqlen"] * s["nheads"] * s["headdim"] / (ms * 1e-3),
-                algorithmic_bytes=nb)
+                algorithmic_bytes=nb, traffic_bytes_per_launch=profiled_traffic("ssd_general_mamba2_f32.md"),
+                mfma_busy=profiled_counters("ssd_general_mamba2_f32.md", ("mfma_busy_pct",)))
 
 
 def bench_copy(args):

@@ -89,9 +89,14 @@ __global__ __launch_bounds__(256) void ssd_general_kernel(
     __shared__ __align__(16) float sM[kGK][kXS];      // masked scores
     __shared__ float sS[kGK], sDt[kGK], sE[kGK];     // running sum (log2 units), dt, 2^s
 
+    // Blocks are dispatched round-robin over the 8 XCDs; number them so that
+    // consecutive ids (the heads of one batch row, which read the same B and
+    // C rows) share an XCD and its L2.
+    uint32_t lid = blockIdx.x;
+    if ((gridDim.x & 7u) == 0u) lid = (blockIdx.x & 7u) * (gridDim.x >> 3) + (blockIdx.x >> 3);
     const int npt = (P + kGP - 1) / kGP;
-    const int pt = blockIdx.x % npt;
-    const int bh = blockIdx.x / npt;
+    const int pt = lid % npt;
+    const int bh = lid / npt;
     const int h = bh % H;
     const int64_t b = bh / H;
     const int g = h / (H / G);
