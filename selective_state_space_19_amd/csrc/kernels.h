@@ -90,6 +90,10 @@ struct SSDUParams {
 
 // Each returns hipSuccess or the launch error; is_bf16 selects the storage type.
 hipError_t launch_s6_scan(const S6Params& p, bool is_bf16, bool zoh, hipStream_t stream);   // zoh: hold input term
+// Only the backward pass's chunk-start states (p.ckpt), as the forward with
+// saving would store them; nothing else is read beyond u, delta, A, B, h0 or
+// written.
+hipError_t launch_s6_save_states(const S6Params& p, bool is_bf16, hipStream_t stream);
 hipError_t launch_s6_scan_fused(const S6Params& p, const S6FrontEnd& fe, bool is_bf16, hipStream_t stream);
 hipError_t launch_state_update(const SUParams& p, bool is_bf16, hipStream_t stream);
 // Backward of the scan; zeroes dA and dD and then accumulates into them.

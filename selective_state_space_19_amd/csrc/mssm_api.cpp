@@ -274,10 +274,24 @@ static int scan_bwd(const char* fn, bool saved, const void* u, const void* delta
     const int64_t blocks = ((d_inner + 63) / 64) * batch;
     if (blocks > INT32_MAX) return fail(MSSM_ERR_UNSUPPORTED, "%s: batch*d_inner too large", fn);
     float* ws = static_cast<float*>(workspace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // Without saved states, the forward scan kernel writes them first (states
+    // only: no C, no outputs) when one batch row's states fit its 32-bit
+    // offsets; the backward kernel then starts from them, as after
+    // mssm_selective_scan_fwd_save.  Otherwise the backward kernel runs its
+    // own forward sweep.
+    bool from_states = saved;
+    if (!saved && mssm::s6_bwd_ckpt_floats(1, d_inner, seqlen, d_state) * 4 < (int64_t(1) << 31)) {
+        mssm::S6Params f{u, delta, Bm, Cm, nullptr, A, nullptr, h0, const_cast<void*>(u), nullptr, batch, d_inner,
+                         (int32_t)seqlen, (int32_t)d_state, ws};
+        const hipError_t e = mssm::launch_s6_save_states(f, dtype == MSSM_BF16, s);
+        if (e != hipSuccess) return launched(fn, e);
+        from_states = true;
+    }
     mssm::S6BwdParams p{u, delta, Bm, Cm, z, dout, A, Dskip, h0, dh_final, du, ddelta, dz, dA, dB, dC, dD, dh0,
                         ws, ws + mssm::s6_bwd_ckpt_floats(batch, d_inner, seqlen, d_state), batch, d_inner,
-                        (int32_t)seqlen, (int32_t)d_state, saved ? 1 : 0};
-    return launched(fn, mssm::launch_s6_scan_bwd(p, dtype == MSSM_BF16, static_cast<hipStream_t>(stream)));
+                        (int32_t)seqlen, (int32_t)d_state, from_states ? 1 : 0};
+    return launched(fn, mssm::launch_s6_scan_bwd(p, dtype == MSSM_BF16, s));
 }
 
 int mssm_selective_scan_bwd(const void* u, const void* delta, const float* A, const void* Bm, const void* Cm,

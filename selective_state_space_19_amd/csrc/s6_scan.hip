@@ -23,7 +23,8 @@
 //   * 4 row waves: thread = (row, TPT-token segment of the chunk), a row's
 //     segments on consecutive lanes, so each load or store instruction moves
 //     whole 64-byte row runs.  They stream u, delta, z through a register
-//     ring (the loads of the next RING-1 chunks in flight), stage
+//     ring (the loads of the next chunks in flight; in bf16 the two chunks
+//     that share each 128-byte line are loaded back to back), stage
 //     (delta, delta*u) in LDS for the scan, and run the epilogue: the sum of
 //     the 8 per-wave partial outputs sum_n C*h, the D*u term, the silu(z)
 //     gate and the y store (streaming cache policy).
@@ -86,7 +87,7 @@ template <typename T, int TC> constexpr int kRing = TC * int(sizeof(T)) < 128 ? 
 // (its chunk length: 16 with up to 2 states per lane, else 8).
 template <int NS> constexpr int kCkptLen = NS <= 2 ? 16 : 8;
 
-template <typename T, int NS, int TC, bool ALIGNED, bool FULLN, bool FUSED, bool ZOH, bool CKPT, int RING>
+template <typename T, int NS, int TC, bool ALIGNED, bool FULLN, bool FUSED, bool ZOH, bool CKPT, bool NOY, int RING>
 __global__ __launch_bounds__((kScanWaves + kRowWaves) * 64) void s6_scan_kernel(
     const T* __restrict__ u_in, const T* __restrict__ dl_in, const T* __restrict__ B_in,
     const T* __restrict__ C_in, const T* __restrict__ z_in, const float* __restrict__ A_in,
@@ -101,6 +102,9 @@ __global__ __launch_bounds__((kScanWaves + kRowWaves) * 64) void s6_scan_kernel(
     // is applied) for the backward pass, which then need not re-run the
     // recurrence to find its chunk starts ("State-Space Model Optimization
     // Patterns" page, section 4: recompute within chunks from saved states).
+    // NOY (with CKPT): the saved states are the only output -- no C, no
+    // partial outputs, no z, no epilogue; the backward pass's own call runs
+    // this ahead of its chunked sweep.
     // Pointers are separate __restrict__ arguments so the compiler may fetch the
     // wave-uniform B / C words with scalar loads (it must know no store aliases them).
     constexpr int NW = kScanWaves;
@@ -178,16 +182,17 @@ __global__ __launch_bounds__((kScanWaves + kRowWaves) * 64) void s6_scan_kernel(
                     // N is zeroed where C is used, after the group's wait, so
                     // these loads stay in flight meanwhile.
                     const Words8 x = *reinterpret_cast<const Words8*>(brow[s] + tc);
-                    const Words8 y = *reinterpret_cast<const Words8*>(crow[s] + tc);
 #pragma unroll
-                    for (int i = 0; i < BCW; ++i) {
-                        bw[s][i] = x.w[i];
-                        cw[s][i] = y.w[i];
+                    for (int i = 0; i < BCW; ++i) bw[s][i] = x.w[i];
+                    if constexpr (!NOY) {
+                        const Words8 y = *reinterpret_cast<const Words8*>(crow[s] + tc);
+#pragma unroll
+                        for (int i = 0; i < BCW; ++i) cw[s][i] = y.w[i];
                     }
                 } else {
                     const int valid = sval[s] ? L - t : 0;
                     load_run<T, G>(brow[s] + t, valid, false, bw[s]);
-                    load_run<T, G>(crow[s] + t, valid, false, cw[s]);
+                    if constexpr (!NOY) load_run<T, G>(crow[s] + t, valid, false, cw[s]);
                 }
             }
         };
@@ -256,10 +261,10 @@ __global__ __launch_bounds__((kScanWaves + kRowWaves) * 64) void s6_scan_kernel(
 #pragma unroll
                     for (int s = 0; s < NS; ++s) {
                         h[s] = fmaf(dA[k + kk][s], h[s], bu[k + kk][s]);
-                        yv[kk] = fmaf(cval(buf, s, k + kk), h[s], yv[kk]);
+                        if constexpr (!NOY) yv[kk] = fmaf(cval(buf, s, k + kk), h[s], yv[kk]);
                     }
                 }
-                s_y[par][w][gi * (G / 4) + k / 4][cs] = make_float4(yv[0], yv[1], yv[2], yv[3]);
+                if constexpr (!NOY) s_y[par][w][gi * (G / 4) + k / 4][cs] = make_float4(yv[0], yv[1], yv[2], yv[3]);
             }
         };
 
@@ -368,12 +373,12 @@ __global__ __launch_bounds__((kScanWaves + kRowWaves) * 64) void s6_scan_kernel(
                 const uint32_t off = run_off(t);
                 buf_load<WPT>(rs_u, off, wu);
                 buf_load<WPT>(rs_dl, off, wdl);
-                buf_load<WPT>(rs_z, off, wz);
+                if constexpr (!NOY) buf_load<WPT>(rs_z, off, wz);
             } else {
                 const int valid = rval ? (L - t) : 0;
                 load_run<T, TPT>(u_row + t, valid, false, wu);
                 load_run<T, TPT>(dl_row + t, valid, false, wdl);
-                if (z_row) load_run<T, TPT>(z_row + t, valid, false, wz);
+                if (!NOY && z_row) load_run<T, TPT>(z_row + t, valid, false, wz);
             }
         };
 
@@ -437,6 +442,7 @@ __global__ __launch_bounds__((kScanWaves + kRowWaves) * 64) void s6_scan_kernel(
         // gate, store.  Chunk -1 (the first iteration) reads an unused buffer
         // and stores nothing (its offsets are out of range).
         auto epilogue = [&](int ck, const uint32_t (&cz)[WPT], const float (&uk)[TPT]) {
+            if constexpr (NOY) return;
             const int t0 = ck * TC;
             const int par = ck & 1;
             float out[TPT];
@@ -509,8 +515,17 @@ __global__ __launch_bounds__((kScanWaves + kRowWaves) * 64) void s6_scan_kernel(
     }
 }
 
+// The kernel for one mode: ALIGNED, and FULLN for aligned calls.
+template <typename T, int NS, int TC, bool FUSED, bool ZOH, bool CKPT, bool NOY>
+auto pick_kernel(bool aligned, bool fulln) {
+    return aligned ? (fulln ? s6_scan_kernel<T, NS, TC, true, true, FUSED, ZOH, CKPT, NOY, kRing<T, TC>>
+                            : s6_scan_kernel<T, NS, TC, true, false, FUSED, ZOH, CKPT, NOY, kRing<T, TC>>)
+                   : s6_scan_kernel<T, NS, TC, false, false, FUSED, ZOH, CKPT, NOY, kRing<T, TC>>;
+}
+
+// states_only: p.ckpt receives the saved states and nothing else is written.
 template <typename T, int NS, int TC>
-hipError_t launch_cfg(const S6Params& p, const S6FrontEnd* fe, bool zoh, hipStream_t stream) {
+hipError_t launch_cfg(const S6Params& p, const S6FrontEnd* fe, bool zoh, bool states_only, hipStream_t stream) {
     const int64_t blocks = ((p.dim + 63) / 64) * p.batch;
     // The aligned path addresses a block's rows through 32-bit buffer
     // offsets, and reads B / C in whole 32-byte groups.
@@ -518,18 +533,11 @@ hipError_t launch_cfg(const S6Params& p, const S6FrontEnd* fe, bool zoh, hipStre
     const bool fulln = p.N == kScanWaves * NS;
     // The hold form and the saved states are built for the plain scan only
     // (the fused front end is Euler; the backward pass is of the plain scan).
-    auto kern = fe ? (aligned ? (fulln ? s6_scan_kernel<T, NS, TC, true, true, true, false, false, kRing<T, TC>>
-                                       : s6_scan_kernel<T, NS, TC, true, false, true, false, false, kRing<T, TC>>)
-                              : s6_scan_kernel<T, NS, TC, false, false, true, false, false, kRing<T, TC>>)
-            : zoh ? (aligned ? (fulln ? s6_scan_kernel<T, NS, TC, true, true, false, true, false, kRing<T, TC>>
-                                      : s6_scan_kernel<T, NS, TC, true, false, false, true, false, kRing<T, TC>>)
-                             : s6_scan_kernel<T, NS, TC, false, false, false, true, false, kRing<T, TC>>)
-            : p.ckpt ? (aligned ? (fulln ? s6_scan_kernel<T, NS, TC, true, true, false, false, true, kRing<T, TC>>
-                                         : s6_scan_kernel<T, NS, TC, true, false, false, false, true, kRing<T, TC>>)
-                                : s6_scan_kernel<T, NS, TC, false, false, false, false, true, kRing<T, TC>>)
-                  : (aligned ? (fulln ? s6_scan_kernel<T, NS, TC, true, true, false, false, false, kRing<T, TC>>
-                                      : s6_scan_kernel<T, NS, TC, true, false, false, false, false, kRing<T, TC>>)
-                             : s6_scan_kernel<T, NS, TC, false, false, false, false, false, kRing<T, TC>>);
+    auto kern = fe ? pick_kernel<T, NS, TC, true, false, false, false>(aligned, fulln)
+              : zoh ? pick_kernel<T, NS, TC, false, true, false, false>(aligned, fulln)
+              : p.ckpt ? (states_only ? pick_kernel<T, NS, TC, false, false, true, true>(aligned, fulln)
+                                      : pick_kernel<T, NS, TC, false, false, true, false>(aligned, fulln))
+                       : pick_kernel<T, NS, TC, false, false, false, false>(aligned, fulln);
     const S6FrontEnd none{};
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3((kScanWaves + kRowWaves) * 64), 0, stream,
                        static_cast<const T*>(p.u), static_cast<const T*>(p.delta), static_cast<const T*>(p.Bm),
@@ -539,12 +547,12 @@ hipError_t launch_cfg(const S6Params& p, const S6FrontEnd* fe, bool zoh, hipStre
 }
 
 template <typename T>
-hipError_t launch_t(const S6Params& p, const S6FrontEnd* fe, bool zoh, hipStream_t stream) {
+hipError_t launch_t(const S6Params& p, const S6FrontEnd* fe, bool zoh, bool states_only, hipStream_t stream) {
     // 8 scan waves per 64 channels; NS = ceil(N / 8) states per lane.
-    if (p.N <= 8) return launch_cfg<T, 1, 32>(p, fe, zoh, stream);
-    if (p.N <= 16) return launch_cfg<T, 2, 32>(p, fe, zoh, stream);
-    if (p.N <= 32) return launch_cfg<T, 4, 32>(p, fe, zoh, stream);
-    return launch_cfg<T, 8, 32>(p, fe, zoh, stream);
+    if (p.N <= 8) return launch_cfg<T, 1, 32>(p, fe, zoh, states_only, stream);
+    if (p.N <= 16) return launch_cfg<T, 2, 32>(p, fe, zoh, states_only, stream);
+    if (p.N <= 32) return launch_cfg<T, 4, 32>(p, fe, zoh, states_only, stream);
+    return launch_cfg<T, 8, 32>(p, fe, zoh, states_only, stream);
 }
 
 __global__ void copy_or_zero_kernel(float* dst, const float* src, int64_t n) {
@@ -555,11 +563,15 @@ __global__ void copy_or_zero_kernel(float* dst, const float* src, int64_t n) {
 }  // namespace
 
 hipError_t launch_s6_scan(const S6Params& p, bool is_bf16, bool zoh, hipStream_t stream) {
-    return is_bf16 ? launch_t<uint16_t>(p, nullptr, zoh, stream) : launch_t<float>(p, nullptr, zoh, stream);
+    return is_bf16 ? launch_t<uint16_t>(p, nullptr, zoh, false, stream) : launch_t<float>(p, nullptr, zoh, false, stream);
 }
 
 hipError_t launch_s6_scan_fused(const S6Params& p, const S6FrontEnd& fe, bool is_bf16, hipStream_t stream) {
-    return is_bf16 ? launch_t<uint16_t>(p, &fe, false, stream) : launch_t<float>(p, &fe, false, stream);
+    return is_bf16 ? launch_t<uint16_t>(p, &fe, false, false, stream) : launch_t<float>(p, &fe, false, false, stream);
+}
+
+hipError_t launch_s6_save_states(const S6Params& p, bool is_bf16, hipStream_t stream) {
+    return is_bf16 ? launch_t<uint16_t>(p, nullptr, false, true, stream) : launch_t<float>(p, nullptr, false, true, stream);
 }
 
 hipError_t launch_copy_or_zero(float* dst, const float* src, int64_t n, hipStream_t stream) {

@@ -16,9 +16,10 @@
 //
 // Design: a workgroup of 8 waves owns 64 channels of one batch row; lane =
 // channel, wave w = states [w NS, (w+1) NS).  Row threads (8 per channel)
-// load u, delta, dout, z and the whole block's B / C rows of a chunk one
-// chunk ahead, so their memory latency hides behind the current chunk; B / C
-// reach the waves through LDS (uniform reads).
+// load u, delta, dout, z and the whole block's B / C rows ahead of use, the
+// chunks whose runs share a 128-byte line together (a line group), so their
+// memory latency hides behind the current chunk and each line is fetched
+// once; B / C reach the waves through LDS (uniform reads).
 //   1. Forward sweep over the whole sequence in chunks of TC tokens (16, or 8
 //      when a lane holds more than 2 states), writing
 //      the state at every chunk start to the workspace (one fp32 per
