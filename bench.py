@@ -311,7 +311,8 @@ def bench_s6bwd(args):
     total_s, _ = time_launches(bwd_saved, steps, 1, stream, warm_ms=WARM_MS)
     total_f, _ = time_launches(fwd_save, steps, 1, stream, warm_ms=WARM_MS)
     B, D, L, N = s["batch"], s["d_inner"], s["seqlen"], s["d_state"]
-    # read u, delta, z, dout (twice: forward sweep reads u, delta) ; write du, ddelta, dz; dB, dC; state checkpoints
+    # read u, delta, z, dout (u, delta twice: the states-only forward reads them
+    # too); write du, ddelta, dz; dB, dC; the states and partials written and read
     nb = (6 + 3) * B * D * L * 2 + 2 * B * N * L * (2 + 4) + 2 * ws.numel()
     return {"workload": f"{wl.name} backward: batch {B}, d_inner {D}, seqlen {L}, d_state {N}, bf16, "
                         "gate, skip, h0 and final-state gradient",
@@ -319,11 +320,15 @@ def bench_s6bwd(args):
             "us_forward_saving_states": total_f / steps * 1e3,
             "tokens_ch_per_s": B * D * L / (ms * 1e-3), "bytes_moved_estimate": nb,
             "GBs_estimate": nb / (ms * 1e-3) / 1e9, "workspace_bytes": ws.numel(),
-            "traffic_bytes_per_call": {"s6_scan_bwd_kernel": profiled_traffic("s6_scan_bwd_mamba1p4b_bf16.md"),
-                                       "s6_bwd_reduce_bc_kernel": profiled_traffic("s6_bwd_reduce_bc_mamba1p4b_bf16.md")},
+            # the plain call: the forward kernel writing the chunk-start states
+            # only, the backward kernel from them, the dB / dC block sums
+            "traffic_bytes_per_call": {
+                "s6_scan_kernel, states only": profiled_traffic("s6_scan_states_mamba1p4b_bf16.md"),
+                "s6_scan_bwd_kernel": profiled_traffic("s6_scan_bwd_mamba1p4b_bf16.md"),
+                "s6_bwd_reduce_bc_kernel": profiled_traffic("s6_bwd_reduce_bc_mamba1p4b_bf16.md")},
             "traffic_bytes_saved_pair": {
                 "s6_scan_kernel saving states": profiled_traffic("s6_scan_fwd_save_mamba1p4b_bf16.md"),
-                "s6_scan_bwd_kernel from saved states": profiled_traffic("s6_scan_bwd_saved_mamba1p4b_bf16.md")}}
+                "s6_scan_bwd_kernel": profiled_traffic("s6_scan_bwd_mamba1p4b_bf16.md")}}
 
 
 def bench_s6_130m(args):
