@@ -203,3 +203,52 @@ def test_zero_length_backward(saved):
     assert np.array_equal(host(g["dh0"]), dhT)
     assert not host(g["dA"]).any() and not host(g["dD"]).any()
     assert g["du"].numel() == 0 and g["dB"].numel() == 0
+
+
+def test_backward_own_sweep_beyond_2gib_states():
+    """One batch row whose chunk-start states take 2 GiB (4096 channels x
+    16384 tokens, d_state 64: 8-token chunks) is past what the forward
+    kernel's 32-bit state offsets reach, so the backward kernel runs its own
+    forward sweep.  The same channels split in two halves (1 GiB each) take
+    the states-only forward instead.  Per-channel gradients must agree bit
+    for bit (each (channel, state) of dA and dD gets one atomic with one
+    batch row); dB and dC, sums over channel blocks in another grouping, to
+    rounding.  Eight sampled channels are checked against the oracle."""
+    import torch
+    b, d, L, N, dt = 1, 4096, 16384, 64, "bf16"
+    assert (L // 8) * N * d * 4 >= (1 << 31) > (L // 8) * N * (d // 2) * 4    # states of one batch row
+    inp = synth.s6_inputs(b, d, L, N, dtype=dt, seed=6100, init_state=True, varied=True)
+    rng = np.random.default_rng(61)
+    dout = synth.round_to(rng.standard_normal((b, d, L)), dt)
+    dhT = rng.standard_normal((b, d, N)).astype(np.float32)
+
+    def call(sl):
+        cut = lambda a, ax: None if a is None else np.ascontiguousarray(a[:, sl] if ax else a[sl])  # noqa: E731
+        g = mssm.selective_scan_bwd(dev(cut(inp["u"], 1)), dev(cut(inp["delta"], 1)), dev(cut(inp["A"], 0)),
+                                    dev(inp["B"]), dev(inp["C"]), dev(cut(dout, 1)), dev(cut(inp["D"], 0)),
+                                    dev(cut(inp["z"], 1)), dev(cut(inp["h0"], 1)), dev(cut(dhT, 1)))
+        torch.cuda.synchronize()
+        return g
+
+    say(f"  bwd gpu call, own forward sweep: b{b} d{d} L{L} N{N} {dt}")
+    full = call(slice(0, d))
+    halves = []
+    for sl in (slice(0, d // 2), slice(d // 2, d)):
+        say(f"  bwd gpu call, states-only forward: channels {sl.start}..{sl.stop}")
+        halves.append(call(sl))
+    for k in ("du", "ddelta", "dz", "dh0"):
+        assert torch.equal(full[k], torch.cat([h[k] for h in halves], dim=1)), k
+    for k in ("dA", "dD"):
+        assert torch.equal(full[k], torch.cat([h[k] for h in halves], dim=0)), k
+    for k in ("dB", "dC"):
+        assert normwise(host(full[k]), host(halves[0][k]) + host(halves[1][k])) <= 1e-6, k
+    ds = np.array([0, 63, 64, 1000, 2047, 2048, 3333, 4095])
+    wd = lambda a: None if a is None else synth.widen(a, dt)  # noqa: E731
+    o = oracle.s6_scan_bwd(wd(inp["u"][:, ds]), wd(inp["delta"][:, ds]), inp["A"][ds], wd(inp["B"]), wd(inp["C"]),
+                           inp["D"][ds], wd(inp["z"][:, ds]), inp["h0"][:, ds], wd(dout[:, ds]), dhT[:, ds])
+    ix = torch.as_tensor(ds, device=full["du"].device)
+    errs = {k: normwise(host(full[k][:, ix] if full[k].dim() == 3 else full[k][ix]), o[k])
+            for k in ("du", "ddelta", "dz", "dh0", "dA", "dD")}
+    say("  own-sweep bwd sampled: " + ", ".join(f"{k} {v:.2e}" for k, v in sorted(errs.items())))
+    for k, v in errs.items():
+        assert v <= TOL[dt], f"{k} normwise error {v}"
