@@ -311,12 +311,20 @@ size_t mssm_ssd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads,
  *              owned by the caller; contents on entry are ignored and on exit
  *              are unspecified.  May be NULL if that size is 0.
  *
- * Limits: dtype MSSM_BF16 only; headdim = 64; d_state in {32, 64, 128,
- * 256}; chunk in {64, 128, 256}; nheads % ngroups == 0; one batch row of x,
- * B and C below 2 GiB.  Other sizes return MSSM_ERR_UNSUPPORTED.  Any
+ * Limits: dtype MSSM_F32 or MSSM_BF16; headdim >= 1; 1 <= d_state <= 256;
+ * chunk in {64, 128, 256}; nheads a multiple of ngroups; one batch row of
+ * x, B and C below 2 GiB.  Other sizes return MSSM_ERR_UNSUPPORTED.  Any
  * seqlen >= 0 is accepted (a last partial chunk is handled).  The chunk is
  * the length of the blocks of the quadratic (attention-like) form; the
  * result does not depend on it beyond rounding.
+ *
+ * Two implementations, chosen from the arguments: bf16 with headdim a
+ * multiple of 32 and d_state in {32, 64, 128, 256} runs on the bf16 matrix
+ * cores with the chunk as given, and uses the workspace; every other call
+ * (float32 storage, other headdims or d_state) runs on the fp32 matrix
+ * cores in chunks of 32 tokens and needs no workspace.
+ * mssm_ssd_workspace_size reports the first's size whenever the sizes fit
+ * it, whatever the dtype.
  */
 int mssm_ssd_chunk_fwd(const void* x, const void* dt, const float* A, const void* Bm,
                        const void* Cm, const float* Dskip, const void* z, const float* h0,

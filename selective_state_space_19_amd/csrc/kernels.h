@@ -100,13 +100,13 @@ hipError_t launch_state_update(const SUParams& p, bool is_bf16, hipStream_t stre
 hipError_t launch_s6_scan_bwd(const S6BwdParams& p, bool is_bf16, hipStream_t stream);
 size_t s6_bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t L, int64_t N);
 int64_t s6_bwd_ckpt_floats(int64_t batch, int64_t dim, int64_t L, int64_t N);  // offset of the partials
-// Mamba-2 SSD on MFMA (bf16 storage): the sizes it implements (headdim 64,
-// d_state 32 / 64 / 128 / 256, chunk 64 / 128 / 256, 32-bit offsets within a
-// batch row) and its workspace.
+// Mamba-2 SSD on the bf16 matrix cores (bf16 storage): the sizes it
+// implements (headdim a multiple of 32, d_state 32 / 64 / 128 / 256, chunk
+// 64 / 128 / 256, 32-bit offsets within a batch row) and its workspace.
 hipError_t launch_ssd_fast(const SSDParams& p, hipStream_t stream);
 size_t ssd_fast_workspace_bytes(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int64_t Q);
 bool ssd_fast_supported(int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int64_t Q);
-// Mamba-2 SSD in plain fp32 arithmetic for every other size (any headdim,
+// Mamba-2 SSD on the fp32 matrix cores for every other size (any headdim,
 // d_state <= 256; fp32 or bf16 storage); no workspace.
 hipError_t launch_ssd_general(const SSDParams& p, bool is_bf16, hipStream_t stream);
 bool ssd_general_supported(int64_t P, int64_t N);

@@ -405,8 +405,8 @@ static int ssd_fwd(const char* fn, const void* x, const void* dt, const float* A
         return fail(MSSM_ERR_UNSUPPORTED, "%s: chunk %lld (64, 128 or 256)", fn, (long long)chunk);
     if (seqlen > INT32_MAX || nheads > INT32_MAX || headdim > INT32_MAX)
         return fail(MSSM_ERR_UNSUPPORTED, "%s: size too large", fn);
-    // bf16 at the sizes the MFMA kernels take runs there; everything else in
-    // the plain fp32 kernel (which needs no workspace)
+    // bf16 at the sizes the bf16 MFMA kernels take runs there; everything else
+    // in the general kernel on the fp32 matrix cores (which needs no workspace)
     const bool fast = dtype == MSSM_BF16 && mssm::ssd_fast_supported(seqlen, nheads, headdim, d_state, ngroups, chunk);
     if (!prod_ok(batch, seqlen, nheads * headdim, nullptr) || !prod_ok(batch, nheads * headdim, d_state, nullptr) ||
         !prod_ok(batch, seqlen, ngroups * d_state, nullptr))

@@ -17,7 +17,8 @@
 //   blocks the causal mask keeps, stored bf16; and B^T (state-major), so the
 //   main kernel's contractions over tokens read their A operands contiguously.
 //   Both depend on the group only, so they are computed once for all heads.
-// - ssd_main_kernel, one workgroup (4 waves) per (b, head, half of headdim):
+// - ssd_main_kernel, one workgroup (8 waves: 4 output, 4 state) per (b,
+//   head, block of 32 head channels; headdim is a multiple of 32):
 //   walks the chunks in order with the fp32 state H (32 x N) held in MFMA
 //   accumulators -- the state never round-trips through HBM.  Per chunk:
 //   running sum s (wave scan), x staged transposed in LDS (plain, and scaled
@@ -45,8 +46,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kP = 64;     // head dim handled by this kernel
-constexpr int kPW = 32;    // head channels per workgroup (half of kP)
+constexpr int kPW = 32;    // head channels per workgroup (headdim is a multiple of it)
 constexpr float kDiagSpan = 64.f;   // largest decay (log2 units) over a token block for the factored diagonal
 
 __device__ __forceinline__ f32x4_t mfma16(const u32x4_t a, const u32x4_t b, f32x4_t c) {
@@ -254,7 +254,7 @@ __global__ __launch_bounds__(512) void ssd_main_kernel(
     const float* __restrict__ Dh, const uint16_t* __restrict__ Z,
     const float* __restrict__ h0, uint16_t* __restrict__ Y, float* __restrict__ hT,
     const uint16_t* __restrict__ Gw, const uint16_t* __restrict__ BTw, const uint16_t* __restrict__ Cw,
-    int L, int H, int G, int nc) {
+    int L, int H, int P, int G, int nc) {
     constexpr int RB = Q / 16;                   // row blocks (16 tokens)
     constexpr int RBW = RB / 4;                  // rounds of row blocks (4 row blocks each)
     constexpr int SRB = RBW > 1 ? 1 : 0;         // rounds the state waves take (the cheapest one)
@@ -280,8 +280,9 @@ __global__ __launch_bounds__(512) void ssd_main_kernel(
     // where that row's G, B^T and C tiles are cached.
     uint32_t lid = blockIdx.x;
     if ((gridDim.x & 7u) == 0u) lid = (blockIdx.x & 7u) * (gridDim.x >> 3) + (blockIdx.x >> 3);
-    const int ph = lid & 1;
-    const int bh = lid >> 1;
+    const int npb = P / kPW;                     // channel blocks per head
+    const int ph = lid % npb;
+    const int bh = lid / npb;
     const int h = bh % H;
     const int64_t b = bh / H;
     const int g = h / (H / G);
@@ -293,14 +294,14 @@ __global__ __launch_bounds__(512) void ssd_main_kernel(
     const float a_h = Ah[h] * kLog2e;
 
     // Buffers over batch row b (32-bit offsets; the host checks the sizes).
-    const uint32_t xrow = (uint32_t)H * kP * 2u;               // bytes per token of x / y / z
-    const rsrc_t rX = make_rsrc(X + b * (int64_t)L * H * kP, (uint32_t)L * xrow);
-    const uint32_t chan0 = ((uint32_t)h * kP + kPW * ph) * 2u;  // byte offset of this half-head in a token row
+    const uint32_t xrow = (uint32_t)H * P * 2u;                // bytes per token of x / y / z
+    const rsrc_t rX = make_rsrc(X + b * (int64_t)L * H * P, (uint32_t)L * xrow);
+    const uint32_t chan0 = ((uint32_t)h * P + kPW * ph) * 2u;   // byte offset of this channel block in a token row
     auto send = [&](int pb, int J) { return s_s[pb][32 * J + 31]; };   // s at the end of token block J
 
     const float dskip = Dh ? Dh[h] : 0.f;
-    const rsrc_t rY = make_rsrc(Y + b * (int64_t)L * H * kP, (uint32_t)L * xrow);
-    const rsrc_t rZ = make_rsrc(Z ? Z + b * (int64_t)L * H * kP : X, Z ? (uint32_t)L * xrow : 0u);
+    const rsrc_t rY = make_rsrc(Y + b * (int64_t)L * H * P, (uint32_t)L * xrow);
+    const rsrc_t rZ = make_rsrc(Z ? Z + b * (int64_t)L * H * P : X, Z ? (uint32_t)L * xrow : 0u);
     const uint32_t gbytes = (uint32_t)Q * Q * 2u;
     const uint32_t cbytes = (uint32_t)Q * N * 2u;
     const int jhi = wr >> 1;                 // row block I = wr + 4 rb lies in token block 2 rb + jhi
@@ -558,7 +559,7 @@ __global__ __launch_bounds__(512) void ssd_main_kernel(
                 if (h0 && nb < NB) {
                     const int p = kPW * ph + 16 * pt + m;
                     const float4 q = *reinterpret_cast<const float4*>(
-                        h0 + (((b * H + h) * kP + p) * (int64_t)N + 16 * nb + 4 * kg));
+                        h0 + (((b * H + h) * P + p) * (int64_t)N + 16 * nb + 4 * kg));
                     v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
                 }
                 accH[k][pt] = v;
@@ -753,7 +754,7 @@ __global__ __launch_bounds__(512) void ssd_main_kernel(
                     for (int pt = 0; pt < 2; ++pt) {
                         const int p = kPW * ph + 16 * pt + m;
                         const f32x4_t v = accH[k][pt];
-                        *reinterpret_cast<float4*>(hT + (((b * H + h) * kP + p) * (int64_t)N + 16 * nb + 4 * kg)) =
+                        *reinterpret_cast<float4*>(hT + (((b * H + h) * P + p) * (int64_t)N + 16 * nb + 4 * kg)) =
                             make_float4(v[0], v[1], v[2], v[3]);
                     }
                 }
@@ -770,16 +771,17 @@ hipError_t launch_qn(const SSDParams& p, hipStream_t stream) {
     uint16_t* BTw = Gw + (int64_t)p.batch * nc * p.G * Q * Q;
     uint16_t* Cw = BTw + (int64_t)p.batch * nc * p.G * N * Q;
     const int64_t prep_blocks = p.batch * nc * p.G * (Q / 32);
+    const int64_t blocks = p.batch * p.H * (p.P / kPW);
+    if (prep_blocks > INT32_MAX || blocks > INT32_MAX) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((ssd_prep_kernel<Q, N>), dim3((unsigned)prep_blocks), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(p.Bm), static_cast<const uint16_t*>(p.Cm), Gw, BTw, Cw, p.L, p.G,
                        nc);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t blocks = p.batch * p.H * 2;
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(512), 0, stream,
                        static_cast<const uint16_t*>(p.x), static_cast<const uint16_t*>(p.dt), p.A,
                        p.Dskip, static_cast<const uint16_t*>(p.z), p.h0,
-                       static_cast<uint16_t*>(p.y), p.h_final, Gw, BTw, Cw, p.L, p.H, p.G, nc);
+                       static_cast<uint16_t*>(p.y), p.h_final, Gw, BTw, Cw, p.L, p.H, p.P, p.G, nc);
     return hipGetLastError();
 }
 
@@ -806,7 +808,7 @@ size_t ssd_fast_workspace_bytes(int64_t batch, int64_t L, int64_t H, int64_t P, 
 }
 
 bool ssd_fast_supported(int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int64_t Q) {
-    if (P != kP) return false;
+    if (P < kPW || P % kPW != 0) return false;
     if (!(N == 32 || N == 64 || N == 128 || N == 256)) return false;
     if (!(Q == 64 || Q == 128 || Q == 256)) return false;
     const int64_t lim = int64_t(1) << 31;

@@ -68,8 +68,9 @@ def test_ragged_shapes(i, case):
     _check(inp, Q, "x".join(map(str, case)) + ("_varied" if varied else ""))
 
 
-# Sizes the MFMA kernels do not take run in the plain-fp32 chunked kernel:
-# float32 storage, headdim other than 64, d_state not in {32, 64, 128, 256}.
+# Sizes the bf16 MFMA kernels do not take run in the general chunked kernel
+# (fp32 matrix cores): float32 storage, headdim not a multiple of 32, d_state
+# not in {32, 64, 128, 256}.
 GENERAL = [
     # (batch, L, H, P, N, G, chunk, dtype, gate, skip, h0)
     (1, 1, 1, 64, 128, 1, 64, "f32", True, True, True),
@@ -81,7 +82,7 @@ GENERAL = [
     (2, 300, 4, 32, 16, 1, 128, "bf16", True, True, True),
     (1, 500, 2, 128, 48, 2, 256, "bf16", False, True, True),
     (1, 200, 2, 16, 80, 1, 64, "bf16", True, True, False),
-    (1, 130, 2, 96, 32, 1, 128, "bf16", True, False, True),
+    (1, 130, 2, 96, 48, 1, 128, "bf16", True, False, True),
 ]
 
 
@@ -93,6 +94,29 @@ def test_general_sizes(i, case):
     inp = synth.ssd_inputs(b, L, H, P, N, G, dtype=dt, seed=900 + L + P + N, gate=gate, skip=skip, init_state=h0,
                            varied=i % 2 == 1)
     _check(inp, Q, "general_" + "x".join(map(str, case)), tol=TOL[dt])
+
+
+# bf16 at headdims other than 64 that are multiples of 32: the MFMA kernels,
+# one workgroup per 32-channel block of a head.
+FAST_HEADDIMS = [
+    # (batch, L, H, P, N, G, chunk, gate, skip, h0)
+    (1, 130, 2, 96, 32, 1, 128, True, False, True),
+    (2, 300, 4, 128, 128, 2, 256, True, True, True),
+    (1, 513, 3, 32, 64, 1, 64, False, True, True),
+    (1, 200, 2, 256, 256, 1, 128, True, True, False),
+    (2, 1000, 2, 128, 64, 1, 256, False, True, True),
+]
+
+
+@pytest.mark.parametrize("i,case", list(enumerate(FAST_HEADDIMS)),
+                         ids=lambda c: "b{}_L{}_H{}_P{}_N{}_G{}_Q{}_z{}_D{}_h{}".format(*c) if isinstance(c, tuple)
+                         else None)
+def test_mfma_path_other_headdims(i, case):
+    b, L, H, P, N, G, Q, gate, skip, h0 = case
+    assert mssm.ssd_workspace_size(b, L, H, P, N, G, Q) > 0        # the MFMA path (the other needs none)
+    inp = synth.ssd_inputs(b, L, H, P, N, G, dtype="bf16", seed=950 + L + P + N, gate=gate, skip=skip,
+                           init_state=h0, varied=i % 2 == 1)
+    _check(inp, Q, "headdim_" + "x".join(map(str, case)))
 
 
 def test_mamba2_shape_fp32():
