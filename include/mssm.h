@@ -320,11 +320,11 @@ size_t mssm_ssd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads,
  *
  * Two implementations, chosen from the arguments: bf16 with headdim a
  * multiple of 32 and d_state in {32, 64, 128, 256} runs on the bf16 matrix
- * cores with the chunk as given, and uses the workspace; every other call
- * (float32 storage, other headdims or d_state) runs on the fp32 matrix
- * cores in chunks of 32 tokens and needs no workspace.
- * mssm_ssd_workspace_size reports the first's size whenever the sizes fit
- * it, whatever the dtype.
+ * cores with the chunk as given; every other call (float32 storage, other
+ * headdims or d_state) runs on the fp32 matrix cores in chunks of 32 tokens.
+ * The workspace holds the first's operand tiles, or the second's chunk
+ * scores (none at d_state above 128); mssm_ssd_workspace_size reports a size
+ * enough for whichever of the two the sizes lead to, whatever the dtype.
  */
 int mssm_ssd_chunk_fwd(const void* x, const void* dt, const float* A, const void* Bm,
                        const void* Cm, const float* Dskip, const void* z, const float* h0,

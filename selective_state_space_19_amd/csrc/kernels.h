@@ -107,9 +107,11 @@ hipError_t launch_ssd_fast(const SSDParams& p, hipStream_t stream);
 size_t ssd_fast_workspace_bytes(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int64_t Q);
 bool ssd_fast_supported(int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int64_t Q);
 // Mamba-2 SSD on the fp32 matrix cores for every other size (any headdim,
-// d_state <= 256; fp32 or bf16 storage); no workspace.
+// d_state <= 256; fp32 or bf16 storage) and its workspace (the chunks' raw
+// scores at d_state <= 128; none above).
 hipError_t launch_ssd_general(const SSDParams& p, bool is_bf16, hipStream_t stream);
 bool ssd_general_supported(int64_t P, int64_t N);
+size_t ssd_general_workspace_bytes(int64_t batch, int64_t L, int64_t N, int64_t G);
 hipError_t launch_ssd_state_update(const SSDUParams& p, bool is_bf16, hipStream_t stream);
 // d_state values the Mamba-2 decode kernel implements.
 bool ssd_state_update_supported(int64_t N);

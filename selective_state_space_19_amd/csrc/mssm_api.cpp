@@ -379,9 +379,13 @@ size_t mssm_ssd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads, in
                                int64_t d_state, int64_t ngroups, int64_t chunk) {
     if (batch < 0 || seqlen < 0 || nheads < 1 || headdim < 1 || d_state < 1 || ngroups < 1 || chunk < 1)
         return 0;
-    // the MFMA path's workspace where it applies (bf16); the other path needs none
-    if (!mssm::ssd_fast_supported(seqlen, nheads, headdim, d_state, ngroups, chunk)) return 0;
-    return mssm::ssd_fast_workspace_bytes(batch, seqlen, nheads, headdim, d_state, ngroups, chunk);
+    // enough for either kernel: the bf16 MFMA path's where the sizes fit it
+    // (its tiles take more than the general kernel's scores), else the
+    // general kernel's
+    const size_t general = d_state <= 256 ? mssm::ssd_general_workspace_bytes(batch, seqlen, d_state, ngroups) : 0;
+    if (!mssm::ssd_fast_supported(seqlen, nheads, headdim, d_state, ngroups, chunk)) return general;
+    const size_t fast = mssm::ssd_fast_workspace_bytes(batch, seqlen, nheads, headdim, d_state, ngroups, chunk);
+    return fast > general ? fast : general;
 }
 
 // scratch: the caller passed no workspace; once the arguments pass, this
@@ -406,7 +410,7 @@ static int ssd_fwd(const char* fn, const void* x, const void* dt, const float* A
     if (seqlen > INT32_MAX || nheads > INT32_MAX || headdim > INT32_MAX)
         return fail(MSSM_ERR_UNSUPPORTED, "%s: size too large", fn);
     // bf16 at the sizes the bf16 MFMA kernels take runs there; everything else
-    // in the general kernel on the fp32 matrix cores (which needs no workspace)
+    // in the general kernel on the fp32 matrix cores
     const bool fast = dtype == MSSM_BF16 && mssm::ssd_fast_supported(seqlen, nheads, headdim, d_state, ngroups, chunk);
     if (!prod_ok(batch, seqlen, nheads * headdim, nullptr) || !prod_ok(batch, nheads * headdim, d_state, nullptr) ||
         !prod_ok(batch, seqlen, ngroups * d_state, nullptr))
@@ -427,8 +431,8 @@ static int ssd_fwd(const char* fn, const void* x, const void* dt, const float* A
     CHECK_PTR(y);
     CHECK_OPT(Dskip);
     CHECK_OPT(z);
-    const size_t need =
-        fast ? mssm::ssd_fast_workspace_bytes(batch, seqlen, nheads, headdim, d_state, ngroups, chunk) : 0;
+    const size_t need = fast ? mssm::ssd_fast_workspace_bytes(batch, seqlen, nheads, headdim, d_state, ngroups, chunk)
+                             : mssm::ssd_general_workspace_bytes(batch, seqlen, d_state, ngroups);
     if (scratch) {
         if (need > workspace_bytes)
             return fail(MSSM_ERR_WORKSPACE,

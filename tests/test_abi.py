@@ -167,10 +167,12 @@ def test_workspace_size_is_pure(lib):
     a = lib.mssm_ssd_workspace_size(4, 4096, 32, 64, 128, 1, 256)
     assert a == lib.mssm_ssd_workspace_size(4, 4096, 32, 64, 128, 1, 256) > 0
     assert lib.mssm_ssd_workspace_size(-1, 4096, 32, 64, 128, 1, 256) == 0
-    # sizes only the general kernel takes need no workspace: headdim not a
-    # multiple of 32, d_state outside {32, 64, 128, 256}
-    assert lib.mssm_ssd_workspace_size(4, 4096, 32, 48, 128, 1, 256) == 0
-    assert lib.mssm_ssd_workspace_size(4, 4096, 32, 64, 48, 1, 256) == 0
+    # sizes only the general kernel takes (headdim not a multiple of 32,
+    # d_state outside {32, 64, 128, 256}): its chunks' raw scores, 32 x 32
+    # fp32 per 32 tokens and group, up to d_state 128; none above
+    assert lib.mssm_ssd_workspace_size(4, 4096, 32, 48, 128, 1, 256) == 4 * 128 * 1 * 4096
+    assert lib.mssm_ssd_workspace_size(2, 4097, 8, 64, 48, 2, 256) == 2 * 129 * 2 * 4096
+    assert lib.mssm_ssd_workspace_size(4, 4096, 32, 48, 192, 1, 256) == 0
     # the MFMA path's workspace (tiles of C B^T, B^T and C per group) does not
     # depend on the headdim
     assert lib.mssm_ssd_workspace_size(4, 4096, 32, 32, 128, 1, 256) == a

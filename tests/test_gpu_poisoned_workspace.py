@@ -20,26 +20,28 @@ def _ws(nbytes, fill):
     return torch.full((max(nbytes, 1),), fill, dtype=torch.uint8, device="cuda")
 
 
-@pytest.mark.parametrize("case", [(2, 300, 4, 64, 128, 1, 256), (1, 200, 2, 64, 64, 2, 64),
-                                  (1, 513, 2, 64, 256, 1, 128)],
-                         ids=lambda c: "b{}_L{}_H{}_P{}_N{}_G{}_Q{}".format(*c))
+@pytest.mark.parametrize("case", [(2, 300, 4, 64, 128, 1, 256, "bf16"), (1, 200, 2, 64, 64, 2, 64, "bf16"),
+                                  (1, 513, 2, 64, 256, 1, 128, "bf16"),
+                                  # the general kernel's scores workspace (fp32; bf16 at headdim 48)
+                                  (2, 300, 4, 64, 128, 2, 256, "f32"), (1, 201, 3, 48, 64, 1, 64, "bf16")],
+                         ids=lambda c: "b{}_L{}_H{}_P{}_N{}_G{}_Q{}_{}".format(*c))
 def test_ssd_ignores_workspace_contents(case):
     import torch
-    b, L, H, P, N, G, Q = case
-    inp = synth.ssd_inputs(b, L, H, P, N, G, dtype="bf16", seed=4100 + L, gate=True, init_state=True, varied=True)
+    b, L, H, P, N, G, Q, dt = case
+    inp = synth.ssd_inputs(b, L, H, P, N, G, dtype=dt, seed=4100 + L, gate=True, init_state=True, varied=True)
     need = mssm.ssd_workspace_size(b, L, H, P, N, G, Q)
-    assert need > 0                               # the MFMA path, which uses it
+    assert need > 0                               # both kernels use one at these sizes
     args = [dev(inp[k]) for k in ("x", "dt", "A", "B", "C", "D", "z", "h0")]
     outs = []
     for fill in (0xFF, 0x00):
-        say(f"  ssd gpu call, workspace filled with {fill:#04x}: x{inp['x'].shape} N{N} G{G} Q{Q}")
+        say(f"  ssd gpu call, workspace filled with {fill:#04x}: x{inp['x'].shape} N{N} G{G} Q{Q} {dt}")
         outs.append(mssm.ssd_chunk(*args, chunk=Q, return_final_state=True, workspace=_ws(need, fill)))
         torch.cuda.synchronize()
     (y1, h1), (y2, h2) = outs
     assert torch.equal(y1, y2) and torch.equal(h1, h2)
     yo, ho = oracle.ssd(*(synth.widen(inp[k], "bf16") if inp[k] is not None and inp[k].dtype == np.uint16
                           else inp[k] for k in ("x", "dt", "A", "B", "C", "D", "z", "h0")))
-    assert normwise(host(y1), yo) <= TOL["bf16"] and normwise(host(h1), ho) <= TOL["bf16"]
+    assert normwise(host(y1), yo) <= TOL[dt] and normwise(host(h1), ho) <= TOL[dt]
 
 
 @pytest.mark.parametrize("case", [(2, 100, 200, 16, "bf16"), (1, 70, 77, 32, "f32"), (1, 64, 33, 64, "bf16")],

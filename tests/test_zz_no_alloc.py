@@ -1,8 +1,8 @@
 """The SSD entry point that allocates nothing (mssm_ssd_chunk_fwd_noalloc,
 static per-GPU scratch) against mssm_ssd_chunk_fwd with a caller workspace:
-two calls in a row, the second smaller (the scratch keeps the first call's
-contents), each equal to the workspace call bit for bit and to the oracle
-within the bf16 tolerance."""
+calls in a row, the second smaller (the scratch keeps the first call's
+contents), the third on the general kernel; each equal to the workspace
+call bit for bit and to the oracle within its dtype's tolerance."""
 import numpy as np
 import pytest
 
@@ -33,7 +33,10 @@ def test_noalloc_matches_workspace_call_twice():
     import torch
     big = synth.ssd_inputs(4, 4096, 32, 64, 128, 1, dtype="bf16", seed=19004, varied=True)
     small = synth.ssd_inputs(2, 700, 8, 64, 64, 2, dtype="bf16", seed=55, gate=True, init_state=True, varied=True)
-    for name, inp, chunk in (("Mamba-2 layer, chunk 256", big, 256), ("smaller, gated, h0, chunk 128", small, 128)):
+    # then the general kernel, whose raw scores also go to the scratch
+    general = synth.ssd_inputs(2, 300, 4, 48, 64, 1, dtype="f32", seed=56, gate=True, init_state=True, varied=True)
+    for name, inp, chunk in (("Mamba-2 layer, chunk 256", big, 256), ("smaller, gated, h0, chunk 128", small, 128),
+                             ("float32, headdim 48 (general kernel)", general, 64)):
         say(f"  noalloc ssd call: {name} x{inp['x'].shape}")
         (y0, h0), (y1, h1) = _pair(inp, chunk)
         assert torch.equal(y0, y1) and torch.equal(h0, h1), name
@@ -41,7 +44,7 @@ def test_noalloc_matches_workspace_call_twice():
                               else inp[k] for k in KEYS))
         ey, eh = normwise(host(y1), yo), normwise(host(h1), ho)
         say(f"  {name}: y err {ey:.3e}  h_final err {eh:.3e}")
-        assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
+        assert ey <= TOL[inp["dtype"]] and eh <= TOL[inp["dtype"]]
 
 
 def test_noalloc_rejects_sizes_beyond_its_scratch():
