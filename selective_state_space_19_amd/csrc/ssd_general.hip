@@ -490,11 +490,22 @@ __global__ __launch_bounds__(512) void ssd_general_roles_kernel(
             __syncthreads();
             // ---- phase B: this wave's output tile ----
             {
+                // C H^T over KQ columns: lane group lk takes the columns
+                // [lk KQ/4, (lk + 1) KQ/4) in order (any assignment of columns
+                // to (step, lane group) sums the same products), so a lane reads
+                // its operands as 16-byte runs
+                constexpr int KL = KQ / 4;
+                const float* ca = &sC[pi][16 * ob + lr][lk * KL];
+                const float* ha = &sH[16 * oc + lr][lk * KL];
                 f32x4_t y0 = {0.f, 0.f, 0.f, 0.f}, y1 = y0;
 #pragma unroll
-                for (int k0 = 0; k0 < KQ; k0 += 8) {      // C H^T
-                    y0 = mfma4(sC[pi][16 * ob + lr][k0 + lk], sH[16 * oc + lr][k0 + lk], y0);
-                    y1 = mfma4(sC[pi][16 * ob + lr][k0 + 4 + lk], sH[16 * oc + lr][k0 + 4 + lk], y1);
+                for (int q = 0; q < KL; q += 4) {
+                    const float4 av = *reinterpret_cast<const float4*>(ca + q);
+                    const float4 hv = *reinterpret_cast<const float4*>(ha + q);
+                    y0 = mfma4(av.x, hv.x, y0);
+                    y1 = mfma4(av.y, hv.y, y1);
+                    y0 = mfma4(av.z, hv.z, y0);
+                    y1 = mfma4(av.w, hv.w, y1);
                 }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) y0[r] = (y0[r] + y1[r]) * sE[pi][16 * ob + 4 * lk + r];
