@@ -718,8 +718,8 @@ def bench_ssd(args):
 
 def bench_ssd_f32(args):
     """The SSD at the Mamba-2 layer shape with float32 storage, which runs on
-    the general chunked kernel (fp32 matrix cores; the bf16 MFMA kernels
-    take bf16).  One input
+    the general chunked kernels (fp32 matrix cores: the chunk scores, then
+    the two-role walk; the bf16 MFMA kernels take bf16).  One input
     set (x and y 134 MB each, with dt, B, C about 290 MB: beyond the 256 MB
     Infinity Cache)."""
     import torch
@@ -732,10 +732,14 @@ def bench_ssd_f32(args):
                            dtype="f32", seed=wl.seed)
     d = {k: to_dev(inp[k]) for k in ("x", "dt", "A", "B", "C", "D")}
     y = torch.empty_like(d["x"])
+    need = mssm.ssd_workspace_size(s["batch"], s["seqlen"], s["nheads"], s["headdim"], s["d_state"], s["ngroups"],
+                                   s["chunk"])
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
     def step():
-        mssm.ssd_chunk(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], chunk=s["chunk"], out=y, stream=stream)
+        mssm.ssd_chunk(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], chunk=s["chunk"], out=y, workspace=ws,
+                       stream=stream)
 
     total, _ = time_launches(step, 10, 2, stream, warm_ms=WARM_MS)
     ms = total / 10
@@ -744,7 +748,9 @@ def bench_ssd_f32(args):
                          f"ngroups 1 (general chunked kernel, fp32 MFMA)",
                 us=ms * 1e3, GBs=nb / (ms * 1e-3) / 1e9, hbm_frac=nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                 tokens_ch_per_s=s["batch"] * s["seqlen"] * s["nheads"] * s["headdim"] / (ms * 1e-3),
-                algorithmic_bytes=nb, traffic_bytes_per_launch=profiled_traffic("ssd_general_mamba2_f32.md"),
+                algorithmic_bytes=nb,
+                traffic_bytes_per_call={"ssd_general_scores_kernel": profiled_traffic("ssd_general_scores_mamba2_f32.md"),
+                                        "ssd_general_roles_kernel": profiled_traffic("ssd_general_mamba2_f32.md")},
                 mfma_busy=profiled_counters("ssd_general_mamba2_f32.md", ("mfma_busy_pct",)))
 
 
