@@ -51,6 +51,7 @@ VALU_LANE_SLOTS = 256 * 4 * 16 * 2.4e9           # the 16-lane figure, reported 
 S6_SLOTS_PER_ELEM, S6_FLOP_PER_ELEM = 8, 7
 S6_ALU_PEAK_TFLOPS = FP32_FMA_LANE_PEAK / S6_SLOTS_PER_ELEM * S6_FLOP_PER_ELEM / 1e12   # 68.8
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+MFMA_FP32_PEAK_TFLOPS = 157.3          # dense fp32 matrix (v_mfma_f32_*_f32), published
 
 
 def log(*a):
@@ -744,8 +745,12 @@ def bench_ssd_f32(args):
     total, _ = time_launches(step, 10, 2, stream, warm_ms=WARM_MS)
     ms = total / 10
     nb = ssd_bytes(s["batch"], s["seqlen"], s["nheads"], s["headdim"], s["d_state"], s["ngroups"], 4)
+    # the flops of the form these kernels compute: 32-token chunks
+    fl = ssd_flops(s["batch"], s["seqlen"], s["nheads"], s["headdim"], s["d_state"], s["ngroups"], 32)
     return dict(workload=f"{wl.name} shape with float32 storage: batch 4, seqlen 4096, 32 heads x 64, d_state 128, "
-                         f"ngroups 1 (general chunked kernel, fp32 MFMA)",
+                         f"ngroups 1 (general chunked kernels, fp32 MFMA, 32-token chunks)",
+                flops_32_token_chunks=fl, mfma_TFLOPs=fl / (ms * 1e-3) / 1e12,
+                mfma_frac_fp32_matrix=fl / (ms * 1e-3) / 1e12 / MFMA_FP32_PEAK_TFLOPS,
                 us=ms * 1e3, GBs=nb / (ms * 1e-3) / 1e9, hbm_frac=nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                 tokens_ch_per_s=s["batch"] * s["seqlen"] * s["nheads"] * s["headdim"] / (ms * 1e-3),
                 algorithmic_bytes=nb,
