@@ -382,7 +382,8 @@ __global__ __launch_bounds__(256) void ssd_general_scores_kernel(const T* __rest
             s1 = mfma4(sC[16 * ti + lr][k0 + 4 + lk], sB[16 * tj + lr][k0 + 4 + lk], s1);
         }
         const f32x4_t sc = s0 + s1;
-        *reinterpret_cast<float4*>(ws + blockIdx.x * 1024 + 256 * w + 4 * l) = make_float4(sc[0], sc[1], sc[2], sc[3]);
+        *reinterpret_cast<float4*>(ws + (int64_t)blockIdx.x * 1024 + 256 * w + 4 * l) =
+            make_float4(sc[0], sc[1], sc[2], sc[3]);
     }
 }
 
