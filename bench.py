@@ -786,7 +786,7 @@ def main():
     ap.add_argument("--no-parity", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(the scan shards by batch / channel with no exchange).", file=sys.stderr)
         sys.exit(2)
     parts = set(args.only.split(","))
