@@ -481,11 +481,14 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
         // and 1 for C; s runs to NSP = max(NS, 2), the padding states are 0.
         // The (s, c) values of a token are reduced at once (tree steps 0 ..
         // log2(2 NSP) - 1), leaving rk[k]; the tokens after the walk.
+        // Per token, du and ddelta share sum_n lambda_n B_n (du takes it times
+        // delta, ddelta times u, once per token), and ddelta and dA share
+        // lambda_n a_n h_{t-1,n} (times A_n and delta).
         float rk[kTC];
 #pragma unroll
         for (int k = kTC - 1; k >= 0; --k) {
             const float4 q = s_tk[k][cs];
-            float dup = 0.f, ddp = 0.f;
+            float sb = 0.f, ddp = 0.f;
             float v[2 * kNSP];
 #pragma unroll
             for (int s = NS; s < kNSP; ++s) v[2 * s] = v[2 * s + 1] = 0.f;
@@ -497,18 +500,17 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
                 float a;
                 if constexpr (kKeepA) a = as[k][s];
                 else a = fast_exp2(q.x * a2[s]);
-                const float ah = a * hp;              // a_t h_{t-1}, shared by ddelta and dA
-                const float ltx = lt * q.x;           // lambda_t delta_t
+                const float pah = lt * (a * hp);      // lambda_t a_t h_{t-1}
                 v[2 * s] = lt * q.y;
                 v[2 * s + 1] = q.w * hs[k][s];
-                dup = fmaf(ltx, bv, dup);
-                ddp = fmaf(lt, fmaf(Af[s], ah, q.z * bv), ddp);
-                dAacc[s] = fmaf(ltx, ah, dAacc[s]);
+                sb = fmaf(lt, bv, sb);
+                ddp = fmaf(pah, Af[s], ddp);
+                dAacc[s] = fmaf(pah, q.x, dAacc[s]);
                 lam[s] = a * lt;
             }
             tree<0, 2 * kNSP>(v);
             rk[k] = v[0];
-            s_p[w][k][cs] = make_float2(dup, ddp);
+            s_p[w][k][cs] = make_float2(q.x * sb, fmaf(q.z, sb, ddp));
         }
         tree<log2i(2 * kNSP), kTC>(rk);
         {
