@@ -73,7 +73,7 @@ def ssd_shapes(draw):
     G = draw(st.sampled_from([1, 2]))
     H = G * draw(st.integers(1, 3))
     P = draw(st.sampled_from([16, 32, 64, 64, 80, 96, 128]))
-    N = draw(st.sampled_from([16, 32, 48, 64, 128, 256]))
+    N = draw(st.sampled_from([16, 32, 48, 64, 128, 256, 5, 37, 100, 130]))
     return draw(st.integers(1, 2)), draw(st.integers(1, 300)), H, P, N, G
 
 

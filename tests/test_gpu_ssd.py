@@ -83,6 +83,14 @@ GENERAL = [
     (1, 500, 2, 128, 48, 2, 256, "bf16", False, True, True),
     (1, 200, 2, 16, 80, 1, 64, "bf16", True, True, False),
     (1, 130, 2, 96, 48, 1, 128, "bf16", True, False, True),
+    # d_state not a multiple of 16 (padded tiles) or of 4 (element loads of B
+    # and C), and odd headdims: both general kernels (d_state above 128: the
+    # wide one)
+    (1, 70, 2, 7, 1, 1, 64, "f32", True, True, True),
+    (2, 129, 3, 33, 37, 3, 128, "f32", False, True, True),
+    (1, 100, 2, 40, 100, 2, 256, "bf16", True, False, True),
+    (1, 65, 2, 24, 130, 1, 64, "f32", True, True, False),
+    (1, 90, 1, 16, 255, 1, 256, "bf16", True, True, True),
 ]
 
 
