@@ -383,7 +383,8 @@ int mssm_ssd_chunk_fwd_noalloc(const void* x, const void* dt, const float* A, co
  *   z          (device) [batch, nheads, headdim] dtype, NULL => no gate
  *   y          (device) [batch, nheads, headdim] dtype, output
  *
- * Limits: d_state in {16, 32, 64, 128, 256} (MSSM_ERR_UNSUPPORTED otherwise);
+ * Limits: 1 <= d_state <= 256 (MSSM_ERR_UNSUPPORTED otherwise; the sizes
+ * mssm_ssd_chunk_fwd takes, so its h_final can seed decoding);
  * nheads % ngroups == 0 (MSSM_ERR_SHAPE).  batch, nheads or headdim = 0 is a
  * no-op.
  */

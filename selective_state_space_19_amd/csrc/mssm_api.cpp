@@ -356,7 +356,7 @@ int mssm_ssd_state_update(float* state, const void* x, const void* dt, const flo
         return fail(MSSM_ERR_SHAPE, "%s: nheads %lld not a multiple of ngroups %lld", fn, (long long)nheads,
                     (long long)ngroups);
     if (!mssm::ssd_state_update_supported(d_state))
-        return fail(MSSM_ERR_UNSUPPORTED, "%s: d_state %lld not in {16, 32, 64, 128, 256}", fn, (long long)d_state);
+        return fail(MSSM_ERR_UNSUPPORTED, "%s: d_state %lld (1 .. 256)", fn, (long long)d_state);
     int64_t rows = 0;
     if (!prod_ok(batch, nheads, headdim, &rows) || !prod_ok(rows, d_state, 1, nullptr) || nheads > INT32_MAX ||
         headdim > INT32_MAX || !prod_ok(batch, ngroups, d_state, nullptr))

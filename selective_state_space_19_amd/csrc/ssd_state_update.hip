@@ -17,6 +17,8 @@
 // partial outputs are summed with log2(LPR) shuffles and the row's first
 // lane writes y.  Loads use clamped indices and are unconditional; stores
 // are predicated.  The state is streamed with non-temporal loads and stores.
+// d_state 16, 32, 64, 128 and 256 take that kernel; every other d_state up to
+// 256 a plain one with element loads.
 #include "common.h"
 #include "kernels.h"
 
@@ -106,6 +108,52 @@ __global__ __launch_bounds__(kThreads) void ssd_state_update_kernel(SSDUParams p
     }
 }
 
+// Any d_state up to 256 (the sizes the kernel above does not take): 16 lanes
+// per (b, h, p) row, lane l owning states l, l + 16, ...; element loads at
+// clamped indices, the states past d_state masked out.  One row per 16 lanes,
+// 16 rows per block.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void ssd_state_update_any_kernel(SSDUParams p) {
+    constexpr int LPR = 16, MAXI = 256 / LPR;
+    const int l = threadIdx.x % LPR;
+    const int64_t nrows = p.batch * p.H * p.P;
+    const int64_t r = (int64_t)blockIdx.x * (kThreads / LPR) + threadIdx.x / LPR;
+    const bool ok = r < nrows;
+    const int64_t row = ok ? r : nrows - 1;
+    const int64_t bh = row / p.P;
+    const int hh = (int)(bh % p.H);
+    const int64_t bg = (bh / p.H) * p.G + hh / (p.H / p.G);
+    const int N = p.N;
+    const float xv = Elem<T>::load1(static_cast<const T*>(p.x) + row);
+    const float dtv = Elem<T>::load1(static_cast<const T*>(p.dt) + bh);
+    const float zv = p.z ? Elem<T>::load1(static_cast<const T*>(p.z) + row) : 0.f;
+    const float dA = fast_exp2(dtv * (p.A[hh] * kLog2e));
+    const float dx = dtv * xv;
+    float* st = p.state + row * N;
+    const T* Bb = static_cast<const T*>(p.Bm) + bg * N;
+    const T* Cb = static_cast<const T*>(p.Cm) + bg * N;
+    float yp = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) {
+        if (LPR * i >= N) break;                 // the same for every lane
+        const int n = l + LPR * i;
+        const bool nv = n < N;
+        const int nn = nv ? n : N - 1;
+        const float hv = fmaf(dA, st[nn], dx * Elem<T>::load1(Bb + nn));
+        if (nv) {
+            yp = fmaf(Elem<T>::load1(Cb + nn), hv, yp);
+            if (ok) st[n] = hv;
+        }
+    }
+#pragma unroll
+    for (int d = 1; d < LPR; d <<= 1) yp += __shfl_xor(yp, d, LPR);
+    if (ok && l == 0) {
+        float o = fmaf(p.Dskip ? p.Dskip[hh] : 0.f, xv, yp);
+        if (p.z) o *= silu(zv);
+        Elem<T>::store1(static_cast<T*>(p.y) + row, o);
+    }
+}
+
 template <typename T, int LPR, int NV>
 hipError_t launch_cfg(const SSDUParams& p, hipStream_t stream) {
     constexpr int RPT = 2;
@@ -126,13 +174,19 @@ hipError_t launch_t(const SSDUParams& p, hipStream_t stream) {
         case 64: return launch_cfg<T, 16, 1>(p, stream);
         case 128: return launch_cfg<T, 32, 1>(p, stream);
         case 256: return launch_cfg<T, 32, 2>(p, stream);
-        default: return hipErrorInvalidValue;
+        default: {
+            if (p.N < 1 || p.N > 256) return hipErrorInvalidValue;
+            const int64_t blocks = (p.batch * p.H * p.P + 15) / 16;
+            if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+            hipLaunchKernelGGL((ssd_state_update_any_kernel<T>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+            return hipGetLastError();
+        }
     }
 }
 
 }  // namespace
 
-bool ssd_state_update_supported(int64_t N) { return N == 16 || N == 32 || N == 64 || N == 128 || N == 256; }
+bool ssd_state_update_supported(int64_t N) { return N >= 1 && N <= 256; }
 
 hipError_t launch_ssd_state_update(const SSDUParams& p, bool is_bf16, hipStream_t stream) {
     return is_bf16 ? launch_t<uint16_t>(p, stream) : launch_t<float>(p, stream);

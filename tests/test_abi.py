@@ -191,8 +191,8 @@ def test_ssd_state_update_argument_errors(lib):
     assert _m2(lib, state=None) == ERR_NULL
     assert _m2(lib, dt=None) == ERR_NULL
     assert _m2(lib, dtype=5) == ERR_DTYPE
-    assert _m2(lib, N=48) == ERR_UNSUP
-    assert _m2(lib, N=512) == ERR_UNSUP
+    assert _m2(lib, N=0) == ERR_UNSUP
+    assert _m2(lib, N=257) == ERR_UNSUP
     assert _m2(lib, H=3, G=2) == ERR_SHAPE
     assert _m2(lib, P=-1) == ERR_SHAPE
     assert _m2(lib, z=MISALIGNED) == ERR_ALIGN

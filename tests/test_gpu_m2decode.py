@@ -41,6 +41,9 @@ SMALL = [
     (1, 1, 1, 16, 1, 3, "f32"), (2, 3, 5, 32, 1, 4, "f32"), (3, 4, 7, 64, 2, 3, "f32"),
     (1, 2, 9, 256, 1, 3, "f32"), (2, 2, 64, 128, 1, 4, "bf16"), (1, 4, 16, 256, 2, 3, "bf16"),
     (2, 8, 64, 128, 4, 3, "bf16"), (1, 1, 3, 16, 1, 2, "bf16"),
+    # d_state other than 16 / 32 / 64 / 128 / 256: the element-load kernel
+    (1, 2, 5, 1, 1, 3, "f32"), (2, 4, 9, 48, 2, 3, "bf16"), (1, 3, 33, 100, 1, 3, "f32"),
+    (2, 2, 64, 200, 1, 2, "bf16"), (1, 1, 17, 255, 1, 2, "f32"),
 ]
 
 
@@ -103,13 +106,16 @@ def test_decode_equals_ssd_kernel():
     assert normwise(host(st), host(h_ssd)) <= TOL["bf16"]
 
 
-def test_prefill_then_decode_matches_oracle():
+@pytest.mark.parametrize("P,N,dt", [(64, 128, "bf16"), (40, 48, "bf16"), (64, 100, "f32")],
+                         ids=["P64_N128_bf16", "P40_N48_bf16", "P64_N100_f32"])
+def test_prefill_then_decode_matches_oracle(P, N, dt):
     """Prefill -> decode: the chunked SSD over the first L1 tokens (chunk 256,
     from h0) hands its h_final to L2 decode steps; their outputs and the last
-    state match the fp64 oracle run over all L1 + L2 tokens."""
+    state match the fp64 oracle run over all L1 + L2 tokens.  Also at sizes
+    only the general SSD kernels and the element-load decode kernel take."""
     import torch
-    b, L1, L2, H, P, N, G = 2, 300, 6, 4, 64, 128, 1
-    inp = synth.ssd_inputs(b, L1 + L2, H, P, N, G, dtype="bf16", seed=81, gate=True, init_state=True)
+    b, L1, L2, H, G = 2, 300, 6, 4, 1
+    inp = synth.ssd_inputs(b, L1 + L2, H, P, N, G, dtype=dt, seed=81, gate=True, init_state=True)
     pre = {k: (None if inp[k] is None else
                (np.ascontiguousarray(inp[k][:, :L1]) if k in ("x", "dt", "B", "C", "z") else inp[k]))
            for k in ("x", "dt", "A", "B", "C", "D", "z", "h0")}
@@ -127,13 +133,13 @@ def test_prefill_then_decode_matches_oracle():
     ey = normwise(np.stack([host(y) for y in ys], axis=1), yo[:, L1:])
     es = normwise(host(st), ho)
     say(f"  prefill + decode: y err {ey:.3e}, final state err {es:.3e}")
-    assert ey <= TOL["bf16"] and es <= TOL["bf16"]
+    assert ey <= TOL[dt] and es <= TOL[dt]
 
 
 def test_errors_and_noop():
     import torch
-    init = synth.mamba2_decode_initial(1, 2, 4, 48, seed=1)
-    tk = synth.mamba2_decode_step(init, 0, 1, 2, 4, 48, dtype="bf16", seed=1)
+    init = synth.mamba2_decode_initial(1, 2, 4, 300, seed=1)         # d_state above 256: rejected
+    tk = synth.mamba2_decode_step(init, 0, 1, 2, 4, 300, dtype="bf16", seed=1)
     st = dev(init["state"])
     with pytest.raises(mssm.MssmError) as e:
         mssm.ssd_state_update(st, dev(tk["x"]), dev(tk["dt"]), dev(init["A"]), dev(tk["B"]), dev(tk["C"]))
