@@ -236,7 +236,7 @@ __device__ __forceinline__ float wave_incl_scan(float v) {
 }
 
 // ---------------------------------------------------------------------------
-// Main: one workgroup per (b, head, half of headdim); chunks in order.
+// Main: one workgroup per (b, head, block of 32 head channels); chunks in order.
 // 512 threads in two roles (one wave of each on every SIMD):
 //   output waves 0-3: the chunk's outputs from the staged chunk and the
 //     carried-in state (Y_diag, Y_off, skip, gate, store);

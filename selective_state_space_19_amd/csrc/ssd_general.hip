@@ -14,21 +14,24 @@
 // s the running sum of dt*A over the chunk, and the state passed to the next
 // chunk is exp(s_end) H_in + sum_j exp(s_end - s_j) dt_j x_j B_j^T.
 //
-// Design: one workgroup (4 waves) per (b, head, 32 head channels) walks the
-// sequence in chunks of K = 32 tokens.  Per chunk it stages dt, x, B and C
-// in LDS as fp32 (rows of B, C padded with zeros to whole 16-state tiles),
-// forms the running sum, then computes the three products on the fp32
-// matrix cores (v_mfma_f32_16x16x4_f32: fp32 operands and accumulation, so
-// float32 inputs keep float32 accuracy), 16 x 16 tiles:
-//   scores   M = C B^T     the three tiles on or below the diagonal (waves
-//                          0-2), then masked and scaled by the decay and dt;
-//   outputs  Y = diag(e^s) C H^T + M X    one tile per wave;
-//   state    H = e^{s_end} H + Xw^T B     the state's tiles spread over the
-//                          waves and held in their accumulators across
-//                          chunks (copied to LDS for the next chunk's C H^T).
-// The next chunk's dt, x, z, B and C are loaded into registers while the
-// current one is computed.  The chunk length of the call is a tile size that
-// does not change the result beyond rounding; this path always uses 32.
+// Design: a workgroup per (b, head, 32 head channels) walks the sequence in
+// chunks of K = 32 tokens.  Per chunk it stages dt, x, B and C in LDS as fp32
+// (rows of B, C padded with zeros to whole 16-state tiles), forms the running
+// sum, then computes the three products on the fp32 matrix cores
+// (v_mfma_f32_16x16x4_f32: fp32 operands and accumulation, so float32 inputs
+// keep float32 accuracy), 16 x 16 tiles:
+//   scores   M = C B^T     the three tiles on or below the diagonal, masked
+//                          and scaled by the decay and dt;
+//   outputs  Y = diag(e^s) C H^T + M X    one tile per output wave;
+//   state    H = e^{s_end} H + Xw^T B     the state's tiles held in wave
+//                          accumulators across chunks (copied to LDS for the
+//                          next chunk's C H^T).
+// Up to d_state 128 a scores kernel forms C B^T once per (b, chunk, group)
+// and an 8-wave two-role kernel does the rest with one barrier pair per
+// chunk; above, a 4-wave kernel does all of it in four phases per chunk.  The
+// next chunk's inputs are loaded into registers while the current one is
+// computed.  The chunk length of the call is a tile size that does not
+// change the result beyond rounding; this path always uses 32.
 // Every exponent s_i - s_j (j <= i), s_i and s_end - s_j is <= 0 for A_h <= 0,
 // so no factor exceeds 1.
 #include <type_traits>

@@ -121,7 +121,7 @@ FAST_HEADDIMS = [
                          else None)
 def test_mfma_path_other_headdims(i, case):
     b, L, H, P, N, G, Q, gate, skip, h0 = case
-    assert mssm.ssd_workspace_size(b, L, H, P, N, G, Q) > 0        # the MFMA path (the other needs none)
+    assert mssm.ssd_workspace_size(b, L, H, P, N, G, Q) > 0        # the MFMA path: its operand tiles
     inp = synth.ssd_inputs(b, L, H, P, N, G, dtype="bf16", seed=950 + L + P + N, gate=gate, skip=skip,
                            init_state=h0, varied=i % 2 == 1)
     _check(inp, Q, "headdim_" + "x".join(map(str, case)))
