@@ -403,7 +403,7 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
         const int t0 = ck * kTC;
         const int g0 = ck / kLG * kLG, c = ck - g0;
         // stage (delta, delta*u, u, g) -- the row thread keeps its own tokens
-        float uu[kTPT], zz[kTPT], go[kTPT], gg[kTPT], dlv[kTPT], hc[NS];
+        float uu[kTPT], zz[kTPT], go[kTPT], gg[kTPT], sgv[kTPT], dlv[kTPT], hc[NS];
         {
             const Pair pdl = pick(b_dl, c), pu = pick(b_u, c), pgo = pick(b_go, c), pz = pick(b_z, c);
 #pragma unroll
@@ -430,7 +430,9 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
         stage_bc(ck, bcv, 0);
 #pragma unroll
         for (int j = 0; j < kTPT; ++j) {
-            gg[j] = z_in ? go[j] * silu(zz[j]) : go[j];
+            // sigmoid(z), kept for dz: g = dout silu(z) = dout z sigmoid(z)
+            sgv[j] = __builtin_amdgcn_rcpf(1.f + fast_exp2(-zz[j] * kLog2e));
+            gg[j] = z_in ? go[j] * (zz[j] * sgv[j]) : go[j];
             s_tk[toff + j][cr] = make_float4(dlv[j], dlv[j] * uu[j], uu[j], gg[j]);
         }
         __syncthreads();
@@ -469,8 +471,7 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
             float y = dskip * uu[j];
 #pragma unroll
             for (int q = 0; q < kNW; ++q) y += s_y[q][toff + j][cr];
-            const float e = fast_exp2(-zz[j] * kLog2e);
-            const float sg = __builtin_amdgcn_rcpf(1.f + e);
+            const float sg = sgv[j];
             dzv[j] = go[j] * y * (sg * (1.f + zz[j] * (1.f - sg)));
             dDacc = fmaf(gg[j], uu[j], dDacc);
         }
