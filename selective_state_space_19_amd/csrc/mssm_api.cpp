@@ -379,6 +379,12 @@ size_t mssm_ssd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads, in
                                int64_t d_state, int64_t ngroups, int64_t chunk) {
     if (batch < 0 || seqlen < 0 || nheads < 1 || headdim < 1 || d_state < 1 || ngroups < 1 || chunk < 1)
         return 0;
+    // sizes mssm_ssd_chunk_fwd would reject as too large: 0, not a wrapped product
+    int64_t hp = 0, gn = 0;
+    if (!prod_ok(nheads, headdim, 1, &hp) || !prod_ok(ngroups, d_state, 1, &gn) ||
+        !prod_ok(batch, seqlen, hp, nullptr) || !prod_ok(batch, hp, d_state, nullptr) ||
+        !prod_ok(batch, seqlen, gn, nullptr))
+        return 0;
     // enough for either kernel: the bf16 MFMA path's where the sizes fit it
     // (its tiles take more than the general kernel's scores), else the
     // general kernel's

@@ -167,6 +167,7 @@ def test_workspace_size_is_pure(lib):
     a = lib.mssm_ssd_workspace_size(4, 4096, 32, 64, 128, 1, 256)
     assert a == lib.mssm_ssd_workspace_size(4, 4096, 32, 64, 128, 1, 256) > 0
     assert lib.mssm_ssd_workspace_size(-1, 4096, 32, 64, 128, 1, 256) == 0
+    assert lib.mssm_ssd_workspace_size(1 << 40, 1 << 30, 32, 64, 128, 1, 256) == 0    # too large: 0, not wrapped
     # sizes only the general kernel takes (headdim not a multiple of 32,
     # d_state outside {32, 64, 128, 256}): its chunks' raw scores, 32 x 32
     # fp32 per 32 tokens and group, up to d_state 128; none above
