@@ -3,9 +3,9 @@ decode loop, the S6 scan forward variants and backward, the SSD with a
 caller's workspace and the no-alloc SSD.  Each graph is replayed several
 times with eager work and synchronisations between the replays; the
 outputs are filled with NaN before each replay and must come back equal to
-the eager calls' bit for bit (dA and dD, summed with atomics, with two
-addends each here, are too), so nothing a graph records -- a clear, a fill,
-a workspace -- holds only on its first replay."""
+the eager calls' bit for bit (dA and dD, summed with atomics, to 1e-6), so
+nothing a graph records -- a clear, a fill, a workspace -- holds only on its
+first replay."""
 import numpy as np
 import pytest
 
