@@ -582,9 +582,19 @@ __global__ void s6_bwd_reduce_bc_kernel(S6BwdParams p) {
     const int n = w * NS + s;
     const int t = ck * kTC + k;
     if (s >= NS || n >= p.N || t >= p.L) return;
-    float acc = 0.f;
+    // eight loads in flight per step, summed in a fixed order (deterministic)
     const float* src = p.part + (b * nblk * nck + ck) * (int64_t)PER + j;
-    for (int64_t blk = 0; blk < nblk; ++blk) acc += src[blk * nck * (int64_t)PER];
+    const int64_t stride = nck * (int64_t)PER;
+    float part[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int64_t blk = 0;
+    for (; blk + 8 <= nblk; blk += 8) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) part[q] += src[(blk + q) * stride];
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+        if (blk + q < nblk) part[q] += src[(blk + q) * stride];
+    const float acc = ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
     (c ? p.dC : p.dB)[(b * p.N + n) * (int64_t)p.L + t] = acc;
 }
 
