@@ -127,6 +127,17 @@ def test_mfma_path_other_headdims(i, case):
     _check(inp, Q, "headdim_" + "x".join(map(str, case)))
 
 
+def test_headdim128_layer_shape():
+    """A layer of the same width with 16 heads x 128 (batch 2, seqlen 4096,
+    d_state 128, chunk 256, gated, from h0): four 32-channel workgroups per
+    head on the MFMA kernels; every output and the final state against the
+    oracle."""
+    b, L, H, P, N, G, Q = 2, 4096, 16, 128, 128, 1, 256
+    assert mssm.ssd_workspace_size(b, L, H, P, N, G, Q) > 0
+    inp = synth.ssd_inputs(b, L, H, P, N, G, dtype="bf16", seed=1280, gate=True, init_state=True, varied=True)
+    _check(inp, Q, "headdim 128 layer")
+
+
 def test_mamba2_shape_fp32():
     """The Mamba-2 layer shape (batch 4, seqlen 4096, 32 heads x 64, d_state
     128) with float32 storage: every output within the fp32 tolerance."""
