@@ -70,8 +70,10 @@ __device__ __forceinline__ float combine(float x, float y) {
         constexpr int CTRL = ST == 2 ? 0x128 : ST == 3 ? 0x141 : ST == 4 ? 0x4e : 0xb1;
         const bool hi = (__lane_id() >> (5 - ST)) & 1;
         const float keep = hi ? y : x, send = hi ? x : y;
-        return keep + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, send), CTRL, 0xf,
-                                                                          0xf, false));
+        // (every lane has a source lane for these patterns; the zero `old`
+        // lets the move fold into the add as one DPP instruction)
+        return keep + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, send), CTRL,
+                                                                             0xf, 0xf, false));
     }
 }
 
@@ -484,7 +486,8 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
         // log2(2 NSP) - 1), leaving rk[k]; the tokens after the walk.
         // Per token, du and ddelta share sum_n lambda_n B_n (du takes it times
         // delta, ddelta times u, once per token), and ddelta and dA share
-        // lambda_n a_n h_{t-1,n} (times A_n and delta).
+        // lambda_n a_n h_{t-1,n} (times A_n and delta), which is the carried
+        // adjoint a_n lambda_n times h_{t-1,n}.
         float rk[kTC];
 #pragma unroll
         for (int k = kTC - 1; k >= 0; --k) {
@@ -501,13 +504,13 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
                 float a;
                 if constexpr (kKeepA) a = as[k][s];
                 else a = fast_exp2(q.x * a2[s]);
-                const float pah = lt * (a * hp);      // lambda_t a_t h_{t-1}
+                lam[s] = a * lt;                      // a_t lambda_t, carried to token t - 1
+                const float pah = lam[s] * hp;        // lambda_t a_t h_{t-1}
                 v[2 * s] = lt * q.y;
                 v[2 * s + 1] = q.w * hs[k][s];
                 sb = fmaf(lt, bv, sb);
                 ddp = fmaf(pah, Af[s], ddp);
                 dAacc[s] = fmaf(pah, q.x, dAacc[s]);
-                lam[s] = a * lt;
             }
             tree<0, 2 * kNSP>(v);
             rk[k] = v[0];
