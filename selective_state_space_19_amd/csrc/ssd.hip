@@ -274,6 +274,8 @@ __global__ __launch_bounds__(512) void ssd_main_kernel(
     __shared__ __align__(16) uint32_t xwT[2][kPW][XS];   // (dt * e^(s_chunkend - s) * x)^T
     __shared__ __align__(16) uint32_t Hb[2][kPW][HS];    // carried-in state, bf16 pairs along n
     __shared__ __align__(16) uint32_t ytile[8][16][kPW / 2];  // per wave: one 16 x 32 bf16 output tile
+    __shared__ __align__(16) float s_fs[4][Q];                 // per state wave: dt e^(s_blockend - s) by token
+    __shared__ __align__(16) float s_fw[4][Q];                 // per state wave: dt e^(s_chunkend - s) by token
 
     // Blocks are dispatched round-robin over the 8 XCDs; number them so that
     // consecutive ids (the heads of one batch row) share an XCD and its L2,
@@ -657,17 +659,25 @@ __global__ __launch_bounds__(512) void ssd_main_kernel(
                 fw[i] = dv[i] * fast_exp2(s_end - sv[i]);
             }
             const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+            // the factors go through this wave's own LDS rows (indexed by
+            // token), so each lane reads its 4 consecutive tokens' factors
+            // as two 16-byte loads rather than 8 lane shuffles
+#pragma unroll
+            for (int i = 0; i < TPL; ++i) {
+                s_fs[wr][lane * TPL + i] = fs[i];
+                s_fw[wr][lane * TPL + i] = fw[i];
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
             for (int k = 0; k < XU; ++k) {
                 const int tb = wr + 4 * k;
-                // the factors of this lane's tokens 16 tb + 4 kg + r, from the lanes that scanned them
-                float f1[4], f2[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int tok = 16 * tb + 4 * kg + r;
-                    f1[r] = __shfl(fs[r % TPL], tok / TPL, 64);
-                    f2[r] = __shfl(fw[r % TPL], tok / TPL, 64);
-                }
+                // the factors of this lane's tokens 16 tb + 4 kg + r
+                const float4 a4 = *reinterpret_cast<const float4*>(&s_fs[wr][16 * tb + 4 * kg]);
+                const float4 b4 = *reinterpret_cast<const float4*>(&s_fw[wr][16 * tb + 4 * kg]);
+                const float f1[4] = {a4.x, a4.y, a4.z, a4.w};
+                const float f2[4] = {b4.x, b4.y, b4.z, b4.w};
                 const int wd = 8 * tb + 2 * kg;
 #pragma unroll
                 for (int cb = 0; cb < 2; ++cb) {
