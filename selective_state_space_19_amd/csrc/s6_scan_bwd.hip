@@ -90,6 +90,13 @@ __device__ __forceinline__ void tree(float (&v)[CAP]) {
 
 constexpr int log2i(int n) { return n <= 1 ? 0 : 1 + log2i(n / 2); }
 
+// f(integral_constant<int, i>) for i = I, I - 1, .., 0, unrolled at compile time.
+template <int I, typename F>
+__device__ __forceinline__ void down_for(F&& f) {
+    f(std::integral_constant<int, I>{});
+    if constexpr (I > 0) down_for<I - 1>(f);
+}
+
 // Chunks whose row runs (TC tokens of T) share one 128-byte line, at most 4.
 // The row threads load the runs of such a group of chunks together, so every
 // line is fetched from HBM once, not once per chunk when L2 has evicted it in
@@ -123,6 +130,15 @@ __device__ __forceinline__ V pick(const V (&a)[G], int i) {
     }
     return v;
 }
+
+// Element c of a line group's registers: a direct index when c is a
+// compile-time constant, else the select chain of `pick`.
+template <int G, typename V, int C>
+__device__ __forceinline__ V sel(const V (&a)[G], std::integral_constant<int, C>) { return a[C]; }
+template <int G, typename V>
+__device__ __forceinline__ V sel(const V (&a)[G], int c) { return pick(a, c); }
+template <int C> constexpr int index_of(std::integral_constant<int, C>) { return C; }
+__device__ __forceinline__ int index_of(int c) { return c; }
 
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
@@ -401,13 +417,19 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
         fetch_bwd((nck - 1) / kLG * kLG);
         fetch_hc(nck - 1);
     }
-    for (int ck = nck - 1; ck >= 0; --ck) {
+    // Chunk ck, the c-th of its line group.  With up to 4 states per lane c
+    // is a compile-time constant (the loop below runs the chunks of a group
+    // as separate copies of this code), so the group's registers are indexed
+    // directly; with more states, where registers are short, one copy and
+    // selects.
+    auto chunk = [&](int ck, auto cc) {
+        const int c = index_of(cc);
         const int t0 = ck * kTC;
-        const int g0 = ck / kLG * kLG, c = ck - g0;
+        const int g0 = ck - c;
         // stage (delta, delta*u, u, g) -- the row thread keeps its own tokens
         float uu[kTPT], zz[kTPT], go[kTPT], gg[kTPT], sgv[kTPT], dlv[kTPT], hc[NS];
         {
-            const Pair pdl = pick(b_dl, c), pu = pick(b_u, c), pgo = pick(b_go, c), pz = pick(b_z, c);
+            const Pair pdl = sel(b_dl, cc), pu = sel(b_u, cc), pgo = sel(b_go, cc), pz = sel(b_z, cc);
 #pragma unroll
             for (int j = 0; j < kTPT; ++j) {
                 const int t = t0 + toff + j;
@@ -425,7 +447,7 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
             T col[kLG];
 #pragma unroll
             for (int g = 0; g < kLG; ++g) col[g] = b_bc[g][q];
-            bcv[q] = pick(col, c);
+            bcv[q] = sel(col, cc);
         }
         if (ck > 0) fetch_hc(ck - 1);
         if (c == 0 && ck > 0) fetch_bwd(g0 - kLG);
@@ -543,6 +565,18 @@ __global__ __launch_bounds__(kNW * 64) void s6_scan_bwd_kernel(S6BwdParams p) {
         }
         st(static_cast<T*>(p.du), t0 + toff, duv);
         st(static_cast<T*>(p.ddelta), t0 + toff, ddv);
+    };
+    // groups last first, and in a group its chunks last first (the first
+    // group visited may be partial: its chunks past the end are skipped, a
+    // test uniform over the workgroup)
+    if constexpr (NS <= 4) {
+        for (int g0 = nck > 0 ? (nck - 1) / kLG * kLG : -1; g0 >= 0; g0 -= kLG)
+            down_for<kLG - 1>([&](auto cc) {
+                const int ck = g0 + decltype(cc)::value;
+                if (ck < nck) chunk(ck, cc);
+            });
+    } else {
+        for (int ck = nck - 1; ck >= 0; --ck) chunk(ck, ck % kLG);
     }
 
     // ---- ends: dh0, dA, dD -------------------------------------------------------
