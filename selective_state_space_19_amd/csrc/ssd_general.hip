@@ -417,7 +417,7 @@ __global__ __launch_bounds__(512) void ssd_general_roles_kernel(
     __shared__ __align__(16) float sH[kGP][kRRS];      // state entering the chunk, H[p][n]
     __shared__ __align__(16) float sX[2][kGK][kXS];
     __shared__ __align__(16) float sXw[2][kGK][kXS];   // dt_j exp(s_end - s_j) x[j][p]
-    __shared__ __align__(16) float sM[kGK][kXS];       // masked scores
+    __shared__ __align__(16) float sM[2][kGK][kXS];    // masked scores, by chunk parity
     __shared__ float sS[2][kGK], sDt[2][kGK], sE[2][kGK];
 
     uint32_t lid = blockIdx.x;
@@ -449,7 +449,7 @@ __global__ __launch_bounds__(512) void ssd_general_roles_kernel(
     const T* Cb = Cm + b * L * brow + (int64_t)g * N;
     const T* dtb = DT + b * (int64_t)L * H + h;
 
-    for (int e = tid; e < 16 * 16; e += 512) sM[e >> 4][16 + (e & 15)] = 0.f;   // above the diagonal, never written
+    for (int e = tid; e < 2 * 16 * 16; e += 512) sM[e >> 8][(e >> 4) & 15][16 + (e & 15)] = 0.f;   // above the diagonal, never written
     for (int e = tid; e < kGK * KQ; e += 512) {   // columns NQ .. KQ of C and H: zero, never written
         const int r = e / KQ, k = e % KQ;
         if (k >= NQ) sC[0][r][k] = sC[1][r][k] = sH[r][k] = 0.f;
@@ -457,6 +457,11 @@ __global__ __launch_bounds__(512) void ssd_general_roles_kernel(
 
     if (w < 4) {
         // ======== waves 0-3: scores, scaled inputs, outputs ========
+        // The outputs of chunk c are formed in two halves: C H^T (which needs
+        // the state entering the chunk) in phase B of chunk c, and the rest
+        // (M X, skip, gate, store) in phase A of chunk c + 1, beside the next
+        // chunk's masking.  Each phase then holds about as much work for
+        // these waves as for the state waves.
         const int ob = w >> 1, oc = w & 1;        // output tile: tokens 16 ob + 4 lk + r, channel 16 oc + lr
         float r_z[4] = {0.f, 0.f, 0.f, 0.f};
         float4 r_g = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -469,11 +474,41 @@ __global__ __launch_bounds__(512) void ssd_general_roles_kernel(
                     r_z[r] = ldx(zb + (int64_t)min(t0 + 16 * ob + 4 * lk + r, L - 1) * xrow + min(16 * oc + lr, np - 1));
             }
         };
+        f32x4_t yo = {0.f, 0.f, 0.f, 0.f};        // C H^T of the pending chunk, rows scaled by 2^s
+        float z_pend[4] = {0.f, 0.f, 0.f, 0.f};   // its gate values
+        // the pending chunk cp's outputs: + M X (M is zero past the diagonal
+        // tile: 16 or 32 tokens, two chains), skip, gate, store
+        auto finish = [&](int cp) {
+            const int t0 = cp * kGK, nt = min(kGK, L - t0), pi = cp & 1;
+            f32x4_t y0 = yo, ym = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k0 = 0; k0 < 16; k0 += 8) {
+                y0 = mfma4(sM[pi][16 * ob + lr][k0 + lk], sX[pi][k0 + lk][16 * oc + lr], y0);
+                ym = mfma4(sM[pi][16 * ob + lr][k0 + 4 + lk], sX[pi][k0 + 4 + lk][16 * oc + lr], ym);
+            }
+            if (ob) {
+#pragma unroll
+                for (int k0 = 16; k0 < 32; k0 += 8) {
+                    y0 = mfma4(sM[pi][16 * ob + lr][k0 + lk], sX[pi][k0 + lk][16 * oc + lr], y0);
+                    ym = mfma4(sM[pi][16 * ob + lr][k0 + 4 + lk], sX[pi][k0 + 4 + lk][16 * oc + lr], ym);
+                }
+            }
+            y0 += ym;
+            const int p = 16 * oc + lr;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * ob + 4 * lk + r;
+                float out = y0[r] + dskip * sX[pi][i][p];
+                if (zb) out *= silu(z_pend[r]);
+                if (i < nt && p < np) Elem<T>::store1(yb + (int64_t)(t0 + i) * xrow + p, out);
+            }
+        };
         fetch_o(0);
         __syncthreads();                          // chunk 0 staged, the initial state in sH
         for (int c = 0; c < nch; ++c) {
-            const int t0 = c * kGK, nt = min(kGK, L - t0), pi = c & 1;
-            // ---- phase A ----
+            const int t0 = c * kGK, pi = c & 1;
+            // ---- phase A: the previous chunk's outputs; this chunk's masked scores and Xw ----
+            if (c > 0) finish(c - 1);
             if (w < 3) {
                 const int ti = w == 0 ? 0 : 1, tj = w == 2 ? 1 : 0;
                 const float sc[4] = {r_g.x, r_g.y, r_g.z, r_g.w};
@@ -481,7 +516,7 @@ __global__ __launch_bounds__(512) void ssd_general_roles_kernel(
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = 16 * ti + 4 * lk + r;
-                    sM[i][j] = j <= i ? sc[r] * fast_exp2(sS[pi][i] - sS[pi][j]) * sDt[pi][j] : 0.f;
+                    sM[pi][i][j] = j <= i ? sc[r] * fast_exp2(sS[pi][i] - sS[pi][j]) * sDt[pi][j] : 0.f;
                 }
             } else {
                 const float send = sS[pi][kGK - 1];
@@ -492,7 +527,7 @@ __global__ __launch_bounds__(512) void ssd_general_roles_kernel(
                 }
             }
             __syncthreads();
-            // ---- phase B: this wave's output tile ----
+            // ---- phase B: C H^T of this chunk (the state entering it is in sH) ----
             {
                 // C H^T over KQ columns: lane group lk takes the columns
                 // [lk KQ/4, (lk + 1) KQ/4) in order (any assignment of columns
@@ -512,37 +547,14 @@ __global__ __launch_bounds__(512) void ssd_general_roles_kernel(
                     y1 = mfma4(av.w, hv.w, y1);
                 }
 #pragma unroll
-                for (int r = 0; r < 4; ++r) y0[r] = (y0[r] + y1[r]) * sE[pi][16 * ob + 4 * lk + r];
-                // + M X (M is zero past the diagonal tile: 16 or 32 tokens), two chains
-                f32x4_t ym = {0.f, 0.f, 0.f, 0.f};
+                for (int r = 0; r < 4; ++r) yo[r] = (y0[r] + y1[r]) * sE[pi][16 * ob + 4 * lk + r];
 #pragma unroll
-                for (int k0 = 0; k0 < 16; k0 += 8) {
-                    y0 = mfma4(sM[16 * ob + lr][k0 + lk], sX[pi][k0 + lk][16 * oc + lr], y0);
-                    ym = mfma4(sM[16 * ob + lr][k0 + 4 + lk], sX[pi][k0 + 4 + lk][16 * oc + lr], ym);
-                }
-                if (ob) {
-#pragma unroll
-                    for (int k0 = 16; k0 < 32; k0 += 8) {
-                        y0 = mfma4(sM[16 * ob + lr][k0 + lk], sX[pi][k0 + lk][16 * oc + lr], y0);
-                        ym = mfma4(sM[16 * ob + lr][k0 + 4 + lk], sX[pi][k0 + 4 + lk][16 * oc + lr], ym);
-                    }
-                }
-                y0 += ym;
-                const int p = 16 * oc + lr;
-                float z_cur[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) z_cur[r] = r_z[r];
+                for (int r = 0; r < 4; ++r) z_pend[r] = r_z[r];
                 if (c + 1 < nch) fetch_o(t0 + kGK);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = 16 * ob + 4 * lk + r;
-                    float out = y0[r] + dskip * sX[pi][i][p];
-                    if (zb) out *= silu(z_cur[r]);
-                    if (i < nt && p < np) Elem<T>::store1(yb + (int64_t)(t0 + i) * xrow + p, out);
-                }
             }
             __syncthreads();
         }
+        if (nch > 0) finish(nch - 1);
         __syncthreads();                          // the last state update (waves 4-7)
     } else {
         // ======== waves 4-7: the state; loads and staging ========
